@@ -1,0 +1,65 @@
+"""The pins must catch plausible mistakes in the oracle.
+
+Each case plants one mistake in a copy of the oracle's C source (on the CPU,
+in a temporary directory), builds it, and runs the pin suite against that
+build in a subprocess; the suite must fail.  The unmodified source must pass.
+"""
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "mssm_oracle.c")
+
+MUTATIONS = {
+    "dropped_input_term": ("h[n] = Abar * h[n] + Bbar * x_t;", "h[n] = Abar * h[n];"),
+    "wrong_exp_sign": ("exp(delta_t * a)", "exp(-delta_t * a)"),
+    "readout_uses_B": ("y_t += j->C[s + n] * h[n];", "y_t += j->B[s + n] * h[n];"),
+    "A_transposed": ("j->A[d * N + n]", "j->A[n * D + d]"),
+    "readout_before_update": (
+        "h[n] = Abar * h[n] + Bbar * x_t;\n            y_t += j->C[s + n] * h[n];",
+        "y_t += j->C[s + n] * h[n];\n            h[n] = Abar * h[n] + Bbar * x_t;"),
+    "zoh_missing_divide": ("(Abar - 1.0) / a * j->B[s + n]", "(Abar - 1.0) * j->B[s + n]"),
+    "euler_missing_delta": ("            else\n                Bbar = delta_t * j->B[s + n];",
+                            "            else\n                Bbar = j->B[s + n];"),
+    "x_off_by_one_step": ("const double x_t = j->x[i];",
+                          "const double x_t = j->x[i >= D ? i - D : i];"),
+    "h0_ignored": ("h[n] = j->h0 ? j->h0[(b * D + d) * N + n] : 0.0;", "h[n] = 0.0;"),
+    "BC_row_stride_D": ("const int64_t s = (b * L + t) * N;", "const int64_t s = (b * L + t) * D;"),
+    "feedthrough_dropped": ("if (j->Dskip) y_t += j->Dskip[d] * x_t;", ""),
+    "gate_sign": ("oracle_silu(j->z[i])", "oracle_silu(-j->z[i])"),
+    "delta_uses_x": ("const double delta_t = j->delta[i];", "const double delta_t = j->x[i] * j->x[i];"),
+}
+
+
+def _build(src_text, tmp_path, name):
+    c = tmp_path / f"{name}.c"
+    so = tmp_path / f"lib{name}.so"
+    c.write_text(src_text)
+    subprocess.run(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fno-fast-math",
+                    "-ffp-contract=off", "-pthread", str(c), "-o", str(so), "-lm"], check=True)
+    return so
+
+
+def _run_pins(so):
+    env = dict(os.environ, MSSM_ORACLE_LIBRARY=str(so))
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                        os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+                       cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
+    return r.returncode
+
+
+def test_unmodified_source_passes(tmp_path):
+    so = _build(open(SRC).read(), tmp_path, "clean")
+    assert _run_pins(so) == 0
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_planted_mistake_is_caught(tmp_path, name):
+    src = open(SRC).read()
+    old, new = MUTATIONS[name]
+    assert old in src, f"mutation {name} no longer applies to the source"
+    so = _build(src.replace(old, new, 1), tmp_path, name)
+    assert _run_pins(so) != 0, f"the pins did not catch mutation {name}"
