@@ -1,0 +1,228 @@
+#!/usr/bin/env python3
+"""Selective-scan benchmark on one MI355X; prints ONE JSON line.
+
+A step is one full pass of the hot path (discretise, recurrence with chunk
+carries, read-out, store) over one batch of the workload, inputs already in
+HBM.  The headline workload is the Mamba-130M-layer-shaped float32 scan
+(batch 8, L 2048, D 1536, N 16); the other synthetic workloads are measured
+the same way with fewer steps and reported under "workloads".
+
+value    = algorithmic bytes per step * steps / wall time of the timed region
+           (bytes = (x + delta + y) over batch*L*D plus (B + C) over batch*L*N)
+roofline = the scan kernels against their binding roof.  The scan is bound by
+           vector-ALU issue: each (b, t, d, n) element needs 4 single-rate fp32
+           VALU operations and one half-rate v_exp_f32 = 6 lane-issue slots; the
+           chip issues 256 CU * 4 SIMD * 16 lanes * 2.4 GHz = 39.32e12 slots/s,
+           so the element roof is 6553.6 Gelem/s.  Kernel time comes from HIP
+           events recorded on the stream the kernels are launched on.
+"""
+from __future__ import annotations
+
+import argparse
+import glob
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+VALU_LANE_SLOTS_PER_S = 256 * 4 * 16 * 2.4e9
+SLOTS_PER_ELEMENT = 6
+ELEM_PEAK_GPS = VALU_LANE_SLOTS_PER_S / SLOTS_PER_ELEMENT / 1e9
+HEADLINE = "mamba130m_layer_fp32"
+OTHERS = ["tiny_fp32", "mid_bf16", "long_seq_bf16"]
+
+
+def algorithmic_bytes(w) -> int:
+    e = 4 if w.dtype == "fp32" else 2
+    return (3 * w.batch * w.L * w.D + 2 * w.batch * w.L * w.N) * e
+
+
+def elements(w) -> int:
+    return w.batch * w.L * w.D * w.N
+
+
+def kernel_sources_digest() -> str:
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(ROOT, "selective_state_space_54_amd", "csrc", "*"))):
+        with open(p, "rb") as f:
+            h.update(os.path.basename(p).encode())
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def load_traffic(workload: str):
+    """HBM bytes per step measured with rocprofv3 counters, if they were taken
+    on the current kernel sources (else None)."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f).get(workload)
+    if not rec or rec.get("kernel_sources_sha256") != kernel_sources_digest():
+        return None
+    return rec.get("hbm_bytes_per_step")
+
+
+def device_inputs(g, torch):
+    import numpy as np
+    out = {}
+    for k in ("x", "delta", "A", "B", "C"):
+        a = np.ascontiguousarray(g[k])
+        t = torch.from_numpy(a.view(np.int16)).view(torch.bfloat16) if a.dtype == np.uint16 \
+            else torch.from_numpy(a)
+        out[k] = t.cuda()
+    return out
+
+
+def time_workload(name, steps, warmup, rotate, torch, mssm, workloads):
+    w = workloads.workload(name)
+    sets = []
+    for r in range(rotate):
+        g = workloads.generate(name, seed=w.seed + 1000 * r)
+        d = device_inputs(g, torch)
+        d["y"] = torch.empty(d["x"].shape, dtype=torch.float32, device="cuda")
+        sets.append(d)
+        del g
+    nbytes = mssm.mssm_selective_scan_workspace_size(w.batch, w.L, w.D, w.N, sets[0]["x"].dtype)
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device="cuda")
+
+    def step(i):
+        d = sets[i % rotate]
+        mssm.mssm_selective_scan_fwd_ws(d["x"], d["delta"], d["A"], d["B"], d["C"], d["y"], ws)
+
+    for i in range(warmup):
+        step(i)
+    stream = torch.cuda.current_stream()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        starts[i].record(stream)
+        step(i)
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    kernel_ms = sum(kms) / len(kms)
+    del sets, ws
+    torch.cuda.empty_cache()
+    return w, wall, kernel_ms
+
+
+def cpu_baseline(name, workloads, oracle, threads):
+    """The float64 oracle on the host cores, on the whole headline workload."""
+    g = workloads.generate(name)
+    w = g["workload"]
+    x = workloads.to_float64(g["x"])
+    dl = workloads.to_float64(g["delta"])
+    A = g["A"].astype("float64")
+    B = workloads.to_float64(g["B"])
+    C = workloads.to_float64(g["C"])
+    oracle.selective_scan(x[:, :64], dl[:, :64], A, B[:, :64], C[:, :64], nthreads=threads)
+    # repeat whole passes until about 10 s of wall time (bounded to 50 passes)
+    passes, t0 = 0, time.perf_counter()
+    while True:
+        oracle.selective_scan(x, dl, A, B, C, nthreads=threads)
+        passes += 1
+        dt = time.perf_counter() - t0
+        if dt >= 10.0 or passes >= 50:
+            break
+    return {"value": round(algorithmic_bytes(w) * passes / dt / 1e9, 4), "unit": "GB/s",
+            "cores": threads, "kind": "oracle", "seconds": round(dt, 3),
+            "sample": f"{passes} pass(es) over the whole {name} workload "
+                      f"({w.batch}x{w.L}x{w.D}x{w.N}), float64, {threads} threads over "
+                      f"independent (batch, channel) chains"}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default=HEADLINE)
+    ap.add_argument("--headline-only", action="store_true", help="skip the other workloads")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args(argv)
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: the scan does not shard across GPUs in this build "
+              f"(asked for --gpus {args.gpus}).", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import workloads
+    from selective_state_space_54_amd import mssm
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    torch.cuda.set_device(0)
+    mssm.load()
+
+    w, wall, kernel_ms = time_workload(args.workload, args.steps, args.warmup, 2, torch, mssm,
+                                       workloads)
+    nb = algorithmic_bytes(w)
+    gbs = nb * args.steps / wall / 1e9
+    elem_rate = elements(w) / (kernel_ms * 1e-3) / 1e9
+    line = {
+        "metric": "selective-scan GB/s achieved (% of HBM peak) and B·L·D tokens-channels/sec",
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "L": w.L, "D": w.D, "N": w.N,
+                   "storage": w.dtype, "parallelism": "single GPU"},
+        "hbm_peak_frac": round(gbs / HBM_PEAK_GBS, 4),
+        "tokens_channels_per_s": round(w.batch * w.L * w.D * args.steps / wall, 1),
+        "roofline": {
+            "bound": "alu",
+            "kernel": "chunk_summary_kernel + chunk_output_kernel (one scan call)",
+            "achieved": round(elem_rate, 1),
+            "peak": round(ELEM_PEAK_GPS, 1),
+            "unit": "Gelem/s",
+            "frac": round(elem_rate / ELEM_PEAK_GPS, 4),
+            "kernel_ms": round(kernel_ms, 4),
+            "hbm_GBps_at_kernel_time": round(nb / (kernel_ms * 1e-3) / 1e9, 1),
+            "traffic": load_traffic(w.name),
+        },
+    }
+    if not args.headline_only:
+        others = {}
+        for name in OTHERS:
+            if name == w.name:
+                continue
+            wo, wall_o, kms_o = time_workload(name, 5, 2, 1, torch, mssm, workloads)
+            nbo = algorithmic_bytes(wo)
+            others[name] = {
+                "ms_per_step": round(wall_o * 1e3 / 5, 4),
+                "kernel_ms": round(kms_o, 4),
+                "GB/s": round(nbo / (kms_o * 1e-3) / 1e9, 1),
+                "hbm_peak_frac": round(nbo / (kms_o * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                "tokens_channels_per_s": round(wo.batch * wo.L * wo.D / (kms_o * 1e-3), 1),
+                "Gelem/s": round(elements(wo) / (kms_o * 1e-3) / 1e9, 1),
+                "alu_frac": round(elements(wo) / (kms_o * 1e-3) / 1e9 / ELEM_PEAK_GPS, 4),
+            }
+        line["workloads"] = others
+    if not args.no_cpu_baseline:
+        import oracle
+        threads = min(os.cpu_count() or 1, 16)
+        line["cpu_baseline"] = cpu_baseline(w.name, workloads, oracle, threads)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,124 @@
+/*
+ * mssm -- Mamba selective scan for AMD Instinct MI355X (gfx950).  C ABI.
+ *
+ * What the library computes (the selective state-space recurrence):
+ *
+ *   For every batch row b, channel d and step t (time order), state index n:
+ *       Abar      = exp(delta[b,t,d] * A[d,n])          discretisation of the
+ *                                                       state matrix
+ *                   ("Understanding Mamba", section 2.2, eq. (2))
+ *       Bbar      = delta[b,t,d] * B[b,t,n]             first-order input term,
+ *                   the form "Selective State Space Models" (section
+ *                   "Selection") states Mamba uses, and the Euler form of
+ *                   "State Space Models and Mamba" (scalar recurrence section)
+ *       h[b,d,n]  = Abar * h[b,d,n] + Bbar * x[b,t,d]   diagonal recurrence
+ *                   ("Understanding Mamba", section 2.3, eq. (3)), h = 0 at
+ *                   the start of every sequence
+ *       y[b,t,d]  = sum_n C[b,t,n] * h[b,d,n]           read-out, eq. (3) with
+ *                   the feedthrough term set to zero as in section 2.1
+ *
+ *   The kernels evaluate this with an associative scan over time: the
+ *   affine-pair operator of "Understanding Mamba" section 7.1 (eq. (8)) lets
+ *   the sequence be cut into chunks that are scanned independently and then
+ *   joined.  The [batch, L, D, N] state never leaves the chip (section 7.3);
+ *   only small per-chunk summaries do.
+ *
+ * Layouts: dense, row-major, contiguous.
+ *   x, delta    : [batch, L, D]   (d fastest)
+ *   B, C        : [batch, L, N]   (n fastest; one B_t, C_t shared by every
+ *                                  channel, as in the PyTorch listing of
+ *                                  "Selective State Space Models")
+ *   A           : [D, N] float32  (the real, negative diagonal; the caller
+ *                                  applies any A = -exp(A_log) itself)
+ *   y           : [batch, L, D] float32 for every input type
+ *   Element type of x, delta, B, C (and of the fused path's weights) is given
+ *   by `dtype`; arithmetic, the state and the output are float32 in every
+ *   case (bfloat16 inputs are widened exactly).
+ *
+ * Pointers: device pointers (hipMalloc'ed or equivalent).  The caller owns
+ * every buffer.  Outputs must not alias inputs.  Any element-aligned address
+ * is accepted.
+ *
+ * Streams: `stream` is a hipStream_t passed as void*; NULL means the null
+ * stream.  Work is enqueued asynchronously; the call does not synchronise.
+ *
+ * Errors: every entry point returns an mssm_status.  Arguments are checked
+ * before any HIP call is made, so argument errors are reported on machines
+ * without a GPU.  Nothing is printed and nothing aborts.  On MSSM_ERROR_HIP
+ * mssm_last_error_string() gives the HIP error text (thread-local, valid until
+ * the next call on the same thread).  Sizes with batch, L or D equal to zero
+ * are valid and do nothing.
+ */
+#ifndef MSSM_H_
+#define MSSM_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MSSM_ABI_VERSION 1
+
+typedef enum {
+    MSSM_SUCCESS = 0,
+    MSSM_ERROR_INVALID_VALUE = 1,   /* null pointer, negative size, bad enum   */
+    MSSM_ERROR_NOT_SUPPORTED = 2,   /* N or R outside what the kernels handle  */
+    MSSM_ERROR_SIZE_OVERFLOW = 3,   /* an element count does not fit int64      */
+    MSSM_ERROR_WORKSPACE = 4,       /* workspace missing or too small           */
+    MSSM_ERROR_HIP = 5              /* a HIP call or kernel launch failed       */
+} mssm_status;
+
+typedef enum {
+    MSSM_FLOAT32 = 0,
+    MSSM_BFLOAT16 = 1
+} mssm_dtype;
+
+/* ABI version of the loaded library (MSSM_ABI_VERSION it was built with). */
+int mssm_abi_version(void);
+
+/* Static text for a status code. */
+const char *mssm_status_string(mssm_status status);
+
+/* Text of the last HIP error seen by this thread ("" if none). */
+const char *mssm_last_error_string(void);
+
+/* State sizes N the scan kernels are built for (1, 2, 4, 8, 16, 32): returns 1
+ * when supported, 0 otherwise. */
+int mssm_supports_state_size(int64_t N);
+
+/*
+ * Bytes of device workspace mssm_selective_scan_fwd_ws needs for this shape
+ * (0 when no chunk summaries are needed).  Returns MSSM_SUCCESS and writes
+ * *bytes, or an argument error.
+ */
+mssm_status mssm_selective_scan_workspace_size(int64_t batch, int64_t L, int64_t D, int64_t N,
+                                               mssm_dtype dtype, size_t *bytes);
+
+/*
+ * Selective scan forward, y = scan(x, delta, A, B, C) as defined above.
+ * Workspace is allocated stream-ordered on `stream` (hipMallocAsync) and
+ * released the same way; use mssm_selective_scan_fwd_ws to pass your own.
+ * `delta` is the step size after softplus (positive).
+ */
+mssm_status mssm_selective_scan_fwd(const void *x, const void *delta, const float *A,
+                                    const void *B, const void *C, void *y,
+                                    int64_t batch, int64_t L, int64_t D, int64_t N,
+                                    mssm_dtype dtype, void *stream);
+
+/* As mssm_selective_scan_fwd, with caller-provided device workspace of at
+ * least mssm_selective_scan_workspace_size bytes (may be NULL when that size
+ * is 0).  The workspace is overwritten; its contents are not needed after the
+ * call's work completes on `stream`. */
+mssm_status mssm_selective_scan_fwd_ws(const void *x, const void *delta, const float *A,
+                                       const void *B, const void *C, void *y,
+                                       void *workspace, size_t workspace_bytes,
+                                       int64_t batch, int64_t L, int64_t D, int64_t N,
+                                       mssm_dtype dtype, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MSSM_H_ */

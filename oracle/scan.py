@@ -113,7 +113,7 @@ def selective_scan(x, delta, A, B, C, *, bbar: str = "euler", Dskip=None, z=None
     y = np.zeros((batch, L, D), dtype=np.float64)
     hl = np.zeros((batch, D, N), dtype=np.float64) if return_last_state else None
     if nthreads is None:
-        nthreads = os.cpu_count() or 1
+        nthreads = min(os.cpu_count() or 1, 16)
     rc = load_library().oracle_selective_scan(
         _ptr(xs), _ptr(ds), _ptr(As), _ptr(Bs), _ptr(Cs), _ptr(Dk), _ptr(zs), _ptr(h0s),
         _ptr(y), _ptr(hl), batch, L, D, N, _BBAR_MODES[bbar], int(nthreads))

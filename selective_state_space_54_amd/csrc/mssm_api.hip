@@ -1,0 +1,138 @@
+// C-ABI front end of the mssm library: argument checks, workspace, dispatch.
+//
+// Every check runs before the first HIP call, so argument errors come back on
+// a machine without a GPU.  No static initialiser touches HIP.
+#include <cstdio>
+#include <cstring>
+#include <limits>
+
+#include "mssm_internal.h"
+
+namespace {
+
+thread_local char g_last_error[256] = "";
+
+void set_hip_error(hipError_t e, const char* where) {
+  std::snprintf(g_last_error, sizeof(g_last_error), "%s: %s (%d)", where, hipGetErrorString(e),
+                static_cast<int>(e));
+}
+
+bool mul_ok(int64_t a, int64_t b, int64_t* out) {
+  if (a == 0 || b == 0) { *out = 0; return true; }
+  if (a > std::numeric_limits<int64_t>::max() / b) return false;
+  *out = a * b;
+  return true;
+}
+
+// Shape checks shared by every scan entry point.
+mssm_status check_shape(int64_t batch, int64_t L, int64_t D, int64_t N, mssm_dtype dtype) {
+  if (batch < 0 || L < 0 || D < 0 || N < 0) return MSSM_ERROR_INVALID_VALUE;
+  if (dtype != MSSM_FLOAT32 && dtype != MSSM_BFLOAT16) return MSSM_ERROR_INVALID_VALUE;
+  if (!mssm::state_size_supported(N)) return MSSM_ERROR_NOT_SUPPORTED;
+  int64_t bl, bld, bln, dn, bytes;
+  if (!mul_ok(batch, L, &bl) || !mul_ok(bl, D, &bld) || !mul_ok(bl, N, &bln) ||
+      !mul_ok(D, N, &dn) || !mul_ok(bld, 8, &bytes) || !mul_ok(bln, 8, &bytes) ||
+      !mul_ok(dn, 8, &bytes))
+    return MSSM_ERROR_SIZE_OVERFLOW;
+  return MSSM_SUCCESS;
+}
+
+bool empty_problem(int64_t batch, int64_t L, int64_t D) { return batch == 0 || L == 0 || D == 0; }
+
+mssm_status check_grid(const mssm::ScanPlan& p, int64_t batch, int64_t D) {
+  const int64_t n_dtiles = (D + 255) / 256;
+  int64_t blocks;
+  if (!mul_ok(n_dtiles, static_cast<int64_t>(p.K), &blocks) || !mul_ok(blocks, batch, &blocks))
+    return MSSM_ERROR_SIZE_OVERFLOW;
+  if (blocks * 256 > static_cast<int64_t>(std::numeric_limits<uint32_t>::max()))
+    return MSSM_ERROR_NOT_SUPPORTED;
+  return MSSM_SUCCESS;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mssm_abi_version(void) { return MSSM_ABI_VERSION; }
+
+const char* mssm_status_string(mssm_status s) {
+  switch (s) {
+    case MSSM_SUCCESS: return "success";
+    case MSSM_ERROR_INVALID_VALUE: return "invalid value (null pointer, negative size or bad enum)";
+    case MSSM_ERROR_NOT_SUPPORTED: return "not supported (state size, rank or grid outside the built kernels)";
+    case MSSM_ERROR_SIZE_OVERFLOW: return "size overflow (an element count does not fit in int64)";
+    case MSSM_ERROR_WORKSPACE: return "workspace missing or too small";
+    case MSSM_ERROR_HIP: return "HIP error (see mssm_last_error_string)";
+  }
+  return "unknown status";
+}
+
+const char* mssm_last_error_string(void) { return g_last_error; }
+
+int mssm_supports_state_size(int64_t N) { return mssm::state_size_supported(N) ? 1 : 0; }
+
+mssm_status mssm_selective_scan_workspace_size(int64_t batch, int64_t L, int64_t D, int64_t N,
+                                               mssm_dtype dtype, size_t* bytes) {
+  if (!bytes) return MSSM_ERROR_INVALID_VALUE;
+  const mssm_status s = check_shape(batch, L, D, N, dtype);
+  if (s != MSSM_SUCCESS) return s;
+  *bytes = empty_problem(batch, L, D) ? 0 : mssm::plan_scan(batch, L, D, N).workspace_bytes;
+  return MSSM_SUCCESS;
+}
+
+mssm_status mssm_selective_scan_fwd_ws(const void* x, const void* delta, const float* A,
+                                       const void* B, const void* C, void* y, void* workspace,
+                                       size_t workspace_bytes, int64_t batch, int64_t L,
+                                       int64_t D, int64_t N, mssm_dtype dtype, void* stream) {
+  mssm_status s = check_shape(batch, L, D, N, dtype);
+  if (s != MSSM_SUCCESS) return s;
+  if (empty_problem(batch, L, D)) return MSSM_SUCCESS;
+  if (!x || !delta || !A || !B || !C || !y) return MSSM_ERROR_INVALID_VALUE;
+  const mssm::ScanPlan plan = mssm::plan_scan(batch, L, D, N);
+  s = check_grid(plan, batch, D);
+  if (s != MSSM_SUCCESS) return s;
+  if (plan.workspace_bytes > 0 && (!workspace || workspace_bytes < plan.workspace_bytes))
+    return MSSM_ERROR_WORKSPACE;
+  const mssm::ScanArgs a{x, delta, A, B, C, y, batch, L, D, N, dtype};
+  const hipError_t e = mssm::launch_scan(a, plan, workspace, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) {
+    set_hip_error(e, "selective scan launch");
+    return MSSM_ERROR_HIP;
+  }
+  return MSSM_SUCCESS;
+}
+
+mssm_status mssm_selective_scan_fwd(const void* x, const void* delta, const float* A,
+                                    const void* B, const void* C, void* y, int64_t batch,
+                                    int64_t L, int64_t D, int64_t N, mssm_dtype dtype,
+                                    void* stream) {
+  mssm_status s = check_shape(batch, L, D, N, dtype);
+  if (s != MSSM_SUCCESS) return s;
+  if (empty_problem(batch, L, D)) return MSSM_SUCCESS;
+  if (!x || !delta || !A || !B || !C || !y) return MSSM_ERROR_INVALID_VALUE;
+  const mssm::ScanPlan plan = mssm::plan_scan(batch, L, D, N);
+  s = check_grid(plan, batch, D);
+  if (s != MSSM_SUCCESS) return s;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  void* ws = nullptr;
+  if (plan.workspace_bytes > 0) {
+    const hipError_t e = hipMallocAsync(&ws, plan.workspace_bytes, st);
+    if (e != hipSuccess) {
+      set_hip_error(e, "workspace hipMallocAsync");
+      return MSSM_ERROR_HIP;
+    }
+  }
+  const mssm::ScanArgs a{x, delta, A, B, C, y, batch, L, D, N, dtype};
+  hipError_t e = mssm::launch_scan(a, plan, ws, st);
+  if (ws) {
+    const hipError_t f = hipFreeAsync(ws, st);
+    if (e == hipSuccess) e = f;
+  }
+  if (e != hipSuccess) {
+    set_hip_error(e, "selective scan launch");
+    return MSSM_ERROR_HIP;
+  }
+  return MSSM_SUCCESS;
+}
+
+}  // extern "C"

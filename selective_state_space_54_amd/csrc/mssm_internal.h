@@ -1,0 +1,46 @@
+// Host-side internals shared by the C-ABI front end and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "mssm.h"
+
+namespace mssm {
+
+// How one scan call is cut along time.  The sequence is split into K chunks
+// of chunk_len steps (the last may be shorter).  Chunks 0..K-2 first produce
+// summaries (their local end state from a zero start, and their total step
+// size); each chunk then folds the summaries before it into its carry-in with
+// the affine-pair operator and scans its own steps from that carry.
+struct ScanPlan {
+  int K = 1;
+  int64_t chunk_len = 0;
+  size_t sum_h_bytes = 0;     // float  [batch][K-1][N][D]
+  size_t sum_dt_offset = 0;   // byte offset of double [batch][K-1][D]
+  size_t workspace_bytes = 0;
+};
+
+struct ScanArgs {
+  const void* x;
+  const void* delta;
+  const float* A;
+  const void* B;
+  const void* C;
+  void* y;
+  int64_t batch, L, D, N;
+  mssm_dtype dtype;
+};
+
+ScanPlan plan_scan(int64_t batch, int64_t L, int64_t D, int64_t N);
+
+// Enqueues the scan kernels on `stream`.  Arguments are already validated and
+// the workspace holds at least plan.workspace_bytes.  Returns hipSuccess or
+// the launch error.
+hipError_t launch_scan(const ScanArgs& a, const ScanPlan& plan, void* workspace,
+                       hipStream_t stream);
+
+bool state_size_supported(int64_t N);
+
+}  // namespace mssm

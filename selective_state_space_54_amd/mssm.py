@@ -1,0 +1,177 @@
+"""Python binding of the mssm C ABI (libmssm.so), argument marshalling only.
+
+Every function here carries the name of the C entry point it calls and does
+no arithmetic of the method: it checks tensors (device, dtype, shape,
+contiguity), passes raw device pointers and the current HIP stream, and turns
+status codes into exceptions.  PyTorch supplies device memory and streams.
+There is no fallback: if the library is missing, loading fails loudly.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmssm.so")
+
+MSSM_SUCCESS = 0
+MSSM_FLOAT32 = 0
+MSSM_BFLOAT16 = 1
+_DTYPES = {torch.float32: MSSM_FLOAT32, torch.bfloat16: MSSM_BFLOAT16}
+_STATUS_NAMES = {0: "MSSM_SUCCESS", 1: "MSSM_ERROR_INVALID_VALUE", 2: "MSSM_ERROR_NOT_SUPPORTED",
+                 3: "MSSM_ERROR_SIZE_OVERFLOW", 4: "MSSM_ERROR_WORKSPACE", 5: "MSSM_ERROR_HIP"}
+
+_lib = None
+
+# (name, restype, argtypes) of every exported entry point declared in include/mssm.h
+_vp = ctypes.c_void_p
+_i64 = ctypes.c_int64
+_SIGNATURES = {
+    "mssm_abi_version": (ctypes.c_int, []),
+    "mssm_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "mssm_last_error_string": (ctypes.c_char_p, []),
+    "mssm_supports_state_size": (ctypes.c_int, [_i64]),
+    "mssm_selective_scan_workspace_size": (ctypes.c_int, [_i64, _i64, _i64, _i64, ctypes.c_int,
+                                                          ctypes.POINTER(ctypes.c_size_t)]),
+    "mssm_selective_scan_fwd": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64,
+                                               _i64, ctypes.c_int, _vp]),
+    "mssm_selective_scan_fwd_ws": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                                  ctypes.c_size_t, _i64, _i64, _i64, _i64,
+                                                  ctypes.c_int, _vp]),
+}
+
+
+class MssmError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        lib = load()
+        text = lib.mssm_status_string(status).decode()
+        extra = lib.mssm_last_error_string().decode() if status == 5 else ""
+        super().__init__(f"{where}: {_STATUS_NAMES.get(status, status)} ({text}) {extra}".strip())
+        self.status = status
+
+
+def load():
+    """Load libmssm.so (built by selective_state_space_54_amd.build)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run selective_state_space_54_amd.build.build()")
+    lib = ctypes.CDLL(LIB_PATH)
+    for name, (res, args) in _SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def exported_symbols():
+    return sorted(_SIGNATURES)
+
+
+def _check(status: int, where: str):
+    if status != MSSM_SUCCESS:
+        raise MssmError(status, where)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _stream_handle(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dense(t: torch.Tensor, name: str, dtype, shape, device):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _dtype_code(dtype) -> int:
+    if dtype not in _DTYPES:
+        raise TypeError(f"dtype {dtype} not supported (float32 or bfloat16)")
+    return _DTYPES[dtype]
+
+
+def mssm_abi_version() -> int:
+    return load().mssm_abi_version()
+
+
+def mssm_supports_state_size(N: int) -> bool:
+    return bool(load().mssm_supports_state_size(N))
+
+
+def mssm_selective_scan_workspace_size(batch: int, L: int, D: int, N: int,
+                                       dtype: torch.dtype) -> int:
+    out = ctypes.c_size_t(0)
+    _check(load().mssm_selective_scan_workspace_size(batch, L, D, N, _dtype_code(dtype),
+                                                     ctypes.byref(out)),
+           "mssm_selective_scan_workspace_size")
+    return out.value
+
+
+def _scan_shapes(x, A):
+    if x.dim() != 3:
+        raise ValueError("x must be [batch, L, D]")
+    if A.dim() != 2:
+        raise ValueError("A must be [D, N]")
+    batch, L, D = x.shape
+    N = A.shape[1]
+    return batch, L, D, N
+
+
+def _check_scan_args(x, delta, A, B, C, y):
+    batch, L, D, N = _scan_shapes(x, A)
+    _dtype_code(x.dtype)
+    dev = x.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a GPU device")
+    _dense(x, "x", x.dtype, (batch, L, D), dev)
+    _dense(delta, "delta", x.dtype, (batch, L, D), dev)
+    _dense(A, "A", torch.float32, (D, N), dev)
+    _dense(B, "B", x.dtype, (batch, L, N), dev)
+    _dense(C, "C", x.dtype, (batch, L, N), dev)
+    _dense(y, "y", torch.float32, (batch, L, D), dev)
+    return batch, L, D, N
+
+
+def mssm_selective_scan_fwd(x, delta, A, B, C, y, *, stream=None):
+    """y <- selective scan of (x, delta, A, B, C); library-managed workspace."""
+    batch, L, D, N = _check_scan_args(x, delta, A, B, C, y)
+    _check(load().mssm_selective_scan_fwd(
+        _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(y), batch, L, D, N,
+        _DTYPES[x.dtype], _stream_handle(stream)), "mssm_selective_scan_fwd")
+    return y
+
+
+def mssm_selective_scan_fwd_ws(x, delta, A, B, C, y, workspace, *, stream=None):
+    """y <- selective scan with a caller-provided uint8 device workspace tensor."""
+    batch, L, D, N = _check_scan_args(x, delta, A, B, C, y)
+    ws_ptr = _ptr(workspace) if workspace is not None and workspace.numel() > 0 else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(load().mssm_selective_scan_fwd_ws(
+        _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(y), ws_ptr, ws_bytes,
+        batch, L, D, N, _DTYPES[x.dtype], _stream_handle(stream)), "mssm_selective_scan_fwd_ws")
+    return y
+
+
+def selective_scan(x, delta, A, B, C, *, stream=None):
+    """Allocate y and the workspace with torch, then run mssm_selective_scan_fwd_ws."""
+    batch, L, D, N = _scan_shapes(x, A)
+    y = torch.empty(x.shape, dtype=torch.float32, device=x.device)
+    nbytes = mssm_selective_scan_workspace_size(batch, L, D, N, x.dtype)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=x.device) if nbytes else None
+    return mssm_selective_scan_fwd_ws(x, delta, A, B, C, y, ws, stream=stream)
