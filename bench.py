@@ -148,6 +148,9 @@ def main(argv=None):
     ap.add_argument("--workload", default=HEADLINE)
     ap.add_argument("--headline-only", action="store_true", help="skip the other workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB (5 times) and exit; "
+                         "used to scale rocprofv3 FETCH_SIZE/WRITE_SIZE counters")
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the scan does not shard across GPUs in this build "
@@ -163,6 +166,15 @@ def main(argv=None):
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
     torch.cuda.set_device(0)
+    if args.calibrate_copy:
+        n = args.calibrate_copy * (1 << 20) // 4
+        a = torch.ones(n, dtype=torch.float32, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(5):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes_read": n * 4, "bytes_written": n * 4}))
+        return 0
     mssm.load()
 
     w, wall, kernel_ms = time_workload(args.workload, args.steps, args.warmup, 2, torch, mssm,

@@ -39,10 +39,12 @@ mssm_status check_shape(int64_t batch, int64_t L, int64_t D, int64_t N, mssm_dty
 
 bool empty_problem(int64_t batch, int64_t L, int64_t D) { return batch == 0 || L == 0 || D == 0; }
 
-mssm_status check_grid(const mssm::ScanPlan& p, int64_t batch, int64_t D) {
+mssm_status check_grid(const mssm::ScanPlan& p, int64_t batch, int64_t D, int64_t N) {
+  // largest launch: chunk blocks (n_dtiles * K * batch) or carry blocks (n_dtiles * N * batch)
   const int64_t n_dtiles = (D + 255) / 256;
   int64_t blocks;
-  if (!mul_ok(n_dtiles, static_cast<int64_t>(p.K), &blocks) || !mul_ok(blocks, batch, &blocks))
+  const int64_t per_row = p.K > N ? static_cast<int64_t>(p.K) : N;
+  if (!mul_ok(n_dtiles, per_row, &blocks) || !mul_ok(blocks, batch, &blocks))
     return MSSM_ERROR_SIZE_OVERFLOW;
   if (blocks * 256 > static_cast<int64_t>(std::numeric_limits<uint32_t>::max()))
     return MSSM_ERROR_NOT_SUPPORTED;
@@ -89,7 +91,7 @@ mssm_status mssm_selective_scan_fwd_ws(const void* x, const void* delta, const f
   if (empty_problem(batch, L, D)) return MSSM_SUCCESS;
   if (!x || !delta || !A || !B || !C || !y) return MSSM_ERROR_INVALID_VALUE;
   const mssm::ScanPlan plan = mssm::plan_scan(batch, L, D, N);
-  s = check_grid(plan, batch, D);
+  s = check_grid(plan, batch, D, N);
   if (s != MSSM_SUCCESS) return s;
   if (plan.workspace_bytes > 0 && (!workspace || workspace_bytes < plan.workspace_bytes))
     return MSSM_ERROR_WORKSPACE;
@@ -111,7 +113,7 @@ mssm_status mssm_selective_scan_fwd(const void* x, const void* delta, const floa
   if (empty_problem(batch, L, D)) return MSSM_SUCCESS;
   if (!x || !delta || !A || !B || !C || !y) return MSSM_ERROR_INVALID_VALUE;
   const mssm::ScanPlan plan = mssm::plan_scan(batch, L, D, N);
-  s = check_grid(plan, batch, D);
+  s = check_grid(plan, batch, D, N);
   if (s != MSSM_SUCCESS) return s;
   hipStream_t st = static_cast<hipStream_t>(stream);
   void* ws = nullptr;

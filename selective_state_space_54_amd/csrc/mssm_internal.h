@@ -11,14 +11,15 @@ namespace mssm {
 
 // How one scan call is cut along time.  The sequence is split into K chunks
 // of chunk_len steps (the last may be shorter).  Chunks 0..K-2 first produce
-// summaries (their local end state from a zero start, and their total step
-// size); each chunk then folds the summaries before it into its carry-in with
-// the affine-pair operator and scans its own steps from that carry.
+// summaries (their local end state from a zero start, and their decay
+// exp(A * total step size)); each chunk then folds the summaries before it
+// into its carry-in with the affine-pair operator and scans its own steps from
+// that carry.
 struct ScanPlan {
   int K = 1;
   int64_t chunk_len = 0;
-  size_t sum_h_bytes = 0;     // float  [batch][K-1][N][D]
-  size_t sum_dt_offset = 0;   // byte offset of double [batch][K-1][D]
+  size_t sum_h_bytes = 0;     // float [batch][K-1][N][D]: chunk end state from zero
+  size_t sum_p_offset = 0;    // byte offset of float [batch][K-1][N][D]: chunk decay
   size_t workspace_bytes = 0;
 };
 

@@ -64,72 +64,110 @@ __device__ __forceinline__ void load_row_any(const uint16_t* __restrict__ p, flo
 // exp2 on the transcendental unit (v_exp_f32).
 __device__ __forceinline__ float fast_exp2(float v) { return __builtin_amdgcn_exp2f(v); }
 
+// ---- buffer (descriptor-based) access ------------------------------------------------------
+//
+// A buffer resource holds a wave-uniform base address and a byte limit; each
+// access adds a per-lane byte offset (VGPR) and a wave-uniform byte offset
+// (SGPR), so stepping through time costs no vector address arithmetic.  The
+// hardware range check covers only the per-lane part, so callers keep the
+// uniform offset inside the buffer themselves.  Word 3 is the gfx9-family
+// default descriptor format.
+using buf_t = __amdgpu_buffer_rsrc_t;
+constexpr int kBufferWord3 = 0x00020000;
+
+__device__ __forceinline__ buf_t make_buf(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           kBufferWord3);
+}
+__device__ __forceinline__ float buf_load(buf_t r, int voff, int soff, float*) {
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
+}
+__device__ __forceinline__ float buf_load(buf_t r, int voff, int soff, uint16_t*) {
+  return __uint_as_float(static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0)) << 16);
+}
+__device__ __forceinline__ void buf_store(buf_t r, int voff, int soff, float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, voff, soff, 0);
+}
+
 // ---- the per-lane sequential pass over a range of steps -----------------------------------
 //
-// Runs steps [0, nsteps) of one chunk for the lane's chain.  `ld` indexes
-// x/delta/y at the first step (b, t0, d); `bn` indexes B/C at (b, t0, 0).
+// Runs steps [0, nsteps) of one chunk for the lane's chain.  xb/db/yb point at
+// (b, t0, first channel of the block); `lane` is the lane's channel offset
+// inside the block; rows are D elements apart.  Bb/Cb point at row (b, t0) of
+// B/C, read through the scalar unit.  The caller guarantees
+// nsteps * D * sizeof(float) < 2^31.
 // kWithY: also form y_t = sum_n C_t[n] h_t[n] and store it (output pass);
 // otherwise accumulate the chunk's total step size in `S` (summary pass).
-// x and delta are prefetched kTile steps ahead; B_t and C_t one step ahead.
+// x and delta are prefetched kTile steps ahead (values held in registers as
+// float32).  B_t and C_t are loaded one step ahead into two alternating
+// register sets (kTile is even, so the set used by a step is fixed at compile
+// time and no copies are needed).
 template <int N, typename T, bool kPairs, bool kWithY>
-__device__ __forceinline__ void scan_steps(const T* __restrict__ x, const T* __restrict__ delta,
-                                           const T* __restrict__ Bm, const T* __restrict__ Cm,
-                                           float* __restrict__ y, const float (&A2)[N], float (&h)[N],
-                                           double& S, int64_t ld, int64_t bn, int64_t D,
+__device__ __forceinline__ void scan_steps(const T* __restrict__ xb, const T* __restrict__ db,
+                                           const T* __restrict__ Bb, const T* __restrict__ Cb,
+                                           float* __restrict__ yb, const float (&A2)[N],
+                                           float (&h)[N], double& S, int lane, int64_t D,
                                            int nsteps, bool active) {
   constexpr int kTile = 8;
-  T xc[kTile], dc[kTile];
+  static_assert(kTile % 2 == 0, "alternating B/C register sets need an even tile");
+  const uint32_t in_bytes = static_cast<uint32_t>((int64_t)nsteps * D * sizeof(T));
+  const buf_t xr = make_buf(xb, in_bytes);
+  const buf_t dr = make_buf(db, in_bytes);
+  const int in_row = static_cast<int>(D * sizeof(T));
+  const int in_lane = lane * static_cast<int>(sizeof(T));
+  buf_t yr;
+  int out_row = 0, out_lane = 0;
+  if constexpr (kWithY) {
+    yr = make_buf(yb, static_cast<uint32_t>((int64_t)nsteps * D * sizeof(float)));
+    out_row = static_cast<int>(D * sizeof(float));
+    out_lane = lane * static_cast<int>(sizeof(float));
+  }
+  T* tag = nullptr;
+  // prefetches past the chunk re-read its last row (the SGPR offset is not
+  // range-checked by the hardware, so it is clamped here)
+  const int last = nsteps > 0 ? nsteps - 1 : 0;
+  float xc[kTile], dc[kTile];
 #pragma unroll
   for (int j = 0; j < kTile; ++j) {
-    if (j < nsteps) {
-      xc[j] = x[ld + (int64_t)j * D];
-      dc[j] = delta[ld + (int64_t)j * D];
-    }
+    const int soff = __builtin_amdgcn_readfirstlane(min(j, last) * in_row);
+    xc[j] = buf_load(xr, in_lane, soff, tag);
+    dc[j] = buf_load(dr, in_lane, soff, tag);
   }
-  float Bv[N], Cv[N];
+  float Bv[2][N], Cv[2][N];
   if (nsteps > 0) {
-    load_row_any<N, kPairs>(Bm + bn, Bv);
-    if constexpr (kWithY) load_row_any<N, kPairs>(Cm + bn, Cv);
+    load_row_any<N, kPairs>(Bb, Bv[0]);
+    if constexpr (kWithY) load_row_any<N, kPairs>(Cb, Cv[0]);
   }
   for (int base = 0; base < nsteps; base += kTile) {
-    T xn[kTile], dn[kTile];
+    float xn[kTile], dn[kTile];
 #pragma unroll
     for (int j = 0; j < kTile; ++j) {
-      const int s = base + kTile + j;
-      if (s < nsteps) {
-        xn[j] = x[ld + (int64_t)s * D];
-        dn[j] = delta[ld + (int64_t)s * D];
-      }
+      const int soff = __builtin_amdgcn_readfirstlane(min(base + kTile + j, last) * in_row);
+      xn[j] = buf_load(xr, in_lane, soff, tag);
+      dn[j] = buf_load(dr, in_lane, soff, tag);
     }
 #pragma unroll
     for (int j = 0; j < kTile; ++j) {
       const int s = base + j;
       if (s < nsteps) {
-        float Bnext[N], Cnext[N];
+        const int cur = j & 1;
         if (s + 1 < nsteps) {
-          load_row_any<N, kPairs>(Bm + bn + (int64_t)(s + 1) * N, Bnext);
-          if constexpr (kWithY) load_row_any<N, kPairs>(Cm + bn + (int64_t)(s + 1) * N, Cnext);
+          load_row_any<N, kPairs>(Bb + (int64_t)(s + 1) * N, Bv[cur ^ 1]);
+          if constexpr (kWithY) load_row_any<N, kPairs>(Cb + (int64_t)(s + 1) * N, Cv[cur ^ 1]);
         }
-        const float dt = to_float(dc[j]);
-        const float dx = dt * to_float(xc[j]);
+        const float dt = dc[j];
+        const float dx = dt * xc[j];
         float yv = 0.0f;
 #pragma unroll
         for (int n = 0; n < N; ++n) {
-          const float a = fast_exp2(dt * A2[n]);           // Abar = exp(delta * A)
-          h[n] = __builtin_fmaf(a, h[n], dx * Bv[n]);      // h = Abar h + (delta B) x
-          if constexpr (kWithY) yv = __builtin_fmaf(Cv[n], h[n], yv);   // y = C . h
+          const float a = fast_exp2(dt * A2[n]);             // Abar = exp(delta * A)
+          h[n] = __builtin_fmaf(a, h[n], dx * Bv[cur][n]);   // h = Abar h + (delta B) x
+          if constexpr (kWithY) yv = __builtin_fmaf(Cv[cur][n], h[n], yv);   // y = C . h
         }
         if constexpr (kWithY) {
-          if (active) y[ld + (int64_t)s * D] = yv;
+          if (active) buf_store(yr, out_lane, s * out_row, yv);
         } else {
           S += static_cast<double>(dt);
-        }
-        if (s + 1 < nsteps) {
-#pragma unroll
-          for (int n = 0; n < N; ++n) {
-            Bv[n] = Bnext[n];
-            if constexpr (kWithY) Cv[n] = Cnext[n];
-          }
         }
       }
     }

@@ -11,14 +11,17 @@
 //                 S_k.  The chunk's decay is prod_t exp(delta_t A) =
 //                 exp(S_k A), so the pair for the whole chunk is
 //                 (exp(S_k A), hloc_k) and needs N + 1 numbers per chain.
-//   output pass   (all chunks in parallel): fold the pairs of the chunks
-//                 before this one into the carry-in, then scan the chunk's
-//                 steps from it and write y.
+//   carry pass    (per chain and state index): walk the chunk pairs in time
+//                 order, c_{k+1} = P_k c_k + hloc_k, giving the state that
+//                 enters every chunk.
+//   output pass   (all chunks in parallel): scan the chunk's steps from its
+//                 carry-in and write y.
 //
-// Only the summaries ([batch, K-1, N, D] floats and [batch, K-1, D] doubles)
-// travel through memory; per-step states stay in registers ("Understanding
-// Mamba", section 7.3).  S_k is accumulated in float64 so that exp(S_k A)
-// matches the product of the per-step factors to float32 rounding.
+// Only the summaries (two [batch, K-1, N, D] float arrays: hloc and the decay
+// P = exp(S A)) travel through memory; per-step states stay in registers
+// ("Understanding Mamba", section 7.3).  S_k is accumulated in float64 so
+// that exp(S_k A) matches the product of the per-step factors to float32
+// rounding.
 #include "mssm_internal.h"
 #include "scan_device.h"
 
@@ -30,31 +33,36 @@ namespace mssm {
 constexpr int kBlock = 256;   // 4 wavefronts, 256 consecutive channels
 
 struct BlockCoord {
+  int64_t d0;     // first channel of the block
   int64_t d;      // channel of this lane
+  int lane;       // d - d0 for active lanes; clamped to the last channel otherwise
+  bool active;    // d < D
   int k;          // chunk
   int64_t b;      // batch row
 };
 
-__device__ __forceinline__ BlockCoord block_coord(int64_t n_dtiles, int K) {
+__device__ __forceinline__ BlockCoord block_coord(int64_t n_dtiles, int K, int64_t D) {
   const int64_t bid = blockIdx.x;
   const int64_t dtile = bid % n_dtiles;
   const int64_t rest = bid / n_dtiles;
   BlockCoord c;
   c.k = static_cast<int>(rest % K);
   c.b = rest / K;
-  c.d = dtile * kBlock + threadIdx.x;
+  c.d0 = dtile * kBlock;
+  c.d = c.d0 + threadIdx.x;
+  c.active = c.d < D;
+  c.lane = c.active ? static_cast<int>(threadIdx.x) : static_cast<int>(D - 1 - c.d0);
   return c;
 }
 
 template <int N, typename T, bool kPairs>
 __global__ __launch_bounds__(kBlock) void chunk_summary_kernel(
     const T* __restrict__ x, const T* __restrict__ delta, const float* __restrict__ A,
-    const T* __restrict__ Bm, float* __restrict__ sum_h, double* __restrict__ sum_dt,
+    const T* __restrict__ Bm, float* __restrict__ sum_h, float* __restrict__ sum_p,
     int64_t L, int64_t D, int64_t chunk_len, int K, int64_t n_dtiles) {
   // grid: n_dtiles * (K - 1) * batch blocks; block (dtile, k, b), k < K - 1
-  const BlockCoord c = block_coord(n_dtiles, K - 1);
-  const bool active = c.d < D;
-  const int64_t dl = active ? c.d : D - 1;
+  const BlockCoord c = block_coord(n_dtiles, K - 1, D);
+  const int64_t dl = c.d0 + c.lane;
   float A2[N], h[N];
 #pragma unroll
   for (int n = 0; n < N; ++n) {
@@ -63,15 +71,58 @@ __global__ __launch_bounds__(kBlock) void chunk_summary_kernel(
   }
   const int64_t t0 = (int64_t)c.k * chunk_len;
   const int nsteps = static_cast<int>(chunk_len);   // chunks before the last are full
+  const int64_t row0 = (c.b * L + t0) * D + c.d0;
   double S = 0.0;
-  scan_steps<N, T, kPairs, false>(x, delta, Bm, nullptr, nullptr, A2, h, S,
-                                  (c.b * L + t0) * D + dl, (c.b * L + t0) * N, D, nsteps,
-                                  active);
-  if (active) {
+  scan_steps<N, T, kPairs, false>(x + row0, delta + row0, Bm + (c.b * L + t0) * N, nullptr,
+                                  nullptr, A2, h, S, c.lane, D, nsteps, c.active);
+  if (c.active) {
     const int64_t row = c.b * (K - 1) + c.k;
 #pragma unroll
-    for (int n = 0; n < N; ++n) sum_h[(row * N + n) * D + c.d] = h[n];
-    sum_dt[row * D + c.d] = S;
+    for (int n = 0; n < N; ++n) {
+      sum_h[(row * N + n) * D + c.d] = h[n];
+      // the chunk's decay prod_t exp(delta_t A) = exp(S A); S was summed in float64
+      sum_p[(row * N + n) * D + c.d] =
+          fast_exp2(static_cast<float>(static_cast<double>(A2[n]) * S));
+    }
+  }
+}
+
+// Carry pass: one lane per (batch row, state n, channel d).  Walks the chunk
+// pairs in time order, c_{j+1} = P_j c_j + hloc_j (c_0 = 0), and overwrites
+// hloc_j with c_{j+1}, the state entering chunk j + 1.  Loads are issued
+// kBatch chunks ahead of the dependent multiply-add chain.
+__global__ __launch_bounds__(kBlock) void chunk_carry_kernel(float* __restrict__ sum_h,
+                                                             const float* __restrict__ sum_p,
+                                                             int64_t D, int N, int K,
+                                                             int64_t n_dtiles) {
+  constexpr int kBatch = 8;
+  const int64_t bid = blockIdx.x;
+  const int64_t dtile = bid % n_dtiles;
+  const int64_t rest = bid / n_dtiles;
+  const int n = static_cast<int>(rest % N);
+  const int64_t b = rest / N;
+  const int64_t d = dtile * kBlock + threadIdx.x;
+  if (d >= D) return;                       // no barriers in this kernel
+  const int64_t stride = (int64_t)N * D;    // from chunk j to chunk j + 1
+  float* hp = sum_h + (b * (K - 1) * N + n) * D + d;
+  const float* pp = sum_p + (b * (K - 1) * N + n) * D + d;
+  float c = 0.0f;
+  for (int j0 = 0; j0 < K - 1; j0 += kBatch) {
+    float hv[kBatch], pv[kBatch];
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      if (j0 + i < K - 1) {
+        hv[i] = hp[(int64_t)(j0 + i) * stride];
+        pv[i] = pp[(int64_t)(j0 + i) * stride];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      if (j0 + i < K - 1) {
+        c = __builtin_fmaf(pv[i], c, hv[i]);
+        hp[(int64_t)(j0 + i) * stride] = c;
+      }
+    }
   }
 }
 
@@ -79,32 +130,29 @@ template <int N, typename T, bool kPairs>
 __global__ __launch_bounds__(kBlock) void chunk_output_kernel(
     const T* __restrict__ x, const T* __restrict__ delta, const float* __restrict__ A,
     const T* __restrict__ Bm, const T* __restrict__ Cm, float* __restrict__ y,
-    const float* __restrict__ sum_h, const double* __restrict__ sum_dt, int64_t L, int64_t D,
-    int64_t chunk_len, int K, int64_t n_dtiles) {
-  const BlockCoord c = block_coord(n_dtiles, K);
-  const bool active = c.d < D;
-  const int64_t dl = active ? c.d : D - 1;
+    const float* __restrict__ sum_h, int64_t L, int64_t D, int64_t chunk_len, int K,
+    int64_t n_dtiles) {
+  const BlockCoord c = block_coord(n_dtiles, K, D);
+  const int64_t dl = c.d0 + c.lane;
   float A2[N], h[N];
 #pragma unroll
   for (int n = 0; n < N; ++n) {
     A2[n] = A[dl * N + n] * kLog2e;
     h[n] = 0.0f;
   }
-  // carry-in: fold (exp(S_j A), hloc_j) of chunks j < k, oldest first
-  for (int j = 0; j < c.k; ++j) {
-    const int64_t row = c.b * (K - 1) + j;
-    const double S = sum_dt[row * D + dl];
+  // carry-in: the state entering chunk k, left by the carry pass in slot k - 1
+  if (c.k > 0) {
+    const float* cp = sum_h + ((c.b * (K - 1) + (c.k - 1)) * N) * D + dl;
 #pragma unroll
-    for (int n = 0; n < N; ++n) {
-      const float decay = fast_exp2(static_cast<float>(static_cast<double>(A2[n]) * S));
-      h[n] = __builtin_fmaf(decay, h[n], sum_h[(row * N + n) * D + dl]);
-    }
+    for (int n = 0; n < N; ++n) h[n] = cp[(int64_t)n * D];
   }
   const int64_t t0 = (int64_t)c.k * chunk_len;
   const int nsteps = static_cast<int>(std::min<int64_t>(chunk_len, L - t0));
+  const int64_t row0 = (c.b * L + t0) * D + c.d0;
   double S_unused = 0.0;
-  scan_steps<N, T, kPairs, true>(x, delta, Bm, Cm, y, A2, h, S_unused, (c.b * L + t0) * D + dl,
-                                 (c.b * L + t0) * N, D, nsteps, active);
+  scan_steps<N, T, kPairs, true>(x + row0, delta + row0, Bm + (c.b * L + t0) * N,
+                                 Cm + (c.b * L + t0) * N, y + row0, A2, h, S_unused, c.lane, D,
+                                 nsteps, c.active);
 }
 
 bool state_size_supported(int64_t N) {
@@ -116,24 +164,30 @@ static size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 ScanPlan plan_scan(int64_t batch, int64_t L, int64_t D, int64_t N) {
   ScanPlan p;
   if (batch <= 0 || L <= 0 || D <= 0) return p;
-  // Enough wavefronts to give every SIMD of the 256 compute units about two,
-  // with chunks no shorter than 64 steps.  MSSM_CHUNK_LEN overrides the
-  // chunk length (used for tuning sweeps and chunk-boundary tests).
-  const int64_t waves_per_chunk = batch * ((D + 63) / 64);
-  const int64_t target_waves = 2048;
-  int64_t K = (target_waves + waves_per_chunk - 1) / waves_per_chunk;
+  // Chunk count: enough 256-channel blocks to give every compute unit about
+  // eight (two wavefronts per SIMD over the kernel's life), with chunks of at
+  // least 64 steps.  Measured on MI355X with chunk-length sweeps of the
+  // synthetic workloads (the per-chunk cost after the carry pass is small, so
+  // more chunks help until chunks get short).  MSSM_CHUNK_LEN overrides the
+  // chunk length (tuning sweeps and chunk-boundary tests).
+  const int64_t blocks_per_chunk = batch * ((D + kBlock - 1) / kBlock);
+  const int64_t target_blocks = 2048;
+  int64_t K = (target_blocks + blocks_per_chunk / 2) / blocks_per_chunk;
   const int64_t min_chunk = 64;
-  K = std::max<int64_t>(1, std::min<int64_t>(K, (L + min_chunk - 1) / min_chunk));
+  K = std::max<int64_t>(1, std::min<int64_t>(K, L / min_chunk));
   int64_t chunk = (L + K - 1) / K;
   if (const char* env = std::getenv("MSSM_CHUNK_LEN")) {
     const long long v = std::atoll(env);
     if (v > 0) chunk = v;
   }
-  const int64_t max_chunk = int64_t(1) << 30;
+  // buffer offsets inside one chunk are 32-bit: keep (chunk + tile) * D * 4 < 2^31
+  const int64_t max_chunk = std::max<int64_t>(1, ((int64_t(1) << 31) - 1) / (D * 4) - 16);
   chunk = std::min<int64_t>(chunk, max_chunk);
   K = (L + chunk - 1) / chunk;
-  if (K > 65535) {   // keep the summary fold short and the grid within limits
-    K = 65535;
+  // summaries of one batch row are addressed with 32-bit byte offsets
+  const int64_t max_k = std::max<int64_t>(2, ((int64_t(1) << 31) - 1) / (N * D * 4));
+  if (K > std::min<int64_t>(max_k, 65535)) {
+    K = std::min<int64_t>(max_k, 65535);
     chunk = (L + K - 1) / K;
     K = (L + chunk - 1) / chunk;
   }
@@ -141,8 +195,8 @@ ScanPlan plan_scan(int64_t batch, int64_t L, int64_t D, int64_t N) {
   p.chunk_len = chunk;
   if (K > 1) {
     p.sum_h_bytes = round_up(sizeof(float) * (size_t)batch * (size_t)(K - 1) * (size_t)N * (size_t)D, 256);
-    p.sum_dt_offset = p.sum_h_bytes;
-    p.workspace_bytes = p.sum_dt_offset + round_up(sizeof(double) * (size_t)batch * (size_t)(K - 1) * (size_t)D, 256);
+    p.sum_p_offset = p.sum_h_bytes;
+    p.workspace_bytes = 2 * p.sum_h_bytes;
   }
   return p;
 }
@@ -156,20 +210,25 @@ static hipError_t launch_typed(const ScanArgs& a, const ScanPlan& p, void* ws, h
   float* y = static_cast<float*>(a.y);
   const int64_t n_dtiles = (a.D + kBlock - 1) / kBlock;
   float* sum_h = nullptr;
-  double* sum_dt = nullptr;
+  float* sum_p = nullptr;
   if (p.K > 1) {
     sum_h = static_cast<float*>(ws);
-    sum_dt = reinterpret_cast<double*>(static_cast<char*>(ws) + p.sum_dt_offset);
+    sum_p = reinterpret_cast<float*>(static_cast<char*>(ws) + p.sum_p_offset);
     const int64_t grid = n_dtiles * (p.K - 1) * a.batch;
     hipLaunchKernelGGL((chunk_summary_kernel<N, T, kPairs>), dim3((unsigned)grid), dim3(kBlock), 0,
-                       stream, x, delta, a.A, Bm, sum_h, sum_dt, a.L, a.D, p.chunk_len, p.K,
+                       stream, x, delta, a.A, Bm, sum_h, sum_p, a.L, a.D, p.chunk_len, p.K,
                        n_dtiles);
     hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t cgrid = n_dtiles * N * a.batch;
+    hipLaunchKernelGGL(chunk_carry_kernel, dim3((unsigned)cgrid), dim3(kBlock), 0, stream, sum_h,
+                       sum_p, a.D, N, p.K, n_dtiles);
+    e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   const int64_t grid = n_dtiles * p.K * a.batch;
   hipLaunchKernelGGL((chunk_output_kernel<N, T, kPairs>), dim3((unsigned)grid), dim3(kBlock), 0,
-                     stream, x, delta, a.A, Bm, Cm, y, sum_h, sum_dt, a.L, a.D, p.chunk_len, p.K,
+                     stream, x, delta, a.A, Bm, Cm, y, sum_h, a.L, a.D, p.chunk_len, p.K,
                      n_dtiles);
   return hipGetLastError();
 }
