@@ -78,7 +78,7 @@ mssm_status mssm_selective_scan_workspace_size(int64_t batch, int64_t L, int64_t
   if (!bytes) return MSSM_ERROR_INVALID_VALUE;
   const mssm_status s = check_shape(batch, L, D, N, dtype);
   if (s != MSSM_SUCCESS) return s;
-  *bytes = empty_problem(batch, L, D) ? 0 : mssm::plan_scan(batch, L, D, N).workspace_bytes;
+  *bytes = empty_problem(batch, L, D) ? 0 : mssm::workspace_bound(batch, L, D, N);
   return MSSM_SUCCESS;
 }
 
@@ -90,12 +90,12 @@ mssm_status mssm_selective_scan_fwd_ws(const void* x, const void* delta, const f
   if (s != MSSM_SUCCESS) return s;
   if (empty_problem(batch, L, D)) return MSSM_SUCCESS;
   if (!x || !delta || !A || !B || !C || !y) return MSSM_ERROR_INVALID_VALUE;
-  const mssm::ScanPlan plan = mssm::plan_scan(batch, L, D, N);
+  const mssm::ScanArgs a{x, delta, A, B, C, y, batch, L, D, N, dtype};
+  const mssm::ScanPlan plan = mssm::plan_scan(batch, L, D, N, mssm::choose_cpl(a));
   s = check_grid(plan, batch, D, N);
   if (s != MSSM_SUCCESS) return s;
   if (plan.workspace_bytes > 0 && (!workspace || workspace_bytes < plan.workspace_bytes))
     return MSSM_ERROR_WORKSPACE;
-  const mssm::ScanArgs a{x, delta, A, B, C, y, batch, L, D, N, dtype};
   const hipError_t e = mssm::launch_scan(a, plan, workspace, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) {
     set_hip_error(e, "selective scan launch");
@@ -112,7 +112,8 @@ mssm_status mssm_selective_scan_fwd(const void* x, const void* delta, const floa
   if (s != MSSM_SUCCESS) return s;
   if (empty_problem(batch, L, D)) return MSSM_SUCCESS;
   if (!x || !delta || !A || !B || !C || !y) return MSSM_ERROR_INVALID_VALUE;
-  const mssm::ScanPlan plan = mssm::plan_scan(batch, L, D, N);
+  const mssm::ScanArgs a{x, delta, A, B, C, y, batch, L, D, N, dtype};
+  const mssm::ScanPlan plan = mssm::plan_scan(batch, L, D, N, mssm::choose_cpl(a));
   s = check_grid(plan, batch, D, N);
   if (s != MSSM_SUCCESS) return s;
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -124,7 +125,6 @@ mssm_status mssm_selective_scan_fwd(const void* x, const void* delta, const floa
       return MSSM_ERROR_HIP;
     }
   }
-  const mssm::ScanArgs a{x, delta, A, B, C, y, batch, L, D, N, dtype};
   hipError_t e = mssm::launch_scan(a, plan, ws, st);
   if (ws) {
     const hipError_t f = hipFreeAsync(ws, st);

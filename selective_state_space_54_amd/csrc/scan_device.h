@@ -1,13 +1,15 @@
 // Device-side building blocks of the selective scan (gfx950).
 //
-// One lane owns one (batch row, channel) chain and keeps its N state values in
-// registers.  The 64 lanes of a wavefront take 64 consecutive channels of the
-// same batch row, so at every step they read x and delta as one coalesced
-// 256-byte (float32) or 128-byte (bfloat16) row segment, and they all need the
-// same B_t and C_t: those come through the scalar unit (s_load into SGPRs) and
-// are broadcast to the lanes as instruction operands.  Per element the
-// arithmetic is one multiply for the exponent, one v_exp_f32, one multiply for
-// the input term and two fused multiply-adds (state update, read-out).
+// A lane owns CPL adjacent channels of one batch row (CPL = 1 or 2) and keeps
+// their N state values each in registers.  The 64 lanes of a wavefront take
+// 64 * CPL consecutive channels, so at every step they read x and delta as one
+// coalesced row segment, and they all need the same B_t and C_t: those come
+// through the scalar unit (s_load into SGPRs) and are broadcast to the lanes as
+// instruction operands.  Per element the arithmetic is one multiply for the
+// exponent, one v_exp_f32, one multiply for the input term and two fused
+// multiply-adds (state update, read-out).  Two chains per lane give the
+// scheduler two independent dependency chains and halve the scalar loads per
+// element.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -23,7 +25,6 @@ __device__ __forceinline__ float to_float(float v) { return v; }
 __device__ __forceinline__ float to_float(uint16_t v) {
   return __uint_as_float(static_cast<uint32_t>(v) << 16);
 }
-
 
 // Row of N values shared by the whole wavefront (B_t or C_t).  With a
 // wave-uniform address the compiler turns these into scalar loads.
@@ -74,64 +75,87 @@ __device__ __forceinline__ float fast_exp2(float v) { return __builtin_amdgcn_ex
 // default descriptor format.
 using buf_t = __amdgpu_buffer_rsrc_t;
 constexpr int kBufferWord3 = 0x00020000;
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ buf_t make_buf(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
                                            kBufferWord3);
 }
-__device__ __forceinline__ float buf_load(buf_t r, int voff, int soff, float*) {
-  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
+
+// CPL adjacent values of element type T at (voff + soff) bytes, widened to float.
+template <typename T, int CPL>
+__device__ __forceinline__ void buf_load_vals(buf_t r, int voff, int soff, float (&v)[CPL]) {
+  if constexpr (sizeof(T) == 4 && CPL == 1) {
+    v[0] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
+  } else if constexpr (sizeof(T) == 4 && CPL == 2) {
+    const u32x2 u = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
+    v[0] = __uint_as_float(u.x);
+    v[1] = __uint_as_float(u.y);
+  } else if constexpr (sizeof(T) == 2 && CPL == 1) {
+    v[0] = __uint_as_float(
+        static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0)) << 16);
+  } else {
+    static_assert(sizeof(T) == 2 && CPL == 2, "unsupported element/lane combination");
+    const uint32_t u = __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+    v[0] = __uint_as_float(u << 16);          // lower address = first channel
+    v[1] = __uint_as_float(u & 0xffff0000u);
+  }
 }
-__device__ __forceinline__ float buf_load(buf_t r, int voff, int soff, uint16_t*) {
-  return __uint_as_float(static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0)) << 16);
-}
-__device__ __forceinline__ void buf_store(buf_t r, int voff, int soff, float v) {
-  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, voff, soff, 0);
+
+template <int CPL>
+__device__ __forceinline__ void buf_store_vals(buf_t r, int voff, int soff, const float (&v)[CPL]) {
+  if constexpr (CPL == 1) {
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v[0]), r, voff, soff, 0);
+  } else {
+    static_assert(CPL == 2, "CPL is 1 or 2");
+    u32x2 u;
+    u.x = __float_as_uint(v[0]);
+    u.y = __float_as_uint(v[1]);
+    __builtin_amdgcn_raw_buffer_store_b64(u, r, voff, soff, 0);
+  }
 }
 
 // ---- the per-lane sequential pass over a range of steps -----------------------------------
 //
-// Runs steps [0, nsteps) of one chunk for the lane's chain.  xb/db/yb point at
-// (b, t0, first channel of the block); `lane` is the lane's channel offset
-// inside the block; rows are D elements apart.  Bb/Cb point at row (b, t0) of
-// B/C, read through the scalar unit.  The caller guarantees
-// nsteps * D * sizeof(float) < 2^31.
+// Runs steps [0, nsteps) of one chunk for the lane's CPL chains.  xb/db/yb
+// point at (b, t0, first channel of the block); `lane` is the lane index in the
+// block (its channels are lane*CPL + c); rows are D elements apart.  Bb/Cb
+// point at row (b, t0) of B/C, read through the scalar unit.  The caller
+// guarantees nsteps * D * sizeof(float) < 2^31.
 // kWithY: also form y_t = sum_n C_t[n] h_t[n] and store it (output pass);
-// otherwise accumulate the chunk's total step size in `S` (summary pass).
-// x and delta are prefetched kTile steps ahead (values held in registers as
-// float32).  B_t and C_t are loaded one step ahead into two alternating
-// register sets (kTile is even, so the set used by a step is fixed at compile
-// time and no copies are needed).
-template <int N, typename T, bool kPairs, bool kWithY>
+// otherwise accumulate each chain's total step size in S (summary pass).
+// x and delta are prefetched kTile steps ahead.  B_t and C_t are loaded one
+// step ahead into two alternating register sets (kTile is even, so the set
+// used by a step is fixed at compile time and no copies are needed).
+template <int N, int CPL, typename T, bool kPairs, bool kWithY>
 __device__ __forceinline__ void scan_steps(const T* __restrict__ xb, const T* __restrict__ db,
                                            const T* __restrict__ Bb, const T* __restrict__ Cb,
-                                           float* __restrict__ yb, const float (&A2)[N],
-                                           float (&h)[N], double& S, int lane, int64_t D,
-                                           int nsteps, bool active) {
-  constexpr int kTile = 8;
+                                           float* __restrict__ yb, const float (&A2)[CPL][N],
+                                           float (&h)[CPL][N], double (&S)[CPL], int lane,
+                                           int64_t D, int nsteps, bool active) {
+  constexpr int kTile = (CPL == 1) ? 8 : 4;
   static_assert(kTile % 2 == 0, "alternating B/C register sets need an even tile");
   const uint32_t in_bytes = static_cast<uint32_t>((int64_t)nsteps * D * sizeof(T));
   const buf_t xr = make_buf(xb, in_bytes);
   const buf_t dr = make_buf(db, in_bytes);
   const int in_row = static_cast<int>(D * sizeof(T));
-  const int in_lane = lane * static_cast<int>(sizeof(T));
+  const int in_lane = lane * CPL * static_cast<int>(sizeof(T));
   buf_t yr;
   int out_row = 0, out_lane = 0;
   if constexpr (kWithY) {
     yr = make_buf(yb, static_cast<uint32_t>((int64_t)nsteps * D * sizeof(float)));
     out_row = static_cast<int>(D * sizeof(float));
-    out_lane = lane * static_cast<int>(sizeof(float));
+    out_lane = lane * CPL * static_cast<int>(sizeof(float));
   }
-  T* tag = nullptr;
   // prefetches past the chunk re-read its last row (the SGPR offset is not
   // range-checked by the hardware, so it is clamped here)
   const int last = nsteps > 0 ? nsteps - 1 : 0;
-  float xc[kTile], dc[kTile];
+  float xc[kTile][CPL], dc[kTile][CPL];
 #pragma unroll
   for (int j = 0; j < kTile; ++j) {
     const int soff = __builtin_amdgcn_readfirstlane(min(j, last) * in_row);
-    xc[j] = buf_load(xr, in_lane, soff, tag);
-    dc[j] = buf_load(dr, in_lane, soff, tag);
+    buf_load_vals<T, CPL>(xr, in_lane, soff, xc[j]);
+    buf_load_vals<T, CPL>(dr, in_lane, soff, dc[j]);
   }
   float Bv[2][N], Cv[2][N];
   if (nsteps > 0) {
@@ -139,12 +163,12 @@ __device__ __forceinline__ void scan_steps(const T* __restrict__ xb, const T* __
     if constexpr (kWithY) load_row_any<N, kPairs>(Cb, Cv[0]);
   }
   for (int base = 0; base < nsteps; base += kTile) {
-    float xn[kTile], dn[kTile];
+    float xn[kTile][CPL], dn[kTile][CPL];
 #pragma unroll
     for (int j = 0; j < kTile; ++j) {
       const int soff = __builtin_amdgcn_readfirstlane(min(base + kTile + j, last) * in_row);
-      xn[j] = buf_load(xr, in_lane, soff, tag);
-      dn[j] = buf_load(dr, in_lane, soff, tag);
+      buf_load_vals<T, CPL>(xr, in_lane, soff, xn[j]);
+      buf_load_vals<T, CPL>(dr, in_lane, soff, dn[j]);
     }
 #pragma unroll
     for (int j = 0; j < kTile; ++j) {
@@ -155,26 +179,36 @@ __device__ __forceinline__ void scan_steps(const T* __restrict__ xb, const T* __
           load_row_any<N, kPairs>(Bb + (int64_t)(s + 1) * N, Bv[cur ^ 1]);
           if constexpr (kWithY) load_row_any<N, kPairs>(Cb + (int64_t)(s + 1) * N, Cv[cur ^ 1]);
         }
-        const float dt = dc[j];
-        const float dx = dt * xc[j];
-        float yv = 0.0f;
+        float dx[CPL], yv[CPL];
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) {
+          dx[c] = dc[j][c] * xc[j][c];
+          yv[c] = 0.0f;
+        }
 #pragma unroll
         for (int n = 0; n < N; ++n) {
-          const float a = fast_exp2(dt * A2[n]);             // Abar = exp(delta * A)
-          h[n] = __builtin_fmaf(a, h[n], dx * Bv[cur][n]);   // h = Abar h + (delta B) x
-          if constexpr (kWithY) yv = __builtin_fmaf(Cv[cur][n], h[n], yv);   // y = C . h
+#pragma unroll
+          for (int c = 0; c < CPL; ++c) {
+            const float a = fast_exp2(dc[j][c] * A2[c][n]);            // Abar = exp(delta A)
+            h[c][n] = __builtin_fmaf(a, h[c][n], dx[c] * Bv[cur][n]);  // h = Abar h + (delta B) x
+            if constexpr (kWithY) yv[c] = __builtin_fmaf(Cv[cur][n], h[c][n], yv[c]);  // C . h
+          }
         }
         if constexpr (kWithY) {
-          if (active) buf_store(yr, out_lane, s * out_row, yv);
+          if (active) buf_store_vals<CPL>(yr, out_lane, s * out_row, yv);
         } else {
-          S += static_cast<double>(dt);
+#pragma unroll
+          for (int c = 0; c < CPL; ++c) S[c] += static_cast<double>(dc[j][c]);
         }
       }
     }
 #pragma unroll
     for (int j = 0; j < kTile; ++j) {
-      xc[j] = xn[j];
-      dc[j] = dn[j];
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) {
+        xc[j][c] = xn[j][c];
+        dc[j][c] = dn[j][c];
+      }
     }
   }
 }

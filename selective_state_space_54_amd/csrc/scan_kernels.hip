@@ -30,17 +30,18 @@
 
 namespace mssm {
 
-constexpr int kBlock = 256;   // 4 wavefronts, 256 consecutive channels
+constexpr int kBlock = 256;   // 4 wavefronts; a block covers 256 * CPL consecutive channels
 
 struct BlockCoord {
   int64_t d0;     // first channel of the block
-  int64_t d;      // channel of this lane
-  int lane;       // d - d0 for active lanes; clamped to the last channel otherwise
+  int64_t d;      // first channel of this lane (it owns d .. d + CPL - 1)
+  int lane;       // lane index used for addressing; clamped to the last lane if inactive
   bool active;    // d < D
   int k;          // chunk
   int64_t b;      // batch row
 };
 
+template <int CPL>
 __device__ __forceinline__ BlockCoord block_coord(int64_t n_dtiles, int K, int64_t D) {
   const int64_t bid = blockIdx.x;
   const int64_t dtile = bid % n_dtiles;
@@ -48,54 +49,62 @@ __device__ __forceinline__ BlockCoord block_coord(int64_t n_dtiles, int K, int64
   BlockCoord c;
   c.k = static_cast<int>(rest % K);
   c.b = rest / K;
-  c.d0 = dtile * kBlock;
-  c.d = c.d0 + threadIdx.x;
-  c.active = c.d < D;
-  c.lane = c.active ? static_cast<int>(threadIdx.x) : static_cast<int>(D - 1 - c.d0);
+  c.d0 = dtile * kBlock * CPL;
+  c.d = c.d0 + (int64_t)CPL * threadIdx.x;
+  c.active = c.d < D;       // D is a multiple of CPL
+  c.lane = c.active ? static_cast<int>(threadIdx.x) : static_cast<int>((D - c.d0) / CPL - 1);
   return c;
 }
 
-template <int N, typename T, bool kPairs>
+template <int N, int CPL, typename T, bool kPairs>
 __global__ __launch_bounds__(kBlock) void chunk_summary_kernel(
     const T* __restrict__ x, const T* __restrict__ delta, const float* __restrict__ A,
     const T* __restrict__ Bm, float* __restrict__ sum_h, float* __restrict__ sum_p,
     int64_t L, int64_t D, int64_t chunk_len, int K, int64_t n_dtiles) {
   // grid: n_dtiles * (K - 1) * batch blocks; block (dtile, k, b), k < K - 1
-  const BlockCoord c = block_coord(n_dtiles, K - 1, D);
-  const int64_t dl = c.d0 + c.lane;
-  float A2[N], h[N];
+  const BlockCoord c = block_coord<CPL>(n_dtiles, K - 1, D);
+  const int64_t dl = c.d0 + (int64_t)CPL * c.lane;
+  float A2[CPL][N], h[CPL][N];
+  double S[CPL];
 #pragma unroll
-  for (int n = 0; n < N; ++n) {
-    A2[n] = A[dl * N + n] * kLog2e;
-    h[n] = 0.0f;
+  for (int q = 0; q < CPL; ++q) {
+    S[q] = 0.0;
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+      A2[q][n] = A[(dl + q) * N + n] * kLog2e;
+      h[q][n] = 0.0f;
+    }
   }
   const int64_t t0 = (int64_t)c.k * chunk_len;
   const int nsteps = static_cast<int>(chunk_len);   // chunks before the last are full
   const int64_t row0 = (c.b * L + t0) * D + c.d0;
-  double S = 0.0;
-  scan_steps<N, T, kPairs, false>(x + row0, delta + row0, Bm + (c.b * L + t0) * N, nullptr,
-                                  nullptr, A2, h, S, c.lane, D, nsteps, c.active);
+  scan_steps<N, CPL, T, kPairs, false>(x + row0, delta + row0, Bm + (c.b * L + t0) * N, nullptr,
+                                       nullptr, A2, h, S, c.lane, D, nsteps, c.active);
   if (c.active) {
     const int64_t row = c.b * (K - 1) + c.k;
 #pragma unroll
-    for (int n = 0; n < N; ++n) {
-      sum_h[(row * N + n) * D + c.d] = h[n];
-      // the chunk's decay prod_t exp(delta_t A) = exp(S A); S was summed in float64
-      sum_p[(row * N + n) * D + c.d] =
-          fast_exp2(static_cast<float>(static_cast<double>(A2[n]) * S));
+    for (int q = 0; q < CPL; ++q) {
+#pragma unroll
+      for (int n = 0; n < N; ++n) {
+        sum_h[(row * N + n) * D + c.d + q] = h[q][n];
+        // the chunk's decay prod_t exp(delta_t A) = exp(S A); S was summed in float64
+        sum_p[(row * N + n) * D + c.d + q] =
+            fast_exp2(static_cast<float>(static_cast<double>(A2[q][n]) * S[q]));
+      }
     }
   }
 }
 
 // Carry pass: one lane per (batch row, state n, channel d).  Walks the chunk
 // pairs in time order, c_{j+1} = P_j c_j + hloc_j (c_0 = 0), and overwrites
-// hloc_j with c_{j+1}, the state entering chunk j + 1.  Loads are issued
-// kBatch chunks ahead of the dependent multiply-add chain.
+// hloc_j with c_{j+1}, the state entering chunk j + 1.  The loads of up to
+// kBatch chunks are all issued before the dependent multiply-add chain, so a
+// lane pays one memory latency per kBatch chunks.
 __global__ __launch_bounds__(kBlock) void chunk_carry_kernel(float* __restrict__ sum_h,
                                                              const float* __restrict__ sum_p,
                                                              int64_t D, int N, int K,
                                                              int64_t n_dtiles) {
-  constexpr int kBatch = 8;
+  constexpr int kBatch = 32;
   const int64_t bid = blockIdx.x;
   const int64_t dtile = bid % n_dtiles;
   const int64_t rest = bid / n_dtiles;
@@ -126,33 +135,39 @@ __global__ __launch_bounds__(kBlock) void chunk_carry_kernel(float* __restrict__
   }
 }
 
-template <int N, typename T, bool kPairs>
+template <int N, int CPL, typename T, bool kPairs>
 __global__ __launch_bounds__(kBlock) void chunk_output_kernel(
     const T* __restrict__ x, const T* __restrict__ delta, const float* __restrict__ A,
     const T* __restrict__ Bm, const T* __restrict__ Cm, float* __restrict__ y,
     const float* __restrict__ sum_h, int64_t L, int64_t D, int64_t chunk_len, int K,
     int64_t n_dtiles) {
-  const BlockCoord c = block_coord(n_dtiles, K, D);
-  const int64_t dl = c.d0 + c.lane;
-  float A2[N], h[N];
+  const BlockCoord c = block_coord<CPL>(n_dtiles, K, D);
+  const int64_t dl = c.d0 + (int64_t)CPL * c.lane;
+  float A2[CPL][N], h[CPL][N];
+  double S_unused[CPL];
 #pragma unroll
-  for (int n = 0; n < N; ++n) {
-    A2[n] = A[dl * N + n] * kLog2e;
-    h[n] = 0.0f;
+  for (int q = 0; q < CPL; ++q) {
+    S_unused[q] = 0.0;
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+      A2[q][n] = A[(dl + q) * N + n] * kLog2e;
+      h[q][n] = 0.0f;
+    }
   }
   // carry-in: the state entering chunk k, left by the carry pass in slot k - 1
   if (c.k > 0) {
     const float* cp = sum_h + ((c.b * (K - 1) + (c.k - 1)) * N) * D + dl;
 #pragma unroll
-    for (int n = 0; n < N; ++n) h[n] = cp[(int64_t)n * D];
+    for (int q = 0; q < CPL; ++q)
+#pragma unroll
+      for (int n = 0; n < N; ++n) h[q][n] = cp[(int64_t)n * D + q];
   }
   const int64_t t0 = (int64_t)c.k * chunk_len;
   const int nsteps = static_cast<int>(std::min<int64_t>(chunk_len, L - t0));
   const int64_t row0 = (c.b * L + t0) * D + c.d0;
-  double S_unused = 0.0;
-  scan_steps<N, T, kPairs, true>(x + row0, delta + row0, Bm + (c.b * L + t0) * N,
-                                 Cm + (c.b * L + t0) * N, y + row0, A2, h, S_unused, c.lane, D,
-                                 nsteps, c.active);
+  scan_steps<N, CPL, T, kPairs, true>(x + row0, delta + row0, Bm + (c.b * L + t0) * N,
+                                      Cm + (c.b * L + t0) * N, y + row0, A2, h, S_unused, c.lane,
+                                      D, nsteps, c.active);
 }
 
 bool state_size_supported(int64_t N) {
@@ -161,33 +176,43 @@ bool state_size_supported(int64_t N) {
 
 static size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
-ScanPlan plan_scan(int64_t batch, int64_t L, int64_t D, int64_t N) {
+// Two chains per lane pay off for bfloat16 inputs (one 32-bit load brings both
+// channels' x and delta; MI355X sweeps: about 10-13% faster), not for float32
+// (register pressure lowers occupancy more than the extra ILP gains).
+int default_cpl(int64_t D, mssm_dtype dtype) {
+  if (const char* env = std::getenv("MSSM_CPL")) {       // tuning experiments only
+    const int v = std::atoi(env);
+    if (v == 1 || v == 2) return (v == 2 && D % 2 == 0) ? 2 : 1;
+  }
+  return (dtype == MSSM_BFLOAT16 && D % 2 == 0) ? 2 : 1;
+}
+
+ScanPlan plan_scan(int64_t batch, int64_t L, int64_t D, int64_t N, int cpl) {
   ScanPlan p;
+  p.cpl = cpl;
   if (batch <= 0 || L <= 0 || D <= 0) return p;
-  // Chunk count: enough 256-channel blocks to give every compute unit about
-  // eight (two wavefronts per SIMD over the kernel's life), with chunks of at
-  // least 64 steps.  Measured on MI355X with chunk-length sweeps of the
-  // synthetic workloads (the per-chunk cost after the carry pass is small, so
-  // more chunks help until chunks get short).  MSSM_CHUNK_LEN overrides the
-  // chunk length (tuning sweeps and chunk-boundary tests).
-  const int64_t blocks_per_chunk = batch * ((D + kBlock - 1) / kBlock);
+  // Chunk count: enough blocks to give every compute unit about eight (two
+  // wavefronts per SIMD over the kernel's life), with chunks of at least 64
+  // steps (128 with two chains per lane).  Measured on MI355X with chunk-length sweeps of the synthetic
+  // workloads (the per-chunk cost after the carry pass is small, so more
+  // chunks help until chunks get short).  MSSM_CHUNK_LEN overrides the chunk
+  // length (tuning sweeps and chunk-boundary tests).
+  const int64_t blocks_per_chunk = batch * ((D + kBlock * cpl - 1) / (kBlock * cpl));
   const int64_t target_blocks = 2048;
   int64_t K = (target_blocks + blocks_per_chunk / 2) / blocks_per_chunk;
-  const int64_t min_chunk = 64;
+  const int64_t min_chunk = cpl == 1 ? 64 : 128;
   K = std::max<int64_t>(1, std::min<int64_t>(K, L / min_chunk));
   int64_t chunk = (L + K - 1) / K;
   if (const char* env = std::getenv("MSSM_CHUNK_LEN")) {
     const long long v = std::atoll(env);
     if (v > 0) chunk = v;
   }
-  // buffer offsets inside one chunk are 32-bit: keep (chunk + tile) * D * 4 < 2^31
-  const int64_t max_chunk = std::max<int64_t>(1, ((int64_t(1) << 31) - 1) / (D * 4) - 16);
+  // buffer offsets inside one chunk are 32-bit: keep chunk * D * 4 < 2^31
+  const int64_t max_chunk = std::max<int64_t>(1, ((int64_t(1) << 31) - 1) / (D * 4));
   chunk = std::min<int64_t>(chunk, max_chunk);
   K = (L + chunk - 1) / chunk;
-  // summaries of one batch row are addressed with 32-bit byte offsets
-  const int64_t max_k = std::max<int64_t>(2, ((int64_t(1) << 31) - 1) / (N * D * 4));
-  if (K > std::min<int64_t>(max_k, 65535)) {
-    K = std::min<int64_t>(max_k, 65535);
+  if (K > 65535) {
+    K = 65535;
     chunk = (L + K - 1) / K;
     K = (L + chunk - 1) / chunk;
   }
@@ -201,45 +226,67 @@ ScanPlan plan_scan(int64_t batch, int64_t L, int64_t D, int64_t N) {
   return p;
 }
 
-template <int N, typename T, bool kPairs>
+size_t workspace_bound(int64_t batch, int64_t L, int64_t D, int64_t N) {
+  size_t w = plan_scan(batch, L, D, N, 1).workspace_bytes;
+  if (D % 2 == 0) w = std::max(w, plan_scan(batch, L, D, N, 2).workspace_bytes);
+  return w;
+}
+
+int choose_cpl(const ScanArgs& a) {
+  int cpl = default_cpl(a.D, a.dtype);
+  const size_t align = 2 * (a.dtype == MSSM_FLOAT32 ? 4 : 2);
+  if (cpl == 2 && (reinterpret_cast<uintptr_t>(a.x) % align != 0 ||
+                   reinterpret_cast<uintptr_t>(a.delta) % align != 0 ||
+                   reinterpret_cast<uintptr_t>(a.y) % 8 != 0))
+    cpl = 1;
+  return cpl;
+}
+
+template <int N, int CPL, typename T, bool kPairs>
 static hipError_t launch_typed(const ScanArgs& a, const ScanPlan& p, void* ws, hipStream_t stream) {
   const T* x = static_cast<const T*>(a.x);
   const T* delta = static_cast<const T*>(a.delta);
   const T* Bm = static_cast<const T*>(a.B);
   const T* Cm = static_cast<const T*>(a.C);
   float* y = static_cast<float*>(a.y);
-  const int64_t n_dtiles = (a.D + kBlock - 1) / kBlock;
+  const int64_t n_dtiles = (a.D + kBlock * CPL - 1) / (kBlock * CPL);
   float* sum_h = nullptr;
   float* sum_p = nullptr;
   if (p.K > 1) {
     sum_h = static_cast<float*>(ws);
     sum_p = reinterpret_cast<float*>(static_cast<char*>(ws) + p.sum_p_offset);
     const int64_t grid = n_dtiles * (p.K - 1) * a.batch;
-    hipLaunchKernelGGL((chunk_summary_kernel<N, T, kPairs>), dim3((unsigned)grid), dim3(kBlock), 0,
-                       stream, x, delta, a.A, Bm, sum_h, sum_p, a.L, a.D, p.chunk_len, p.K,
-                       n_dtiles);
+    hipLaunchKernelGGL((chunk_summary_kernel<N, CPL, T, kPairs>), dim3((unsigned)grid),
+                       dim3(kBlock), 0, stream, x, delta, a.A, Bm, sum_h, sum_p, a.L, a.D,
+                       p.chunk_len, p.K, n_dtiles);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int64_t cgrid = n_dtiles * N * a.batch;
+    const int64_t carry_tiles = (a.D + kBlock - 1) / kBlock;
+    const int64_t cgrid = carry_tiles * N * a.batch;
     hipLaunchKernelGGL(chunk_carry_kernel, dim3((unsigned)cgrid), dim3(kBlock), 0, stream, sum_h,
-                       sum_p, a.D, N, p.K, n_dtiles);
+                       sum_p, a.D, N, p.K, carry_tiles);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   const int64_t grid = n_dtiles * p.K * a.batch;
-  hipLaunchKernelGGL((chunk_output_kernel<N, T, kPairs>), dim3((unsigned)grid), dim3(kBlock), 0,
-                     stream, x, delta, a.A, Bm, Cm, y, sum_h, a.L, a.D, p.chunk_len, p.K,
+  hipLaunchKernelGGL((chunk_output_kernel<N, CPL, T, kPairs>), dim3((unsigned)grid), dim3(kBlock),
+                     0, stream, x, delta, a.A, Bm, Cm, y, sum_h, a.L, a.D, p.chunk_len, p.K,
                      n_dtiles);
   return hipGetLastError();
 }
 
-template <int N>
-static hipError_t launch_n(const ScanArgs& a, const ScanPlan& p, void* ws, hipStream_t stream) {
-  if (a.dtype == MSSM_FLOAT32) return launch_typed<N, float, false>(a, p, ws, stream);
+template <int N, int CPL>
+static hipError_t launch_nc(const ScanArgs& a, const ScanPlan& p, void* ws, hipStream_t stream) {
+  if (a.dtype == MSSM_FLOAT32) return launch_typed<N, CPL, float, false>(a, p, ws, stream);
   const bool pairs = (N % 2 == 0) && (reinterpret_cast<uintptr_t>(a.B) % 4 == 0) &&
                      (reinterpret_cast<uintptr_t>(a.C) % 4 == 0);
-  if (pairs) return launch_typed<N, uint16_t, true>(a, p, ws, stream);
-  return launch_typed<N, uint16_t, false>(a, p, ws, stream);
+  if (pairs) return launch_typed<N, CPL, uint16_t, true>(a, p, ws, stream);
+  return launch_typed<N, CPL, uint16_t, false>(a, p, ws, stream);
+}
+
+template <int N>
+static hipError_t launch_n(const ScanArgs& a, const ScanPlan& p, void* ws, hipStream_t stream) {
+  return p.cpl == 2 ? launch_nc<N, 2>(a, p, ws, stream) : launch_nc<N, 1>(a, p, ws, stream);
 }
 
 hipError_t launch_scan(const ScanArgs& a, const ScanPlan& p, void* ws, hipStream_t stream) {

@@ -61,6 +61,23 @@ def test_small_shapes(kind, shape, chunk_len):
     assert_parity(host64(y), oracle_scan(g), g["workload"].dtype, f"{kind} {shape}")
 
 
+@pytest.mark.parametrize("cpl", ["1", "2"])
+@pytest.mark.parametrize("kind", ["mamba130m_layer_fp32", "mid_bf16"])
+def test_both_chain_per_lane_variants(kind, cpl):
+    """Both kernel variants (one or two channels per lane) for both dtypes."""
+    old = os.environ.get("MSSM_CPL")
+    os.environ["MSSM_CPL"] = cpl
+    try:
+        g = workloads.generate(kind, batch=2, L=777, D=300, N=16, seed=11)
+        y = run_scan(g)
+    finally:
+        if old is None:
+            os.environ.pop("MSSM_CPL", None)
+        else:
+            os.environ["MSSM_CPL"] = old
+    assert_parity(host64(y), oracle_scan(g), g["workload"].dtype, f"{kind} cpl={cpl}")
+
+
 def test_tiny_workload():
     g = workloads.generate("tiny_fp32")
     y = run_scan(g)
@@ -151,6 +168,26 @@ def test_unaligned_bf16_rows_take_the_elementwise_path():
     y = mssm.selective_scan(t["x"], t["delta"], t["A"], Bs, Cs)
     torch.cuda.synchronize()
     assert_parity(host64(y), oracle_scan(g), "bf16", "unaligned rows")
+
+
+def test_unaligned_x_takes_the_one_chain_per_lane_path():
+    """x and delta at an odd element offset: paired channel loads are not
+    aligned, so the launcher falls back to one chain per lane (even D)."""
+    g = workloads.generate("mid_bf16", batch=2, L=300, D=128, N=16, seed=6)
+    t = inputs_on_device(g)
+    shifted = {}
+    for k in ("x", "delta"):
+        buf = torch.empty(t[k].numel() + 1, dtype=torch.bfloat16, device="cuda")
+        v = buf[1:].view(t[k].shape)
+        v.copy_(t[k])
+        shifted[k] = v
+    assert shifted["x"].data_ptr() % 4 == 2
+    y = mssm.selective_scan(shifted["x"], shifted["delta"], t["A"], t["B"], t["C"])
+    torch.cuda.synchronize()
+    ref = mssm.selective_scan(t["x"], t["delta"], t["A"], t["B"], t["C"])
+    torch.cuda.synchronize()
+    assert_parity(host64(y), oracle_scan(g), "bf16", "unaligned x")
+    assert_parity(host64(ref), oracle_scan(g), "bf16", "aligned x")
 
 
 def test_binding_rejects_bad_tensors():
