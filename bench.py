@@ -34,7 +34,7 @@ VALU_LANE_SLOTS_PER_S = 256 * 4 * 16 * 2.4e9
 SLOTS_PER_ELEMENT = 6
 ELEM_PEAK_GPS = VALU_LANE_SLOTS_PER_S / SLOTS_PER_ELEMENT / 1e9
 HEADLINE = "mamba130m_layer_fp32"
-OTHERS = ["tiny_fp32", "mid_bf16", "long_seq_bf16"]
+OTHERS = ["tiny_fp32", "mid_bf16", "long_seq_bf16", "fused_proj_bf16"]
 
 
 def algorithmic_bytes(w) -> int:
@@ -111,6 +111,45 @@ def time_workload(name, steps, warmup, rotate, torch, mssm, workloads):
     kms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
     kernel_ms = sum(kms) / len(kms)
     del sets, ws
+    torch.cuda.empty_cache()
+    return w, wall, kernel_ms
+
+
+def time_fused(name, steps, warmup, torch, mssm, workloads):
+    """The fused path: x_proj GEMM, dt_low split, W_dt transpose, and the fused
+    summary / carry / output scan kernels, per step."""
+    import numpy as np
+    w = workloads.workload(name)
+    g = workloads.generate(name)
+    d = {}
+    for k in ("x", "W_x", "W_dt", "dt_bias", "A"):
+        a = np.ascontiguousarray(g[k])
+        t = torch.from_numpy(a.view(np.int16)).view(torch.bfloat16) if a.dtype == np.uint16 \
+            else torch.from_numpy(a)
+        d[k] = t.cuda()
+    del g
+    y = torch.empty(d["x"].shape, dtype=torch.float32, device="cuda")
+    nb = mssm.mssm_selective_ssm_fused_workspace_size(w.batch, w.L, w.D, w.N, w.R, torch.bfloat16)
+    ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+
+    def step():
+        mssm.mssm_selective_ssm_fused_fwd(d["x"], d["W_x"], d["W_dt"], d["dt_bias"], d["A"], y, ws)
+
+    for _ in range(warmup):
+        step()
+    stream = torch.cuda.current_stream()
+    s_ev = torch.cuda.Event(enable_timing=True)
+    e_ev = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    s_ev.record(stream)
+    for _ in range(steps):
+        step()
+    e_ev.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kernel_ms = s_ev.elapsed_time(e_ev) / steps
+    del d, y, ws
     torch.cuda.empty_cache()
     return w, wall, kernel_ms
 
@@ -216,7 +255,10 @@ def main(argv=None):
         for name in OTHERS:
             if name == w.name:
                 continue
-            wo, wall_o, kms_o = time_workload(name, 5, 2, 1, torch, mssm, workloads)
+            if workloads.workload(name).fused:
+                wo, wall_o, kms_o = time_fused(name, 5, 2, torch, mssm, workloads)
+            else:
+                wo, wall_o, kms_o = time_workload(name, 5, 2, 1, torch, mssm, workloads)
             nbo = algorithmic_bytes(wo)
             others[name] = {
                 "ms_per_step": round(wall_o * 1e3 / 5, 4),
@@ -227,6 +269,11 @@ def main(argv=None):
                 "Gelem/s": round(elements(wo) / (kms_o * 1e-3) / 1e9, 1),
                 "alu_frac": round(elements(wo) / (kms_o * 1e-3) / 1e9 / ELEM_PEAK_GPS, 4),
             }
+            if wo.fused:
+                flops = 2 * wo.batch * wo.L * (wo.D * (wo.R + 2 * wo.N) + wo.R * wo.D)
+                others[name]["projection_TFLOPs"] = round(flops / 1e12, 2)
+                others[name]["note"] = ("bytes by the scan formula (x + Delta + y, B + C); Delta, B, "
+                                        "C are formed on chip from x and the weights")
         line["workloads"] = others
     if not args.no_cpu_baseline:
         import oracle

@@ -117,6 +117,44 @@ mssm_status mssm_selective_scan_fwd_ws(const void *x, const void *delta, const f
                                        int64_t batch, int64_t L, int64_t D, int64_t N,
                                        mssm_dtype dtype, void *stream);
 
+/*
+ * ---- fused selective SSM: selection projections + scan ----------------------------------
+ *
+ * The selection mechanism of "Understanding Mamba" (section 5.1, eq. (6)) in
+ * the low-rank Mamba shape: each token x_t (D values) is projected by
+ * W_xproj [D, R + 2N] to [dt_low (R) | B_t (N) | C_t (N)] (in that order;
+ * weights are [in, out], i.e. P = x @ W_xproj); Delta_t = softplus(dt_low @
+ * W_dtproj + dt_bias) with W_dtproj [R, D] and one bias per channel
+ * (softplus as in section 5.1); then the scan above runs on (x, Delta, A, B,
+ * C).  x, W_xproj, W_dtproj are bfloat16; dt_bias, A and y are float32.
+ * The projection is accumulated in float32; dt_proj runs on the bf16 matrix
+ * cores with dt_low split into two bfloat16 parts (hi = bf16(dt_low),
+ * lo = bf16(dt_low - hi)), i.e. dt_low kept to about 16 significant bits, and
+ * float32 accumulation; B, C and the pre-softplus values stay float32.  Delta
+ * is formed on chip and never written to memory.
+ *
+ * Supported: dtype MSSM_BFLOAT16 only (MSSM_FLOAT32 -> NOT_SUPPORTED); N in
+ * the scan's set; R a multiple of 16 in [16, 1024]; batch*L and D below 2^31.
+ * The workspace must be 256-byte aligned and at least
+ * mssm_selective_ssm_fused_workspace_size bytes; it is always required (the
+ * projection lands there).  The first call on a device creates a rocBLAS
+ * handle for that device, kept until the process exits.
+ */
+
+/* 1 if the fused path is built for state size N and rank R, else 0. */
+int mssm_fused_supports(int64_t N, int64_t R);
+
+mssm_status mssm_selective_ssm_fused_workspace_size(int64_t batch, int64_t L, int64_t D,
+                                                    int64_t N, int64_t R, mssm_dtype dtype,
+                                                    size_t *bytes);
+
+mssm_status mssm_selective_ssm_fused_fwd(const void *x, const void *W_xproj,
+                                         const void *W_dtproj, const float *dt_bias,
+                                         const float *A, float *y, void *workspace,
+                                         size_t workspace_bytes, int64_t batch, int64_t L,
+                                         int64_t D, int64_t N, int64_t R, mssm_dtype dtype,
+                                         void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -47,9 +47,9 @@ def fused_projections(x, W_x, W_dt, dt_bias, *, R: int, N: int, dt_low_bf16: boo
     """Return (delta, B, C) from the token projections, all float64.
 
     x: [batch, L, D]; W_x: [D, R + 2N]; W_dt: [R, D]; dt_bias: [D].
-    ``dt_low_bf16`` rounds dt_low to bfloat16 before dt_proj (the GPU path feeds
-    dt_low to bf16 matrix cores and rounds it there); B, C and the pre-softplus
-    value are kept unrounded.
+    ``dt_low_bf16`` rounds dt_low to bfloat16 before dt_proj (kept as an option;
+    the GPU path carries dt_low to about 16 significant bits, so parity runs
+    with it off); B, C and the pre-softplus value are kept unrounded.
     """
     x = np.asarray(x, dtype=np.float64)
     batch, L, D = x.shape
@@ -82,7 +82,6 @@ def selective_ssm_fused(x, W_x, W_dt, dt_bias, A, *, R: int, bbar: str = "euler"
     Pinned by the selective worked example of "Understanding Mamba" section 5.3
     (one channel, R = 1: Delta_t = softplus(2 x_t), B_t = C_t = 0.4 x_t) and by
     the reduction to the plain scan when W_dt = 0 (Delta = softplus(bias)).
-    The bf16 rounding of dt_low is a reading of the GPU design, not of the pages.
     """
     A = np.asarray(A)
     N = A.shape[1]

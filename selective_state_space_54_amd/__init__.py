@@ -9,9 +9,13 @@ from .mssm import (  # noqa: F401
     exported_symbols,
     load,
     mssm_abi_version,
+    mssm_fused_supports,
+    mssm_selective_ssm_fused_fwd,
+    mssm_selective_ssm_fused_workspace_size,
     mssm_selective_scan_fwd,
     mssm_selective_scan_fwd_ws,
     mssm_selective_scan_workspace_size,
     mssm_supports_state_size,
     selective_scan,
+    selective_ssm_fused,
 )

@@ -137,4 +137,70 @@ mssm_status mssm_selective_scan_fwd(const void* x, const void* delta, const floa
   return MSSM_SUCCESS;
 }
 
+int mssm_fused_supports(int64_t N, int64_t R) {
+  return (mssm::state_size_supported(N) && R >= 16 && R <= 1024 && R % 16 == 0) ? 1 : 0;
+}
+
+}  // extern "C"
+
+namespace {
+
+mssm_status check_fused(int64_t batch, int64_t L, int64_t D, int64_t N, int64_t R,
+                        mssm_dtype dtype) {
+  if (batch < 0 || L < 0 || D < 0 || N < 0 || R < 0) return MSSM_ERROR_INVALID_VALUE;
+  if (dtype != MSSM_FLOAT32 && dtype != MSSM_BFLOAT16) return MSSM_ERROR_INVALID_VALUE;
+  if (dtype != MSSM_BFLOAT16) return MSSM_ERROR_NOT_SUPPORTED;    // matrix cores take bf16
+  if (!mssm_fused_supports(N, R)) return MSSM_ERROR_NOT_SUPPORTED;
+  const mssm_status s = check_shape(batch, L, D, N, dtype);
+  if (s != MSSM_SUCCESS) return s;
+  int64_t m, t;
+  if (!mul_ok(batch, L, &m) || !mul_ok(m, R + 2 * N, &t) || !mul_ok(t, 8, &t))
+    return MSSM_ERROR_SIZE_OVERFLOW;
+  if (m > std::numeric_limits<int32_t>::max() || D > std::numeric_limits<int32_t>::max())
+    return MSSM_ERROR_NOT_SUPPORTED;                               // 32-bit GEMM sizes
+  return MSSM_SUCCESS;
+}
+
+}  // namespace
+
+extern "C" {
+
+mssm_status mssm_selective_ssm_fused_workspace_size(int64_t batch, int64_t L, int64_t D,
+                                                    int64_t N, int64_t R, mssm_dtype dtype,
+                                                    size_t* bytes) {
+  if (!bytes) return MSSM_ERROR_INVALID_VALUE;
+  const mssm_status s = check_fused(batch, L, D, N, R, dtype);
+  if (s != MSSM_SUCCESS) return s;
+  *bytes = empty_problem(batch, L, D) ? 0 : mssm::fused_workspace_bound(batch, L, D, N, R);
+  return MSSM_SUCCESS;
+}
+
+mssm_status mssm_selective_ssm_fused_fwd(const void* x, const void* W_xproj, const void* W_dtproj,
+                                         const float* dt_bias, const float* A, float* y,
+                                         void* workspace, size_t workspace_bytes, int64_t batch,
+                                         int64_t L, int64_t D, int64_t N, int64_t R,
+                                         mssm_dtype dtype, void* stream) {
+  mssm_status s = check_fused(batch, L, D, N, R, dtype);
+  if (s != MSSM_SUCCESS) return s;
+  if (empty_problem(batch, L, D)) return MSSM_SUCCESS;
+  if (!x || !W_xproj || !W_dtproj || !dt_bias || !A || !y) return MSSM_ERROR_INVALID_VALUE;
+  const mssm::FusedPlan plan = mssm::plan_fused(batch, L, D, N, R, mssm::choose_fused_cpl(D));
+  s = check_grid(plan.scan, batch, D, N);
+  if (s != MSSM_SUCCESS) return s;
+  if (!workspace || workspace_bytes < plan.workspace_bytes) return MSSM_ERROR_WORKSPACE;
+  if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return MSSM_ERROR_WORKSPACE;
+  const mssm::FusedArgs a{x, W_xproj, W_dtproj, dt_bias, A, y, batch, L, D, N, R};
+  const mssm::FusedStatus st = mssm::launch_fused(a, plan, workspace,
+                                                  static_cast<hipStream_t>(stream));
+  if (st.blas_failed) {
+    std::snprintf(g_last_error, sizeof(g_last_error), "rocBLAS x_proj GEMM failed");
+    return MSSM_ERROR_HIP;
+  }
+  if (st.hip != hipSuccess) {
+    set_hip_error(st.hip, "fused selective SSM launch");
+    return MSSM_ERROR_HIP;
+  }
+  return MSSM_SUCCESS;
+}
+
 }  // extern "C"

@@ -56,4 +56,44 @@ hipError_t launch_scan(const ScanArgs& a, const ScanPlan& plan, void* workspace,
 
 bool state_size_supported(int64_t N);
 
+// The carry pass over chunk summaries (shared by the plain and fused paths).
+hipError_t launch_carry(float* sum_h, const float* sum_p, int64_t batch, int64_t D, int64_t N,
+                        int K, hipStream_t stream);
+
+// ---- fused projections + scan ------------------------------------------------------------
+
+struct FusedArgs {
+  const void* x;        // [batch, L, D] bf16
+  const void* W_x;      // [D, R + 2N] bf16
+  const void* W_dt;     // [R, D] bf16
+  const float* dt_bias; // [D]
+  const float* A;       // [D, N]
+  float* y;             // [batch, L, D]
+  int64_t batch, L, D, N, R;
+};
+
+// Workspace: P = x @ W_x (float32 [batch*L, R+2N]), dt_low as bf16 hi and lo
+// parts ([batch*L, R] each), W_dt^T (bf16 [D, R]), then the scan's chunk
+// summaries.
+struct FusedPlan {
+  ScanPlan scan;
+  size_t p_bytes = 0;
+  size_t dtl_offset = 0;
+  size_t dtl_lo_offset = 0;
+  size_t wt_offset = 0;
+  size_t scan_offset = 0;
+  size_t workspace_bytes = 0;
+};
+
+struct FusedStatus {
+  hipError_t hip = hipSuccess;
+  bool blas_failed = false;
+};
+
+FusedPlan plan_fused(int64_t batch, int64_t L, int64_t D, int64_t N, int64_t R, int cpl);
+size_t fused_workspace_bound(int64_t batch, int64_t L, int64_t D, int64_t N, int64_t R);
+int choose_fused_cpl(int64_t D);
+FusedStatus launch_fused(const FusedArgs& a, const FusedPlan& f, void* workspace,
+                         hipStream_t stream);
+
 }  // namespace mssm

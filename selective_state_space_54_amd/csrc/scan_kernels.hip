@@ -179,6 +179,15 @@ static size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 // Two chains per lane pay off for bfloat16 inputs (one 32-bit load brings both
 // channels' x and delta; MI355X sweeps: about 10-13% faster), not for float32
 // (register pressure lowers occupancy more than the extra ILP gains).
+hipError_t launch_carry(float* sum_h, const float* sum_p, int64_t batch, int64_t D, int64_t N,
+                        int K, hipStream_t stream) {
+  const int64_t carry_tiles = (D + kBlock - 1) / kBlock;
+  const int64_t cgrid = carry_tiles * N * batch;
+  hipLaunchKernelGGL(chunk_carry_kernel, dim3((unsigned)cgrid), dim3(kBlock), 0, stream, sum_h,
+                     sum_p, D, static_cast<int>(N), K, carry_tiles);
+  return hipGetLastError();
+}
+
 int default_cpl(int64_t D, mssm_dtype dtype) {
   if (const char* env = std::getenv("MSSM_CPL")) {       // tuning experiments only
     const int v = std::atoi(env);
@@ -261,11 +270,7 @@ static hipError_t launch_typed(const ScanArgs& a, const ScanPlan& p, void* ws, h
                        p.chunk_len, p.K, n_dtiles);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int64_t carry_tiles = (a.D + kBlock - 1) / kBlock;
-    const int64_t cgrid = carry_tiles * N * a.batch;
-    hipLaunchKernelGGL(chunk_carry_kernel, dim3((unsigned)cgrid), dim3(kBlock), 0, stream, sum_h,
-                       sum_p, a.D, N, p.K, carry_tiles);
-    e = hipGetLastError();
+    e = launch_carry(sum_h, sum_p, a.batch, a.D, N, p.K, stream);
     if (e != hipSuccess) return e;
   }
   const int64_t grid = n_dtiles * p.K * a.batch;

@@ -40,6 +40,13 @@ _SIGNATURES = {
     "mssm_selective_scan_fwd_ws": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                                   ctypes.c_size_t, _i64, _i64, _i64, _i64,
                                                   ctypes.c_int, _vp]),
+    "mssm_fused_supports": (ctypes.c_int, [_i64, _i64]),
+    "mssm_selective_ssm_fused_workspace_size": (ctypes.c_int, [_i64, _i64, _i64, _i64, _i64,
+                                                               ctypes.c_int,
+                                                               ctypes.POINTER(ctypes.c_size_t)]),
+    "mssm_selective_ssm_fused_fwd": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                                    ctypes.c_size_t, _i64, _i64, _i64, _i64,
+                                                    _i64, ctypes.c_int, _vp]),
 }
 
 
@@ -175,3 +182,59 @@ def selective_scan(x, delta, A, B, C, *, stream=None):
     nbytes = mssm_selective_scan_workspace_size(batch, L, D, N, x.dtype)
     ws = torch.empty(nbytes, dtype=torch.uint8, device=x.device) if nbytes else None
     return mssm_selective_scan_fwd_ws(x, delta, A, B, C, y, ws, stream=stream)
+
+
+# ---- fused selective SSM (projections + scan) ----------------------------------------------
+
+def mssm_fused_supports(N: int, R: int) -> bool:
+    return bool(load().mssm_fused_supports(N, R))
+
+
+def mssm_selective_ssm_fused_workspace_size(batch: int, L: int, D: int, N: int, R: int,
+                                            dtype: torch.dtype) -> int:
+    out = ctypes.c_size_t(0)
+    _check(load().mssm_selective_ssm_fused_workspace_size(batch, L, D, N, R, _dtype_code(dtype),
+                                                          ctypes.byref(out)),
+           "mssm_selective_ssm_fused_workspace_size")
+    return out.value
+
+
+def _check_fused_args(x, W_x, W_dt, dt_bias, A, y):
+    batch, L, D, N = _scan_shapes(x, A)
+    if W_dt.dim() != 2:
+        raise ValueError("W_dt must be [R, D]")
+    R = W_dt.shape[0]
+    _dtype_code(x.dtype)
+    dev = x.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a GPU device")
+    _dense(x, "x", x.dtype, (batch, L, D), dev)
+    _dense(W_x, "W_x", x.dtype, (D, R + 2 * N), dev)
+    _dense(W_dt, "W_dt", x.dtype, (R, D), dev)
+    _dense(dt_bias, "dt_bias", torch.float32, (D,), dev)
+    _dense(A, "A", torch.float32, (D, N), dev)
+    _dense(y, "y", torch.float32, (batch, L, D), dev)
+    return batch, L, D, N, R
+
+
+def mssm_selective_ssm_fused_fwd(x, W_x, W_dt, dt_bias, A, y, workspace, *, stream=None):
+    """y <- scan(x, softplus(x_proj(x)[:R] @ W_dt + dt_bias), A, B, C) with B, C the
+    remaining x_proj outputs; workspace is a uint8 device tensor."""
+    batch, L, D, N, R = _check_fused_args(x, W_x, W_dt, dt_bias, A, y)
+    ws_ptr = _ptr(workspace) if workspace is not None and workspace.numel() > 0 else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(load().mssm_selective_ssm_fused_fwd(
+        _ptr(x), _ptr(W_x), _ptr(W_dt), _ptr(dt_bias), _ptr(A), _ptr(y), ws_ptr, ws_bytes,
+        batch, L, D, N, R, _dtype_code(x.dtype), _stream_handle(stream)),
+        "mssm_selective_ssm_fused_fwd")
+    return y
+
+
+def selective_ssm_fused(x, W_x, W_dt, dt_bias, A, *, stream=None):
+    """Allocate y and the workspace with torch, then run mssm_selective_ssm_fused_fwd."""
+    batch, L, D, N = _scan_shapes(x, A)
+    R = W_dt.shape[0]
+    y = torch.empty(x.shape, dtype=torch.float32, device=x.device)
+    nbytes = mssm_selective_ssm_fused_workspace_size(batch, L, D, N, R, x.dtype)
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=x.device)
+    return mssm_selective_ssm_fused_fwd(x, W_x, W_dt, dt_bias, A, y, ws, stream=stream)

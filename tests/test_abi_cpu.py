@@ -100,3 +100,38 @@ def test_workspace_too_small_is_rejected(lib):
     assert r == 4
     r = lib.mssm_selective_scan_fwd_ws(*([FAKE] * 6), None, 0, 8, 2048, 1536, 16, 0, None)
     assert r == 4
+
+
+def _fws(lib, *args):
+    out = ctypes.c_size_t(12345)
+    st = lib.mssm_selective_ssm_fused_workspace_size(*args, ctypes.byref(out))
+    return st, out.value
+
+
+def test_fused_support_and_workspace_queries(lib):
+    assert lib.mssm_fused_supports(16, 160) == 1
+    assert lib.mssm_fused_supports(16, 20) == 0            # R must be a multiple of 16
+    assert lib.mssm_fused_supports(3, 160) == 0
+    st, nbytes = _fws(lib, 16, 2048, 5120, 16, 160, 1)
+    assert st == 0 and nbytes > 16 * 2048 * 192 * 4        # holds the projection
+    assert _fws(lib, 16, 2048, 5120, 16, 160, 0)[0] == 2    # float32: not supported
+    assert _fws(lib, 1, 64, 64, 16, 20, 1)[0] == 2
+    assert _fws(lib, -1, 64, 64, 16, 16, 1)[0] == 1
+    assert _fws(lib, 0, 64, 64, 16, 16, 1) == (0, 0)
+
+
+def test_fused_argument_errors(lib):
+    def call(ptrs, ws, wsb, batch, L, D, N, R, dtype=1):
+        return lib.mssm_selective_ssm_fused_fwd(*ptrs, ws, wsb, batch, L, D, N, R, dtype, None)
+    p6 = [FAKE] * 6
+    assert call(p6, FAKE, 1 << 40, 1, 64, 64, 16, 20) == 2
+    assert call(p6, FAKE, 1 << 40, 1, 64, 64, 16, 16, dtype=0) == 2
+    assert call(p6, FAKE, 1 << 40, -1, 64, 64, 16, 16) == 1
+    for i in range(6):
+        ptrs = list(p6)
+        ptrs[i] = None
+        assert call(ptrs, FAKE, 1 << 40, 1, 64, 64, 16, 16) == 1
+    st, nbytes = _fws(lib, 1, 64, 64, 16, 16, 1)
+    assert call(p6, FAKE, nbytes - 1, 1, 64, 64, 16, 16) == 4
+    assert call(p6, None, 0, 1, 64, 64, 16, 16) == 4
+    assert call([None] * 6, None, 0, 0, 64, 64, 16, 16) == 0   # empty problem
