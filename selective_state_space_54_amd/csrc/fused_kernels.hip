@@ -115,8 +115,8 @@ __device__ __forceinline__ void fused_steps(const uint16_t* __restrict__ xb,
                                             int64_t ldbc, float* __restrict__ yb,
                                             const float (&A2)[CPL][N], float (&h)[CPL][N],
                                             double (&S)[CPL], int wlane, int wave_ch0, int ch_valid,
-                                            int64_t D, int nsteps, bool active,
-                                            float* __restrict__ lds, int stride) {
+                                            int64_t D, int nsteps, float* __restrict__ lds,
+                                            int stride) {
   constexpr int kTile = (CPL == 1) ? 8 : 4;
   const uint32_t in_bytes = static_cast<uint32_t>((int64_t)nsteps * D * sizeof(uint16_t));
   const buf_t xr = make_buf(xb, in_bytes);
@@ -158,6 +158,7 @@ __device__ __forceinline__ void fused_steps(const uint16_t* __restrict__ xb,
       const int s = base + j;
       if (s < nsteps) {
         const int cur = j & 1;
+        wait_scalar_loads();
         if (s + 1 < nsteps) {
           load_row<N>(Bb + (int64_t)(s + 1) * ldbc, Bv[cur ^ 1]);
           if constexpr (kWithY) load_row<N>(Cb + (int64_t)(s + 1) * ldbc, Cv[cur ^ 1]);
@@ -176,11 +177,13 @@ __device__ __forceinline__ void fused_steps(const uint16_t* __restrict__ xb,
           for (int c = 0; c < CPL; ++c) {
             const float a = fast_exp2(dt[c] * A2[c][n]);
             h[c][n] = __builtin_fmaf(a, h[c][n], dx[c] * Bv[cur][n]);
-            if constexpr (kWithY) yv[c] = __builtin_fmaf(Cv[cur][n], h[c][n], yv[c]);
+            if constexpr (kWithY) yv[c] = __builtin_fmaf(Cv[cur][n], h[c][n], yv[c]);  // C . h
           }
         }
         if constexpr (kWithY) {
-          if (active) buf_store_vals<CPL>(yr, out_lane, s * out_row, yv);
+          // lanes past the last channel repeat the last valid channel (clamped
+          // addressing), so they store the same value to the same place
+          buf_store_vals<CPL>(yr, out_lane, s * out_row, yv);
         } else {
 #pragma unroll
           for (int c = 0; c < CPL; ++c) S[c] += static_cast<double>(dt[c]);
@@ -259,7 +262,7 @@ __global__ __launch_bounds__(kFBlock) void fused_summary_kernel(
   fused_steps<N, CPL, false>(x + tok0 * D + c.d0, dtlow + tok0 * R, dtlow_lo + tok0 * R,
                              wT + wave_d * R, bias + wave_d,
                              R, P + tok0 * ldbc + R, nullptr, ldbc, nullptr, A2, h, S, c.wlane,
-                             c.wave_ch0, c.ch_valid, D, nsteps, c.active, lds, lds_stride<CPL>());
+                             c.wave_ch0, c.ch_valid, D, nsteps, lds, lds_stride<CPL>());
   if (c.active) {
     const int64_t row = c.b * (K - 1) + c.k;
 #pragma unroll
@@ -313,7 +316,7 @@ __global__ __launch_bounds__(kFBlock) void fused_output_kernel(
                             wT + wave_d * R, bias + wave_d,
                             R, P + tok0 * ldbc + R, P + tok0 * ldbc + R + N, ldbc,
                             y + tok0 * D + c.d0, A2, h, S_unused, c.wlane, c.wave_ch0, c.ch_valid,
-                            D, nsteps, c.active, lds, lds_stride<CPL>());
+                            D, nsteps, lds, lds_stride<CPL>());
 }
 
 __device__ __forceinline__ uint16_t bf16_rne(float f) {

@@ -65,6 +65,14 @@ __device__ __forceinline__ void load_row_any(const uint16_t* __restrict__ p, flo
 // exp2 on the transcendental unit (v_exp_f32).
 __device__ __forceinline__ float fast_exp2(float v) { return __builtin_amdgcn_exp2f(v); }
 
+// Wait until every scalar-memory (and LDS) access issued so far has returned:
+// s_waitcnt lgkmcnt(0), with the vector-memory and export counters left at
+// their maximum (gfx9 encoding).  Scalar loads can return out of order, so
+// the only usable wait is "all of them": the step loop waits here for the
+// current step's B_t/C_t *before* issuing the next step's loads, so the next
+// loads overlap the current step's arithmetic instead of being waited for.
+__device__ __forceinline__ void wait_scalar_loads() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
 // ---- buffer (descriptor-based) access ------------------------------------------------------
 //
 // A buffer resource holds a wave-uniform base address and a byte limit; each
@@ -132,7 +140,7 @@ __device__ __forceinline__ void scan_steps(const T* __restrict__ xb, const T* __
                                            const T* __restrict__ Bb, const T* __restrict__ Cb,
                                            float* __restrict__ yb, const float (&A2)[CPL][N],
                                            float (&h)[CPL][N], double (&S)[CPL], int lane,
-                                           int64_t D, int nsteps, bool active) {
+                                           int64_t D, int nsteps) {
   constexpr int kTile = (CPL == 1) ? 8 : 4;
   static_assert(kTile % 2 == 0, "alternating B/C register sets need an even tile");
   const uint32_t in_bytes = static_cast<uint32_t>((int64_t)nsteps * D * sizeof(T));
@@ -175,6 +183,7 @@ __device__ __forceinline__ void scan_steps(const T* __restrict__ xb, const T* __
       const int s = base + j;
       if (s < nsteps) {
         const int cur = j & 1;
+        wait_scalar_loads();
         if (s + 1 < nsteps) {
           load_row_any<N, kPairs>(Bb + (int64_t)(s + 1) * N, Bv[cur ^ 1]);
           if constexpr (kWithY) load_row_any<N, kPairs>(Cb + (int64_t)(s + 1) * N, Cv[cur ^ 1]);
@@ -195,7 +204,9 @@ __device__ __forceinline__ void scan_steps(const T* __restrict__ xb, const T* __
           }
         }
         if constexpr (kWithY) {
-          if (active) buf_store_vals<CPL>(yr, out_lane, s * out_row, yv);
+          // lanes past the last channel repeat the last valid channel (clamped
+          // addressing), so they store the same value to the same place
+          buf_store_vals<CPL>(yr, out_lane, s * out_row, yv);
         } else {
 #pragma unroll
           for (int c = 0; c < CPL; ++c) S[c] += static_cast<double>(dc[j][c]);

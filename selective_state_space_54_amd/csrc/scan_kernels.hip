@@ -79,7 +79,7 @@ __global__ __launch_bounds__(kBlock) void chunk_summary_kernel(
   const int nsteps = static_cast<int>(chunk_len);   // chunks before the last are full
   const int64_t row0 = (c.b * L + t0) * D + c.d0;
   scan_steps<N, CPL, T, kPairs, false>(x + row0, delta + row0, Bm + (c.b * L + t0) * N, nullptr,
-                                       nullptr, A2, h, S, c.lane, D, nsteps, c.active);
+                                       nullptr, A2, h, S, c.lane, D, nsteps);
   if (c.active) {
     const int64_t row = c.b * (K - 1) + c.k;
 #pragma unroll
@@ -167,7 +167,7 @@ __global__ __launch_bounds__(kBlock) void chunk_output_kernel(
   const int64_t row0 = (c.b * L + t0) * D + c.d0;
   scan_steps<N, CPL, T, kPairs, true>(x + row0, delta + row0, Bm + (c.b * L + t0) * N,
                                       Cm + (c.b * L + t0) * N, y + row0, A2, h, S_unused, c.lane,
-                                      D, nsteps, c.active);
+                                      D, nsteps);
 }
 
 bool state_size_supported(int64_t N) {

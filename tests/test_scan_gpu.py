@@ -122,12 +122,19 @@ def test_impulse_survives_every_chunk_carry(chunk_len):
 
 
 def test_delta_limits():
-    """Delta -> 0 keeps the state (skip); Delta |A| >= 100 forgets it (reset)."""
+    """Delta -> 0 keeps the state (skip); Delta |A| >= 100 forgets it (reset).
+
+    On the reset tokens x is divided by Delta, so the new state Delta B x keeps
+    the workload's magnitude: with unit x the state, and the terms C_n h_n that
+    y sums, would be ~150 times larger than y itself, and float32 rounding of
+    those terms alone could exceed a bound that is relative to |y|."""
     g = workloads.generate("mamba130m_layer_fp32", batch=2, L=300, D=128, N=16, seed=7)
     d = g["delta"].copy()
+    x = g["x"].copy()
     d[:, 50:120, :] = 1e-8
     d[:, 200:210, :] = 150.0
-    g["delta"] = d
+    x[:, 200:210, :] /= np.float32(150.0)
+    g["delta"], g["x"] = d, x
     y = run_scan(g)
     assert_parity(host64(y), oracle_scan(g), "fp32", "delta limits")
 
