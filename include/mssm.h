@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define MSSM_ABI_VERSION 1
+#define MSSM_ABI_VERSION 2
 
 typedef enum {
     MSSM_SUCCESS = 0,
@@ -74,6 +74,15 @@ typedef enum {
     MSSM_FLOAT32 = 0,
     MSSM_BFLOAT16 = 1
 } mssm_dtype;
+
+/* Form of the discretised input term Bbar (Abar = exp(delta A) in both). */
+typedef enum {
+    MSSM_BBAR_EULER = 0,   /* first order, Bbar = delta * B (the default form)      */
+    MSSM_BBAR_ZOH = 1      /* exact zero-order hold, Bbar = (Abar - 1) / A * B,
+                              "Understanding Mamba" eq. (2) for a diagonal A.
+                              Needs every A[d, n] nonzero (a zero entry gives NaN
+                              in that channel); stable A is negative anyway.    */
+} mssm_bbar;
 
 /* ABI version of the loaded library (MSSM_ABI_VERSION it was built with). */
 int mssm_abi_version(void);
@@ -116,6 +125,62 @@ mssm_status mssm_selective_scan_fwd_ws(const void *x, const void *delta, const f
                                        void *workspace, size_t workspace_bytes,
                                        int64_t batch, int64_t L, int64_t D, int64_t N,
                                        mssm_dtype dtype, void *stream);
+
+/*
+ * ---- the scan with its optional parts: input-term form, feedthrough, gate, state ---------
+ *
+ * mssm_selective_scan_fwd_ex computes, per chain (b, d), starting from
+ * h = h0[b, d, :] (zero when h0 is NULL):
+ *     h        = Abar * h + Bbar * x[b,t,d]     Bbar per `bbar` (see mssm_bbar)
+ *     out      = C[b,t,:] . h + Dskip[d] * x[b,t,d]
+ *                  (feedthrough: "Understanding Mamba" eq. (1)/(3), section
+ *                   2.1 explains it is a separate term added after the read-out;
+ *                   omitted when Dskip is NULL)
+ *     y[b,t,d] = out * SiLU(z[b,t,d])           SiLU(v) = v / (1 + exp(-v)), the
+ *                  gate of the Mamba block ("Understanding Mamba", section 8.1,
+ *                  eq. (9)); omitted when z is NULL
+ * and, when h_last is not NULL, writes the state after the last step to
+ * h_last[b, d, :].  Passing h_last of one call as h0 of the next continues
+ * the sequence (the state summarises the whole past, section 3.2), so a long
+ * sequence can be processed in pieces.
+ *
+ *   Dskip  : [D] float32 or NULL
+ *   z      : [batch, L, D] of `dtype` or NULL
+ *   h0     : [batch, D, N] float32 (n fastest) or NULL
+ *   h_last : [batch, D, N] float32 or NULL; must not overlap h0 or any
+ *            other argument (chunks of the sequence run concurrently, so the
+ *            last chunk may finish before the first has read h0)
+ *   workspace: as mssm_selective_scan_fwd_ws (same size query).
+ * With L == 0 and batch, D > 0 the call only sets h_last = h0 (or zero).
+ * An invalid `bbar` gives MSSM_ERROR_INVALID_VALUE.
+ */
+mssm_status mssm_selective_scan_fwd_ex(const void *x, const void *delta, const float *A,
+                                       const void *B, const void *C, const float *Dskip,
+                                       const void *z, const float *h0, float *y, float *h_last,
+                                       mssm_bbar bbar, void *workspace, size_t workspace_bytes,
+                                       int64_t batch, int64_t L, int64_t D, int64_t N,
+                                       mssm_dtype dtype, void *stream);
+
+/*
+ * One recurrent step (decode): the constant-cost-per-token form of
+ * "Understanding Mamba" (section 3.2, section 9.1), for every (b, d):
+ *     h[b,d,:] = Abar * h[b,d,:] + Bbar * x[b,d]     (in place)
+ *     y[b,d]   = (C[b,:] . h[b,d,:] + Dskip[d] x[b,d]) * SiLU(z[b,d])
+ * with Abar, Bbar as in the scan (`bbar` selects the form), i.e. exactly one
+ * step of mssm_selective_scan_fwd_ex with h0 = h_last = h.
+ *
+ *   x, delta, z : [batch, D] of `dtype` (z may be NULL)
+ *   B, C        : [batch, N] of `dtype`
+ *   A           : [D, N] float32;  Dskip : [D] float32 or NULL
+ *   h           : [batch, D, N] float32, read and overwritten
+ *   y           : [batch, D] float32
+ * Needs no workspace.  batch or D equal to zero is a no-op.
+ */
+mssm_status mssm_selective_scan_step(const void *x, const void *delta, const float *A,
+                                     const void *B, const void *C, const float *Dskip,
+                                     const void *z, float *h, float *y, mssm_bbar bbar,
+                                     int64_t batch, int64_t D, int64_t N, mssm_dtype dtype,
+                                     void *stream);
 
 /*
  * ---- fused selective SSM: selection projections + scan ----------------------------------

@@ -13,9 +13,13 @@ from .mssm import (  # noqa: F401
     mssm_selective_ssm_fused_fwd,
     mssm_selective_ssm_fused_workspace_size,
     mssm_selective_scan_fwd,
+    mssm_selective_scan_fwd_ex,
     mssm_selective_scan_fwd_ws,
+    mssm_selective_scan_step,
     mssm_selective_scan_workspace_size,
     mssm_supports_state_size,
     selective_scan,
+    selective_scan_ex,
+    selective_scan_step,
     selective_ssm_fused,
 )

@@ -411,7 +411,7 @@ static hipError_t launch_fused_scan(const FusedArgs& a, const FusedPlan& f, char
                        n_dtiles);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    e = launch_carry(sum_h, sum_p, a.batch, a.D, a.N, p.K, stream);
+    e = launch_carry(sum_h, sum_p, nullptr, a.batch, a.D, a.N, p.K, stream);
     if (e != hipSuccess) return e;
   }
   const int64_t grid = n_dtiles * p.K * a.batch;

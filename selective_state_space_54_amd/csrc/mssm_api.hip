@@ -137,6 +137,71 @@ mssm_status mssm_selective_scan_fwd(const void* x, const void* delta, const floa
   return MSSM_SUCCESS;
 }
 
+mssm_status mssm_selective_scan_fwd_ex(const void* x, const void* delta, const float* A,
+                                       const void* B, const void* C, const float* Dskip,
+                                       const void* z, const float* h0, float* y, float* h_last,
+                                       mssm_bbar bbar, void* workspace, size_t workspace_bytes,
+                                       int64_t batch, int64_t L, int64_t D, int64_t N,
+                                       mssm_dtype dtype, void* stream) {
+  mssm_status s = check_shape(batch, L, D, N, dtype);
+  if (s != MSSM_SUCCESS) return s;
+  if (bbar != MSSM_BBAR_EULER && bbar != MSSM_BBAR_ZOH) return MSSM_ERROR_INVALID_VALUE;
+  if (batch == 0 || D == 0) return MSSM_SUCCESS;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (L == 0) {
+    if (!h_last) return MSSM_SUCCESS;
+    const hipError_t e = mssm::launch_state_init(h_last, h0, batch * D * N, st);
+    if (e != hipSuccess) {
+      set_hip_error(e, "state copy launch");
+      return MSSM_ERROR_HIP;
+    }
+    return MSSM_SUCCESS;
+  }
+  if (!x || !delta || !A || !B || !C || !y) return MSSM_ERROR_INVALID_VALUE;
+  mssm::ScanArgs a{x, delta, A, B, C, y, batch, L, D, N, dtype};
+  a.Dskip = Dskip;
+  a.z = z;
+  a.h0 = h0;
+  a.h_last = h_last;
+  a.bbar = bbar;
+  const mssm::ScanPlan plan = mssm::plan_scan(batch, L, D, N, mssm::choose_cpl(a));
+  s = check_grid(plan, batch, D, N);
+  if (s != MSSM_SUCCESS) return s;
+  if (plan.workspace_bytes > 0 && (!workspace || workspace_bytes < plan.workspace_bytes))
+    return MSSM_ERROR_WORKSPACE;
+  const hipError_t e = mssm::launch_scan(a, plan, workspace, st);
+  if (e != hipSuccess) {
+    set_hip_error(e, "selective scan launch");
+    return MSSM_ERROR_HIP;
+  }
+  return MSSM_SUCCESS;
+}
+
+mssm_status mssm_selective_scan_step(const void* x, const void* delta, const float* A,
+                                     const void* B, const void* C, const float* Dskip,
+                                     const void* z, float* h, float* y, mssm_bbar bbar,
+                                     int64_t batch, int64_t D, int64_t N, mssm_dtype dtype,
+                                     void* stream) {
+  mssm_status s = check_shape(batch, 1, D, N, dtype);
+  if (s != MSSM_SUCCESS) return s;
+  if (bbar != MSSM_BBAR_EULER && bbar != MSSM_BBAR_ZOH) return MSSM_ERROR_INVALID_VALUE;
+  if (batch == 0 || D == 0) return MSSM_SUCCESS;
+  if (!x || !delta || !A || !B || !C || !h || !y) return MSSM_ERROR_INVALID_VALUE;
+  // one lane per (chain, group of up to 4 state values); 256-lane blocks
+  const int64_t lanes_per_chain = N < 4 ? 1 : N / 4;
+  int64_t lanes;
+  if (!mul_ok(batch * D, lanes_per_chain, &lanes)) return MSSM_ERROR_SIZE_OVERFLOW;
+  if ((lanes + 255) / 256 > static_cast<int64_t>(std::numeric_limits<uint32_t>::max()))
+    return MSSM_ERROR_NOT_SUPPORTED;
+  const mssm::StepArgs a{x, delta, A, B, C, Dskip, z, h, y, batch, D, N, dtype, bbar};
+  const hipError_t e = mssm::launch_step(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) {
+    set_hip_error(e, "selective scan step launch");
+    return MSSM_ERROR_HIP;
+  }
+  return MSSM_SUCCESS;
+}
+
 int mssm_fused_supports(int64_t N, int64_t R) {
   return (mssm::state_size_supported(N) && R >= 16 && R <= 1024 && R % 16 == 0) ? 1 : 0;
 }

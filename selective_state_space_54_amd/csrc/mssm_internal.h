@@ -35,6 +35,11 @@ struct ScanArgs {
   void* y;
   int64_t batch, L, D, N;
   mssm_dtype dtype;
+  const float* Dskip = nullptr;   // [D] feedthrough, or null
+  const void* z = nullptr;        // [batch, L, D] gate input, or null
+  const float* h0 = nullptr;      // [batch, D, N] initial state, or null (zero)
+  float* h_last = nullptr;        // [batch, D, N] final state out, or null
+  mssm_bbar bbar = MSSM_BBAR_EULER;
 };
 
 // Plan for `cpl` chains per lane.
@@ -56,9 +61,31 @@ hipError_t launch_scan(const ScanArgs& a, const ScanPlan& plan, void* workspace,
 
 bool state_size_supported(int64_t N);
 
-// The carry pass over chunk summaries (shared by the plain and fused paths).
-hipError_t launch_carry(float* sum_h, const float* sum_p, int64_t batch, int64_t D, int64_t N,
-                        int K, hipStream_t stream);
+// The carry pass over chunk summaries (shared by the plain and fused paths);
+// h0 ([batch, D, N], or null for a zero start) is the state before chunk 0.
+hipError_t launch_carry(float* sum_h, const float* sum_p, const float* h0, int64_t batch,
+                        int64_t D, int64_t N, int K, hipStream_t stream);
+
+// h_last = h0 (or zero when h0 is null), `count` floats: the final state of an
+// empty sequence.
+hipError_t launch_state_init(float* h_last, const float* h0, int64_t count, hipStream_t stream);
+
+// One recurrent step per (batch row, channel): h is updated in place.
+struct StepArgs {
+  const void* x;        // [batch, D]
+  const void* delta;    // [batch, D]
+  const float* A;       // [D, N]
+  const void* B;        // [batch, N]
+  const void* C;        // [batch, N]
+  const float* Dskip;   // [D] or null
+  const void* z;        // [batch, D] or null
+  float* h;             // [batch, D, N]
+  float* y;             // [batch, D]
+  int64_t batch, D, N;
+  mssm_dtype dtype;
+  mssm_bbar bbar;
+};
+hipError_t launch_step(const StepArgs& a, hipStream_t stream);
 
 // ---- fused projections + scan ------------------------------------------------------------
 

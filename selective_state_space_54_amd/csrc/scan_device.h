@@ -123,29 +123,64 @@ __device__ __forceinline__ void buf_store_vals(buf_t r, int voff, int soff, cons
   }
 }
 
+// SiLU(v) = v * sigmoid(v), the gate of the Mamba block ("Understanding
+// Mamba", section 8.1, eq. (9)).  exp2 and the reciprocal run on the
+// transcendental unit (about 1 ulp each).
+__device__ __forceinline__ float silu(float v) {
+  return v * __builtin_amdgcn_rcpf(1.0f + fast_exp2(-v * kLog2e));
+}
+
+// Which optional parts of the recurrence and the read-out a kernel carries.
+//   kZoh : exact zero-order-hold input term Bbar = (Abar - 1) / A * B
+//          ("Understanding Mamba", eq. (2)) instead of the first-order Delta B
+//   kSkip: feedthrough y += Dskip[d] * x ("Understanding Mamba", eq. (1)/(3))
+//   kGate: y *= SiLU(z)  (the gate branch of the Mamba block, eq. (9))
+template <bool kZoh_, bool kSkip_, bool kGate_>
+struct Variant {
+  static constexpr bool kZoh = kZoh_;
+  static constexpr bool kSkip = kSkip_;
+  static constexpr bool kGate = kGate_;
+};
+using PlainVariant = Variant<false, false, false>;
+
+// Per-lane constants of one chain: A * log2(e), and 1 / A for the exact
+// zero-order hold (only read when kZoh).
+template <int N, int CPL>
+struct ChainConsts {
+  float A2[CPL][N];
+  float Ainv[CPL][N];
+  float Dd[CPL];      // feedthrough (only read when kSkip)
+};
+
 // ---- the per-lane sequential pass over a range of steps -----------------------------------
 //
-// Runs steps [0, nsteps) of one chunk for the lane's CPL chains.  xb/db/yb
+// Runs steps [0, nsteps) of one chunk for the lane's CPL chains.  xb/db/yb/zb
 // point at (b, t0, first channel of the block); `lane` is the lane index in the
 // block (its channels are lane*CPL + c); rows are D elements apart.  Bb/Cb
 // point at row (b, t0) of B/C, read through the scalar unit.  The caller
 // guarantees nsteps * D * sizeof(float) < 2^31.
-// kWithY: also form y_t = sum_n C_t[n] h_t[n] and store it (output pass);
-// otherwise accumulate each chain's total step size in S (summary pass).
-// x and delta are prefetched kTile steps ahead.  B_t and C_t are loaded one
-// step ahead into two alternating register sets (kTile is even, so the set
-// used by a step is fixed at compile time and no copies are needed).
-template <int N, int CPL, typename T, bool kPairs, bool kWithY>
+// kWithY: also form y_t = sum_n C_t[n] h_t[n] (plus the variant's feedthrough
+// and gate) and store it (output pass); otherwise accumulate each chain's
+// total step size in S (summary pass).
+// x, delta (and z) are prefetched kTile steps ahead.  B_t and C_t are loaded
+// one step ahead into two alternating register sets (kTile is even, so the
+// set used by a step is fixed at compile time and no copies are needed).
+// Lanes past the last channel run the last channel's chain (their addressing
+// is clamped), so their stores repeat that channel's value at its address.
+template <int N, int CPL, typename T, bool kPairs, bool kWithY, class V = PlainVariant>
 __device__ __forceinline__ void scan_steps(const T* __restrict__ xb, const T* __restrict__ db,
                                            const T* __restrict__ Bb, const T* __restrict__ Cb,
-                                           float* __restrict__ yb, const float (&A2)[CPL][N],
-                                           float (&h)[CPL][N], double (&S)[CPL], int lane,
-                                           int64_t D, int nsteps) {
+                                           const T* __restrict__ zb, float* __restrict__ yb,
+                                           const ChainConsts<N, CPL>& k, float (&h)[CPL][N],
+                                           double (&S)[CPL], int lane, int64_t D, int nsteps) {
   constexpr int kTile = (CPL == 1) ? 8 : 4;
+  constexpr bool kGate = kWithY && V::kGate;
   static_assert(kTile % 2 == 0, "alternating B/C register sets need an even tile");
   const uint32_t in_bytes = static_cast<uint32_t>((int64_t)nsteps * D * sizeof(T));
   const buf_t xr = make_buf(xb, in_bytes);
   const buf_t dr = make_buf(db, in_bytes);
+  buf_t zr;
+  if constexpr (kGate) zr = make_buf(zb, in_bytes);
   const int in_row = static_cast<int>(D * sizeof(T));
   const int in_lane = lane * CPL * static_cast<int>(sizeof(T));
   buf_t yr;
@@ -158,12 +193,13 @@ __device__ __forceinline__ void scan_steps(const T* __restrict__ xb, const T* __
   // prefetches past the chunk re-read its last row (the SGPR offset is not
   // range-checked by the hardware, so it is clamped here)
   const int last = nsteps > 0 ? nsteps - 1 : 0;
-  float xc[kTile][CPL], dc[kTile][CPL];
+  float xc[kTile][CPL], dc[kTile][CPL], zc[kGate ? kTile : 1][CPL];
 #pragma unroll
   for (int j = 0; j < kTile; ++j) {
     const int soff = __builtin_amdgcn_readfirstlane(min(j, last) * in_row);
     buf_load_vals<T, CPL>(xr, in_lane, soff, xc[j]);
     buf_load_vals<T, CPL>(dr, in_lane, soff, dc[j]);
+    if constexpr (kGate) buf_load_vals<T, CPL>(zr, in_lane, soff, zc[j]);
   }
   float Bv[2][N], Cv[2][N];
   if (nsteps > 0) {
@@ -171,12 +207,13 @@ __device__ __forceinline__ void scan_steps(const T* __restrict__ xb, const T* __
     if constexpr (kWithY) load_row_any<N, kPairs>(Cb, Cv[0]);
   }
   for (int base = 0; base < nsteps; base += kTile) {
-    float xn[kTile][CPL], dn[kTile][CPL];
+    float xn[kTile][CPL], dn[kTile][CPL], zn[kGate ? kTile : 1][CPL];
 #pragma unroll
     for (int j = 0; j < kTile; ++j) {
       const int soff = __builtin_amdgcn_readfirstlane(min(base + kTile + j, last) * in_row);
       buf_load_vals<T, CPL>(xr, in_lane, soff, xn[j]);
       buf_load_vals<T, CPL>(dr, in_lane, soff, dn[j]);
+      if constexpr (kGate) buf_load_vals<T, CPL>(zr, in_lane, soff, zn[j]);
     }
 #pragma unroll
     for (int j = 0; j < kTile; ++j) {
@@ -198,14 +235,23 @@ __device__ __forceinline__ void scan_steps(const T* __restrict__ xb, const T* __
         for (int n = 0; n < N; ++n) {
 #pragma unroll
           for (int c = 0; c < CPL; ++c) {
-            const float a = fast_exp2(dc[j][c] * A2[c][n]);            // Abar = exp(delta A)
-            h[c][n] = __builtin_fmaf(a, h[c][n], dx[c] * Bv[cur][n]);  // h = Abar h + (delta B) x
+            const float a = fast_exp2(dc[j][c] * k.A2[c][n]);          // Abar = exp(delta A)
+            if constexpr (V::kZoh) {
+              // (Abar - 1) / A * B * x: u = x B / A, then a u - u in one rounding
+              const float u = (xc[j][c] * k.Ainv[c][n]) * Bv[cur][n];
+              h[c][n] = __builtin_fmaf(a, h[c][n], __builtin_fmaf(a, u, -u));
+            } else {
+              h[c][n] = __builtin_fmaf(a, h[c][n], dx[c] * Bv[cur][n]);  // h = Abar h + (delta B) x
+            }
             if constexpr (kWithY) yv[c] = __builtin_fmaf(Cv[cur][n], h[c][n], yv[c]);  // C . h
           }
         }
         if constexpr (kWithY) {
-          // lanes past the last channel repeat the last valid channel (clamped
-          // addressing), so they store the same value to the same place
+#pragma unroll
+          for (int c = 0; c < CPL; ++c) {
+            if constexpr (V::kSkip) yv[c] = __builtin_fmaf(k.Dd[c], xc[j][c], yv[c]);
+            if constexpr (kGate) yv[c] *= silu(zc[j][c]);
+          }
           buf_store_vals<CPL>(yr, out_lane, s * out_row, yv);
         } else {
 #pragma unroll
@@ -219,6 +265,7 @@ __device__ __forceinline__ void scan_steps(const T* __restrict__ xb, const T* __
       for (int c = 0; c < CPL; ++c) {
         xc[j][c] = xn[j][c];
         dc[j][c] = dn[j][c];
+        if constexpr (kGate) zc[j][c] = zn[j][c];
       }
     }
   }

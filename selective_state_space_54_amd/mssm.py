@@ -19,6 +19,9 @@ LIB_PATH = os.path.join(_HERE, "libmssm.so")
 MSSM_SUCCESS = 0
 MSSM_FLOAT32 = 0
 MSSM_BFLOAT16 = 1
+MSSM_BBAR_EULER = 0
+MSSM_BBAR_ZOH = 1
+_BBAR = {"euler": MSSM_BBAR_EULER, "zoh": MSSM_BBAR_ZOH}
 _DTYPES = {torch.float32: MSSM_FLOAT32, torch.bfloat16: MSSM_BFLOAT16}
 _STATUS_NAMES = {0: "MSSM_SUCCESS", 1: "MSSM_ERROR_INVALID_VALUE", 2: "MSSM_ERROR_NOT_SUPPORTED",
                  3: "MSSM_ERROR_SIZE_OVERFLOW", 4: "MSSM_ERROR_WORKSPACE", 5: "MSSM_ERROR_HIP"}
@@ -40,6 +43,12 @@ _SIGNATURES = {
     "mssm_selective_scan_fwd_ws": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                                   ctypes.c_size_t, _i64, _i64, _i64, _i64,
                                                   ctypes.c_int, _vp]),
+    "mssm_selective_scan_fwd_ex": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                                  _vp, ctypes.c_int, _vp, ctypes.c_size_t, _i64,
+                                                  _i64, _i64, _i64, ctypes.c_int, _vp]),
+    "mssm_selective_scan_step": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                                ctypes.c_int, _i64, _i64, _i64, ctypes.c_int,
+                                                _vp]),
     "mssm_fused_supports": (ctypes.c_int, [_i64, _i64]),
     "mssm_selective_ssm_fused_workspace_size": (ctypes.c_int, [_i64, _i64, _i64, _i64, _i64,
                                                                ctypes.c_int,
@@ -182,6 +191,88 @@ def selective_scan(x, delta, A, B, C, *, stream=None):
     nbytes = mssm_selective_scan_workspace_size(batch, L, D, N, x.dtype)
     ws = torch.empty(nbytes, dtype=torch.uint8, device=x.device) if nbytes else None
     return mssm_selective_scan_fwd_ws(x, delta, A, B, C, y, ws, stream=stream)
+
+
+def _bbar_code(bbar) -> int:
+    if bbar not in _BBAR:
+        raise ValueError(f"bbar must be one of {sorted(_BBAR)}")
+    return _BBAR[bbar]
+
+
+def _check_optional(t, name, dtype, shape, device):
+    if t is not None:
+        _dense(t, name, dtype, shape, device)
+
+
+def mssm_selective_scan_fwd_ex(x, delta, A, B, C, y, workspace, *, Dskip=None, z=None, h0=None,
+                               h_last=None, bbar="euler", stream=None):
+    """y (and h_last) <- the scan with its optional parts: ``bbar`` "euler" or
+    "zoh", feedthrough Dskip [D], gate z [batch, L, D], initial state h0 and
+    final state h_last [batch, D, N] (float32)."""
+    batch, L, D, N = _check_scan_args(x, delta, A, B, C, y)
+    dev = x.device
+    _check_optional(Dskip, "Dskip", torch.float32, (D,), dev)
+    _check_optional(z, "z", x.dtype, (batch, L, D), dev)
+    _check_optional(h0, "h0", torch.float32, (batch, D, N), dev)
+    _check_optional(h_last, "h_last", torch.float32, (batch, D, N), dev)
+    ws_ptr = _ptr(workspace) if workspace is not None and workspace.numel() > 0 else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(load().mssm_selective_scan_fwd_ex(
+        _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(Dskip), _ptr(z), _ptr(h0), _ptr(y),
+        _ptr(h_last), _bbar_code(bbar), ws_ptr, ws_bytes, batch, L, D, N, _DTYPES[x.dtype],
+        _stream_handle(stream)), "mssm_selective_scan_fwd_ex")
+    return y
+
+
+def selective_scan_ex(x, delta, A, B, C, *, Dskip=None, z=None, h0=None,
+                      return_last_state=False, bbar="euler", stream=None):
+    """Allocate y (and the final state) with torch, then run
+    mssm_selective_scan_fwd_ex.  Returns y, or (y, h_last)."""
+    batch, L, D, N = _scan_shapes(x, A)
+    y = torch.empty(x.shape, dtype=torch.float32, device=x.device)
+    h_last = (torch.empty((batch, D, N), dtype=torch.float32, device=x.device)
+              if return_last_state else None)
+    nbytes = mssm_selective_scan_workspace_size(batch, L, D, N, x.dtype)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=x.device) if nbytes else None
+    mssm_selective_scan_fwd_ex(x, delta, A, B, C, y, ws, Dskip=Dskip, z=z, h0=h0, h_last=h_last,
+                               bbar=bbar, stream=stream)
+    return (y, h_last) if return_last_state else y
+
+
+def mssm_selective_scan_step(x, delta, A, B, C, h, y, *, Dskip=None, z=None, bbar="euler",
+                             stream=None):
+    """One decode step: h [batch, D, N] float32 is updated in place and
+    y [batch, D] float32 receives the output; x, delta, z are [batch, D],
+    B, C are [batch, N]."""
+    if x.dim() != 2 or A.dim() != 2:
+        raise ValueError("x must be [batch, D] and A [D, N]")
+    batch, D = x.shape
+    N = A.shape[1]
+    _dtype_code(x.dtype)
+    dev = x.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a GPU device")
+    _dense(x, "x", x.dtype, (batch, D), dev)
+    _dense(delta, "delta", x.dtype, (batch, D), dev)
+    _dense(A, "A", torch.float32, (D, N), dev)
+    _dense(B, "B", x.dtype, (batch, N), dev)
+    _dense(C, "C", x.dtype, (batch, N), dev)
+    _dense(h, "h", torch.float32, (batch, D, N), dev)
+    _dense(y, "y", torch.float32, (batch, D), dev)
+    _check_optional(Dskip, "Dskip", torch.float32, (D,), dev)
+    _check_optional(z, "z", x.dtype, (batch, D), dev)
+    _check(load().mssm_selective_scan_step(
+        _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(Dskip), _ptr(z), _ptr(h), _ptr(y),
+        _bbar_code(bbar), batch, D, N, _DTYPES[x.dtype], _stream_handle(stream)),
+        "mssm_selective_scan_step")
+    return y
+
+
+def selective_scan_step(x, delta, A, B, C, h, *, Dskip=None, z=None, bbar="euler", stream=None):
+    """Allocate y, run mssm_selective_scan_step (h updated in place), return y."""
+    y = torch.empty(x.shape, dtype=torch.float32, device=x.device)
+    return mssm_selective_scan_step(x, delta, A, B, C, h, y, Dskip=Dskip, z=z, bbar=bbar,
+                                    stream=stream)
 
 
 # ---- fused selective SSM (projections + scan) ----------------------------------------------

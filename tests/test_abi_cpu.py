@@ -33,7 +33,8 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_strings(lib):
-    assert lib.mssm_abi_version() == 1
+    text = open(HEADER).read()
+    assert lib.mssm_abi_version() == int(re.search(r"#define MSSM_ABI_VERSION (\d+)", text).group(1))
     for s in range(6):
         assert lib.mssm_status_string(s)
     assert b"unknown" in lib.mssm_status_string(99)
@@ -135,3 +136,51 @@ def test_fused_argument_errors(lib):
     assert call(p6, FAKE, nbytes - 1, 1, 64, 64, 16, 16) == 4
     assert call(p6, None, 0, 1, 64, 64, 16, 16) == 4
     assert call([None] * 6, None, 0, 0, 64, 64, 16, 16) == 0   # empty problem
+
+
+def _ex(lib, ptrs, bbar, ws, wsb, batch, L, D, N, dtype=0):
+    return lib.mssm_selective_scan_fwd_ex(*ptrs, bbar, ws, wsb, batch, L, D, N, dtype, None)
+
+
+def test_scan_ex_argument_errors(lib):
+    p10 = [FAKE] * 10          # x, delta, A, B, C, Dskip, z, h0, y, h_last
+    assert _ex(lib, p10, 2, FAKE, 1 << 40, 1, 4, 4, 4) == 1        # bad bbar enum
+    assert _ex(lib, p10, -1, FAKE, 1 << 40, 1, 4, 4, 4) == 1
+    assert _ex(lib, p10, 0, FAKE, 1 << 40, -1, 4, 4, 4) == 1
+    assert _ex(lib, p10, 1, FAKE, 1 << 40, 1, 4, 4, 3) == 2
+    assert _ex(lib, p10, 0, FAKE, 1 << 40, 1, 4, 4, 4, dtype=5) == 1
+    assert _ex(lib, p10, 0, FAKE, 1 << 40, 1 << 40, 1 << 40, 4, 4) == 3
+    for i in (0, 1, 2, 3, 4, 8):                                   # required pointers
+        ptrs = list(p10)
+        ptrs[i] = None
+        assert _ex(lib, ptrs, 0, FAKE, 1 << 40, 1, 4, 4, 4) == 1, f"null pointer {i} accepted"
+    st, nbytes = _ws(lib, 8, 2048, 1536, 16, 0)
+    assert _ex(lib, p10, 1, FAKE, nbytes - 1, 8, 2048, 1536, 16) == 4
+    assert _ex(lib, p10, 1, None, 0, 8, 2048, 1536, 16) == 4
+
+
+def test_scan_ex_empty_problems(lib):
+    nulls = [None] * 10
+    for shape in [(0, 4, 4), (1, 4, 0), (0, 0, 0)]:
+        assert _ex(lib, nulls, 0, None, 0, *shape, 16) == 0
+    # L == 0 without h_last has nothing to do
+    assert _ex(lib, nulls, 1, None, 0, 2, 0, 8, 16) == 0
+
+
+def _step(lib, ptrs, bbar, batch, D, N, dtype=0):
+    return lib.mssm_selective_scan_step(*ptrs, bbar, batch, D, N, dtype, None)
+
+
+def test_step_argument_errors(lib):
+    p9 = [FAKE] * 9            # x, delta, A, B, C, Dskip, z, h, y
+    assert _step(lib, p9, 3, 1, 4, 4) == 1
+    assert _step(lib, p9, 0, -1, 4, 4) == 1
+    assert _step(lib, p9, 0, 1, 4, 4, dtype=9) == 1
+    assert _step(lib, p9, 0, 1, 4, 12) == 2
+    assert _step(lib, p9, 0, 1 << 40, 1 << 40, 16) == 3
+    for i in (0, 1, 2, 3, 4, 7, 8):
+        ptrs = list(p9)
+        ptrs[i] = None
+        assert _step(lib, ptrs, 0, 2, 4, 4) == 1, f"null pointer {i} accepted"
+    assert _step(lib, [None] * 9, 0, 0, 4, 4) == 0
+    assert _step(lib, [None] * 9, 1, 3, 0, 4) == 0

@@ -55,8 +55,18 @@ WORKLOADS = {
                              "state; x ~ N(0,1); x_proj W [D, R+2N] ~ N(0, 1/D); "
                              "dt_proj W [R, D] ~ N(0, 1/R); softplus(dt_bias) "
                              "log-uniform in [1e-3, 1e-1]; A[d,n] = -(n+1)"),
+        Workload("decode_step_bf16", 256, 1, 5120, 16, "bf16", 5406,
+                 description="one recurrent (decode) step for 256 sequences of a "
+                             "D = 5120, N = 16 layer; bf16 token inputs, fp32 state "
+                             "[batch, D, N] ~ N(0, 1/4); x, z, B, C ~ N(0,1); Delta "
+                             "log-uniform in [1e-3, 1e-1]; Dskip ~ N(0,1); "
+                             "A[d,n] = -(n+1)"),
     )
 }
+
+# Workloads that are one full-sequence scan (the others: the decode step).
+SCAN_WORKLOADS = ("tiny_fp32", "mamba130m_layer_fp32", "mid_bf16", "long_seq_bf16",
+                  "fused_proj_bf16")
 
 
 def workload(name: str, **overrides) -> Workload:
@@ -155,5 +165,48 @@ def generate(w: Workload | str, **overrides) -> dict:
     out["delta"] = delta.reshape(w.batch, w.L, w.D)
     out["B"] = _draw(rng, BLN, w.dtype, "normal", 0.0, bc_std).reshape(w.batch, w.L, w.N)
     out["C"] = _draw(rng, BLN, w.dtype, "normal", 0.0, bc_std).reshape(w.batch, w.L, w.N)
+    out["A"] = _a_matrix(w)
+    return out
+
+
+def generate_extras(w: Workload | str, seed_offset: int = 1000, **overrides) -> dict:
+    """Inputs for the scan's optional parts, for workload ``w``'s shape.
+
+    Dskip [D] ~ N(0,1) float32, z [batch, L, D] ~ N(0,1) in the workload's
+    storage type, h0 [batch, D, N] ~ N(0, 1/4) float32; drawn in that order
+    from default_rng(seed + seed_offset).
+    """
+    if isinstance(w, str):
+        w = workload(w, **overrides)
+    elif overrides:
+        w = replace(w, **overrides)
+    rng = np.random.default_rng(w.seed + seed_offset)
+    return {
+        "Dskip": _draw(rng, w.D, "fp32", "normal", 0.0, 1.0),
+        "z": _draw(rng, w.batch * w.L * w.D, w.dtype, "normal", 0.0, 1.0).reshape(
+            w.batch, w.L, w.D),
+        "h0": _draw(rng, w.batch * w.D * w.N, "fp32", "normal", 0.0, 0.5).reshape(
+            w.batch, w.D, w.N),
+    }
+
+
+def generate_step(w: Workload | str = "decode_step_bf16", **overrides) -> dict:
+    """Inputs of one decode step: x, delta, z [batch, D]; B, C [batch, N];
+    A [D, N]; Dskip [D]; h [batch, D, N] float32 (the state before the step).
+    Draw order: x, delta, B, C, z, Dskip, h."""
+    if isinstance(w, str):
+        w = workload(w, **overrides)
+    elif overrides:
+        w = replace(w, **overrides)
+    rng = np.random.default_rng(w.seed)
+    BD, BN = w.batch * w.D, w.batch * w.N
+    out = {"workload": w}
+    out["x"] = _draw(rng, BD, w.dtype, "normal", 0.0, 1.0).reshape(w.batch, w.D)
+    out["delta"] = _draw(rng, BD, w.dtype, "loguniform", 1e-3, 1e-1).reshape(w.batch, w.D)
+    out["B"] = _draw(rng, BN, w.dtype, "normal", 0.0, 1.0).reshape(w.batch, w.N)
+    out["C"] = _draw(rng, BN, w.dtype, "normal", 0.0, 1.0).reshape(w.batch, w.N)
+    out["z"] = _draw(rng, BD, w.dtype, "normal", 0.0, 1.0).reshape(w.batch, w.D)
+    out["Dskip"] = _draw(rng, w.D, "fp32", "normal", 0.0, 1.0)
+    out["h"] = _draw(rng, BD * w.N, "fp32", "normal", 0.0, 0.5).reshape(w.batch, w.D, w.N)
     out["A"] = _a_matrix(w)
     return out
