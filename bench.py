@@ -154,6 +154,105 @@ def time_fused(name, steps, warmup, torch, mssm, workloads):
     return w, wall, kernel_ms
 
 
+def _to_device(a, torch):
+    import numpy as np
+    a = np.ascontiguousarray(a)
+    t = torch.from_numpy(a.view(np.int16)).view(torch.bfloat16) if a.dtype == np.uint16 \
+        else torch.from_numpy(a)
+    return t.cuda()
+
+
+def time_scan_ex(name, steps, warmup, torch, mssm, workloads):
+    """The scan with every optional part on: exact zero-order hold, feedthrough,
+    SiLU(z) gate, initial state in and final state out."""
+    w = workloads.workload(name)
+    g = workloads.generate(name)
+    e = workloads.generate_extras(w)
+    d = device_inputs(g, torch)
+    for k in ("Dskip", "z", "h0"):
+        d[k] = _to_device(e[k], torch)
+    del g, e
+    d["y"] = torch.empty(d["x"].shape, dtype=torch.float32, device="cuda")
+    d["h_last"] = torch.empty(d["h0"].shape, dtype=torch.float32, device="cuda")
+    nbytes = mssm.mssm_selective_scan_workspace_size(w.batch, w.L, w.D, w.N, d["x"].dtype)
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device="cuda")
+
+    def step():
+        mssm.mssm_selective_scan_fwd_ex(d["x"], d["delta"], d["A"], d["B"], d["C"], d["y"], ws,
+                                        Dskip=d["Dskip"], z=d["z"], h0=d["h0"],
+                                        h_last=d["h_last"], bbar="zoh")
+
+    for _ in range(warmup):
+        step()
+    stream = torch.cuda.current_stream()
+    s_ev = torch.cuda.Event(enable_timing=True)
+    e_ev = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    s_ev.record(stream)
+    for _ in range(steps):
+        step()
+    e_ev.record(stream)
+    torch.cuda.synchronize()
+    kernel_ms = s_ev.elapsed_time(e_ev) / steps
+    el = 4 if w.dtype == "fp32" else 2
+    nb = (4 * w.batch * w.L * w.D * el + 2 * w.batch * w.L * w.N * el
+          + 2 * w.batch * w.D * w.N * 4 + w.D * 4)
+    del d, ws
+    torch.cuda.empty_cache()
+    return {"kernel_ms": round(kernel_ms, 4),
+            "GB/s": round(nb / (kernel_ms * 1e-3) / 1e9, 1),
+            "Gelem/s": round(elements(w) / (kernel_ms * 1e-3) / 1e9, 1),
+            "note": "bbar zoh, Dskip, z gate, h0 in, h_last out; bytes = x + Delta + z + y, "
+                    "B + C, h0 + h_last, Dskip"}
+
+
+def decode_bytes(w) -> int:
+    el = 4 if w.dtype == "fp32" else 2
+    return (2 * w.batch * w.D * w.N * 4            # state read and written
+            + 3 * w.batch * w.D * el + w.batch * w.D * 4   # x, delta, z in; y out
+            + 2 * w.batch * w.N * el                # B, C
+            + w.D * w.N * 4 + w.D * 4)              # A, Dskip
+
+
+def time_decode(name, steps, warmup, torch, mssm, workloads, states=4):
+    """One decode step per call over `states` rotating state buffers (their
+    total exceeds the 256 MB last-level cache, so the state comes from HBM)."""
+    w = workloads.workload(name)
+    s = workloads.generate_step(name)
+    d = {k: _to_device(s[k], torch) for k in ("x", "delta", "A", "B", "C", "z", "Dskip")}
+    hs = [_to_device(s["h"], torch) for _ in range(states)]
+    del s
+    y = torch.empty(d["x"].shape, dtype=torch.float32, device="cuda")
+
+    def step(i):
+        mssm.mssm_selective_scan_step(d["x"], d["delta"], d["A"], d["B"], d["C"], hs[i % states],
+                                      y, Dskip=d["Dskip"], z=d["z"])
+
+    for i in range(warmup):
+        step(i)
+    stream = torch.cuda.current_stream()
+    s_ev = torch.cuda.Event(enable_timing=True)
+    e_ev = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    s_ev.record(stream)
+    for i in range(steps):
+        step(i)
+    e_ev.record(stream)
+    torch.cuda.synchronize()
+    kernel_ms = s_ev.elapsed_time(e_ev) / steps
+    nb = decode_bytes(w)
+    del d, hs, y
+    torch.cuda.empty_cache()
+    gbs = nb / (kernel_ms * 1e-3) / 1e9
+    return {"kernel_ms": round(kernel_ms, 5), "GB/s": round(gbs, 1),
+            "hbm_peak_frac": round(gbs / HBM_PEAK_GBS, 4),
+            "tokens_channels_per_s": round(w.batch * w.D / (kernel_ms * 1e-3), 1),
+            "roofline": {"bound": "hbm", "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "bytes_per_launch": nb},
+            "note": f"selective_step_kernel, batch {w.batch}, D {w.D}, N {w.N}, bf16 token "
+                    f"inputs, fp32 state; Dskip and z gate on; {states} rotating states"}
+
+
 def cpu_baseline(name, workloads, oracle, threads):
     """The float64 oracle on the host cores, on the whole headline workload."""
     g = workloads.generate(name)
@@ -274,6 +373,10 @@ def main(argv=None):
                 others[name]["projection_TFLOPs"] = round(flops / 1e12, 2)
                 others[name]["note"] = ("bytes by the scan formula (x + Delta + y, B + C); Delta, B, "
                                         "C are formed on chip from x and the weights")
+        others["mamba130m_layer_fp32 zoh+skip+gate+state"] = time_scan_ex(
+            HEADLINE, 10, 2, torch, mssm, workloads)
+        others["decode_step_bf16"] = time_decode("decode_step_bf16", 200, 10, torch, mssm,
+                                                 workloads)
         line["workloads"] = others
     if not args.no_cpu_baseline:
         import oracle

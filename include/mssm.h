@@ -174,7 +174,8 @@ mssm_status mssm_selective_scan_fwd_ex(const void *x, const void *delta, const f
  *   A           : [D, N] float32;  Dskip : [D] float32 or NULL
  *   h           : [batch, D, N] float32, read and overwritten
  *   y           : [batch, D] float32
- * Needs no workspace.  batch or D equal to zero is a no-op.
+ * Needs no workspace.  batch or D equal to zero is a no-op.  batch above
+ * 65535 gives MSSM_ERROR_NOT_SUPPORTED (one grid row per batch row).
  */
 mssm_status mssm_selective_scan_step(const void *x, const void *delta, const float *A,
                                      const void *B, const void *C, const float *Dskip,

@@ -187,11 +187,13 @@ mssm_status mssm_selective_scan_step(const void* x, const void* delta, const flo
   if (bbar != MSSM_BBAR_EULER && bbar != MSSM_BBAR_ZOH) return MSSM_ERROR_INVALID_VALUE;
   if (batch == 0 || D == 0) return MSSM_SUCCESS;
   if (!x || !delta || !A || !B || !C || !h || !y) return MSSM_ERROR_INVALID_VALUE;
-  // one lane per (chain, group of up to 4 state values); 256-lane blocks
-  const int64_t lanes_per_chain = N < 4 ? 1 : N / 4;
-  int64_t lanes;
-  if (!mul_ok(batch * D, lanes_per_chain, &lanes)) return MSSM_ERROR_SIZE_OVERFLOW;
-  if ((lanes + 255) / 256 > static_cast<int64_t>(std::numeric_limits<uint32_t>::max()))
+  // grid: one row of blocks per batch row (at most 65535 rows), each row
+  // covering D * (N / min(N, 4)) lane-slots
+  if (batch > 65535) return MSSM_ERROR_NOT_SUPPORTED;
+  const int64_t slots_per_chain = N < 4 ? 1 : N / 4;
+  int64_t row_slots;
+  if (!mul_ok(D, slots_per_chain, &row_slots)) return MSSM_ERROR_SIZE_OVERFLOW;
+  if (row_slots > static_cast<int64_t>(std::numeric_limits<int32_t>::max()))
     return MSSM_ERROR_NOT_SUPPORTED;
   const mssm::StepArgs a{x, delta, A, B, C, Dskip, z, h, y, batch, D, N, dtype, bbar};
   const hipError_t e = mssm::launch_step(a, static_cast<hipStream_t>(stream));

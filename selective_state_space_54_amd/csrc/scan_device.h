@@ -135,11 +135,15 @@ __device__ __forceinline__ float silu(float v) {
 //          ("Understanding Mamba", eq. (2)) instead of the first-order Delta B
 //   kSkip: feedthrough y += Dskip[d] * x ("Understanding Mamba", eq. (1)/(3))
 //   kGate: y *= SiLU(z)  (the gate branch of the Mamba block, eq. (9))
-template <bool kZoh_, bool kSkip_, bool kGate_>
+//   kState: the output pass also writes the final state.  A compile-time
+//          switch because keeping the store's address live across the step
+//          loop costs registers, and with them a wavefront per SIMD.
+template <bool kZoh_, bool kSkip_, bool kGate_, bool kState_ = false>
 struct Variant {
   static constexpr bool kZoh = kZoh_;
   static constexpr bool kSkip = kSkip_;
   static constexpr bool kGate = kGate_;
+  static constexpr bool kState = kState_;
 };
 using PlainVariant = Variant<false, false, false>;
 

@@ -39,7 +39,10 @@ namespace mssm {
 constexpr int kBlock = 256;   // 4 wavefronts; a block covers 256 * CPL consecutive channels
 
 // Everything a chunk kernel reads or writes.  Element pointers are typed by
-// the kernel (float or bfloat16 bits).
+// the kernel (float or bfloat16 bits).  The kernels take the pointers as
+// separate __restrict__ parameters: only then can the compiler prove that the
+// stores to y never overwrite B and C, which lets it read B_t and C_t with
+// scalar loads into SGPRs (shared by the wavefront) instead of vector loads.
 struct ScanParams {
   const void* x;
   const void* delta;
@@ -53,6 +56,13 @@ struct ScanParams {
   float* y;
   float* sum_h;         // chunk summaries, [batch, K-1, N, D]
   float* sum_p;
+  int64_t L, D, chunk_len;
+  int K;
+  int64_t n_dtiles;
+};
+
+// The sizes part of ScanParams, passed by value next to the pointers.
+struct ScanDims {
   int64_t L, D, chunk_len;
   int K;
   int64_t n_dtiles;
@@ -84,30 +94,33 @@ __device__ __forceinline__ BlockCoord block_coord(int64_t n_dtiles, int K, int64
 
 // Per-lane constants for channels dl .. dl + CPL - 1.
 template <int N, int CPL, class V>
-__device__ __forceinline__ void load_chain_consts(const ScanParams& p, int64_t dl,
+__device__ __forceinline__ void load_chain_consts(const float* __restrict__ A,
+                                                  const float* __restrict__ Dskip, int64_t dl,
                                                   ChainConsts<N, CPL>& k) {
 #pragma unroll
   for (int q = 0; q < CPL; ++q) {
 #pragma unroll
     for (int n = 0; n < N; ++n) {
-      const float a = p.A[(dl + q) * N + n];
+      const float a = A[(dl + q) * N + n];
       k.A2[q][n] = a * kLog2e;
       if constexpr (V::kZoh) k.Ainv[q][n] = 1.0f / a;
     }
-    if constexpr (V::kSkip) k.Dd[q] = p.Dskip[dl + q];
+    if constexpr (V::kSkip) k.Dd[q] = Dskip[dl + q];
   }
 }
 
 template <int N, int CPL, typename T, bool kPairs, bool kZoh>
-__global__ __launch_bounds__(kBlock) void chunk_summary_kernel(ScanParams p) {
+__global__ __launch_bounds__(kBlock) void chunk_summary_kernel(
+    const T* __restrict__ x, const T* __restrict__ delta, const float* __restrict__ A,
+    const T* __restrict__ Bm, float* __restrict__ sum_h, float* __restrict__ sum_p, ScanDims dm) {
   using V = Variant<kZoh, false, false>;
   // grid: n_dtiles * (K - 1) * batch blocks; block (dtile, k, b), k < K - 1
-  const int64_t D = p.D, L = p.L;
-  const int K = p.K;
-  const BlockCoord c = block_coord<CPL>(p.n_dtiles, K - 1, D);
+  const int64_t D = dm.D, L = dm.L;
+  const int K = dm.K;
+  const BlockCoord c = block_coord<CPL>(dm.n_dtiles, K - 1, D);
   const int64_t dl = c.d0 + (int64_t)CPL * c.lane;
   ChainConsts<N, CPL> k;
-  load_chain_consts<N, CPL, V>(p, dl, k);
+  load_chain_consts<N, CPL, V>(A, nullptr, dl, k);
   float h[CPL][N];
   double S[CPL];
 #pragma unroll
@@ -116,12 +129,9 @@ __global__ __launch_bounds__(kBlock) void chunk_summary_kernel(ScanParams p) {
 #pragma unroll
     for (int n = 0; n < N; ++n) h[q][n] = 0.0f;
   }
-  const int64_t t0 = (int64_t)c.k * p.chunk_len;
-  const int nsteps = static_cast<int>(p.chunk_len);   // chunks before the last are full
+  const int64_t t0 = (int64_t)c.k * dm.chunk_len;
+  const int nsteps = static_cast<int>(dm.chunk_len);   // chunks before the last are full
   const int64_t row0 = (c.b * L + t0) * D + c.d0;
-  const T* x = static_cast<const T*>(p.x);
-  const T* delta = static_cast<const T*>(p.delta);
-  const T* Bm = static_cast<const T*>(p.B);
   scan_steps<N, CPL, T, kPairs, false, V>(x + row0, delta + row0, Bm + (c.b * L + t0) * N,
                                           nullptr, nullptr, nullptr, k, h, S, c.lane, D, nsteps);
   if (c.active) {
@@ -130,9 +140,9 @@ __global__ __launch_bounds__(kBlock) void chunk_summary_kernel(ScanParams p) {
     for (int q = 0; q < CPL; ++q) {
 #pragma unroll
       for (int n = 0; n < N; ++n) {
-        p.sum_h[(row * N + n) * D + c.d + q] = h[q][n];
+        sum_h[(row * N + n) * D + c.d + q] = h[q][n];
         // the chunk's decay prod_t exp(delta_t A) = exp(S A); S was summed in float64
-        p.sum_p[(row * N + n) * D + c.d + q] =
+        sum_p[(row * N + n) * D + c.d + q] =
             fast_exp2(static_cast<float>(static_cast<double>(k.A2[q][n]) * S[q]));
       }
     }
@@ -140,13 +150,17 @@ __global__ __launch_bounds__(kBlock) void chunk_summary_kernel(ScanParams p) {
 }
 
 template <int N, int CPL, typename T, bool kPairs, class V>
-__global__ __launch_bounds__(kBlock) void chunk_output_kernel(ScanParams p) {
-  const int64_t D = p.D, L = p.L;
-  const int K = p.K;
-  const BlockCoord c = block_coord<CPL>(p.n_dtiles, K, D);
+__global__ __launch_bounds__(kBlock) void chunk_output_kernel(
+    const T* __restrict__ x, const T* __restrict__ delta, const float* __restrict__ A,
+    const T* __restrict__ Bm, const T* __restrict__ Cm, const float* __restrict__ Dskip,
+    const T* __restrict__ z, const float* __restrict__ h0, float* __restrict__ h_last,
+    float* __restrict__ y, const float* __restrict__ sum_h, ScanDims dm) {
+  const int64_t D = dm.D, L = dm.L;
+  const int K = dm.K;
+  const BlockCoord c = block_coord<CPL>(dm.n_dtiles, K, D);
   const int64_t dl = c.d0 + (int64_t)CPL * c.lane;
   ChainConsts<N, CPL> k;
-  load_chain_consts<N, CPL, V>(p, dl, k);
+  load_chain_consts<N, CPL, V>(A, Dskip, dl, k);
   float h[CPL][N];
   double S_unused[CPL];
 #pragma unroll
@@ -157,35 +171,34 @@ __global__ __launch_bounds__(kBlock) void chunk_output_kernel(ScanParams p) {
   }
   if (c.k > 0) {
     // carry-in: the state entering chunk k, left by the carry pass in slot k - 1
-    const float* cp = p.sum_h + ((c.b * (K - 1) + (c.k - 1)) * N) * D + dl;
+    const float* cp = sum_h + ((c.b * (K - 1) + (c.k - 1)) * N) * D + dl;
 #pragma unroll
     for (int q = 0; q < CPL; ++q)
 #pragma unroll
       for (int n = 0; n < N; ++n) h[q][n] = cp[(int64_t)n * D + q];
-  } else if (p.h0 != nullptr) {
-    const float* hp = p.h0 + (c.b * D + dl) * N;
+  } else if (h0 != nullptr) {
+    const float* hp = h0 + (c.b * D + dl) * N;
 #pragma unroll
     for (int q = 0; q < CPL; ++q)
 #pragma unroll
       for (int n = 0; n < N; ++n) h[q][n] = hp[q * N + n];
   }
-  const int64_t t0 = (int64_t)c.k * p.chunk_len;
-  const int nsteps = static_cast<int>(std::min<int64_t>(p.chunk_len, L - t0));
+  const int64_t t0 = (int64_t)c.k * dm.chunk_len;
+  const int nsteps = static_cast<int>(std::min<int64_t>(dm.chunk_len, L - t0));
   const int64_t row0 = (c.b * L + t0) * D + c.d0;
-  const T* x = static_cast<const T*>(p.x);
-  const T* delta = static_cast<const T*>(p.delta);
-  const T* Bm = static_cast<const T*>(p.B);
-  const T* Cm = static_cast<const T*>(p.C);
-  const T* z = V::kGate ? static_cast<const T*>(p.z) + row0 : nullptr;
   scan_steps<N, CPL, T, kPairs, true, V>(x + row0, delta + row0, Bm + (c.b * L + t0) * N,
-                                         Cm + (c.b * L + t0) * N, z, p.y + row0, k, h, S_unused,
-                                         c.lane, D, nsteps);
-  if (c.k == K - 1 && p.h_last != nullptr && c.active) {
-    float* hp = p.h_last + (c.b * D + c.d) * N;
+                                         Cm + (c.b * L + t0) * N, V::kGate ? z + row0 : nullptr,
+                                         y + row0, k, h, S_unused, c.lane, D, nsteps);
+  if constexpr (V::kState) {
+    if (c.k == K - 1) {
+      // lanes past the last channel hold that channel's state: same value, same place
+      float* hp = h_last + (c.b * D + c.d0) * N;
+      const int lo = c.lane * CPL * N;
 #pragma unroll
-    for (int q = 0; q < CPL; ++q)
+      for (int q = 0; q < CPL; ++q)
 #pragma unroll
-      for (int n = 0; n < N; ++n) hp[q * N + n] = h[q][n];
+        for (int n = 0; n < N; ++n) hp[lo + q * N + n] = h[q][n];
+    }
   }
 }
 
@@ -229,8 +242,11 @@ struct SummaryLaunch {
   template <int N, int CPL, typename T, bool kPairs>
   hipError_t run() const {
     const int64_t grid = p.n_dtiles * (p.K - 1) * batch;
+    const ScanDims dm{p.L, p.D, p.chunk_len, p.K, p.n_dtiles};
     hipLaunchKernelGGL((chunk_summary_kernel<N, CPL, T, kPairs, kZoh>), dim3((unsigned)grid),
-                       dim3(kBlock), 0, stream, p);
+                       dim3(kBlock), 0, stream, static_cast<const T*>(p.x),
+                       static_cast<const T*>(p.delta), p.A, static_cast<const T*>(p.B), p.sum_h,
+                       p.sum_p, dm);
     return hipGetLastError();
   }
 };
@@ -243,8 +259,12 @@ struct OutputLaunch {
   template <int N, int CPL, typename T, bool kPairs>
   hipError_t run() const {
     const int64_t grid = p.n_dtiles * p.K * batch;
+    const ScanDims dm{p.L, p.D, p.chunk_len, p.K, p.n_dtiles};
     hipLaunchKernelGGL((chunk_output_kernel<N, CPL, T, kPairs, V>), dim3((unsigned)grid),
-                       dim3(kBlock), 0, stream, p);
+                       dim3(kBlock), 0, stream, static_cast<const T*>(p.x),
+                       static_cast<const T*>(p.delta), p.A, static_cast<const T*>(p.B),
+                       static_cast<const T*>(p.C), p.Dskip, static_cast<const T*>(p.z), p.h0,
+                       p.h_last, p.y, p.sum_h, dm);
     return hipGetLastError();
   }
 };
@@ -254,12 +274,20 @@ template <class V>
 hipError_t launch_output_variant(const ScanArgs& a, const ScanPlan& plan, const ScanParams& p,
                                  hipStream_t stream);
 
+// Defines the launchers of one (input term, feedthrough, gate) combination,
+// with and without the final-state store.
 #define MSSM_DEFINE_OUTPUT_VARIANT(ZOH, SKIP, GATE)                                           \
   template <>                                                                                 \
-  hipError_t launch_output_variant<Variant<ZOH, SKIP, GATE>>(                                 \
+  hipError_t launch_output_variant<Variant<ZOH, SKIP, GATE, false>>(                          \
       const ScanArgs& a, const ScanPlan& plan, const ScanParams& p, hipStream_t stream) {     \
     return dispatch_shape(a, plan.cpl,                                                        \
-                          OutputLaunch<Variant<ZOH, SKIP, GATE>>{p, a.batch, stream});        \
+                          OutputLaunch<Variant<ZOH, SKIP, GATE, false>>{p, a.batch, stream}); \
+  }                                                                                           \
+  template <>                                                                                 \
+  hipError_t launch_output_variant<Variant<ZOH, SKIP, GATE, true>>(                           \
+      const ScanArgs& a, const ScanPlan& plan, const ScanParams& p, hipStream_t stream) {     \
+    return dispatch_shape(a, plan.cpl,                                                        \
+                          OutputLaunch<Variant<ZOH, SKIP, GATE, true>>{p, a.batch, stream});  \
   }
 
 // Defined by scan_summary_{euler,zoh}.hip.

@@ -147,6 +147,30 @@ int choose_cpl(const ScanArgs& a) {
   return cpl;
 }
 
+template <bool kZoh, bool kSkip, bool kGate>
+static hipError_t launch_output_state(const ScanArgs& a, const ScanPlan& plan,
+                                      const ScanParams& p, hipStream_t stream) {
+  if (a.h_last != nullptr)
+    return launch_output_variant<Variant<kZoh, kSkip, kGate, true>>(a, plan, p, stream);
+  return launch_output_variant<Variant<kZoh, kSkip, kGate, false>>(a, plan, p, stream);
+}
+
+template <bool kZoh>
+static hipError_t launch_output_zoh(const ScanArgs& a, const ScanPlan& plan, const ScanParams& p,
+                                    hipStream_t stream) {
+  const bool skip = a.Dskip != nullptr, gate = a.z != nullptr;
+  if (skip && gate) return launch_output_state<kZoh, true, true>(a, plan, p, stream);
+  if (skip) return launch_output_state<kZoh, true, false>(a, plan, p, stream);
+  if (gate) return launch_output_state<kZoh, false, true>(a, plan, p, stream);
+  return launch_output_state<kZoh, false, false>(a, plan, p, stream);
+}
+
+static hipError_t launch_output(const ScanArgs& a, const ScanPlan& plan, const ScanParams& p,
+                                hipStream_t stream) {
+  return a.bbar == MSSM_BBAR_ZOH ? launch_output_zoh<true>(a, plan, p, stream)
+                                 : launch_output_zoh<false>(a, plan, p, stream);
+}
+
 hipError_t launch_scan(const ScanArgs& a, const ScanPlan& plan, void* ws, hipStream_t stream) {
   ScanParams p{};
   p.x = a.x;
@@ -174,17 +198,7 @@ hipError_t launch_scan(const ScanArgs& a, const ScanPlan& plan, void* ws, hipStr
     e = launch_carry(p.sum_h, p.sum_p, a.h0, a.batch, a.D, a.N, plan.K, stream);
     if (e != hipSuccess) return e;
   }
-  const bool skip = a.Dskip != nullptr, gate = a.z != nullptr;
-  if (zoh) {
-    if (skip && gate) return launch_output_variant<Variant<true, true, true>>(a, plan, p, stream);
-    if (skip) return launch_output_variant<Variant<true, true, false>>(a, plan, p, stream);
-    if (gate) return launch_output_variant<Variant<true, false, true>>(a, plan, p, stream);
-    return launch_output_variant<Variant<true, false, false>>(a, plan, p, stream);
-  }
-  if (skip && gate) return launch_output_variant<Variant<false, true, true>>(a, plan, p, stream);
-  if (skip) return launch_output_variant<Variant<false, true, false>>(a, plan, p, stream);
-  if (gate) return launch_output_variant<Variant<false, false, true>>(a, plan, p, stream);
-  return launch_output_variant<Variant<false, false, false>>(a, plan, p, stream);
+  return launch_output(a, plan, p, stream);
 }
 
 }  // namespace mssm

@@ -8,7 +8,7 @@
 //
 // The step reads and writes the whole [batch, D, N] float32 state once, so it
 // is bound by HBM bandwidth.  Layout on the lanes: a channel's N state values
-// are split over LPD adjacent lanes, NPL = min(N, 4) values each, so a
+// are split over LPD adjacent lane-slots, NPL = min(N, 4) values each, so a
 // wavefront reads and writes contiguous 16-byte pieces of the state; the
 // read-out sum over n is finished with a butterfly over those LPD lanes.
 #include "mssm_internal.h"
@@ -31,7 +31,6 @@ struct StepParams {
   const void* z;
   float* h;
   float* y;
-  int64_t chains;   // batch * D
   int64_t D;
 };
 
@@ -46,59 +45,86 @@ __device__ __forceinline__ void load_f32(const float* p, float (&v)[NPL]) {
   }
 }
 
+// Grid: blockIdx.y is the batch row; along x, each thread takes kSlots
+// lane-slots of that row kStepBlock apart (every load instruction stays
+// contiguous across the wavefront) and issues all their loads before any
+// arithmetic, so several state loads per lane are in flight at once.  Row
+// addressing needs only shifts (LPD is a power of two), no division.
+constexpr int kSlots = 4;
+
 template <int N, typename T, bool kZoh, bool kVec>
 __global__ __launch_bounds__(kStepBlock) void selective_step_kernel(StepParams p) {
-  constexpr int NPL = N < 4 ? N : 4;   // state values per lane
-  constexpr int LPD = N / NPL;         // lanes per channel: 1, 2, 4 or 8
-  const int64_t tid = (int64_t)blockIdx.x * kStepBlock + threadIdx.x;
-  const int64_t g = tid / LPD;         // chain (b, d), row-major over [batch, D]
-  const int part = static_cast<int>(tid % LPD);
-  // LPD divides the block, so a chain's lanes leave together and every lane
-  // that takes part in the butterfly below is active
-  if (g >= p.chains) return;
-  const int64_t b = g / p.D;
-  const int64_t d = g - b * p.D;
+  constexpr int NPL = N < 4 ? N : 4;   // state values per lane-slot
+  constexpr int LPD = N / NPL;         // lane-slots per channel: 1, 2, 4 or 8
+  const int64_t b = blockIdx.y;
+  const int64_t D = p.D;
+  const int64_t total = D * LPD;       // lane-slots in this row
+  const int64_t base = (int64_t)blockIdx.x * (kStepBlock * kSlots) + threadIdx.x;
+  const int part = static_cast<int>(threadIdx.x % LPD);   // same for all of this lane's slots
   const int n0 = part * NPL;
-  const T* xs = static_cast<const T*>(p.x);
-  const T* ds = static_cast<const T*>(p.delta);
-  const T* Bs = static_cast<const T*>(p.B) + b * N + n0;
-  const T* Cs = static_cast<const T*>(p.C) + b * N + n0;
-  const float xv = to_float(xs[g]);
-  const float dv = to_float(ds[g]);
-  float* hp = p.h + g * N + n0;
-  float hv[NPL], av[NPL];
-  load_f32<NPL, kVec>(hp, hv);
-  load_f32<NPL, kVec>(p.A + d * N + n0, av);
-  const float dx = dv * xv;
-  float yp = 0.0f;
+  const T* xs = static_cast<const T*>(p.x) + b * D;
+  const T* ds = static_cast<const T*>(p.delta) + b * D;
+  float* hrow = p.h + b * D * N;
+  float Bv[NPL], Cv[NPL];
+  {
+    const T* Bs = static_cast<const T*>(p.B) + b * N + n0;
+    const T* Cs = static_cast<const T*>(p.C) + b * N + n0;
 #pragma unroll
-  for (int j = 0; j < NPL; ++j) {
-    const float Bn = to_float(Bs[j]);
-    const float abar = fast_exp2(dv * (av[j] * kLog2e));
-    float bx;
-    if constexpr (kZoh) {
-      const float u = xv * Bn / av[j];
-      bx = __builtin_fmaf(abar, u, -u);          // (Abar - 1) / A * B * x
-    } else {
-      bx = dx * Bn;                              // delta B x
+    for (int j = 0; j < NPL; ++j) {
+      Bv[j] = to_float(Bs[j]);
+      Cv[j] = to_float(Cs[j]);
     }
-    hv[j] = __builtin_fmaf(abar, hv[j], bx);
-    yp = __builtin_fmaf(to_float(Cs[j]), hv[j], yp);
+  }
+  float hv[kSlots][NPL], av[kSlots][NPL], xv[kSlots], dv[kSlots];
+#pragma unroll
+  for (int s = 0; s < kSlots; ++s) {
+    // a slot past the row's end re-reads the row's last channel (not stored)
+    const int64_t slot = min(base + (int64_t)s * kStepBlock, total - LPD + part);
+    const int64_t d = slot / LPD;
+    load_f32<NPL, kVec>(hrow + d * N + n0, hv[s]);
+    load_f32<NPL, kVec>(p.A + d * N + n0, av[s]);
+    xv[s] = to_float(xs[d]);
+    dv[s] = to_float(ds[d]);
   }
 #pragma unroll
-  for (int o = 1; o < LPD; o <<= 1) yp += __shfl_xor(yp, o, LPD);
-  if constexpr (kVec && NPL == 4) {
-    f32x4 u;
-    u.x = hv[0]; u.y = hv[1]; u.z = hv[2]; u.w = hv[3];
-    *reinterpret_cast<f32x4*>(hp) = u;
-  } else {
+  for (int s = 0; s < kSlots; ++s) {
+    const int64_t slot = base + (int64_t)s * kStepBlock;
+    const int64_t d = slot / LPD;
+    const float dx = dv[s] * xv[s];
+    float yp = 0.0f;
 #pragma unroll
-    for (int j = 0; j < NPL; ++j) hp[j] = hv[j];
-  }
-  if (part == 0) {
-    if (p.Dskip != nullptr) yp = __builtin_fmaf(p.Dskip[d], xv, yp);
-    if (p.z != nullptr) yp *= silu(to_float(static_cast<const T*>(p.z)[g]));
-    p.y[g] = yp;
+    for (int j = 0; j < NPL; ++j) {
+      const float abar = fast_exp2(dv[s] * (av[s][j] * kLog2e));
+      float bx;
+      if constexpr (kZoh) {
+        const float u = xv[s] * Bv[j] / av[s][j];
+        bx = __builtin_fmaf(abar, u, -u);        // (Abar - 1) / A * B * x
+      } else {
+        bx = dx * Bv[j];                         // delta B x
+      }
+      hv[s][j] = __builtin_fmaf(abar, hv[s][j], bx);
+      yp = __builtin_fmaf(Cv[j], hv[s][j], yp);
+    }
+    // the lane-slots of one channel are adjacent lanes (LPD divides 64 and the
+    // block), and all of them are past the end or none is
+#pragma unroll
+    for (int o = 1; o < LPD; o <<= 1) yp += __shfl_xor(yp, o, LPD);
+    if (slot < total) {
+      float* hp = hrow + d * N + n0;
+      if constexpr (kVec && NPL == 4) {
+        f32x4 u;
+        u.x = hv[s][0]; u.y = hv[s][1]; u.z = hv[s][2]; u.w = hv[s][3];
+        *reinterpret_cast<f32x4*>(hp) = u;
+      } else {
+#pragma unroll
+        for (int j = 0; j < NPL; ++j) hp[j] = hv[s][j];
+      }
+      if (part == 0) {
+        if (p.Dskip != nullptr) yp = __builtin_fmaf(p.Dskip[d], xv[s], yp);
+        if (p.z != nullptr) yp *= silu(to_float(static_cast<const T*>(p.z)[b * D + d]));
+        p.y[b * D + d] = yp;
+      }
+    }
   }
 }
 
@@ -106,16 +132,17 @@ template <int N, typename T, bool kZoh>
 hipError_t launch_step_t(const StepArgs& a, const StepParams& p, hipStream_t stream) {
   constexpr int NPL = N < 4 ? N : 4;
   constexpr int LPD = N / NPL;
-  const int64_t threads = p.chains * LPD;
-  const int64_t grid = (threads + kStepBlock - 1) / kStepBlock;
+  const int64_t row_slots = a.D * LPD;
+  const dim3 grid((unsigned)((row_slots + kStepBlock * kSlots - 1) / (kStepBlock * kSlots)),
+                  (unsigned)a.batch);
   const bool vec = NPL == 4 && reinterpret_cast<uintptr_t>(a.h) % 16 == 0 &&
                    reinterpret_cast<uintptr_t>(a.A) % 16 == 0;
   if (vec)
-    hipLaunchKernelGGL((selective_step_kernel<N, T, kZoh, true>), dim3((unsigned)grid),
-                       dim3(kStepBlock), 0, stream, p);
+    hipLaunchKernelGGL((selective_step_kernel<N, T, kZoh, true>), grid, dim3(kStepBlock), 0,
+                       stream, p);
   else
-    hipLaunchKernelGGL((selective_step_kernel<N, T, kZoh, false>), dim3((unsigned)grid),
-                       dim3(kStepBlock), 0, stream, p);
+    hipLaunchKernelGGL((selective_step_kernel<N, T, kZoh, false>), grid, dim3(kStepBlock), 0,
+                       stream, p);
   return hipGetLastError();
 }
 
@@ -132,7 +159,7 @@ hipError_t launch_step_n(const StepArgs& a, const StepParams& p, hipStream_t str
 }  // namespace
 
 hipError_t launch_step(const StepArgs& a, hipStream_t stream) {
-  StepParams p{a.x, a.delta, a.A, a.B, a.C, a.Dskip, a.z, a.h, a.y, a.batch * a.D, a.D};
+  StepParams p{a.x, a.delta, a.A, a.B, a.C, a.Dskip, a.z, a.h, a.y, a.D};
   switch (a.N) {
     case 1: return launch_step_n<1>(a, p, stream);
     case 2: return launch_step_n<2>(a, p, stream);

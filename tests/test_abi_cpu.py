@@ -178,6 +178,7 @@ def test_step_argument_errors(lib):
     assert _step(lib, p9, 0, 1, 4, 4, dtype=9) == 1
     assert _step(lib, p9, 0, 1, 4, 12) == 2
     assert _step(lib, p9, 0, 1 << 40, 1 << 40, 16) == 3
+    assert _step(lib, p9, 0, 65536, 64, 16) == 2                  # one grid row per batch row
     for i in (0, 1, 2, 3, 4, 7, 8):
         ptrs = list(p9)
         ptrs[i] = None
