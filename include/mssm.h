@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define MSSM_ABI_VERSION 2
+#define MSSM_ABI_VERSION 3
 
 typedef enum {
     MSSM_SUCCESS = 0,
@@ -220,6 +220,59 @@ mssm_status mssm_selective_ssm_fused_fwd(const void *x, const void *W_xproj,
                                          size_t workspace_bytes, int64_t batch, int64_t L,
                                          int64_t D, int64_t N, int64_t R, mssm_dtype dtype,
                                          void *stream);
+
+/*
+ * ---- the Mamba block around the scan -------------------------------------------------------
+ *
+ * "Understanding Mamba", section 8.1, eq. (9), and its block listing (section
+ * 10.2):
+ *     [u | z] = u0 @ W_in                      W_in [Dm, 2 Di]: columns 0..Di-1
+ *                                              give u, columns Di..2Di-1 give z
+ *     x       = SiLU(causal_conv1d(u) + conv_b)
+ *     y       = the fused selective SSM on x  (Delta, B, C from x as in
+ *               mssm_selective_ssm_fused_fwd) with feedthrough Dskip * x
+ *     out     = (y * SiLU(z)) @ W_out          W_out [Di, Dm]
+ * The block has no normalisation and no residual add (they belong to the
+ * model around it, section 8.2).
+ *
+ * causal_conv1d is depthwise: for channel d with taps conv_w[d, 0..k-1],
+ *     c[b,t,d] = sum_i conv_w[d, i] * u[b, t - (k-1) + i, d],   u = 0 before t = 0,
+ * so tap k-1 weighs the current token (the listing's left padding by k - 1
+ * zeros).  k is 1..8.
+ *
+ * mssm_causal_conv1d_silu: out = SiLU(causal_conv1d(u) + conv_b) alone.
+ *   u [batch, L, D] of `dtype`; conv_w [D, k] float32; conv_b [D] float32 or
+ *   NULL; out [batch, L, D] float32.  No workspace.
+ *
+ * mssm_mamba_block_fwd: u0 [batch, L, Dm], W_in, W_x [Di, R + 2N], W_dt [R, Di],
+ * W_out bf16 (dtype must be MSSM_BFLOAT16); conv_w, conv_b (may be NULL),
+ * dt_bias [Di], A [Di, N], Dskip [Di] (may be NULL) float32; out [batch, L, Dm]
+ * float32.  Precision: the projections accumulate in float32; x stays float32
+ * for the scan and the feedthrough; x_proj and W_out take their float32 inputs
+ * (x, and the gated result) as bf16 hi + lo pairs, about 16 significant bits,
+ * one accumulating GEMM per part.  The workspace (256-byte aligned,
+ * mssm_mamba_block_workspace_size bytes) holds u, z, x (float32
+ * [batch*L, Di]), the two bf16 pairs and the fused scan's buffers.  batch, L or Dm equal to zero is a no-op; Di equal to zero writes
+ * zeros to out.
+ */
+mssm_status mssm_causal_conv1d_silu(const void *u, const float *conv_w, const float *conv_b,
+                                    float *out, int64_t batch, int64_t L, int64_t D, int64_t k,
+                                    mssm_dtype dtype, void *stream);
+
+/* 1 if the block is built for state size N, rank R and conv width k, else 0. */
+int mssm_mamba_block_supports(int64_t N, int64_t R, int64_t k);
+
+mssm_status mssm_mamba_block_workspace_size(int64_t batch, int64_t L, int64_t Dm, int64_t Di,
+                                            int64_t N, int64_t R, int64_t k, mssm_dtype dtype,
+                                            size_t *bytes);
+
+mssm_status mssm_mamba_block_fwd(const void *u0, const void *W_in, const float *conv_w,
+                                 const float *conv_b, const void *W_x, const void *W_dt,
+                                 const float *dt_bias, const float *A, const float *Dskip,
+                                 const void *W_out, float *out, void *workspace,
+                                 size_t workspace_bytes, int64_t batch, int64_t L, int64_t Dm,
+                                 int64_t Di, int64_t N, int64_t R, int64_t k, mssm_dtype dtype,
+                                 void *stream);
 
 #ifdef __cplusplus
 }

@@ -28,9 +28,12 @@ Modules:
     selection  -- softplus, SiLU, the fused x_proj/dt_proj projections
     forms      -- independent closed forms used as pins: combine operator and
                   tree scans, unrolled sum, semiseparable matrix, convolution
+    block      -- the Mamba block around the scan: causal depthwise conv1d,
+                  SiLU, projections, gate (eq. (9))
 Parity status of each function is stated in its docstring; every function is
 pinned by a ``-m "not gpu"`` test unless it says "parity unpinned".
 """
 from .scan import selective_scan, selective_scan_step, load_library, build_library  # noqa: F401
 from .selection import softplus, silu, selective_ssm_fused, round_to_bf16  # noqa: F401
 from . import forms  # noqa: F401
+from . import block  # noqa: F401

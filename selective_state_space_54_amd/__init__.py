@@ -6,10 +6,16 @@ binding (mssm.py) whose functions carry the C entry points' names.
 """
 from .mssm import (  # noqa: F401
     MssmError,
+    causal_conv1d_silu,
     exported_symbols,
     load,
+    mamba_block,
     mssm_abi_version,
+    mssm_causal_conv1d_silu,
     mssm_fused_supports,
+    mssm_mamba_block_fwd,
+    mssm_mamba_block_supports,
+    mssm_mamba_block_workspace_size,
     mssm_selective_ssm_fused_fwd,
     mssm_selective_ssm_fused_workspace_size,
     mssm_selective_scan_fwd,

@@ -20,6 +20,11 @@
 //             unit, and is parked in the wavefront's slice of LDS for the step
 //             loop.  B_t and C_t are read as float32 rows of P (stride R + 2N)
 //             through the scalar unit.
+//
+// The same scan kernels serve the Mamba block ("Understanding Mamba", section
+// 8.1, eq. (9)): there x is the float32 output of the conv + SiLU prologue, the
+// feedthrough D x and the SiLU(z) gate are applied per step, and the gated
+// result is stored as bfloat16 for the output projection (FusedVariant).
 #include <rocblas/rocblas.h>
 
 #include <algorithm>
@@ -103,39 +108,68 @@ __device__ __forceinline__ void delta_tile(const uint16_t* __restrict__ dtl,
   }
 }
 
+// What the fused scan reads and writes:
+//   TX    : element type of x (bfloat16 bits or float32)
+//   kSkip : y += Dskip[d] * x
+//   kGate : y *= SiLU(z[b, t, d]), z float32 [batch, L, D]
+//   TY    : element type of the stored y: float32, or bfloat16 bits, in which
+//           case y is stored as a pair of arrays hi = bf16(y), lo = bf16(y - hi)
+//           (round to nearest even; hi + lo keeps about 16 significant bits)
+template <typename TX_, bool kSkip_, bool kGate_, typename TY_>
+struct FusedVariant {
+  using TX = TX_;
+  using TY = TY_;
+  static constexpr bool kSkip = kSkip_;
+  static constexpr bool kGate = kGate_;
+};
+using FusedPlainVariant = FusedVariant<uint16_t, false, false, float>;
+
 // The fused step loop: as scan_steps, with Delta from the LDS tile and B/C
 // float32 rows of P (row stride ldbc floats).
-template <int N, int CPL, bool kWithY>
-__device__ __forceinline__ void fused_steps(const uint16_t* __restrict__ xb,
+template <int N, int CPL, bool kWithY, class FV>
+__device__ __forceinline__ void fused_steps(const typename FV::TX* __restrict__ xb,
+                                            const float* __restrict__ zb,
                                             const uint16_t* __restrict__ dtl,
                                             const uint16_t* __restrict__ dtl_lo,
                                             const uint16_t* __restrict__ wT,
                                             const float* __restrict__ bias, int R,
                                             const float* __restrict__ Bb, const float* __restrict__ Cb,
-                                            int64_t ldbc, float* __restrict__ yb,
-                                            const float (&A2)[CPL][N], float (&h)[CPL][N],
-                                            double (&S)[CPL], int wlane, int wave_ch0, int ch_valid,
-                                            int64_t D, int nsteps, float* __restrict__ lds,
-                                            int stride) {
+                                            int64_t ldbc, typename FV::TY* __restrict__ yb,
+                                            typename FV::TY* __restrict__ ylo,
+                                            const float (&A2)[CPL][N], const float (&Dd)[CPL],
+                                            float (&h)[CPL][N], double (&S)[CPL], int wlane,
+                                            int wave_ch0, int ch_valid, int64_t D, int nsteps,
+                                            float* __restrict__ lds, int stride) {
+  using TX = typename FV::TX;
+  using TY = typename FV::TY;
+  constexpr bool kGate = kWithY && FV::kGate;
   constexpr int kTile = (CPL == 1) ? 8 : 4;
-  const uint32_t in_bytes = static_cast<uint32_t>((int64_t)nsteps * D * sizeof(uint16_t));
+  const uint32_t in_bytes = static_cast<uint32_t>((int64_t)nsteps * D * sizeof(TX));
   const buf_t xr = make_buf(xb, in_bytes);
-  const int in_row = static_cast<int>(D * sizeof(uint16_t));
+  const int in_row = static_cast<int>(D * sizeof(TX));
   const int lane_blk = wave_ch0 + wlane * CPL;   // lane's first channel inside the block
-  const int in_lane = lane_blk * static_cast<int>(sizeof(uint16_t));
-  buf_t yr;
+  const int in_lane = lane_blk * static_cast<int>(sizeof(TX));
+  buf_t zr;
+  if constexpr (kGate) zr = make_buf(zb, static_cast<uint32_t>((int64_t)nsteps * D * sizeof(float)));
+  const int z_row = static_cast<int>(D * sizeof(float));
+  const int z_lane = lane_blk * static_cast<int>(sizeof(float));
+  buf_t yr, ylr;
   int out_row = 0, out_lane = 0;
   if constexpr (kWithY) {
-    yr = make_buf(yb, static_cast<uint32_t>((int64_t)nsteps * D * sizeof(float)));
-    out_row = static_cast<int>(D * sizeof(float));
-    out_lane = lane_blk * static_cast<int>(sizeof(float));
+    yr = make_buf(yb, static_cast<uint32_t>((int64_t)nsteps * D * sizeof(TY)));
+    if constexpr (sizeof(TY) == 2)
+      ylr = make_buf(ylo, static_cast<uint32_t>((int64_t)nsteps * D * sizeof(TY)));
+    out_row = static_cast<int>(D * sizeof(TY));
+    out_lane = lane_blk * static_cast<int>(sizeof(TY));
   }
   const int last = nsteps > 0 ? nsteps - 1 : 0;
-  float xc[kTile][CPL];
+  float xc[kTile][CPL], zc[kGate ? kTile : 1][CPL];
 #pragma unroll
   for (int j = 0; j < kTile; ++j) {
-    const int soff = __builtin_amdgcn_readfirstlane(min(j, last) * in_row);
-    buf_load_vals<uint16_t, CPL>(xr, in_lane, soff, xc[j]);
+    const int r = min(j, last);
+    buf_load_vals<TX, CPL>(xr, in_lane, __builtin_amdgcn_readfirstlane(r * in_row), xc[j]);
+    if constexpr (kGate)
+      buf_load_vals<float, CPL>(zr, z_lane, __builtin_amdgcn_readfirstlane(r * z_row), zc[j]);
   }
   float Bv[2][N], Cv[2][N];
   if (nsteps > 0) {
@@ -147,11 +181,13 @@ __device__ __forceinline__ void fused_steps(const uint16_t* __restrict__ xb,
       delta_tile<CPL>(dtl + (int64_t)base * R, dtl_lo + (int64_t)base * R,
                       min(kDTile, nsteps - base), wT, bias, R, lds, stride,
                       static_cast<int>(threadIdx.x % 64), ch_valid);
-    float xn[kTile][CPL];
+    float xn[kTile][CPL], zn[kGate ? kTile : 1][CPL];
 #pragma unroll
     for (int j = 0; j < kTile; ++j) {
-      const int soff = __builtin_amdgcn_readfirstlane(min(base + kTile + j, last) * in_row);
-      buf_load_vals<uint16_t, CPL>(xr, in_lane, soff, xn[j]);
+      const int r = min(base + kTile + j, last);
+      buf_load_vals<TX, CPL>(xr, in_lane, __builtin_amdgcn_readfirstlane(r * in_row), xn[j]);
+      if constexpr (kGate)
+        buf_load_vals<float, CPL>(zr, z_lane, __builtin_amdgcn_readfirstlane(r * z_row), zn[j]);
     }
 #pragma unroll
     for (int j = 0; j < kTile; ++j) {
@@ -181,9 +217,25 @@ __device__ __forceinline__ void fused_steps(const uint16_t* __restrict__ xb,
           }
         }
         if constexpr (kWithY) {
+#pragma unroll
+          for (int c = 0; c < CPL; ++c) {
+            if constexpr (FV::kSkip) yv[c] = __builtin_fmaf(Dd[c], xc[j][c], yv[c]);
+            if constexpr (kGate) yv[c] *= silu(zc[j][c]);
+          }
           // lanes past the last channel repeat the last valid channel (clamped
           // addressing), so they store the same value to the same place
-          buf_store_vals<CPL>(yr, out_lane, s * out_row, yv);
+          if constexpr (sizeof(TY) == 2) {
+            float hi[CPL], lo[CPL];
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) {
+              hi[c] = __uint_as_float(bf16_rne_bits(yv[c]) << 16);
+              lo[c] = yv[c] - hi[c];
+            }
+            buf_store_bf16<CPL>(yr, out_lane, s * out_row, hi);
+            buf_store_bf16<CPL>(ylr, out_lane, s * out_row, lo);
+          } else {
+            buf_store_vals<CPL>(yr, out_lane, s * out_row, yv);
+          }
         } else {
 #pragma unroll
           for (int c = 0; c < CPL; ++c) S[c] += static_cast<double>(dt[c]);
@@ -193,7 +245,10 @@ __device__ __forceinline__ void fused_steps(const uint16_t* __restrict__ xb,
 #pragma unroll
     for (int j = 0; j < kTile; ++j)
 #pragma unroll
-      for (int c = 0; c < CPL; ++c) xc[j][c] = xn[j][c];
+      for (int c = 0; c < CPL; ++c) {
+        xc[j][c] = xn[j][c];
+        if constexpr (kGate) zc[j][c] = zn[j][c];
+      }
   }
 }
 
@@ -230,25 +285,27 @@ __device__ __forceinline__ FusedCoord fused_coord(int64_t n_dtiles, int K, int64
 template <int CPL>
 constexpr int lds_stride() { return 64 * CPL + 2 * CPL; }   // padded against bank conflicts
 
-template <int N, int CPL>
+template <int N, int CPL, typename TX>
 __global__ __launch_bounds__(kFBlock) void fused_summary_kernel(
-    const uint16_t* __restrict__ x, const uint16_t* __restrict__ dtlow,
+    const TX* __restrict__ x, const uint16_t* __restrict__ dtlow,
     const uint16_t* __restrict__ dtlow_lo,
     const uint16_t* __restrict__ wT, const float* __restrict__ bias,
     const float* __restrict__ A, const float* __restrict__ P, float* __restrict__ sum_h,
     float* __restrict__ sum_p, int64_t L, int64_t D, int R, int64_t chunk_len, int K,
     int64_t n_dtiles) {
+  using FV = FusedVariant<TX, false, false, float>;
   __shared__ float lds_all[4][kDTile * lds_stride<CPL>()];
   const FusedCoord c = fused_coord<CPL>(n_dtiles, K - 1, D);
   if (c.d0 + c.wave_ch0 >= D) return;   // wavefront past the last channel (no barriers here)
   float* lds = lds_all[threadIdx.x / 64];
   const int64_t wave_d = c.d0 + c.wave_ch0;
   const int64_t dl = wave_d + (int64_t)c.wlane * CPL;
-  float A2[CPL][N], h[CPL][N];
+  float A2[CPL][N], h[CPL][N], Dd[CPL];
   double S[CPL];
 #pragma unroll
   for (int q = 0; q < CPL; ++q) {
     S[q] = 0.0;
+    Dd[q] = 0.0f;
 #pragma unroll
     for (int n = 0; n < N; ++n) {
       A2[q][n] = A[(dl + q) * N + n] * kLog2e;
@@ -259,10 +316,11 @@ __global__ __launch_bounds__(kFBlock) void fused_summary_kernel(
   const int nsteps = static_cast<int>(chunk_len);
   const int64_t ldbc = R + 2 * N;
   const int64_t tok0 = c.b * L + t0;
-  fused_steps<N, CPL, false>(x + tok0 * D + c.d0, dtlow + tok0 * R, dtlow_lo + tok0 * R,
-                             wT + wave_d * R, bias + wave_d,
-                             R, P + tok0 * ldbc + R, nullptr, ldbc, nullptr, A2, h, S, c.wlane,
-                             c.wave_ch0, c.ch_valid, D, nsteps, lds, lds_stride<CPL>());
+  fused_steps<N, CPL, false, FV>(x + tok0 * D + c.d0, nullptr, dtlow + tok0 * R,
+                                 dtlow_lo + tok0 * R, wT + wave_d * R, bias + wave_d, R,
+                                 P + tok0 * ldbc + R, nullptr, ldbc, nullptr, nullptr, A2, Dd, h, S,
+                                 c.wlane, c.wave_ch0, c.ch_valid, D, nsteps, lds,
+                                 lds_stride<CPL>());
   if (c.active) {
     const int64_t row = c.b * (K - 1) + c.k;
 #pragma unroll
@@ -276,25 +334,27 @@ __global__ __launch_bounds__(kFBlock) void fused_summary_kernel(
   }
 }
 
-template <int N, int CPL>
+template <int N, int CPL, class FV>
 __global__ __launch_bounds__(kFBlock) void fused_output_kernel(
-    const uint16_t* __restrict__ x, const uint16_t* __restrict__ dtlow,
+    const typename FV::TX* __restrict__ x, const float* __restrict__ z,
+    const float* __restrict__ Dskip, const uint16_t* __restrict__ dtlow,
     const uint16_t* __restrict__ dtlow_lo,
     const uint16_t* __restrict__ wT, const float* __restrict__ bias,
     const float* __restrict__ A, const float* __restrict__ P, const float* __restrict__ sum_h,
-    float* __restrict__ y, int64_t L, int64_t D, int R, int64_t chunk_len, int K,
-    int64_t n_dtiles) {
+    typename FV::TY* __restrict__ y, typename FV::TY* __restrict__ y_lo, int64_t L, int64_t D,
+    int R, int64_t chunk_len, int K, int64_t n_dtiles) {
   __shared__ float lds_all[4][kDTile * lds_stride<CPL>()];
   const FusedCoord c = fused_coord<CPL>(n_dtiles, K, D);
   if (c.d0 + c.wave_ch0 >= D) return;   // wavefront past the last channel (no barriers here)
   float* lds = lds_all[threadIdx.x / 64];
   const int64_t wave_d = c.d0 + c.wave_ch0;
   const int64_t dl = wave_d + (int64_t)c.wlane * CPL;
-  float A2[CPL][N], h[CPL][N];
+  float A2[CPL][N], h[CPL][N], Dd[CPL];
   double S_unused[CPL];
 #pragma unroll
   for (int q = 0; q < CPL; ++q) {
     S_unused[q] = 0.0;
+    Dd[q] = FV::kSkip ? Dskip[dl + q] : 0.0f;
 #pragma unroll
     for (int n = 0; n < N; ++n) {
       A2[q][n] = A[(dl + q) * N + n] * kLog2e;
@@ -312,18 +372,13 @@ __global__ __launch_bounds__(kFBlock) void fused_output_kernel(
   const int nsteps = static_cast<int>(std::min<int64_t>(chunk_len, L - t0));
   const int64_t ldbc = R + 2 * N;
   const int64_t tok0 = c.b * L + t0;
-  fused_steps<N, CPL, true>(x + tok0 * D + c.d0, dtlow + tok0 * R, dtlow_lo + tok0 * R,
-                            wT + wave_d * R, bias + wave_d,
-                            R, P + tok0 * ldbc + R, P + tok0 * ldbc + R + N, ldbc,
-                            y + tok0 * D + c.d0, A2, h, S_unused, c.wlane, c.wave_ch0, c.ch_valid,
-                            D, nsteps, lds, lds_stride<CPL>());
-}
-
-__device__ __forceinline__ uint16_t bf16_rne(float f) {
-  const uint32_t u = __float_as_uint(f);
-  uint32_t v = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
-  if ((u & 0x7fffffffu) > 0x7f800000u) v = (u >> 16) | 0x40u;   // NaN stays NaN
-  return static_cast<uint16_t>(v);
+  fused_steps<N, CPL, true, FV>(x + tok0 * D + c.d0, FV::kGate ? z + tok0 * D + c.d0 : nullptr,
+                                dtlow + tok0 * R, dtlow_lo + tok0 * R, wT + wave_d * R,
+                                bias + wave_d, R, P + tok0 * ldbc + R, P + tok0 * ldbc + R + N,
+                                ldbc, y + tok0 * D + c.d0,
+                                sizeof(typename FV::TY) == 2 ? y_lo + tok0 * D + c.d0 : nullptr,
+                                A2, Dd, h, S_unused, c.wlane,
+                                c.wave_ch0, c.ch_valid, D, nsteps, lds, lds_stride<CPL>());
 }
 
 // hi[m, r] = bf16(P[m, r]), lo[m, r] = bf16(P[m, r] - hi[m, r]) (round to nearest
@@ -336,9 +391,9 @@ __global__ void dtlow_split_kernel(const float* __restrict__ P, uint16_t* __rest
     const int64_t m = i / R;
     const int r = static_cast<int>(i % R);
     const float v = P[m * ldp + r];
-    const uint16_t h = bf16_rne(v);
-    hi[i] = h;
-    lo[i] = bf16_rne(v - __uint_as_float(static_cast<uint32_t>(h) << 16));
+    const uint32_t h = bf16_rne_bits(v);
+    hi[i] = static_cast<uint16_t>(h);
+    lo[i] = static_cast<uint16_t>(bf16_rne_bits(v - __uint_as_float(h << 16)));
   }
 }
 
@@ -360,7 +415,101 @@ size_t align256(size_t v) { return (v + 255) / 256 * 256; }
 std::mutex g_blas_mutex;
 rocblas_handle g_blas[64] = {};
 
+template <int N, int CPL, class FV>
+hipError_t launch_fused_scan_t(const FusedScanArgs& a, const ScanPlan& p, hipStream_t stream) {
+  using TX = typename FV::TX;
+  using TY = typename FV::TY;
+  const TX* x = static_cast<const TX*>(a.x);
+  TY* y = static_cast<TY*>(a.y);
+  const int64_t n_dtiles = (a.D + kFBlock * CPL - 1) / (kFBlock * CPL);
+  const int R = static_cast<int>(a.R);
+  if (p.K > 1) {
+    const int64_t grid = n_dtiles * (p.K - 1) * a.batch;
+    hipLaunchKernelGGL((fused_summary_kernel<N, CPL, TX>), dim3((unsigned)grid), dim3(kFBlock), 0,
+                       stream, x, a.dtl, a.dtl_lo, a.wT, a.dt_bias, a.A, a.P, a.sum_h, a.sum_p,
+                       a.L, a.D, R, p.chunk_len, p.K, n_dtiles);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    e = launch_carry(a.sum_h, a.sum_p, nullptr, a.batch, a.D, a.N, p.K, stream);
+    if (e != hipSuccess) return e;
+  }
+  const int64_t grid = n_dtiles * p.K * a.batch;
+  hipLaunchKernelGGL((fused_output_kernel<N, CPL, FV>), dim3((unsigned)grid), dim3(kFBlock), 0,
+                     stream, x, a.z, a.Dskip, a.dtl, a.dtl_lo, a.wT, a.dt_bias, a.A, a.P, a.sum_h,
+                     y, static_cast<TY*>(a.y_lo), a.L, a.D, R, p.chunk_len, p.K, n_dtiles);
+  return hipGetLastError();
+}
+
+template <int N, class FV>
+hipError_t launch_fused_scan_n(const FusedScanArgs& a, const ScanPlan& p, hipStream_t stream) {
+  return p.cpl == 2 ? launch_fused_scan_t<N, 2, FV>(a, p, stream)
+                    : launch_fused_scan_t<N, 1, FV>(a, p, stream);
+}
+
+template <class FV>
+hipError_t launch_fused_scan_v(const FusedScanArgs& a, const ScanPlan& p, hipStream_t stream) {
+  switch (a.N) {
+    case 1: return launch_fused_scan_n<1, FV>(a, p, stream);
+    case 2: return launch_fused_scan_n<2, FV>(a, p, stream);
+    case 4: return launch_fused_scan_n<4, FV>(a, p, stream);
+    case 8: return launch_fused_scan_n<8, FV>(a, p, stream);
+    case 16: return launch_fused_scan_n<16, FV>(a, p, stream);
+    case 32: return launch_fused_scan_n<32, FV>(a, p, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 }  // namespace
+
+bool blas_handle(hipStream_t stream, rocblas_handle* out, hipError_t* hip_error) {
+  *hip_error = hipSuccess;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) { *hip_error = e; return false; }
+  if (dev < 0 || dev >= 64) { *hip_error = hipErrorInvalidDevice; return false; }
+  std::lock_guard<std::mutex> lock(g_blas_mutex);
+  if (!g_blas[dev]) {
+    if (rocblas_create_handle(&g_blas[dev]) != rocblas_status_success) {
+      g_blas[dev] = nullptr;
+      return false;
+    }
+  }
+  if (rocblas_set_stream(g_blas[dev], stream) != rocblas_status_success) return false;
+  *out = g_blas[dev];
+  return true;
+}
+
+bool gemm_rm_bf16(rocblas_handle h, int64_t M, int64_t n, int64_t k, const void* A, int64_t lda,
+                  const void* B, int64_t ldb, float* C, int64_t ldc, float beta) {
+  // row-major C = A B is column-major C^T = B^T A^T: (n x M) = (n x k)(k x M)
+  const float alpha = 1.0f;
+  return rocblas_gemm_ex(h, rocblas_operation_none, rocblas_operation_none, (rocblas_int)n,
+                         (rocblas_int)M, (rocblas_int)k, &alpha, B, rocblas_datatype_bf16_r,
+                         (rocblas_int)ldb, A, rocblas_datatype_bf16_r, (rocblas_int)lda, &beta, C,
+                         rocblas_datatype_f32_r, (rocblas_int)ldc, C, rocblas_datatype_f32_r,
+                         (rocblas_int)ldc, rocblas_datatype_f32_r, rocblas_gemm_algo_standard, 0,
+                         0) == rocblas_status_success;
+}
+
+hipError_t launch_fused_prep(const float* P, int64_t M, int64_t R, int64_t ldp, const void* W_dt,
+                             int64_t D, uint16_t* dtl, uint16_t* dtl_lo, uint16_t* wT,
+                             hipStream_t stream) {
+  hipLaunchKernelGGL(dtlow_split_kernel, dim3(2048), dim3(256), 0, stream, P, dtl, dtl_lo, M,
+                     static_cast<int>(R), ldp);
+  hipLaunchKernelGGL(transpose_bf16_kernel, dim3(1024), dim3(256), 0, stream,
+                     static_cast<const uint16_t*>(W_dt), wT, static_cast<int>(R), D);
+  return hipGetLastError();
+}
+
+hipError_t launch_fused_scan(const FusedScanArgs& a, const ScanPlan& p, hipStream_t stream) {
+  if (!a.x_f32) {
+    if (a.z || a.Dskip || a.y_bf16) return hipErrorInvalidValue;
+    return launch_fused_scan_v<FusedPlainVariant>(a, p, stream);
+  }
+  if (!a.z || !a.y_bf16 || !a.y_lo) return hipErrorInvalidValue;   // the block's form only
+  if (a.Dskip) return launch_fused_scan_v<FusedVariant<float, true, true, uint16_t>>(a, p, stream);
+  return launch_fused_scan_v<FusedVariant<float, false, true, uint16_t>>(a, p, stream);
+}
 
 FusedPlan plan_fused(int64_t batch, int64_t L, int64_t D, int64_t N, int64_t R, int cpl) {
   FusedPlan f;
@@ -388,47 +537,6 @@ int choose_fused_cpl(int64_t D) {
   return D % 2 == 0 ? 2 : 1;
 }
 
-template <int N, int CPL>
-static hipError_t launch_fused_scan(const FusedArgs& a, const FusedPlan& f, char* ws,
-                                    hipStream_t stream) {
-  const ScanPlan& p = f.scan;
-  const uint16_t* x = static_cast<const uint16_t*>(a.x);
-  const float* P = reinterpret_cast<const float*>(ws);
-  const uint16_t* dtl = reinterpret_cast<const uint16_t*>(ws + f.dtl_offset);
-  const uint16_t* dtl_lo = reinterpret_cast<const uint16_t*>(ws + f.dtl_lo_offset);
-  const uint16_t* wT = reinterpret_cast<const uint16_t*>(ws + f.wt_offset);
-  float* sum_h = nullptr;
-  float* sum_p = nullptr;
-  const int64_t n_dtiles = (a.D + kFBlock * CPL - 1) / (kFBlock * CPL);
-  const int R = static_cast<int>(a.R);
-  if (p.K > 1) {
-    sum_h = reinterpret_cast<float*>(ws + f.scan_offset);
-    sum_p = reinterpret_cast<float*>(ws + f.scan_offset + p.sum_p_offset);
-    const int64_t grid = n_dtiles * (p.K - 1) * a.batch;
-    hipLaunchKernelGGL((fused_summary_kernel<N, CPL>), dim3((unsigned)grid), dim3(kFBlock), 0, stream,
-                       x, dtl, dtl_lo, wT, a.dt_bias, a.A, P, sum_h, sum_p, a.L, a.D, R, p.chunk_len,
-                       p.K,
-                       n_dtiles);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    e = launch_carry(sum_h, sum_p, nullptr, a.batch, a.D, a.N, p.K, stream);
-    if (e != hipSuccess) return e;
-  }
-  const int64_t grid = n_dtiles * p.K * a.batch;
-  hipLaunchKernelGGL((fused_output_kernel<N, CPL>), dim3((unsigned)grid), dim3(kFBlock), 0, stream,
-                     x, dtl, dtl_lo, wT, a.dt_bias, a.A, P, sum_h, a.y, a.L, a.D, R, p.chunk_len,
-                     p.K,
-                     n_dtiles);
-  return hipGetLastError();
-}
-
-template <int N>
-static hipError_t launch_fused_n(const FusedArgs& a, const FusedPlan& f, char* ws,
-                                 hipStream_t stream) {
-  return f.scan.cpl == 2 ? launch_fused_scan<N, 2>(a, f, ws, stream)
-                         : launch_fused_scan<N, 1>(a, f, ws, stream);
-}
-
 FusedStatus launch_fused(const FusedArgs& a, const FusedPlan& f, void* workspace,
                          hipStream_t stream) {
   FusedStatus st;
@@ -436,49 +544,40 @@ FusedStatus launch_fused(const FusedArgs& a, const FusedPlan& f, void* workspace
   float* P = reinterpret_cast<float*>(ws);
   const int64_t M = a.batch * a.L;
   const int64_t ldp = a.R + 2 * a.N;
-  // x_proj on rocBLAS (column-major view: P^T[ldp, M] = W_x^T[ldp, D] * x^T[D, M])
-  {
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) { st.hip = e; return st; }
-    if (dev < 0 || dev >= 64) { st.hip = hipErrorInvalidDevice; return st; }
-    std::lock_guard<std::mutex> lock(g_blas_mutex);
-    if (!g_blas[dev]) {
-      if (rocblas_create_handle(&g_blas[dev]) != rocblas_status_success) {
-        g_blas[dev] = nullptr;
-        st.blas_failed = true;
-        return st;
-      }
-    }
-    rocblas_handle hb = g_blas[dev];
-    if (rocblas_set_stream(hb, stream) != rocblas_status_success) { st.blas_failed = true; return st; }
-    const float alpha = 1.0f, beta = 0.0f;
-    const rocblas_status bs = rocblas_gemm_ex(
-        hb, rocblas_operation_none, rocblas_operation_none, (rocblas_int)ldp, (rocblas_int)M,
-        (rocblas_int)a.D, &alpha, a.W_x, rocblas_datatype_bf16_r, (rocblas_int)ldp, a.x,
-        rocblas_datatype_bf16_r, (rocblas_int)a.D, &beta, P, rocblas_datatype_f32_r,
-        (rocblas_int)ldp, P, rocblas_datatype_f32_r, (rocblas_int)ldp, rocblas_datatype_f32_r,
-        rocblas_gemm_algo_standard, 0, 0);
-    if (bs != rocblas_status_success) { st.blas_failed = true; return st; }
+  rocblas_handle hb;
+  if (!blas_handle(stream, &hb, &st.hip)) {
+    st.blas_failed = st.hip == hipSuccess;
+    return st;
+  }
+  // x_proj: P[M, R + 2N] = x[M, D] W_x[D, R + 2N]
+  if (!gemm_rm_bf16(hb, M, ldp, a.D, a.x, a.D, a.W_x, ldp, P, ldp, 0.0f)) {
+    st.blas_failed = true;
+    return st;
   }
   uint16_t* dtl = reinterpret_cast<uint16_t*>(ws + f.dtl_offset);
   uint16_t* dtl_lo = reinterpret_cast<uint16_t*>(ws + f.dtl_lo_offset);
   uint16_t* wT = reinterpret_cast<uint16_t*>(ws + f.wt_offset);
-  hipLaunchKernelGGL(dtlow_split_kernel, dim3(2048), dim3(256), 0, stream, P, dtl, dtl_lo, M,
-                     static_cast<int>(a.R), ldp);
-  hipLaunchKernelGGL(transpose_bf16_kernel, dim3(1024), dim3(256), 0, stream,
-                     static_cast<const uint16_t*>(a.W_dt), wT, static_cast<int>(a.R), a.D);
-  st.hip = hipGetLastError();
+  st.hip = launch_fused_prep(P, M, a.R, ldp, a.W_dt, a.D, dtl, dtl_lo, wT, stream);
   if (st.hip != hipSuccess) return st;
-  switch (a.N) {
-    case 1: st.hip = launch_fused_n<1>(a, f, ws, stream); break;
-    case 2: st.hip = launch_fused_n<2>(a, f, ws, stream); break;
-    case 4: st.hip = launch_fused_n<4>(a, f, ws, stream); break;
-    case 8: st.hip = launch_fused_n<8>(a, f, ws, stream); break;
-    case 16: st.hip = launch_fused_n<16>(a, f, ws, stream); break;
-    case 32: st.hip = launch_fused_n<32>(a, f, ws, stream); break;
-    default: st.hip = hipErrorInvalidValue;
+  FusedScanArgs sa{};
+  sa.x = a.x;
+  sa.y = a.y;
+  sa.P = P;
+  sa.dtl = dtl;
+  sa.dtl_lo = dtl_lo;
+  sa.wT = wT;
+  sa.dt_bias = a.dt_bias;
+  sa.A = a.A;
+  if (f.scan.K > 1) {
+    sa.sum_h = reinterpret_cast<float*>(ws + f.scan_offset);
+    sa.sum_p = reinterpret_cast<float*>(ws + f.scan_offset + f.scan.sum_p_offset);
   }
+  sa.batch = a.batch;
+  sa.L = a.L;
+  sa.D = a.D;
+  sa.N = a.N;
+  sa.R = a.R;
+  st.hip = launch_fused_scan(sa, f.scan, stream);
   return st;
 }
 

@@ -271,3 +271,129 @@ mssm_status mssm_selective_ssm_fused_fwd(const void* x, const void* W_xproj, con
 }
 
 }  // extern "C"
+
+namespace {
+
+bool fits_grid(int64_t blocks) {
+  return blocks <= static_cast<int64_t>(std::numeric_limits<uint32_t>::max());
+}
+
+mssm_status check_conv(int64_t batch, int64_t L, int64_t D, int64_t k, mssm_dtype dtype) {
+  if (batch < 0 || L < 0 || D < 0 || k < 1) return MSSM_ERROR_INVALID_VALUE;
+  if (dtype != MSSM_FLOAT32 && dtype != MSSM_BFLOAT16) return MSSM_ERROR_INVALID_VALUE;
+  if (k > 8) return MSSM_ERROR_NOT_SUPPORTED;
+  int64_t bl, bld, bytes;
+  if (!mul_ok(batch, L, &bl) || !mul_ok(bl, D, &bld) || !mul_ok(bld, 8, &bytes))
+    return MSSM_ERROR_SIZE_OVERFLOW;
+  int64_t blocks;
+  if (!mul_ok((D + 255) / 256, (L + 63) / 64, &blocks) || !mul_ok(blocks, batch, &blocks))
+    return MSSM_ERROR_SIZE_OVERFLOW;
+  if (!fits_grid(blocks)) return MSSM_ERROR_NOT_SUPPORTED;
+  return MSSM_SUCCESS;
+}
+
+}  // namespace
+
+extern "C" {
+
+mssm_status mssm_causal_conv1d_silu(const void* u, const float* conv_w, const float* conv_b,
+                                    float* out, int64_t batch, int64_t L, int64_t D, int64_t k,
+                                    mssm_dtype dtype, void* stream) {
+  const mssm_status s = check_conv(batch, L, D, k, dtype);
+  if (s != MSSM_SUCCESS) return s;
+  if (batch == 0 || L == 0 || D == 0) return MSSM_SUCCESS;
+  if (!u || !conv_w || !out) return MSSM_ERROR_INVALID_VALUE;
+  const hipError_t e = mssm::launch_conv1d_silu(u, dtype == MSSM_FLOAT32, conv_w, conv_b, out,
+                                                nullptr, nullptr, batch, L, D,
+                                                static_cast<int>(k),
+                                                static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) {
+    set_hip_error(e, "causal conv1d launch");
+    return MSSM_ERROR_HIP;
+  }
+  return MSSM_SUCCESS;
+}
+
+int mssm_mamba_block_supports(int64_t N, int64_t R, int64_t k) {
+  return (mssm_fused_supports(N, R) && k >= 1 && k <= 8) ? 1 : 0;
+}
+
+}  // extern "C"
+
+namespace {
+
+mssm_status check_block(int64_t batch, int64_t L, int64_t Dm, int64_t Di, int64_t N, int64_t R,
+                        int64_t k, mssm_dtype dtype) {
+  if (Dm < 0 || k < 1) return MSSM_ERROR_INVALID_VALUE;
+  mssm_status s = check_fused(batch, L, Di, N, R, dtype);
+  if (s != MSSM_SUCCESS) return s;
+  s = check_conv(batch, L, Di, k, dtype);
+  if (s != MSSM_SUCCESS) return s;
+  int64_t m, t;
+  if (!mul_ok(batch, L, &m) || !mul_ok(m, Dm, &t) || !mul_ok(t, 8, &t) ||
+      !mul_ok(m, Di, &t) || !mul_ok(t, 24, &t))
+    return MSSM_ERROR_SIZE_OVERFLOW;
+  if (Dm > std::numeric_limits<int32_t>::max() || 2 * Di > std::numeric_limits<int32_t>::max())
+    return MSSM_ERROR_NOT_SUPPORTED;                               // 32-bit GEMM sizes
+  return MSSM_SUCCESS;
+}
+
+}  // namespace
+
+extern "C" {
+
+mssm_status mssm_mamba_block_workspace_size(int64_t batch, int64_t L, int64_t Dm, int64_t Di,
+                                            int64_t N, int64_t R, int64_t k, mssm_dtype dtype,
+                                            size_t* bytes) {
+  if (!bytes) return MSSM_ERROR_INVALID_VALUE;
+  const mssm_status s = check_block(batch, L, Dm, Di, N, R, k, dtype);
+  if (s != MSSM_SUCCESS) return s;
+  *bytes = (batch == 0 || L == 0 || Di == 0 || Dm == 0)
+               ? 0
+               : mssm::block_workspace_bound(batch, L, Dm, Di, N, R);
+  return MSSM_SUCCESS;
+}
+
+mssm_status mssm_mamba_block_fwd(const void* u0, const void* W_in, const float* conv_w,
+                                 const float* conv_b, const void* W_x, const void* W_dt,
+                                 const float* dt_bias, const float* A, const float* Dskip,
+                                 const void* W_out, float* out, void* workspace,
+                                 size_t workspace_bytes, int64_t batch, int64_t L, int64_t Dm,
+                                 int64_t Di, int64_t N, int64_t R, int64_t k, mssm_dtype dtype,
+                                 void* stream) {
+  mssm_status s = check_block(batch, L, Dm, Di, N, R, k, dtype);
+  if (s != MSSM_SUCCESS) return s;
+  if (batch == 0 || L == 0 || Dm == 0) return MSSM_SUCCESS;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (!out) return MSSM_ERROR_INVALID_VALUE;
+  if (Di == 0) {   // an empty inner dimension: the output projection sums nothing
+    const hipError_t e = mssm::launch_state_init(out, nullptr, batch * L * Dm, st);
+    if (e != hipSuccess) {
+      set_hip_error(e, "zero fill launch");
+      return MSSM_ERROR_HIP;
+    }
+    return MSSM_SUCCESS;
+  }
+  if (!u0 || !W_in || !conv_w || !W_x || !W_dt || !dt_bias || !A || !W_out)
+    return MSSM_ERROR_INVALID_VALUE;
+  const mssm::BlockPlan plan =
+      mssm::plan_block(batch, L, Dm, Di, N, R, mssm::choose_fused_cpl(Di));
+  s = check_grid(plan.scan, batch, Di, N);
+  if (s != MSSM_SUCCESS) return s;
+  if (!workspace || workspace_bytes < plan.workspace_bytes) return MSSM_ERROR_WORKSPACE;
+  if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return MSSM_ERROR_WORKSPACE;
+  const mssm::BlockArgs a{u0, W_in, conv_w, conv_b, W_x, W_dt, dt_bias, A, Dskip, W_out, out,
+                          batch, L, Dm, Di, N, R, static_cast<int>(k)};
+  const mssm::FusedStatus r = mssm::launch_block(a, plan, workspace, st);
+  if (r.blas_failed) {
+    std::snprintf(g_last_error, sizeof(g_last_error), "rocBLAS projection GEMM failed");
+    return MSSM_ERROR_HIP;
+  }
+  if (r.hip != hipSuccess) {
+    set_hip_error(r.hip, "Mamba block launch");
+    return MSSM_ERROR_HIP;
+  }
+  return MSSM_SUCCESS;
+}
+
+}  // extern "C"

@@ -2,6 +2,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <rocblas/rocblas.h>
 #include <stddef.h>
 #include <stdint.h>
 
@@ -116,6 +117,89 @@ struct FusedStatus {
   hipError_t hip = hipSuccess;
   bool blas_failed = false;
 };
+
+// The fused scan kernels' inputs: x is bf16 (the fused selective SSM) or
+// float32 (the Mamba block, where x comes from the conv + SiLU prologue);
+// the block also applies the feedthrough and the SiLU(z) gate and stores y as
+// a bf16 hi + lo pair (y and y_lo) for the output projection.  P holds [dt_low | B | C] rows; dtl/dtl_lo the bf16 parts of dt_low;
+// wT = W_dt^T.
+struct FusedScanArgs {
+  const void* x = nullptr;
+  bool x_f32 = false;
+  const float* z = nullptr;       // [batch, L, D] or null
+  const float* Dskip = nullptr;   // [D] or null
+  void* y = nullptr;
+  bool y_bf16 = false;
+  void* y_lo = nullptr;           // with y_bf16: bf16(y - hi)
+  const float* P = nullptr;
+  const uint16_t* dtl = nullptr;
+  const uint16_t* dtl_lo = nullptr;
+  const uint16_t* wT = nullptr;
+  const float* dt_bias = nullptr;
+  const float* A = nullptr;
+  float* sum_h = nullptr;
+  float* sum_p = nullptr;
+  int64_t batch = 0, L = 0, D = 0, N = 0, R = 0;
+};
+hipError_t launch_fused_scan(const FusedScanArgs& a, const ScanPlan& plan, hipStream_t stream);
+
+// dt_low split into bf16 hi + lo parts and W_dt transposed, for the fused scan.
+hipError_t launch_fused_prep(const float* P, int64_t M, int64_t R, int64_t ldp, const void* W_dt,
+                             int64_t D, uint16_t* dtl, uint16_t* dtl_lo, uint16_t* wT,
+                             hipStream_t stream);
+
+// The device's rocBLAS handle (created on first use, kept until exit), bound
+// to `stream`.  false: rocBLAS failed (hip_error == hipSuccess) or a HIP call
+// failed (hip_error set).
+bool blas_handle(hipStream_t stream, rocblas_handle* out, hipError_t* hip_error);
+
+// Row-major C[M, n] (float32, row stride ldc) = A[M, k] B[k, n] + beta C (A, B
+// bf16, row strides lda, ldb), float32 accumulation.  false if rocBLAS fails.
+bool gemm_rm_bf16(rocblas_handle h, int64_t M, int64_t n, int64_t k, const void* A, int64_t lda,
+                  const void* B, int64_t ldb, float* C, int64_t ldc, float beta);
+
+// ---- the Mamba block ------------------------------------------------------------------------
+
+// out[b,t,d] = SiLU(bias[d] + sum_i w[d,i] u[b, t-k+1+i, d]) (u = 0 before t = 0);
+// u float32 or bf16 [batch, L, D]; w [D, k] float32; bias [D] or null;
+// out_hi / out_lo (optional, together) receive the bf16 pair hi = bf16(out),
+// lo = bf16(out - hi).
+hipError_t launch_conv1d_silu(const void* u, bool u_f32, const float* w, const float* bias,
+                              float* out, uint16_t* out_hi, uint16_t* out_lo, int64_t batch,
+                              int64_t L, int64_t D, int k, hipStream_t stream);
+
+struct BlockArgs {
+  const void* u0;        // [batch, L, Dm] bf16
+  const void* W_in;      // [Dm, 2 Di] bf16
+  const float* conv_w;   // [Di, k]
+  const float* conv_b;   // [Di] or null
+  const void* W_x;       // [Di, R + 2N] bf16
+  const void* W_dt;      // [R, Di] bf16
+  const float* dt_bias;  // [Di]
+  const float* A;        // [Di, N]
+  const float* Dskip;    // [Di] or null
+  const void* W_out;     // [Di, Dm] bf16
+  float* out;            // [batch, L, Dm]
+  int64_t batch, L, Dm, Di, N, R;
+  int k;
+};
+
+// Workspace: U, Z, X (float32 [M, Di]), bf16 hi/lo pairs of X and of the
+// gated result G ([M, Di] each), then the fused scan's P, dt_low parts,
+// W_dt^T and chunk summaries.
+struct BlockPlan {
+  ScanPlan scan;
+  size_t u_offset = 0, z_offset = 0, x_offset = 0, xb_offset = 0, xl_offset = 0, g_offset = 0,
+         gl_offset = 0;
+  size_t p_offset = 0, dtl_offset = 0, dtl_lo_offset = 0, wt_offset = 0, scan_offset = 0;
+  size_t workspace_bytes = 0;
+};
+BlockPlan plan_block(int64_t batch, int64_t L, int64_t Dm, int64_t Di, int64_t N, int64_t R,
+                     int cpl);
+size_t block_workspace_bound(int64_t batch, int64_t L, int64_t Dm, int64_t Di, int64_t N,
+                             int64_t R);
+FusedStatus launch_block(const BlockArgs& a, const BlockPlan& plan, void* workspace,
+                         hipStream_t stream);
 
 FusedPlan plan_fused(int64_t batch, int64_t L, int64_t D, int64_t N, int64_t R, int cpl);
 size_t fused_workspace_bound(int64_t batch, int64_t L, int64_t D, int64_t N, int64_t R);

@@ -110,6 +110,27 @@ __device__ __forceinline__ void buf_load_vals(buf_t r, int voff, int soff, float
   }
 }
 
+// float32 -> bfloat16 bits, round to nearest even (NaN stays NaN).
+__device__ __forceinline__ uint32_t bf16_rne_bits(float f) {
+  const uint32_t u = __float_as_uint(f);
+  uint32_t v = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+  if ((u & 0x7fffffffu) > 0x7f800000u) v = (u >> 16) | 0x40u;
+  return v;
+}
+
+// CPL adjacent bfloat16 values (rounded from float32) at (voff + soff) bytes.
+template <int CPL>
+__device__ __forceinline__ void buf_store_bf16(buf_t r, int voff, int soff, const float (&v)[CPL]) {
+  if constexpr (CPL == 1) {
+    __builtin_amdgcn_raw_buffer_store_b16(static_cast<unsigned short>(bf16_rne_bits(v[0])), r,
+                                          voff, soff, 0);
+  } else {
+    static_assert(CPL == 2, "CPL is 1 or 2");
+    __builtin_amdgcn_raw_buffer_store_b32(bf16_rne_bits(v[0]) | (bf16_rne_bits(v[1]) << 16), r,
+                                          voff, soff, 0);
+  }
+}
+
 template <int CPL>
 __device__ __forceinline__ void buf_store_vals(buf_t r, int voff, int soff, const float (&v)[CPL]) {
   if constexpr (CPL == 1) {

@@ -50,6 +50,14 @@ _SIGNATURES = {
                                                 ctypes.c_int, _i64, _i64, _i64, ctypes.c_int,
                                                 _vp]),
     "mssm_fused_supports": (ctypes.c_int, [_i64, _i64]),
+    "mssm_causal_conv1d_silu": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64,
+                                               ctypes.c_int, _vp]),
+    "mssm_mamba_block_supports": (ctypes.c_int, [_i64, _i64, _i64]),
+    "mssm_mamba_block_workspace_size": (ctypes.c_int, [_i64, _i64, _i64, _i64, _i64, _i64, _i64,
+                                                       ctypes.c_int,
+                                                       ctypes.POINTER(ctypes.c_size_t)]),
+    "mssm_mamba_block_fwd": (ctypes.c_int, [_vp] * 12 + [ctypes.c_size_t] + [_i64] * 7 +
+                             [ctypes.c_int, _vp]),
     "mssm_selective_ssm_fused_workspace_size": (ctypes.c_int, [_i64, _i64, _i64, _i64, _i64,
                                                                ctypes.c_int,
                                                                ctypes.POINTER(ctypes.c_size_t)]),
@@ -329,3 +337,92 @@ def selective_ssm_fused(x, W_x, W_dt, dt_bias, A, *, stream=None):
     nbytes = mssm_selective_ssm_fused_workspace_size(batch, L, D, N, R, x.dtype)
     ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=x.device)
     return mssm_selective_ssm_fused_fwd(x, W_x, W_dt, dt_bias, A, y, ws, stream=stream)
+
+
+# ---- the Mamba block -------------------------------------------------------------------------
+
+def mssm_causal_conv1d_silu(u, conv_w, conv_b, out, *, stream=None):
+    """out [batch, L, D] float32 <- SiLU(causal depthwise conv1d(u) + conv_b);
+    conv_w [D, k] float32, conv_b [D] float32 or None."""
+    if u.dim() != 3 or conv_w.dim() != 2:
+        raise ValueError("u must be [batch, L, D] and conv_w [D, k]")
+    batch, L, D = u.shape
+    k = conv_w.shape[1]
+    _dtype_code(u.dtype)
+    dev = u.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a GPU device")
+    _dense(u, "u", u.dtype, (batch, L, D), dev)
+    _dense(conv_w, "conv_w", torch.float32, (D, k), dev)
+    _check_optional(conv_b, "conv_b", torch.float32, (D,), dev)
+    _dense(out, "out", torch.float32, (batch, L, D), dev)
+    _check(load().mssm_causal_conv1d_silu(_ptr(u), _ptr(conv_w), _ptr(conv_b), _ptr(out), batch,
+                                          L, D, k, _DTYPES[u.dtype], _stream_handle(stream)),
+           "mssm_causal_conv1d_silu")
+    return out
+
+
+def causal_conv1d_silu(u, conv_w, conv_b=None, *, stream=None):
+    out = torch.empty(u.shape, dtype=torch.float32, device=u.device)
+    return mssm_causal_conv1d_silu(u, conv_w, conv_b, out, stream=stream)
+
+
+def mssm_mamba_block_supports(N: int, R: int, k: int) -> bool:
+    return bool(load().mssm_mamba_block_supports(N, R, k))
+
+
+def mssm_mamba_block_workspace_size(batch, L, Dm, Di, N, R, k, dtype) -> int:
+    out = ctypes.c_size_t(0)
+    _check(load().mssm_mamba_block_workspace_size(batch, L, Dm, Di, N, R, k, _dtype_code(dtype),
+                                                  ctypes.byref(out)),
+           "mssm_mamba_block_workspace_size")
+    return out.value
+
+
+def mssm_mamba_block_fwd(u0, W_in, conv_w, conv_b, W_x, W_dt, dt_bias, A, Dskip, W_out, out,
+                         workspace, *, stream=None):
+    """out [batch, L, Dm] float32 <- the Mamba block forward (see include/mssm.h)."""
+    if u0.dim() != 3:
+        raise ValueError("u0 must be [batch, L, Dm]")
+    batch, L, Dm = u0.shape
+    if W_in.dim() != 2 or W_in.shape[1] % 2:
+        raise ValueError("W_in must be [Dm, 2 Di]")
+    Di = W_in.shape[1] // 2
+    if A.dim() != 2 or conv_w.dim() != 2 or W_dt.dim() != 2:
+        raise ValueError("A, conv_w and W_dt must be 2-D")
+    N, k, R = A.shape[1], conv_w.shape[1], W_dt.shape[0]
+    _dtype_code(u0.dtype)
+    dev = u0.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a GPU device")
+    dt = u0.dtype
+    _dense(u0, "u0", dt, (batch, L, Dm), dev)
+    _dense(W_in, "W_in", dt, (Dm, 2 * Di), dev)
+    _dense(conv_w, "conv_w", torch.float32, (Di, k), dev)
+    _check_optional(conv_b, "conv_b", torch.float32, (Di,), dev)
+    _dense(W_x, "W_x", dt, (Di, R + 2 * N), dev)
+    _dense(W_dt, "W_dt", dt, (R, Di), dev)
+    _dense(dt_bias, "dt_bias", torch.float32, (Di,), dev)
+    _dense(A, "A", torch.float32, (Di, N), dev)
+    _check_optional(Dskip, "Dskip", torch.float32, (Di,), dev)
+    _dense(W_out, "W_out", dt, (Di, Dm), dev)
+    _dense(out, "out", torch.float32, (batch, L, Dm), dev)
+    ws_ptr = _ptr(workspace) if workspace is not None and workspace.numel() > 0 else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(load().mssm_mamba_block_fwd(
+        _ptr(u0), _ptr(W_in), _ptr(conv_w), _ptr(conv_b), _ptr(W_x), _ptr(W_dt), _ptr(dt_bias),
+        _ptr(A), _ptr(Dskip), _ptr(W_out), _ptr(out), ws_ptr, ws_bytes, batch, L, Dm, Di, N, R,
+        k, _dtype_code(dt), _stream_handle(stream)), "mssm_mamba_block_fwd")
+    return out
+
+
+def mamba_block(u0, W_in, conv_w, conv_b, W_x, W_dt, dt_bias, A, Dskip, W_out, *, stream=None):
+    """Allocate out and the workspace with torch, then run mssm_mamba_block_fwd."""
+    batch, L, Dm = u0.shape
+    Di = W_in.shape[1] // 2
+    out = torch.empty((batch, L, Dm), dtype=torch.float32, device=u0.device)
+    nbytes = mssm_mamba_block_workspace_size(batch, L, Dm, Di, A.shape[1], W_dt.shape[0],
+                                             conv_w.shape[1], u0.dtype)
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=u0.device)
+    return mssm_mamba_block_fwd(u0, W_in, conv_w, conv_b, W_x, W_dt, dt_bias, A, Dskip, W_out,
+                                out, ws, stream=stream)

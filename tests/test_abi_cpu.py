@@ -185,3 +185,47 @@ def test_step_argument_errors(lib):
         assert _step(lib, ptrs, 0, 2, 4, 4) == 1, f"null pointer {i} accepted"
     assert _step(lib, [None] * 9, 0, 0, 4, 4) == 0
     assert _step(lib, [None] * 9, 1, 3, 0, 4) == 0
+
+
+def test_conv_argument_errors(lib):
+    def call(ptrs, batch, L, D, k, dtype=0):
+        return lib.mssm_causal_conv1d_silu(*ptrs, batch, L, D, k, dtype, None)
+    p4 = [FAKE] * 4            # u, conv_w, conv_b, out
+    assert call(p4, -1, 4, 4, 4) == 1
+    assert call(p4, 1, 4, 4, 0) == 1                       # k must be >= 1
+    assert call(p4, 1, 4, 4, 9) == 2                       # widths 1..8 are built
+    assert call(p4, 1, 4, 4, 4, dtype=3) == 1
+    assert call(p4, 1 << 40, 1 << 40, 4, 4) == 3
+    for i in (0, 1, 3):
+        ptrs = list(p4)
+        ptrs[i] = None
+        assert call(ptrs, 1, 4, 4, 4) == 1
+    assert call([None] * 4, 0, 4, 4, 4) == 0
+
+
+def test_block_support_and_argument_errors(lib):
+    assert lib.mssm_mamba_block_supports(16, 160, 4) == 1
+    assert lib.mssm_mamba_block_supports(16, 160, 9) == 0
+    assert lib.mssm_mamba_block_supports(16, 20, 4) == 0
+    out = ctypes.c_size_t(0)
+    assert lib.mssm_mamba_block_workspace_size(16, 2048, 2560, 5120, 16, 160, 4, 1,
+                                               ctypes.byref(out)) == 0
+    assert out.value > 3 * 16 * 2048 * 5120 * 4            # u, z and x in float32
+    assert lib.mssm_mamba_block_workspace_size(1, 8, 32, 64, 16, 16, 4, 0,
+                                               ctypes.byref(out)) == 2    # float32: no
+
+    def call(ptrs, ws, wsb, batch, L, Dm, Di, N, R, k, dtype=1):
+        return lib.mssm_mamba_block_fwd(*ptrs, ws, wsb, batch, L, Dm, Di, N, R, k, dtype, None)
+    p11 = [FAKE] * 11          # u0 W_in conv_w conv_b W_x W_dt dt_bias A Dskip W_out out
+    assert call(p11, FAKE, 1 << 40, 1, 8, 32, 64, 16, 16, 9) == 2
+    assert call(p11, FAKE, 1 << 40, 1, 8, 32, 64, 16, 16, 0) == 1
+    assert call(p11, FAKE, 1 << 40, 1, 8, -32, 64, 16, 16, 4) == 1
+    assert call(p11, FAKE, 1 << 40, 1, 8, 32, 64, 16, 16, 4, dtype=0) == 2
+    for i in (0, 1, 2, 4, 5, 6, 7, 9, 10):                  # conv_b and Dskip may be null
+        ptrs = list(p11)
+        ptrs[i] = None
+        assert call(ptrs, FAKE, 1 << 40, 1, 8, 32, 64, 16, 16, 4) == 1, f"null {i} accepted"
+    assert lib.mssm_mamba_block_workspace_size(1, 8, 32, 64, 16, 16, 4, 1, ctypes.byref(out)) == 0
+    assert call(p11, FAKE, out.value - 1, 1, 8, 32, 64, 16, 16, 4) == 4
+    assert call(p11, ctypes.c_void_p(0x1010), out.value, 1, 8, 32, 64, 16, 16, 4) == 4  # align
+    assert call([None] * 11, None, 0, 0, 8, 32, 64, 16, 16, 4) == 0

@@ -63,3 +63,69 @@ def test_planted_mistake_is_caught(tmp_path, name):
     assert old in src, f"mutation {name} no longer applies to the source"
     so = _build(src.replace(old, new, 1), tmp_path, name)
     assert _run_pins(so) != 0, f"the pins did not catch mutation {name}"
+
+
+# ---- the block oracle (Python): the same idea, in-process ------------------------------
+
+BLOCK_SRC = os.path.join(ROOT, "oracle", "block.py")
+
+BLOCK_MUTATIONS = {
+    "conv_taps_reversed": ("out += w[:, i] * padded[:, i:i + L, :]",
+                           "out += w[:, k - 1 - i] * padded[:, i:i + L, :]"),
+    "conv_pads_the_future": ("padded = np.concatenate([np.zeros((batch, k - 1, D)), u], axis=1)",
+                             "padded = np.concatenate([u, np.zeros((batch, k - 1, D))], axis=1)"),
+    "conv_bias_dropped": ("    if b is not None:\n", "    if False:\n"),
+    "branches_swapped": ("u, z = proj[..., :Di], proj[..., Di:]",
+                         "z, u = proj[..., :Di], proj[..., Di:]"),
+    "no_silu_after_conv": ("x = silu(causal_conv1d(u, conv_w, conv_b))",
+                           "x = causal_conv1d(u, conv_w, conv_b)"),
+    "gate_dropped": ("Dskip=Dskip, z=z,", "Dskip=Dskip, z=None,"),
+    "feedthrough_dropped": ("Dskip=Dskip, z=z,", "Dskip=None, z=z,"),
+    "selection_from_u": ("fused_projections(xq,", "fused_projections(u,"),
+    "scan_input_u": ("gated = selective_scan(x, delta", "gated = selective_scan(u, delta"),
+}
+
+
+def _load_block_variant(text):
+    import importlib.util
+    import types
+    import oracle  # noqa: F401  (the package the relative imports resolve in)
+    mod = types.ModuleType("oracle._block_variant")
+    mod.__package__ = "oracle"
+    mod.__file__ = BLOCK_SRC
+    exec(compile(text, BLOCK_SRC, "exec"), mod.__dict__)
+    return mod
+
+
+def _block_pins_fail(monkeypatch, mod):
+    import oracle
+    import test_oracle_block_pins as pins
+    monkeypatch.setattr(oracle.block, "causal_conv1d", mod.causal_conv1d)
+    monkeypatch.setattr(oracle.block, "mamba_block", mod.mamba_block)
+    cases = [lambda: pins.test_conv_equals_numpy_convolution(4),
+             pins.test_conv_impulse_response_reads_the_taps_backwards,
+             pins.test_single_token_closed_form, pins.test_block_is_causal,
+             pins.test_zero_gate_branch_silences_the_block,
+             pins.test_feedthrough_only_closed_form_over_many_tokens,
+             pins.test_rounding_points_only_touch_the_gemm_inputs]
+    failed = 0
+    for case in cases:
+        try:
+            case()
+        except Exception:   # an assertion, or a shape error from the planted mistake
+            failed += 1
+    return failed
+
+
+def test_unmodified_block_source_passes(monkeypatch):
+    mod = _load_block_variant(open(BLOCK_SRC).read())
+    assert _block_pins_fail(monkeypatch, mod) == 0
+
+
+@pytest.mark.parametrize("name", sorted(BLOCK_MUTATIONS))
+def test_planted_block_mistake_is_caught(monkeypatch, name):
+    old, new = BLOCK_MUTATIONS[name]
+    text = open(BLOCK_SRC).read()
+    assert text.count(old) == 1, f"mutation anchor for {name} not unique"
+    mod = _load_block_variant(text.replace(old, new))
+    assert _block_pins_fail(monkeypatch, mod) > 0, f"no pin caught {name}"

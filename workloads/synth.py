@@ -27,6 +27,8 @@ class Workload:
     seed: int
     R: int | None = None       # dt rank of the fused projection workload
     description: str = ""
+    Dm: int | None = None      # model width of the Mamba-block workload (D is the inner width)
+    conv_k: int | None = None  # causal conv width of the Mamba-block workload
 
     @property
     def fused(self) -> bool:
@@ -64,7 +66,17 @@ WORKLOADS = {
     )
 }
 
-# Workloads that are one full-sequence scan (the others: the decode step).
+WORKLOADS["mamba_block_bf16"] = Workload(
+    "mamba_block_bf16", 16, 2048, 5120, 16, "bf16", 5407, R=160, Dm=2560, conv_k=4,
+    description="Mamba block forward (in_proj, causal conv1d + SiLU, selective SSM with "
+                "x_proj/dt_proj, D x, SiLU(z) gate, out_proj) at the fused workload's inner "
+                "shape: model width 2560, inner width 5120, conv width 4; bf16 u0 ~ N(0,1) "
+                "and weights W_in ~ N(0, 1/2560), W_x ~ N(0, 1/5120), W_dt ~ N(0, 1/160), "
+                "W_out ~ N(0, 1/5120); float32 conv taps ~ N(0, 1/4), conv bias ~ "
+                "N(0, 0.01), Dskip ~ N(0,1); softplus(dt_bias) log-uniform in [1e-3, 1e-1]; "
+                "A[d,n] = -(n+1)")
+
+# Workloads that are one full-sequence scan (the others: the decode step, the block).
 SCAN_WORKLOADS = ("tiny_fp32", "mamba130m_layer_fp32", "mid_bf16", "long_seq_bf16",
                   "fused_proj_bf16")
 
@@ -209,4 +221,32 @@ def generate_step(w: Workload | str = "decode_step_bf16", **overrides) -> dict:
     out["Dskip"] = _draw(rng, w.D, "fp32", "normal", 0.0, 1.0)
     out["h"] = _draw(rng, BD * w.N, "fp32", "normal", 0.0, 0.5).reshape(w.batch, w.D, w.N)
     out["A"] = _a_matrix(w)
+    return out
+
+
+def generate_block(w: Workload | str = "mamba_block_bf16", **overrides) -> dict:
+    """Inputs of the Mamba-block workload: u0 [batch, L, Dm], W_in [Dm, 2 Di],
+    conv_w [Di, k], conv_b [Di], W_x [Di, R + 2N], W_dt [R, Di], dt_bias [Di],
+    A [Di, N], Dskip [Di], W_out [Di, Dm] (Di = D).  Draw order as listed."""
+    if isinstance(w, str):
+        w = workload(w, **overrides)
+    elif overrides:
+        w = replace(w, **overrides)
+    rng = np.random.default_rng(w.seed)
+    Dm, Di, R, N, k = w.Dm, w.D, w.R, w.N, w.conv_k
+    out = {"workload": w}
+    out["u0"] = _draw(rng, w.batch * w.L * Dm, w.dtype, "normal", 0.0, 1.0).reshape(
+        w.batch, w.L, Dm)
+    out["W_in"] = _draw(rng, Dm * 2 * Di, w.dtype, "normal", 0.0, 1.0 / np.sqrt(Dm)).reshape(
+        Dm, 2 * Di)
+    out["conv_w"] = _draw(rng, Di * k, "fp32", "normal", 0.0, 1.0 / np.sqrt(k)).reshape(Di, k)
+    out["conv_b"] = _draw(rng, Di, "fp32", "normal", 0.0, 0.1)
+    out["W_x"] = _draw(rng, Di * (R + 2 * N), w.dtype, "normal", 0.0,
+                       1.0 / np.sqrt(Di)).reshape(Di, R + 2 * N)
+    out["W_dt"] = _draw(rng, R * Di, w.dtype, "normal", 0.0, 1.0 / np.sqrt(R)).reshape(R, Di)
+    d0 = _draw(rng, Di, "fp32", "loguniform", 1e-3, 1e-1).astype(np.float64)
+    out["dt_bias"] = np.log(np.expm1(d0)).astype(np.float32)
+    out["A"] = _a_matrix(w)
+    out["Dskip"] = _draw(rng, Di, "fp32", "normal", 0.0, 1.0)
+    out["W_out"] = _draw(rng, Di * Dm, w.dtype, "normal", 0.0, 1.0 / np.sqrt(Di)).reshape(Di, Dm)
     return out
