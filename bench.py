@@ -253,6 +253,79 @@ def time_decode(name, steps, warmup, torch, mssm, workloads, states=4):
                     f"inputs, fp32 state; Dskip and z gate on; {states} rotating states"}
 
 
+def time_block(name, steps, warmup, torch, mssm, workloads):
+    """The Mamba block forward: in_proj (2 GEMMs), conv1d + SiLU, x_proj (hi and
+    lo GEMMs), dt_low split, the fused scan with feedthrough and gate, out_proj
+    (hi and lo GEMMs)."""
+    w = workloads.workload(name)
+    g = workloads.generate_block(name)
+    keys = ("u0", "W_in", "conv_w", "conv_b", "W_x", "W_dt", "dt_bias", "A", "Dskip", "W_out")
+    d = {k: _to_device(g[k], torch) for k in keys}
+    del g
+    M, Dm, Di, N, R = w.batch * w.L, w.Dm, w.D, w.N, w.R
+    out = torch.empty((w.batch, w.L, Dm), dtype=torch.float32, device="cuda")
+    nb = mssm.mssm_mamba_block_workspace_size(w.batch, w.L, Dm, Di, N, R, w.conv_k,
+                                              torch.bfloat16)
+    ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+
+    def step():
+        mssm.mssm_mamba_block_fwd(*(d[k] for k in keys), out, ws)
+
+    for _ in range(warmup):
+        step()
+    stream = torch.cuda.current_stream()
+    s_ev = torch.cuda.Event(enable_timing=True)
+    e_ev = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    s_ev.record(stream)
+    for _ in range(steps):
+        step()
+    e_ev.record(stream)
+    torch.cuda.synchronize()
+    kernel_ms = s_ev.elapsed_time(e_ev) / steps
+    gemm_flops = 2 * M * Dm * 2 * Di + 2 * 2 * M * Di * (R + 2 * N) + 2 * 2 * M * Di * Dm
+    del d, out, ws
+    torch.cuda.empty_cache()
+    return {"kernel_ms": round(kernel_ms, 4),
+            "tokens_per_s": round(M / (kernel_ms * 1e-3), 1),
+            "Gelem/s": round(M * Di * N / (kernel_ms * 1e-3) / 1e9, 1),
+            "gemm_TFLOP": round(gemm_flops / 1e12, 3),
+            "note": f"batch {w.batch}, L {w.L}, Dm {Dm}, Di {Di}, N {N}, R {R}, conv {w.conv_k}; "
+                    f"in_proj, conv1d+SiLU, x_proj (hi+lo), fused scan (dt_proj on MFMA, D x, "
+                    f"SiLU(z) gate), out_proj (hi+lo)"}
+
+
+def time_conv(torch, mssm, steps=20, warmup=3, batch=16, L=2048, D=5120, k=4):
+    """The causal depthwise conv1d + SiLU alone on float32 [batch, L, D]: HBM-bound,
+    4 bytes read and 4 written per element."""
+    u = [torch.randn((batch, L, D), device="cuda") for _ in range(2)]
+    w = torch.randn((D, k), device="cuda") * 0.5
+    b = torch.randn((D,), device="cuda") * 0.1
+    out = torch.empty((batch, L, D), device="cuda")
+    for i in range(warmup):
+        mssm.mssm_causal_conv1d_silu(u[i % 2], w, b, out)
+    stream = torch.cuda.current_stream()
+    s_ev = torch.cuda.Event(enable_timing=True)
+    e_ev = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    s_ev.record(stream)
+    for i in range(steps):
+        mssm.mssm_causal_conv1d_silu(u[i % 2], w, b, out)
+    e_ev.record(stream)
+    torch.cuda.synchronize()
+    kernel_ms = s_ev.elapsed_time(e_ev) / steps
+    nb = 8 * batch * L * D + 4 * D * (k + 1)
+    del u, w, b, out
+    torch.cuda.empty_cache()
+    gbs = nb / (kernel_ms * 1e-3) / 1e9
+    return {"kernel_ms": round(kernel_ms, 4), "GB/s": round(gbs, 1),
+            "hbm_peak_frac": round(gbs / HBM_PEAK_GBS, 4),
+            "roofline": {"bound": "hbm", "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "bytes_per_launch": nb},
+            "note": f"conv1d_silu_kernel, float32 [{batch}, {L}, {D}], width {k}, bias; "
+                    f"2 rotated inputs"}
+
+
 def cpu_baseline(name, workloads, oracle, threads):
     """The float64 oracle on the host cores, on the whole headline workload."""
     g = workloads.generate(name)
@@ -286,6 +359,10 @@ def main(argv=None):
     ap.add_argument("--workload", default=HEADLINE)
     ap.add_argument("--headline-only", action="store_true", help="skip the other workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", default=None,
+                    choices=["fused_proj_bf16", "scan_ex", "decode_step_bf16", "conv1d_silu_fp32",
+                             "mamba_block_bf16"],
+                    help="time only this extra workload and print its record (for profiling)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (5 times) and exit; "
                          "used to scale rocprofv3 FETCH_SIZE/WRITE_SIZE counters")
@@ -314,6 +391,20 @@ def main(argv=None):
         print(json.dumps({"calibrate_copy_bytes_read": n * 4, "bytes_written": n * 4}))
         return 0
     mssm.load()
+    if args.only:
+        if args.only == "fused_proj_bf16":
+            wo, _, kms = time_fused(args.only, args.steps, args.warmup, torch, mssm, workloads)
+            rec = {"kernel_ms": round(kms, 4)}
+        elif args.only == "scan_ex":
+            rec = time_scan_ex(HEADLINE, args.steps, args.warmup, torch, mssm, workloads)
+        elif args.only == "decode_step_bf16":
+            rec = time_decode(args.only, args.steps, args.warmup, torch, mssm, workloads)
+        elif args.only == "conv1d_silu_fp32":
+            rec = time_conv(torch, mssm, steps=args.steps, warmup=args.warmup)
+        else:
+            rec = time_block(args.only, args.steps, args.warmup, torch, mssm, workloads)
+        print(json.dumps({"only": args.only, **rec}), flush=True)
+        return 0
 
     w, wall, kernel_ms = time_workload(args.workload, args.steps, args.warmup, 2, torch, mssm,
                                        workloads)
@@ -377,6 +468,8 @@ def main(argv=None):
             HEADLINE, 10, 2, torch, mssm, workloads)
         others["decode_step_bf16"] = time_decode("decode_step_bf16", 200, 10, torch, mssm,
                                                  workloads)
+        others["conv1d_silu_fp32"] = time_conv(torch, mssm)
+        others["mamba_block_bf16"] = time_block("mamba_block_bf16", 5, 2, torch, mssm, workloads)
         line["workloads"] = others
     if not args.no_cpu_baseline:
         import oracle
