@@ -30,6 +30,7 @@ Modules:
                   tree scans, unrolled sum, semiseparable matrix, convolution
     block      -- the Mamba block around the scan: causal depthwise conv1d,
                   SiLU, projections, gate (eq. (9))
+    backward   -- gradients of the scan (adjoint recurrence, float64)
 Parity status of each function is stated in its docstring; every function is
 pinned by a ``-m "not gpu"`` test unless it says "parity unpinned".
 """
@@ -37,3 +38,4 @@ from .scan import selective_scan, selective_scan_step, load_library, build_libra
 from .selection import softplus, silu, selective_ssm_fused, round_to_bf16  # noqa: F401
 from . import forms  # noqa: F401
 from . import block  # noqa: F401
+from . import backward  # noqa: F401

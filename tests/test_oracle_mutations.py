@@ -129,3 +129,60 @@ def test_planted_block_mistake_is_caught(monkeypatch, name):
     assert text.count(old) == 1, f"mutation anchor for {name} not unique"
     mod = _load_block_variant(text.replace(old, new))
     assert _block_pins_fail(monkeypatch, mod) > 0, f"no pin caught {name}"
+
+
+# ---- the backward oracle (Python) ------------------------------------------------------
+
+BWD_SRC = os.path.join(ROOT, "oracle", "backward.py")
+
+BWD_MUTATIONS = {
+    "adjoint_not_decayed": ("lam_next = a * lam", "lam_next = lam"),
+    "dA_uses_h_t": ("out[\"dA\"] += lam * db[t][:, None] * a * hprev",
+                    "out[\"dA\"] += lam * db[t][:, None] * a * hist[t + 1]"),
+    "ddelta_drops_decay_term": ("+ A * a * hprev),", "),"),
+    "dB_missing_delta": ("out[\"dB\"][b, t] = (db[t] * xb[t]) @ lam",
+                         "out[\"dB\"][b, t] = xb[t] @ lam"),
+    "gate_slope_wrong": ("s * (1.0 + v * (1.0 - s))", "s"),
+    "dC_from_previous_state": ("out[\"dC\"][b, t] = g[t] @ hist[t + 1]",
+                               "out[\"dC\"][b, t] = g[t] @ hist[t]"),
+    "feedthrough_grad_dropped": ("out[\"dx\"][b] += g * Dk", "pass"),
+}
+
+
+def _bwd_pins_fail(monkeypatch, mod):
+    import oracle
+    import test_oracle_backward_pins as pins
+    monkeypatch.setattr(oracle.backward, "selective_scan_backward", mod.selective_scan_backward)
+    monkeypatch.setattr(pins, "selective_scan_backward", mod.selective_scan_backward)
+    failed = 0
+    cases = [lambda g=g, n=n, k=k: pins.test_gradients_match_finite_differences(g, n, k)
+             for g, n, k in pins.NAMES]
+    cases.append(pins.test_single_step_closed_forms)
+    for case in cases:
+        try:
+            case()
+        except Exception:
+            failed += 1
+    return failed
+
+
+def _load_bwd_variant(text):
+    import types
+    mod = types.ModuleType("oracle._backward_variant")
+    mod.__package__ = "oracle"
+    mod.__file__ = BWD_SRC
+    exec(compile(text, BWD_SRC, "exec"), mod.__dict__)
+    return mod
+
+
+def test_unmodified_backward_source_passes(monkeypatch):
+    assert _bwd_pins_fail(monkeypatch, _load_bwd_variant(open(BWD_SRC).read())) == 0
+
+
+@pytest.mark.parametrize("name", sorted(BWD_MUTATIONS))
+def test_planted_backward_mistake_is_caught(monkeypatch, name):
+    old, new = BWD_MUTATIONS[name]
+    text = open(BWD_SRC).read()
+    assert text.count(old) == 1, f"mutation anchor for {name} not unique"
+    assert _bwd_pins_fail(monkeypatch, _load_bwd_variant(text.replace(old, new))) > 0, \
+        f"no pin caught {name}"
