@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define MSSM_ABI_VERSION 3
+#define MSSM_ABI_VERSION 4
 
 typedef enum {
     MSSM_SUCCESS = 0,
@@ -273,6 +273,42 @@ mssm_status mssm_mamba_block_fwd(const void *u0, const void *W_in, const float *
                                  size_t workspace_bytes, int64_t batch, int64_t L, int64_t Dm,
                                  int64_t Di, int64_t N, int64_t R, int64_t k, mssm_dtype dtype,
                                  void *stream);
+
+/*
+ * ---- backward ------------------------------------------------------------------------------
+ *
+ * Gradients of L = sum(dout * y) for y = mssm_selective_scan_fwd_ex(x, delta,
+ * A, B, C, Dskip, z, h0) with the first-order input term (MSSM_BBAR_EULER), by
+ * the chain rule through the recurrence (the adjoint lam_t = C_t g_t +
+ * a_{t+1} lam_{t+1} is a reverse scan).  The states are recomputed from the
+ * inputs, never stored: the call re-runs the forward chunk summaries, runs the
+ * adjoint's chunk summaries in reverse, then recomputes each 16-step chunk's
+ * states in registers while sweeping it backwards.
+ *
+ *   dout            : [batch, L, D] float32 (the gradient of the float32 y)
+ *   dx, ddelta, dz  : [batch, L, D] float32
+ *   dA              : [D, N] float32;   dDskip : [D] float32
+ *   dB, dC          : [batch, L, N] float32 (summed over the channels d)
+ *   dh0             : [batch, D, N] float32 or NULL
+ * Dskip and dDskip are given together (or both NULL), likewise z and dz; dh0
+ * needs h0.  Every gradient buffer is overwritten, not accumulated into.
+ * dA and dDskip (sums over batch and time) and dB, dC (sums over channels)
+ * are formed from partial sums in a fixed order: results are deterministic.
+ * The workspace (256-byte aligned, mssm_selective_scan_bwd_workspace_size
+ * bytes) holds the chunk summaries of both directions and the partial sums.
+ * With batch, L or D equal to zero the gradients that still have elements are
+ * set to zero.
+ */
+mssm_status mssm_selective_scan_bwd_workspace_size(int64_t batch, int64_t L, int64_t D, int64_t N,
+                                                   mssm_dtype dtype, size_t *bytes);
+
+mssm_status mssm_selective_scan_bwd(const void *x, const void *delta, const float *A,
+                                    const void *B, const void *C, const float *Dskip,
+                                    const void *z, const float *h0, const float *dout, float *dx,
+                                    float *ddelta, float *dA, float *dB, float *dC, float *dDskip,
+                                    float *dz, float *dh0, void *workspace, size_t workspace_bytes,
+                                    int64_t batch, int64_t L, int64_t D, int64_t N,
+                                    mssm_dtype dtype, void *stream);
 
 #ifdef __cplusplus
 }

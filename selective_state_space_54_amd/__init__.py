@@ -18,6 +18,8 @@ from .mssm import (  # noqa: F401
     mssm_mamba_block_workspace_size,
     mssm_selective_ssm_fused_fwd,
     mssm_selective_ssm_fused_workspace_size,
+    mssm_selective_scan_bwd,
+    mssm_selective_scan_bwd_workspace_size,
     mssm_selective_scan_fwd,
     mssm_selective_scan_fwd_ex,
     mssm_selective_scan_fwd_ws,
@@ -25,6 +27,7 @@ from .mssm import (  # noqa: F401
     mssm_selective_scan_workspace_size,
     mssm_supports_state_size,
     selective_scan,
+    selective_scan_bwd,
     selective_scan_ex,
     selective_scan_step,
     selective_ssm_fused,

@@ -397,3 +397,71 @@ mssm_status mssm_mamba_block_fwd(const void* u0, const void* W_in, const float* 
 }
 
 }  // extern "C"
+
+extern "C" {
+
+mssm_status mssm_selective_scan_bwd_workspace_size(int64_t batch, int64_t L, int64_t D, int64_t N,
+                                                   mssm_dtype dtype, size_t* bytes) {
+  if (!bytes) return MSSM_ERROR_INVALID_VALUE;
+  const mssm_status s = check_shape(batch, L, D, N, dtype);
+  if (s != MSSM_SUCCESS) return s;
+  *bytes = (batch == 0 || L == 0 || D == 0) ? 0 : mssm::plan_bwd(batch, L, D, N).workspace_bytes;
+  return MSSM_SUCCESS;
+}
+
+mssm_status mssm_selective_scan_bwd(const void* x, const void* delta, const float* A,
+                                    const void* B, const void* C, const float* Dskip,
+                                    const void* z, const float* h0, const float* dout, float* dx,
+                                    float* ddelta, float* dA, float* dB, float* dC, float* dDskip,
+                                    float* dz, float* dh0, void* workspace, size_t workspace_bytes,
+                                    int64_t batch, int64_t L, int64_t D, int64_t N,
+                                    mssm_dtype dtype, void* stream) {
+  mssm_status s = check_shape(batch, L, D, N, dtype);
+  if (s != MSSM_SUCCESS) return s;
+  if ((Dskip != nullptr) != (dDskip != nullptr) || (z != nullptr) != (dz != nullptr))
+    return MSSM_ERROR_INVALID_VALUE;       // each optional input comes with its gradient
+  if (dh0 != nullptr && h0 == nullptr) return MSSM_ERROR_INVALID_VALUE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (D > 0 && !dA) return MSSM_ERROR_INVALID_VALUE;
+  if (batch == 0 || L == 0 || D == 0) {
+    // nothing flows back: the gradients that still have elements are zero
+    hipError_t e = hipSuccess;
+    if (D > 0) e = mssm::launch_state_init(dA, nullptr, D * N, st);
+    if (e == hipSuccess && dDskip && D > 0) e = mssm::launch_state_init(dDskip, nullptr, D, st);
+    if (e == hipSuccess && dh0 && D > 0) e = mssm::launch_state_init(dh0, nullptr, batch * D * N, st);
+    if (e == hipSuccess && D == 0 && batch * L > 0) {
+      if (!dB || !dC) return MSSM_ERROR_INVALID_VALUE;
+      e = mssm::launch_state_init(dB, nullptr, batch * L * N, st);
+      if (e == hipSuccess) e = mssm::launch_state_init(dC, nullptr, batch * L * N, st);
+    }
+    if (e != hipSuccess) {
+      set_hip_error(e, "zero fill launch");
+      return MSSM_ERROR_HIP;
+    }
+    return MSSM_SUCCESS;
+  }
+  if (!x || !delta || !A || !B || !C || !dout || !dx || !ddelta || !dB || !dC)
+    return MSSM_ERROR_INVALID_VALUE;
+  const mssm::BwdPlan plan = mssm::plan_bwd(batch, L, D, N);
+  {
+    const int64_t n_dtiles = (D + 255) / 256;
+    int64_t blocks;
+    if (!mul_ok(n_dtiles, plan.K, &blocks) || !mul_ok(blocks, batch, &blocks))
+      return MSSM_ERROR_SIZE_OVERFLOW;
+    if (blocks > static_cast<int64_t>(std::numeric_limits<uint32_t>::max()) / 256 ||
+        plan.K > 65535)
+      return MSSM_ERROR_NOT_SUPPORTED;
+  }
+  if (!workspace || workspace_bytes < plan.workspace_bytes) return MSSM_ERROR_WORKSPACE;
+  if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return MSSM_ERROR_WORKSPACE;
+  const mssm::BwdArgs a{x,  delta,  A,  B,  C,      Dskip, z,  h0,  dout,  dx,    ddelta, dA,
+                        dB, dC,     dDskip, dz, dh0, batch, L, D, N, dtype};
+  const hipError_t e = mssm::launch_bwd(a, plan, workspace, st);
+  if (e != hipSuccess) {
+    set_hip_error(e, "selective scan backward launch");
+    return MSSM_ERROR_HIP;
+  }
+  return MSSM_SUCCESS;
+}
+
+}  // extern "C"

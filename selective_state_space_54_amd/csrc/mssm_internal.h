@@ -201,6 +201,44 @@ size_t block_workspace_bound(int64_t batch, int64_t L, int64_t Dm, int64_t Di, i
 FusedStatus launch_block(const BlockArgs& a, const BlockPlan& plan, void* workspace,
                          hipStream_t stream);
 
+// ---- backward ------------------------------------------------------------------------------
+
+struct BwdArgs {
+  const void* x;
+  const void* delta;
+  const float* A;
+  const void* B;
+  const void* C;
+  const float* Dskip;   // or null
+  const void* z;        // or null
+  const float* h0;      // or null
+  const float* dout;    // [batch, L, D]
+  float* dx;
+  float* ddelta;
+  float* dA;
+  float* dB;
+  float* dC;
+  float* dD;            // with Dskip
+  float* dz;            // with z
+  float* dh0;           // or null
+  int64_t batch, L, D, N;
+  mssm_dtype dtype;
+};
+
+// Chunks of `chunk` steps; workspace: forward and reverse chunk summaries
+// ([batch, K-1, N, D] float32 each, 4 arrays), per-wavefront dB/dC partials
+// [ceil(D/64), batch, L, 2N], per-chunk dA partials [batch*K, D, N] and dD
+// partials [batch*K, D].
+struct BwdPlan {
+  int64_t chunk = 0;
+  int K = 1;
+  size_t fwd_h_offset = 0, fwd_p_offset = 0, rev_h_offset = 0, rev_p_offset = 0;
+  size_t part_bc_offset = 0, part_a_offset = 0, part_d_offset = 0;
+  size_t workspace_bytes = 0;
+};
+BwdPlan plan_bwd(int64_t batch, int64_t L, int64_t D, int64_t N);
+hipError_t launch_bwd(const BwdArgs& a, const BwdPlan& plan, void* workspace, hipStream_t stream);
+
 FusedPlan plan_fused(int64_t batch, int64_t L, int64_t D, int64_t N, int64_t R, int cpl);
 size_t fused_workspace_bound(int64_t batch, int64_t L, int64_t D, int64_t N, int64_t R);
 int choose_fused_cpl(int64_t D);

@@ -50,6 +50,11 @@ _SIGNATURES = {
                                                 ctypes.c_int, _i64, _i64, _i64, ctypes.c_int,
                                                 _vp]),
     "mssm_fused_supports": (ctypes.c_int, [_i64, _i64]),
+    "mssm_selective_scan_bwd_workspace_size": (ctypes.c_int, [_i64, _i64, _i64, _i64,
+                                                              ctypes.c_int,
+                                                              ctypes.POINTER(ctypes.c_size_t)]),
+    "mssm_selective_scan_bwd": (ctypes.c_int, [_vp] * 17 + [_vp, ctypes.c_size_t] + [_i64] * 4 +
+                                [ctypes.c_int, _vp]),
     "mssm_causal_conv1d_silu": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64,
                                                ctypes.c_int, _vp]),
     "mssm_mamba_block_supports": (ctypes.c_int, [_i64, _i64, _i64]),
@@ -426,3 +431,71 @@ def mamba_block(u0, W_in, conv_w, conv_b, W_x, W_dt, dt_bias, A, Dskip, W_out, *
     ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=u0.device)
     return mssm_mamba_block_fwd(u0, W_in, conv_w, conv_b, W_x, W_dt, dt_bias, A, Dskip, W_out,
                                 out, ws, stream=stream)
+
+
+# ---- backward --------------------------------------------------------------------------------
+
+def mssm_selective_scan_bwd_workspace_size(batch, L, D, N, dtype) -> int:
+    out = ctypes.c_size_t(0)
+    _check(load().mssm_selective_scan_bwd_workspace_size(batch, L, D, N, _dtype_code(dtype),
+                                                         ctypes.byref(out)),
+           "mssm_selective_scan_bwd_workspace_size")
+    return out.value
+
+
+def mssm_selective_scan_bwd(x, delta, A, B, C, dout, grads, workspace, *, Dskip=None, z=None,
+                            h0=None, stream=None):
+    """Gradients of sum(dout * y) for y = selective_scan_ex(x, delta, A, B, C, Dskip=Dskip,
+    z=z, h0=h0) (first-order input term).  ``grads`` maps dx, ddelta, dA, dB, dC (and dD,
+    dz, dh0 for the parts given) to float32 tensors that are overwritten."""
+    batch, L, D, N = _scan_shapes(x, A)
+    y_like = torch.empty(0)
+    dev = x.device
+    _dtype_code(x.dtype)
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a GPU device")
+    _dense(x, "x", x.dtype, (batch, L, D), dev)
+    _dense(delta, "delta", x.dtype, (batch, L, D), dev)
+    _dense(A, "A", torch.float32, (D, N), dev)
+    _dense(B, "B", x.dtype, (batch, L, N), dev)
+    _dense(C, "C", x.dtype, (batch, L, N), dev)
+    _dense(dout, "dout", torch.float32, (batch, L, D), dev)
+    _check_optional(Dskip, "Dskip", torch.float32, (D,), dev)
+    _check_optional(z, "z", x.dtype, (batch, L, D), dev)
+    _check_optional(h0, "h0", torch.float32, (batch, D, N), dev)
+    shapes = {"dx": (batch, L, D), "ddelta": (batch, L, D), "dA": (D, N), "dB": (batch, L, N),
+              "dC": (batch, L, N), "dD": (D,), "dz": (batch, L, D), "dh0": (batch, D, N)}
+    for k, v in grads.items():
+        if k not in shapes:
+            raise ValueError(f"unknown gradient {k}")
+        _dense(v, k, torch.float32, shapes[k], dev)
+    del y_like
+    g = lambda k: _ptr(grads.get(k))
+    ws_ptr = _ptr(workspace) if workspace is not None and workspace.numel() > 0 else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(load().mssm_selective_scan_bwd(
+        _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(Dskip), _ptr(z), _ptr(h0),
+        _ptr(dout), g("dx"), g("ddelta"), g("dA"), g("dB"), g("dC"), g("dD"), g("dz"), g("dh0"),
+        ws_ptr, ws_bytes, batch, L, D, N, _DTYPES[x.dtype], _stream_handle(stream)),
+        "mssm_selective_scan_bwd")
+    return grads
+
+
+def selective_scan_bwd(x, delta, A, B, C, dout, *, Dskip=None, z=None, h0=None, stream=None):
+    """Allocate the gradients and the workspace with torch, then run
+    mssm_selective_scan_bwd; returns the dict of gradients."""
+    batch, L, D, N = _scan_shapes(x, A)
+    opts = dict(device=x.device, dtype=torch.float32)
+    grads = {"dx": torch.empty((batch, L, D), **opts), "ddelta": torch.empty((batch, L, D), **opts),
+             "dA": torch.empty((D, N), **opts), "dB": torch.empty((batch, L, N), **opts),
+             "dC": torch.empty((batch, L, N), **opts)}
+    if Dskip is not None:
+        grads["dD"] = torch.empty((D,), **opts)
+    if z is not None:
+        grads["dz"] = torch.empty((batch, L, D), **opts)
+    if h0 is not None:
+        grads["dh0"] = torch.empty((batch, D, N), **opts)
+    nbytes = mssm_selective_scan_bwd_workspace_size(batch, L, D, N, x.dtype)
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=x.device)
+    return mssm_selective_scan_bwd(x, delta, A, B, C, dout, grads, ws, Dskip=Dskip, z=z, h0=h0,
+                                   stream=stream)

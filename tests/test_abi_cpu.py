@@ -229,3 +229,33 @@ def test_block_support_and_argument_errors(lib):
     assert call(p11, FAKE, out.value - 1, 1, 8, 32, 64, 16, 16, 4) == 4
     assert call(p11, ctypes.c_void_p(0x1010), out.value, 1, 8, 32, 64, 16, 16, 4) == 4  # align
     assert call([None] * 11, None, 0, 0, 8, 32, 64, 16, 16, 4) == 0
+
+
+def test_backward_argument_errors(lib):
+    out = ctypes.c_size_t(0)
+    assert lib.mssm_selective_scan_bwd_workspace_size(8, 2048, 1536, 16, 0, ctypes.byref(out)) == 0
+    assert out.value > 0
+    nb = out.value
+
+    def call(ptrs, ws, wsb, batch, L, D, N, dtype=0):
+        return lib.mssm_selective_scan_bwd(*ptrs, ws, wsb, batch, L, D, N, dtype, None)
+    # x delta A B C Dskip z h0 dout dx ddelta dA dB dC dD dz dh0
+    p17 = [FAKE] * 17
+    assert call(p17, FAKE, 1 << 40, 1, 4, 4, 3) == 2
+    assert call(p17, FAKE, 1 << 40, -1, 4, 4, 4) == 1
+    for i, j in ((5, 14), (6, 15)):                      # an optional input without its gradient
+        ptrs = list(p17)
+        ptrs[j] = None
+        assert call(ptrs, FAKE, 1 << 40, 1, 4, 4, 4) == 1
+        ptrs = list(p17)
+        ptrs[i] = None
+        assert call(ptrs, FAKE, 1 << 40, 1, 4, 4, 4) == 1
+    ptrs = list(p17)
+    ptrs[7] = None                                       # dh0 without h0
+    assert call(ptrs, FAKE, 1 << 40, 1, 4, 4, 4) == 1
+    for i in (0, 1, 2, 3, 4, 8, 9, 10, 11, 12, 13):
+        ptrs = list(p17)
+        ptrs[i] = None
+        assert call(ptrs, FAKE, 1 << 40, 1, 4, 4, 4) == 1, f"null {i} accepted"
+    assert call(p17, FAKE, nb - 1, 8, 2048, 1536, 16) == 4
+    assert call(p17, ctypes.c_void_p(0x1004), nb, 8, 2048, 1536, 16) == 4

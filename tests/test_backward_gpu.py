@@ -1,0 +1,97 @@
+"""GPU parity of the scan's backward pass (mssm_selective_scan_bwd through the
+C ABI) against the float64 adjoint oracle.  The tolerance stated for y is used
+relative to each gradient tensor's scale: |err| <= tol (|ref| + rms(ref)), since
+dA, dD (sums over batch and time) and dB, dC (sums over channels) can cancel
+to values far below the size of their terms."""
+import numpy as np
+import pytest
+
+import workloads
+from gpu_support import TOL, dev, host64, inputs_on_device
+from oracle.backward import selective_scan_backward
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+from selective_state_space_54_amd import mssm  # noqa: E402
+
+
+def grad_parity(gpu, ref, dtype, what):
+    tol = TOL[dtype]
+    report = {}
+    for k, r in ref.items():
+        g = host64(gpu[k])
+        assert np.isfinite(g).all(), f"{what} {k}: non-finite"
+        scale = np.abs(r) + (np.sqrt(np.mean(r ** 2)) if r.size else 0.0)
+        ratio = float((np.abs(g - r) / (tol * scale + 1e-30)).max()) if r.size else 0.0
+        report[k] = round(ratio, 4)
+        assert ratio <= 1.0, f"{what} {k}: max err / bound = {ratio:.3g}"
+    return report
+
+
+def run_case(g, extras, parts, seed=0):
+    w = g["workload"]
+    rng = np.random.default_rng(seed)
+    dout = rng.standard_normal((w.batch, w.L, w.D)).astype(np.float32)
+    t = inputs_on_device(g)
+    opt = {k: dev(extras[k]) for k in parts}
+    grads = mssm.selective_scan_bwd(t["x"], t["delta"], t["A"], t["B"], t["C"], dev(dout),
+                                    Dskip=opt.get("Dskip"), z=opt.get("z"), h0=opt.get("h0"))
+    torch.cuda.synchronize()
+    f = workloads.to_float64
+    ref = selective_scan_backward(
+        f(g["x"]), f(g["delta"]), g["A"].astype(np.float64), f(g["B"]), f(g["C"]),
+        dout.astype(np.float64),
+        Dskip=extras["Dskip"].astype(np.float64) if "Dskip" in parts else None,
+        z=f(extras["z"]) if "z" in parts else None,
+        h0=extras["h0"].astype(np.float64) if "h0" in parts else None)
+    return grads, ref
+
+
+SHAPES = [  # batch, L, D, N
+    (1, 1, 1, 1), (2, 15, 5, 4), (1, 16, 64, 16), (2, 17, 70, 8), (1, 100, 130, 16),
+    (3, 257, 64, 2), (1, 300, 257, 32), (2, 1000, 96, 16),
+]
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_backward_all_parts(shape, dtype):
+    batch, L, D, N = shape
+    print(f"case bwd {shape} {dtype}", flush=True)
+    name = "mamba130m_layer_fp32" if dtype == "fp32" else "mid_bf16"
+    g = workloads.generate(name, batch=batch, L=L, D=D, N=N, seed=900 + L + D)
+    extras = workloads.generate_extras(g["workload"])
+    grads, ref = run_case(g, extras, ("Dskip", "z", "h0"), seed=L)
+    grad_parity(grads, ref, dtype, f"bwd {shape} {dtype}")
+
+
+@pytest.mark.parametrize("parts", [(), ("Dskip",), ("z",), ("h0",), ("Dskip", "z")],
+                         ids=lambda p: "-".join(p) or "plain")
+def test_backward_each_combination(parts):
+    g = workloads.generate("mamba130m_layer_fp32", batch=2, L=333, D=100, N=16, seed=5)
+    extras = workloads.generate_extras(g["workload"])
+    grads, ref = run_case(g, extras, parts, seed=3)
+    assert set(grads) == set(ref)
+    grad_parity(grads, ref, "fp32", f"bwd {parts}")
+
+
+def test_backward_is_deterministic():
+    g = workloads.generate("mid_bf16", batch=2, L=500, D=256, N=16, seed=6)
+    extras = workloads.generate_extras(g["workload"])
+    a, _ = run_case(g, extras, ("Dskip", "z", "h0"), seed=4)
+    b, _ = run_case(g, extras, ("Dskip", "z", "h0"), seed=4)
+    for k in a:
+        assert torch.equal(a[k], b[k]), k
+
+
+def test_backward_full_size_headline():
+    """batch 8, L 2048, D 1536, N 16 with feedthrough, gate and initial state."""
+    print("case bwd mamba130m_layer_fp32 full size", flush=True)
+    g = workloads.generate("mamba130m_layer_fp32")
+    extras = workloads.generate_extras(g["workload"])
+    grads, ref = run_case(g, extras, ("Dskip", "z", "h0"), seed=11)
+    print("bwd full", grad_parity(grads, ref, "fp32", "bwd full"), flush=True)
