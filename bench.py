@@ -326,6 +326,52 @@ def time_conv(torch, mssm, steps=20, warmup=3, batch=16, L=2048, D=5120, k=4):
                     f"2 rotated inputs"}
 
 
+def time_backward(name, steps, warmup, torch, mssm, workloads, parts=True):
+    """The scan's backward pass (forward and reverse chunk summaries, recompute,
+    partial sums) with feedthrough, gate and initial state."""
+    w = workloads.workload(name)
+    g = workloads.generate(name)
+    d = device_inputs(g, torch)
+    e = workloads.generate_extras(w)
+    opt = {k: _to_device(e[k], torch) for k in ("Dskip", "z", "h0")} if parts else {}
+    del g, e
+    dout = torch.randn((w.batch, w.L, w.D), device="cuda")
+    opts = dict(device="cuda", dtype=torch.float32)
+    grads = {"dx": torch.empty((w.batch, w.L, w.D), **opts),
+             "ddelta": torch.empty((w.batch, w.L, w.D), **opts),
+             "dA": torch.empty((w.D, w.N), **opts), "dB": torch.empty((w.batch, w.L, w.N), **opts),
+             "dC": torch.empty((w.batch, w.L, w.N), **opts)}
+    if parts:
+        grads.update(dD=torch.empty((w.D,), **opts), dz=torch.empty((w.batch, w.L, w.D), **opts),
+                     dh0=torch.empty((w.batch, w.D, w.N), **opts))
+    nb = mssm.mssm_selective_scan_bwd_workspace_size(w.batch, w.L, w.D, w.N, d["x"].dtype)
+    ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+
+    def step():
+        mssm.mssm_selective_scan_bwd(d["x"], d["delta"], d["A"], d["B"], d["C"], dout, grads, ws,
+                                     Dskip=opt.get("Dskip"), z=opt.get("z"), h0=opt.get("h0"))
+
+    for _ in range(warmup):
+        step()
+    stream = torch.cuda.current_stream()
+    s_ev = torch.cuda.Event(enable_timing=True)
+    e_ev = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    s_ev.record(stream)
+    for _ in range(steps):
+        step()
+    e_ev.record(stream)
+    torch.cuda.synchronize()
+    kernel_ms = s_ev.elapsed_time(e_ev) / steps
+    del d, opt, dout, grads, ws
+    torch.cuda.empty_cache()
+    return {"kernel_ms": round(kernel_ms, 4),
+            "Gelem/s": round(elements(w) / (kernel_ms * 1e-3) / 1e9, 1),
+            "note": "backward of the scan with Dskip, z gate and h0: forward chunk summaries "
+                    "+ carries, reverse summaries + carries, per-chunk recompute and "
+                    "reverse sweep, partial-sum reductions"}
+
+
 def cpu_baseline(name, workloads, oracle, threads):
     """The float64 oracle on the host cores, on the whole headline workload."""
     g = workloads.generate(name)
@@ -361,7 +407,7 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", default=None,
                     choices=["fused_proj_bf16", "scan_ex", "decode_step_bf16", "conv1d_silu_fp32",
-                             "mamba_block_bf16"],
+                             "mamba_block_bf16", "backward"],
                     help="time only this extra workload and print its record (for profiling)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (5 times) and exit; "
@@ -401,6 +447,8 @@ def main(argv=None):
             rec = time_decode(args.only, args.steps, args.warmup, torch, mssm, workloads)
         elif args.only == "conv1d_silu_fp32":
             rec = time_conv(torch, mssm, steps=args.steps, warmup=args.warmup)
+        elif args.only == "backward":
+            rec = time_backward(HEADLINE, args.steps, args.warmup, torch, mssm, workloads)
         else:
             rec = time_block(args.only, args.steps, args.warmup, torch, mssm, workloads)
         print(json.dumps({"only": args.only, **rec}), flush=True)
@@ -470,6 +518,8 @@ def main(argv=None):
                                                  workloads)
         others["conv1d_silu_fp32"] = time_conv(torch, mssm)
         others["mamba_block_bf16"] = time_block("mamba_block_bf16", 5, 2, torch, mssm, workloads)
+        others["backward mamba130m_layer_fp32"] = time_backward(HEADLINE, 5, 2, torch, mssm,
+                                                                workloads)
         line["workloads"] = others
     if not args.no_cpu_baseline:
         import oracle

@@ -320,14 +320,38 @@ __global__ void bwd_reduce_bc_kernel(const float* __restrict__ part, float* __re
   }
 }
 
-// out[e] = sum_r part[r * count + e], r < nparts.
-__global__ void bwd_reduce_rows_kernel(const float* __restrict__ part, float* __restrict__ out,
-                                       int64_t count, int64_t nparts) {
-  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < count;
-       e += (int64_t)gridDim.x * blockDim.x) {
-    float s = 0.0f;
-    for (int64_t r = 0; r < nparts; ++r) s += part[r * count + e];
-    out[e] = s;
+// out[e] = sum_r part[r * count + e], r < nparts.  A block takes 16 outputs;
+// its 16 row groups each sum every 16th row (rows issued 4 at a time), then
+// the groups' sums are added in LDS in a fixed order: deterministic.
+constexpr int kRedCols = 16, kRedGroups = 16;
+__global__ __launch_bounds__(kRedCols * kRedGroups) void bwd_reduce_rows_kernel(
+    const float* __restrict__ part, float* __restrict__ out, int64_t count, int64_t nparts) {
+  __shared__ float acc[kRedGroups][kRedCols];
+  const int col = threadIdx.x % kRedCols;
+  const int grp = threadIdx.x / kRedCols;
+  const int64_t e = (int64_t)blockIdx.x * kRedCols + col;
+  float s = 0.0f;
+  if (e < count) {
+    int64_t r = grp;
+    for (; r + 3 * kRedGroups < nparts; r += 4 * kRedGroups) {
+      const float v0 = part[r * count + e];
+      const float v1 = part[(r + kRedGroups) * count + e];
+      const float v2 = part[(r + 2 * kRedGroups) * count + e];
+      const float v3 = part[(r + 3 * kRedGroups) * count + e];
+      s += v0;
+      s += v1;
+      s += v2;
+      s += v3;
+    }
+    for (; r < nparts; r += kRedGroups) s += part[r * count + e];
+  }
+  acc[grp][col] = s;
+  __syncthreads();
+  if (grp == 0 && e < count) {
+    float t = 0.0f;
+#pragma unroll
+    for (int g = 0; g < kRedGroups; ++g) t += acc[g][col];
+    out[e] = t;
   }
 }
 
@@ -410,11 +434,13 @@ hipError_t launch_bwd_t(const BwdArgs& a, const BwdPlan& bp, char* ws, hipStream
   // 4. sums of the partials
   hipLaunchKernelGGL(bwd_reduce_bc_kernel, dim3(2048), dim3(256), 0, stream, p.partBC, a.dB,
                      a.dC, a.batch * a.L, static_cast<int>(a.N), p.n_wt);
-  hipLaunchKernelGGL(bwd_reduce_rows_kernel, dim3(1024), dim3(256), 0, stream, p.partA, a.dA,
-                     a.D * a.N, a.batch * K);
+  const int64_t da_count = a.D * a.N;
+  hipLaunchKernelGGL(bwd_reduce_rows_kernel, dim3((unsigned)((da_count + kRedCols - 1) / kRedCols)),
+                     dim3(kRedCols * kRedGroups), 0, stream, p.partA, a.dA, da_count,
+                     a.batch * K);
   if (kSkip)
-    hipLaunchKernelGGL(bwd_reduce_rows_kernel, dim3(256), dim3(256), 0, stream, p.partD, a.dD,
-                       a.D, a.batch * K);
+    hipLaunchKernelGGL(bwd_reduce_rows_kernel, dim3((unsigned)((a.D + kRedCols - 1) / kRedCols)),
+                       dim3(kRedCols * kRedGroups), 0, stream, p.partD, a.dD, a.D, a.batch * K);
   return hipGetLastError();
 }
 
