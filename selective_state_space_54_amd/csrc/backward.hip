@@ -42,31 +42,46 @@ __device__ __forceinline__ float silu_slope(float v) {
   return s * (1.0f + v * (1.0f - s));
 }
 
+// DPP lane moves within 16-lane rows (row_ror:8 swaps the row's two halves,
+// row_half_mirror reverses each group of 8, the quad permutations swap lanes
+// 2 apart and 1 apart).
+template <int kCtrl>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, 0xF, 0xF, false));
+}
+constexpr int kDppRowRor8 = 0x128, kDppRowHalfMirror = 0x141, kDppQuadXor2 = 0x4E,
+              kDppQuadXor1 = 0xB1;
+
+// a + b per lane after exchanging halves: permlane32_swap leaves lanes 0..31
+// holding (a, a from lanes 32..63) and lanes 32..63 holding (b from lanes
+// 0..31, b); the sum is a summed over lane pairs 32 apart in lanes 0..31 and b
+// in lanes 32..63.  permlane16_swap does the same for rows 16 apart.
+__device__ __forceinline__ float fold32(float a, float b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float fold16(float a, float b) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Sum of v[i] over the wavefront's 64 lanes for i = 0..7, scattered: lane L
-// returns the total of v[L >> 3].  Three halving rounds (xor 32, 16, 8) keep
-// the half selected by the lane's bit, then three plain rounds (xor 4, 2, 1)
-// finish the sums.  Every lane of the wavefront must take part.
+// returns the total of v[L >> 3].  Three halving rounds (lanes 32, 16 and 8
+// apart) keep the half selected by the lane's bit, then three plain DPP rounds
+// within each group of 8 lanes finish the sums.  Every lane must take part.
 __device__ __forceinline__ float wave_reduce_scatter8(const float (&v)[8], int lane) {
   float w4[4], w2[2];
-  bool up = (lane & 32) != 0;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float send = up ? v[i] : v[i + 4];
-    const float keep = up ? v[i + 4] : v[i];
-    w4[i] = keep + __shfl_xor(send, 32);
-  }
-  up = (lane & 16) != 0;
+  for (int i = 0; i < 4; ++i) w4[i] = fold32(v[i], v[i + 4]);     // index 4*bit5 + i
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const float send = up ? w4[i] : w4[i + 2];
-    const float keep = up ? w4[i + 2] : w4[i];
-    w2[i] = keep + __shfl_xor(send, 16);
-  }
-  up = (lane & 8) != 0;
-  float w = (up ? w2[1] : w2[0]) + __shfl_xor(up ? w2[0] : w2[1], 8);
-  w += __shfl_xor(w, 4);
-  w += __shfl_xor(w, 2);
-  w += __shfl_xor(w, 1);
+  for (int i = 0; i < 2; ++i) w2[i] = fold16(w4[i], w4[i + 2]);   // + 2*bit4
+  const bool up = (lane & 8) != 0;                                 // + bit3
+  float w = (up ? w2[1] : w2[0]) + dpp<kDppRowRor8>(up ? w2[0] : w2[1]);
+  w += dpp<kDppRowHalfMirror>(w);
+  w += dpp<kDppQuadXor2>(w);
+  w += dpp<kDppQuadXor1>(w);
   return w;
 }
 
@@ -234,29 +249,35 @@ __global__ __launch_bounds__(kBwdBlock) void bwd_chunk_kernel(
         float gv = buf_load1<float>(gr, f_lane, s * f_row);
         if constexpr (kGate) gv *= silu(buf_load1<T>(zr, in_lane, soff));
         const float dxv = dv * xv;
+        // lanes past the last channel add nothing to dB, dC
+        const float xact = active ? xv : 0.0f, gact = active ? gv : 0.0f;
         float v[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) v[j] = 0.0f;
+        float q = 0.0f, r = 0.0f;    // sum_n lam B, sum_n lam A a h_{t-1}
 #pragma unroll
         for (int j = 0; j < G; ++j) {
           const float Bj = to_float(Bc[s * N + n0 + j]);
           const float lam = __builtin_fmaf(to_float(Cc[s * N + n0 + j]), gv, lamc[j]);
           const float hb = hist[s][j];
-          const float hpa = hb - dxv * Bj;                     // a_t h_{t-1}
-          v[j] = active ? lam * dxv : 0.0f;                    // dB_t[n]
-          v[4 + j] = active ? gv * hb : 0.0f;                  // dC_t[n]
-          dxa[s] = __builtin_fmaf(lam, dv * Bj, dxa[s]);
-          dda[s] = __builtin_fmaf(lam, __builtin_fmaf(Bj, xv, Ar[j] * hpa), dda[s]);
-          dAacc[j] = __builtin_fmaf(lam * dv, hpa, dAacc[j]);
+          const float hpa = __builtin_fmaf(-dxv, Bj, hb);     // a_t h_{t-1}
+          q = __builtin_fmaf(lam, Bj, q);
+          r = __builtin_fmaf(lam * Ar[j], hpa, r);
+          const float ldv = lam * dv;
+          dAacc[j] = __builtin_fmaf(ldv, hpa, dAacc[j]);
+          v[j] = ldv * xact;                                    // dB_t[n]
+          v[4 + j] = gact * hb;                                 // dC_t[n]
           lamc[j] = fast_exp2(dv * A2[j]) * lam;
         }
-        const float r = wave_reduce_scatter8(v, lane);
+        dxa[s] = __builtin_fmaf(dv, q, dxa[s]);
+        dda[s] += __builtin_fmaf(xv, q, r);
+        const float red = wave_reduce_scatter8(v, lane);
         if ((lane & 7) == 0) {
           const int idx = lane >> 3;
           const int j = idx & 3;
           if (j < G) {
             const int col = idx < 4 ? n0 + j : N + n0 + j;
-            p.partBC[((wt * p.batch + b) * L + t0 + s) * (2 * N) + col] = r;
+            p.partBC[((wt * p.batch + b) * L + t0 + s) * (2 * N) + col] = red;
           }
         }
       }
