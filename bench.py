@@ -46,11 +46,18 @@ def elements(w) -> int:
     return w.batch * w.L * w.D * w.N
 
 
+# The sources the headline scan's kernels (summary, carry, output: first-order
+# input term, no optional parts) are built from; the traffic record is tied
+# to their hash.
+HEADLINE_SOURCES = ("scan_device.h", "scan_kernels.h", "scan_kernels.hip", "scan_summary_euler.hip",
+                    "scan_out_euler_plain.hip", "mssm_internal.h")
+
+
 def kernel_sources_digest() -> str:
     h = hashlib.sha256()
-    for p in sorted(glob.glob(os.path.join(ROOT, "selective_state_space_54_amd", "csrc", "*"))):
-        with open(p, "rb") as f:
-            h.update(os.path.basename(p).encode())
+    for name in HEADLINE_SOURCES:
+        with open(os.path.join(ROOT, "selective_state_space_54_amd", "csrc", name), "rb") as f:
+            h.update(name.encode())
             h.update(f.read())
     return h.hexdigest()
 
