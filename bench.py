@@ -389,13 +389,13 @@ def cpu_baseline(name, workloads, oracle, threads):
     B = workloads.to_float64(g["B"])
     C = workloads.to_float64(g["C"])
     oracle.selective_scan(x[:, :64], dl[:, :64], A, B[:, :64], C[:, :64], nthreads=threads)
-    # repeat whole passes until about 10 s of wall time (bounded to 50 passes)
+    # repeat whole passes until about 10 s of wall time (bounded to 1000 passes)
     passes, t0 = 0, time.perf_counter()
     while True:
         oracle.selective_scan(x, dl, A, B, C, nthreads=threads)
         passes += 1
         dt = time.perf_counter() - t0
-        if dt >= 10.0 or passes >= 50:
+        if dt >= 10.0 or passes >= 1000:
             break
     return {"value": round(algorithmic_bytes(w) * passes / dt / 1e9, 4), "unit": "GB/s",
             "cores": threads, "kind": "oracle", "seconds": round(dt, 3),
