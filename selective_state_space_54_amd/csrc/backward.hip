@@ -86,14 +86,15 @@ __device__ __forceinline__ float wave_reduce_scatter8(const float (&v)[8], int l
 }
 
 // Reverse summary of chunk k (1..K-1): the adjoint sweep from zero at the
-// chunk's end, nu = a_{s_k} lam_{s_k}, and the chunk's decay exp(A sum delta),
-// stored in reversed chunk order (slot K-1-k) so that the forward carry kernel
-// produces the adjoint entering each chunk from the right.
+// chunk's end, nu = a_{s_k} lam_{s_k}, and the chunk's step-size total (its
+// decay is exp(A sum delta)), stored in reversed chunk order (slot K-1-k) so
+// that the forward carry kernel produces the adjoint entering each chunk from
+// the right.
 template <int N, typename T, bool kGate>
 __global__ __launch_bounds__(kBwdBlock) void bwd_rev_summary_kernel(
     const T* __restrict__ delta, const float* __restrict__ A, const T* __restrict__ Cm,
     const T* __restrict__ z, const float* __restrict__ dout, float* __restrict__ rev_h,
-    float* __restrict__ rev_p, int64_t L, int64_t D, int64_t chunk, int K, int64_t n_dtiles) {
+    double* __restrict__ rev_s, int64_t L, int64_t D, int64_t chunk, int K, int64_t n_dtiles) {
   const int64_t bid = blockIdx.x;
   const int64_t dtile = bid % n_dtiles;
   const int64_t rest = bid / n_dtiles;
@@ -126,11 +127,8 @@ __global__ __launch_bounds__(kBwdBlock) void bwd_rev_summary_kernel(
   }
   const int64_t slot = b * (K - 1) + (K - 1 - k);
 #pragma unroll
-  for (int n = 0; n < N; ++n) {
-    rev_h[(slot * N + n) * D + d] = lamc[n];
-    rev_p[(slot * N + n) * D + d] =
-        fast_exp2(static_cast<float>(static_cast<double>(A2[n]) * S));
-  }
+  for (int n = 0; n < N; ++n) rev_h[(slot * N + n) * D + d] = lamc[n];
+  rev_s[slot * D + d] = S;
 }
 
 struct BwdParams {
@@ -388,9 +386,9 @@ hipError_t launch_bwd_t(const BwdArgs& a, const BwdPlan& bp, char* ws, hipStream
   const T* Cm = static_cast<const T*>(a.C);
   const T* z = static_cast<const T*>(a.z);
   float* sum_h = reinterpret_cast<float*>(ws + bp.fwd_h_offset);
-  float* sum_p = reinterpret_cast<float*>(ws + bp.fwd_p_offset);
+  double* sum_s = reinterpret_cast<double*>(ws + bp.fwd_s_offset);
   float* rev_h = reinterpret_cast<float*>(ws + bp.rev_h_offset);
-  float* rev_p = reinterpret_cast<float*>(ws + bp.rev_p_offset);
+  double* rev_s = reinterpret_cast<double*>(ws + bp.rev_s_offset);
   hipError_t e;
   if (K > 1) {
     // 1. forward: the state entering every chunk (the forward pass's own kernels)
@@ -406,7 +404,7 @@ hipError_t launch_bwd_t(const BwdArgs& a, const BwdPlan& bp, char* ws, hipStream
     sp.B = a.B;
     sp.C = a.C;
     sp.sum_h = sum_h;
-    sp.sum_p = sum_p;
+    sp.sum_s = sum_s;
     sp.L = a.L;
     sp.D = a.D;
     sp.chunk_len = bp.chunk;
@@ -414,16 +412,16 @@ hipError_t launch_bwd_t(const BwdArgs& a, const BwdPlan& bp, char* ws, hipStream
     sp.n_dtiles = (a.D + kBlock - 1) / kBlock;
     e = launch_summary_euler(sa, plan, sp, stream);
     if (e != hipSuccess) return e;
-    e = launch_carry(sum_h, sum_p, a.h0, a.batch, a.D, a.N, K, stream);
+    e = launch_carry(sum_h, sum_s, a.A, a.h0, a.batch, a.D, a.N, K, stream);
     if (e != hipSuccess) return e;
     // 2. reverse: the adjoint entering every chunk from the right
     const int64_t rgrid = n_dtiles * (K - 1) * a.batch;
     hipLaunchKernelGGL((bwd_rev_summary_kernel<N, T, kGate>), dim3((unsigned)rgrid),
-                       dim3(kBwdBlock), 0, stream, delta, a.A, Cm, z, a.dout, rev_h, rev_p, a.L,
+                       dim3(kBwdBlock), 0, stream, delta, a.A, Cm, z, a.dout, rev_h, rev_s, a.L,
                        a.D, bp.chunk, K, n_dtiles);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    e = launch_carry(rev_h, rev_p, nullptr, a.batch, a.D, a.N, K, stream);
+    e = launch_carry(rev_h, rev_s, a.A, nullptr, a.batch, a.D, a.N, K, stream);
     if (e != hipSuccess) return e;
   }
   // 3. recompute + backwards sweep per chunk
@@ -489,12 +487,14 @@ BwdPlan plan_bwd(int64_t batch, int64_t L, int64_t D, int64_t N) {
   const size_t sums = b.K > 1 ? align256(sizeof(float) * (size_t)batch * (size_t)(b.K - 1) *
                                          (size_t)N * (size_t)D)
                               : 0;
+  const size_t totals =
+      b.K > 1 ? align256(sizeof(double) * (size_t)batch * (size_t)(b.K - 1) * (size_t)D) : 0;
   const size_t n_wt = (size_t)((D + 63) / 64);
   size_t off = 0;
   b.fwd_h_offset = off;   off += sums;
-  b.fwd_p_offset = off;   off += sums;
+  b.fwd_s_offset = off;   off += totals;
   b.rev_h_offset = off;   off += sums;
-  b.rev_p_offset = off;   off += sums;
+  b.rev_s_offset = off;   off += totals;
   b.part_bc_offset = off; off += align256(sizeof(float) * n_wt * (size_t)batch * (size_t)L * 2 * (size_t)N);
   b.part_a_offset = off;  off += align256(sizeof(float) * (size_t)batch * (size_t)b.K * (size_t)D * (size_t)N);
   b.part_d_offset = off;  off += align256(sizeof(float) * (size_t)batch * (size_t)b.K * (size_t)D);

@@ -221,7 +221,7 @@ FusedStatus launch_block(const BlockArgs& a, const BlockPlan& bp, void* workspac
   sa.A = a.A;
   if (bp.scan.K > 1) {
     sa.sum_h = reinterpret_cast<float*>(ws + bp.scan_offset);
-    sa.sum_p = reinterpret_cast<float*>(ws + bp.scan_offset + bp.scan.sum_p_offset);
+    sa.sum_s = reinterpret_cast<double*>(ws + bp.scan_offset + bp.scan.sum_s_offset);
   }
   sa.batch = a.batch;
   sa.L = a.L;

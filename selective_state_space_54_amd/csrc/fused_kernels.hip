@@ -288,7 +288,7 @@ __global__ __launch_bounds__(kFBlock) void fused_summary_kernel(
     const uint16_t* __restrict__ dtlow_lo,
     const uint16_t* __restrict__ wT, const float* __restrict__ bias,
     const float* __restrict__ A, const float* __restrict__ P, float* __restrict__ sum_h,
-    float* __restrict__ sum_p, int64_t L, int64_t D, int R, int64_t chunk_len, int K,
+    double* __restrict__ sum_s, int64_t L, int64_t D, int R, int64_t chunk_len, int K,
     int64_t n_dtiles) {
   using FV = FusedVariant<TX, false, false, float>;
   __shared__ float lds_all[4][kDTile * lds_stride<CPL>()];
@@ -321,13 +321,11 @@ __global__ __launch_bounds__(kFBlock) void fused_summary_kernel(
   if (c.active) {
     const int64_t row = c.b * (K - 1) + c.k;
 #pragma unroll
-    for (int q = 0; q < CPL; ++q)
+    for (int q = 0; q < CPL; ++q) {
 #pragma unroll
-      for (int n = 0; n < N; ++n) {
-        sum_h[(row * N + n) * D + dl + q] = h[q][n];
-        sum_p[(row * N + n) * D + dl + q] =
-            fast_exp2(static_cast<float>(static_cast<double>(A2[q][n]) * S[q]));
-      }
+      for (int n = 0; n < N; ++n) sum_h[(row * N + n) * D + dl + q] = h[q][n];
+      sum_s[row * D + dl + q] = S[q];
+    }
   }
 }
 
@@ -423,11 +421,11 @@ hipError_t launch_fused_scan_t(const FusedScanArgs& a, const ScanPlan& p, hipStr
   if (p.K > 1) {
     const int64_t grid = n_dtiles * (p.K - 1) * a.batch;
     hipLaunchKernelGGL((fused_summary_kernel<N, CPL, TX>), dim3((unsigned)grid), dim3(kFBlock), 0,
-                       stream, x, a.dtl, a.dtl_lo, a.wT, a.dt_bias, a.A, a.P, a.sum_h, a.sum_p,
+                       stream, x, a.dtl, a.dtl_lo, a.wT, a.dt_bias, a.A, a.P, a.sum_h, a.sum_s,
                        a.L, a.D, R, p.chunk_len, p.K, n_dtiles);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    e = launch_carry(a.sum_h, a.sum_p, nullptr, a.batch, a.D, a.N, p.K, stream);
+    e = launch_carry(a.sum_h, a.sum_s, a.A, nullptr, a.batch, a.D, a.N, p.K, stream);
     if (e != hipSuccess) return e;
   }
   const int64_t grid = n_dtiles * p.K * a.batch;
@@ -572,7 +570,7 @@ FusedStatus launch_fused(const FusedArgs& a, const FusedPlan& f, void* workspace
   sa.A = a.A;
   if (f.scan.K > 1) {
     sa.sum_h = reinterpret_cast<float*>(ws + f.scan_offset);
-    sa.sum_p = reinterpret_cast<float*>(ws + f.scan_offset + f.scan.sum_p_offset);
+    sa.sum_s = reinterpret_cast<double*>(ws + f.scan_offset + f.scan.sum_s_offset);
   }
   sa.batch = a.batch;
   sa.L = a.L;

@@ -21,7 +21,7 @@ struct ScanPlan {
   int K = 1;
   int64_t chunk_len = 0;
   size_t sum_h_bytes = 0;     // float [batch][K-1][N][D]: chunk end state from zero
-  size_t sum_p_offset = 0;    // byte offset of float [batch][K-1][N][D]: chunk decay
+  size_t sum_s_offset = 0;    // byte offset of double [batch][K-1][D]: chunk step-size total
   size_t workspace_bytes = 0;
 };
 
@@ -62,10 +62,12 @@ hipError_t launch_scan(const ScanArgs& a, const ScanPlan& plan, void* workspace,
 
 bool state_size_supported(int64_t N);
 
-// The carry pass over chunk summaries (shared by the plain and fused paths);
-// h0 ([batch, D, N], or null for a zero start) is the state before chunk 0.
-hipError_t launch_carry(float* sum_h, const float* sum_p, const float* h0, int64_t batch,
-                        int64_t D, int64_t N, int K, hipStream_t stream);
+// The carry pass over chunk summaries (shared by the plain, fused and backward
+// paths): hloc [batch, K-1, N, D] is overwritten with the carries, sum_s
+// [batch, K-1, D] holds each chunk's step-size total, A [D, N]; h0
+// ([batch, D, N], or null for a zero start) is the state before chunk 0.
+hipError_t launch_carry(float* sum_h, const double* sum_s, const float* A, const float* h0,
+                        int64_t batch, int64_t D, int64_t N, int K, hipStream_t stream);
 
 // h_last = h0 (or zero when h0 is null), `count` floats: the final state of an
 // empty sequence.
@@ -138,7 +140,7 @@ struct FusedScanArgs {
   const float* dt_bias = nullptr;
   const float* A = nullptr;
   float* sum_h = nullptr;
-  float* sum_p = nullptr;
+  double* sum_s = nullptr;
   int64_t batch = 0, L = 0, D = 0, N = 0, R = 0;
 };
 hipError_t launch_fused_scan(const FusedScanArgs& a, const ScanPlan& plan, hipStream_t stream);
@@ -226,13 +228,14 @@ struct BwdArgs {
 };
 
 // Chunks of `chunk` steps; workspace: forward and reverse chunk summaries
-// ([batch, K-1, N, D] float32 each, 4 arrays), per-wavefront dB/dC partials
+// (end states [batch, K-1, N, D] float32 and step-size totals [batch, K-1, D]
+// float64, for each direction), per-wavefront dB/dC partials
 // [ceil(D/64), batch, L, 2N], per-chunk dA partials [batch*K, D, N] and dD
 // partials [batch*K, D].
 struct BwdPlan {
   int64_t chunk = 0;
   int K = 1;
-  size_t fwd_h_offset = 0, fwd_p_offset = 0, rev_h_offset = 0, rev_p_offset = 0;
+  size_t fwd_h_offset = 0, fwd_s_offset = 0, rev_h_offset = 0, rev_s_offset = 0;
   size_t part_bc_offset = 0, part_a_offset = 0, part_d_offset = 0;
   size_t workspace_bytes = 0;
 };

@@ -12,7 +12,8 @@
 //                 state; keep its end state hloc_k and its total step size
 //                 S_k.  The chunk's decay is prod_t exp(delta_t A) =
 //                 exp(S_k A), so the pair for the whole chunk is
-//                 (exp(S_k A), hloc_k) and needs N + 1 numbers per chain.
+//                 (exp(S_k A), hloc_k) and needs N + 1 numbers per chain
+//                 (N floats and S_k as one double).
 //   carry pass    (per chain and state index): walk the chunk pairs in time
 //                 order, c_{k+1} = P_k c_k + hloc_k from c_0 = h0, giving the
 //                 state that enters every chunk.
@@ -20,11 +21,11 @@
 //                 carry-in and write y; the last chunk also writes the final
 //                 state when asked.
 //
-// Only the summaries (two [batch, K-1, N, D] float arrays: hloc and the decay
-// P = exp(S A)) travel through memory; per-step states stay in registers
-// ("Understanding Mamba", section 7.3).  S_k is accumulated in float64 so
-// that exp(S_k A) matches the product of the per-step factors to float32
-// rounding.  The decay does not depend on the input term, so the summary
+// Only the summaries (hloc as [batch, K-1, N, D] floats and S as
+// [batch, K-1, D] doubles) travel through memory; per-step states stay in
+// registers ("Understanding Mamba", section 7.3).  S_k is accumulated in
+// float64 so that exp(S_k A) matches the product of the per-step factors to
+// float32 rounding.  The decay does not depend on the input term, so the summary
 // pass differs between the first-order and the zero-order-hold forms only in
 // Bbar.
 #pragma once
@@ -54,8 +55,8 @@ struct ScanParams {
   const float* h0;      // [batch, D, N] or null (zero start)
   float* h_last;        // [batch, D, N] or null
   float* y;
-  float* sum_h;         // chunk summaries, [batch, K-1, N, D]
-  float* sum_p;
+  float* sum_h;         // chunk end states from zero, [batch, K-1, N, D]
+  double* sum_s;        // chunk step-size totals, [batch, K-1, D]
   int64_t L, D, chunk_len;
   int K;
   int64_t n_dtiles;
@@ -112,7 +113,7 @@ __device__ __forceinline__ void load_chain_consts(const float* __restrict__ A,
 template <int N, int CPL, typename T, bool kPairs, bool kZoh>
 __global__ __launch_bounds__(kBlock) void chunk_summary_kernel(
     const T* __restrict__ x, const T* __restrict__ delta, const float* __restrict__ A,
-    const T* __restrict__ Bm, float* __restrict__ sum_h, float* __restrict__ sum_p, ScanDims dm) {
+    const T* __restrict__ Bm, float* __restrict__ sum_h, double* __restrict__ sum_s, ScanDims dm) {
   using V = Variant<kZoh, false, false>;
   // grid: n_dtiles * (K - 1) * batch blocks; block (dtile, k, b), k < K - 1
   const int64_t D = dm.D, L = dm.L;
@@ -139,12 +140,10 @@ __global__ __launch_bounds__(kBlock) void chunk_summary_kernel(
 #pragma unroll
     for (int q = 0; q < CPL; ++q) {
 #pragma unroll
-      for (int n = 0; n < N; ++n) {
-        sum_h[(row * N + n) * D + c.d + q] = h[q][n];
-        // the chunk's decay prod_t exp(delta_t A) = exp(S A); S was summed in float64
-        sum_p[(row * N + n) * D + c.d + q] =
-            fast_exp2(static_cast<float>(static_cast<double>(k.A2[q][n]) * S[q]));
-      }
+      for (int n = 0; n < N; ++n) sum_h[(row * N + n) * D + c.d + q] = h[q][n];
+      // the chunk's decay prod_t exp(delta_t A) = exp(S A) is formed by the
+      // carry pass from S, summed here in float64
+      sum_s[row * D + c.d + q] = S[q];
     }
   }
 }
@@ -246,7 +245,7 @@ struct SummaryLaunch {
     hipLaunchKernelGGL((chunk_summary_kernel<N, CPL, T, kPairs, kZoh>), dim3((unsigned)grid),
                        dim3(kBlock), 0, stream, static_cast<const T*>(p.x),
                        static_cast<const T*>(p.delta), p.A, static_cast<const T*>(p.B), p.sum_h,
-                       p.sum_p, dm);
+                       p.sum_s, dm);
     return hipGetLastError();
   }
 };

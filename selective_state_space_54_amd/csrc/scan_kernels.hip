@@ -9,12 +9,17 @@
 namespace mssm {
 
 // Carry pass: one lane per (batch row, state n, channel d).  Walks the chunk
-// pairs in time order, c_{j+1} = P_j c_j + hloc_j (c_0 = h0, or 0), and overwrites
-// hloc_j with c_{j+1}, the state entering chunk j + 1.  The loads of up to
-// kBatch chunks are all issued before the dependent multiply-add chain, so a
-// lane pays one memory latency per kBatch chunks.
+// pairs in time order, c_{j+1} = P_j c_j + hloc_j (c_0 = h0, or 0), with the
+// chunk decay P_j = exp(A S_j) = exp2(A log2(e) S_j) formed from the chunk's
+// step-size total S_j (accumulated in float64 by the summary kernels; the
+// product is taken in float32, which moves P by at most ~5e-8 absolute: the
+// exponent's rounding error is relative, and |arg| 2^arg peaks near 0.5),
+// and overwrites hloc_j with c_{j+1}, the state entering chunk j + 1.  The loads of up to kBatch chunks are all issued before the
+// dependent multiply-add chain, so a lane pays one memory latency per kBatch
+// chunks.
 __global__ __launch_bounds__(kBlock) void chunk_carry_kernel(float* __restrict__ sum_h,
-                                                             const float* __restrict__ sum_p,
+                                                             const double* __restrict__ sum_s,
+                                                             const float* __restrict__ A,
                                                              const float* __restrict__ h0,
                                                              int64_t D, int N, int K,
                                                              int64_t n_dtiles) {
@@ -28,21 +33,24 @@ __global__ __launch_bounds__(kBlock) void chunk_carry_kernel(float* __restrict__
   if (d >= D) return;                       // no barriers in this kernel
   const int64_t stride = (int64_t)N * D;    // from chunk j to chunk j + 1
   float* hp = sum_h + (b * (K - 1) * N + n) * D + d;
-  const float* pp = sum_p + (b * (K - 1) * N + n) * D + d;
+  const double* sp = sum_s + b * (K - 1) * D + d;
+  const float a2 = A[d * N + n] * kLog2e;
   float c = h0 != nullptr ? h0[(b * D + d) * N + n] : 0.0f;
   for (int j0 = 0; j0 < K - 1; j0 += kBatch) {
-    float hv[kBatch], pv[kBatch];
+    float hv[kBatch];
+    double sv[kBatch];
 #pragma unroll
     for (int i = 0; i < kBatch; ++i) {
       if (j0 + i < K - 1) {
         hv[i] = hp[(int64_t)(j0 + i) * stride];
-        pv[i] = pp[(int64_t)(j0 + i) * stride];
+        sv[i] = sp[(int64_t)(j0 + i) * D];
       }
     }
 #pragma unroll
     for (int i = 0; i < kBatch; ++i) {
       if (j0 + i < K - 1) {
-        c = __builtin_fmaf(pv[i], c, hv[i]);
+        const float p = fast_exp2(a2 * static_cast<float>(sv[i]));
+        c = __builtin_fmaf(p, c, hv[i]);
         hp[(int64_t)(j0 + i) * stride] = c;
       }
     }
@@ -63,12 +71,12 @@ bool state_size_supported(int64_t N) {
 
 static size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
-hipError_t launch_carry(float* sum_h, const float* sum_p, const float* h0, int64_t batch,
-                        int64_t D, int64_t N, int K, hipStream_t stream) {
+hipError_t launch_carry(float* sum_h, const double* sum_s, const float* A, const float* h0,
+                        int64_t batch, int64_t D, int64_t N, int K, hipStream_t stream) {
   const int64_t carry_tiles = (D + kBlock - 1) / kBlock;
   const int64_t cgrid = carry_tiles * N * batch;
   hipLaunchKernelGGL(chunk_carry_kernel, dim3((unsigned)cgrid), dim3(kBlock), 0, stream, sum_h,
-                     sum_p, h0, D, static_cast<int>(N), K, carry_tiles);
+                     sum_s, A, h0, D, static_cast<int>(N), K, carry_tiles);
   return hipGetLastError();
 }
 
@@ -124,8 +132,9 @@ ScanPlan plan_scan(int64_t batch, int64_t L, int64_t D, int64_t N, int cpl) {
   p.chunk_len = chunk;
   if (K > 1) {
     p.sum_h_bytes = round_up(sizeof(float) * (size_t)batch * (size_t)(K - 1) * (size_t)N * (size_t)D, 256);
-    p.sum_p_offset = p.sum_h_bytes;
-    p.workspace_bytes = 2 * p.sum_h_bytes;
+    p.sum_s_offset = p.sum_h_bytes;
+    p.workspace_bytes =
+        p.sum_h_bytes + round_up(sizeof(double) * (size_t)batch * (size_t)(K - 1) * (size_t)D, 256);
   }
   return p;
 }
@@ -191,11 +200,11 @@ hipError_t launch_scan(const ScanArgs& a, const ScanPlan& plan, void* ws, hipStr
   const bool zoh = a.bbar == MSSM_BBAR_ZOH;
   if (plan.K > 1) {
     p.sum_h = static_cast<float*>(ws);
-    p.sum_p = reinterpret_cast<float*>(static_cast<char*>(ws) + plan.sum_p_offset);
+    p.sum_s = reinterpret_cast<double*>(static_cast<char*>(ws) + plan.sum_s_offset);
     hipError_t e = zoh ? launch_summary_zoh(a, plan, p, stream)
                        : launch_summary_euler(a, plan, p, stream);
     if (e != hipSuccess) return e;
-    e = launch_carry(p.sum_h, p.sum_p, a.h0, a.batch, a.D, a.N, plan.K, stream);
+    e = launch_carry(p.sum_h, p.sum_s, a.A, a.h0, a.batch, a.D, a.N, plan.K, stream);
     if (e != hipSuccess) return e;
   }
   return launch_output(a, plan, p, stream);
