@@ -13,7 +13,8 @@
  *                   "State Space Models and Mamba" (scalar recurrence section)
  *       h[b,d,n]  = Abar * h[b,d,n] + Bbar * x[b,t,d]   diagonal recurrence
  *                   ("Understanding Mamba", section 2.3, eq. (3)), h = 0 at
- *                   the start of every sequence
+ *                   the start of every sequence (mssm_selective_scan_fwd_ex
+ *                   also takes an initial state)
  *       y[b,t,d]  = sum_n C[b,t,n] * h[b,d,n]           read-out, eq. (3) with
  *                   the feedthrough term set to zero as in section 2.1
  *
