@@ -211,3 +211,21 @@ def test_binding_rejects_bad_tensors():
     with pytest.raises(mssm.MssmError) as e:
         mssm.selective_scan(t["x"], t["delta"], A3, B3, B3)
     assert e.value.status == 2
+
+
+def test_very_long_sequence_many_carries():
+    """L = 1,000,000 with few channels: thousands of chunks, so the carry pass
+    walks a long chain (and its batched loads wrap many times)."""
+    print("case very long L", flush=True)
+    g = workloads.generate("mamba130m_layer_fp32", batch=1, L=1_000_000, D=64, N=4, seed=71)
+    y = run_scan(g)
+    assert_parity(host64(y), oracle_scan(g), "fp32", "L = 1e6")
+
+
+def test_wide_ragged_channels():
+    """D = 66050 (not a multiple of the 512 channels a bf16 block covers) with a
+    short sequence: many channel tiles and a ragged last tile."""
+    print("case wide D", flush=True)
+    g = workloads.generate("mid_bf16", batch=2, L=150, D=66050, N=8, seed=72)
+    y = run_scan(g)
+    assert_parity(host64(y), oracle_scan(g), "bf16", "D = 66050")
