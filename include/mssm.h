@@ -18,11 +18,20 @@
  *       y[b,t,d]  = sum_n C[b,t,n] * h[b,d,n]           read-out, eq. (3) with
  *                   the feedthrough term set to zero as in section 2.1
  *
- *   The kernels evaluate this with an associative scan over time: the
- *   affine-pair operator of "Understanding Mamba" section 7.1 (eq. (8)) lets
- *   the sequence be cut into chunks that are scanned independently and then
- *   joined.  The [batch, L, D, N] state never leaves the chip (section 7.3);
- *   only small per-chunk summaries do.
+ *   Two evaluation orders, both keeping the [batch, L, D, N] state on chip
+ *   ("Understanding Mamba", section 7.3):
+ *   - chunked: an associative scan over time.  The affine-pair operator of
+ *     section 7.1 (eq. (8)) lets the sequence be cut into chunks that are
+ *     scanned independently and then joined; only small per-chunk summaries
+ *     reach memory (the workspace).  Any N the library supports, any D.
+ *   - single pass: one GPU lane per (channel, state index) runs the whole
+ *     sequence in time order; no chunks, no workspace.  Used for N = 16, D a
+ *     multiple of 16, inputs aligned to 4 elements and y to 16 bytes, and at
+ *     least 8192 channels (batch * D), where it fills the GPU on its own.
+ *   The library picks one per call from the shape and the pointers.  The
+ *   environment variable MSSM_SCAN_DESIGN=chunked or =chain, read at every
+ *   call, pins the choice (=chain still needs a shape the single pass
+ *   supports); the two agree to within float32 rounding.
  *
  * Layouts: dense, row-major, contiguous.
  *   x, delta    : [batch, L, D]   (d fastest)
@@ -100,8 +109,9 @@ int mssm_supports_state_size(int64_t N);
 
 /*
  * Bytes of device workspace mssm_selective_scan_fwd_ws needs for this shape
- * (0 when no chunk summaries are needed).  Returns MSSM_SUCCESS and writes
- * *bytes, or an argument error.
+ * (0 when no chunk summaries are needed).  The figure covers the chunked
+ * order, so it holds whichever order a call takes (the single pass uses
+ * none).  Returns MSSM_SUCCESS and writes *bytes, or an argument error.
  */
 mssm_status mssm_selective_scan_workspace_size(int64_t batch, int64_t L, int64_t D, int64_t N,
                                                mssm_dtype dtype, size_t *bytes);

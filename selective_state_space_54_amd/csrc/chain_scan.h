@@ -1,0 +1,323 @@
+// Single-pass selective scan with one lane per (channel, state index), N = 16.
+//
+// The chunked kernels give a lane a channel's N states and cut time into
+// chunks for parallelism, which costs a summary pass over every chunk but the
+// last and a second read of x and delta.  When batch * D channels already fill
+// the chip with one lane per state (12288 channels x 16 states = 3072
+// wavefronts, three per SIMD on MI355X), each lane can instead run its
+// (channel, n) chain over the whole sequence once.
+//
+// Layout.  A wavefront holds 4 channels x 16 state indices: DPP row c (16
+// lanes) is channel c, lane n of the row is state n.  A block is 4 wavefronts,
+// 16 adjacent channels of one batch row (D is a multiple of 16).  Time goes in
+// tiles of 16 steps:
+//   * inputs enter through LDS.  Each wavefront loads one whole 16 x 16 tile
+//     per step of the pipeline (wavefront 0: x, and z with the gate; 1: delta;
+//     2: B; 3: C), 4 values per lane, so every load instruction covers 16
+//     rows x 64 bytes instead of each wavefront fetching 16 rows x 16 bytes
+//     of each input (that version spent most of its time in the texture
+//     address unit).  B and C are written transposed so that lane n reads
+//     B[t0 .. t0 + 15][n] with four 16-byte LDS reads;
+//   * loads run two tiles ahead and keep their raw bits until they are
+//     written to LDS, so no wait for them sits inside a tile;
+//   * per step: a = exp2(delta A[n] log2 e); h = a h + (delta x) B_t[n]
+//     (first order) or h = a h + (a - 1) (x B_t[n] / A[n]) (exact zero-order
+//     hold); p_t = C_t[n] h ("Understanding Mamba", eq. (2)-(3)).  delta and
+//     delta x reach the row's lanes as DPP row_newbcast operands, which cost
+//     no extra instruction;
+//   * y_t = sum over the row of p_t: after the 16 steps a reduce-scatter over
+//     the row leaves lane n holding y of step t0 + n of its channel, which is
+//     the (step, channel) of the x value the lane loaded, so the feedthrough
+//     D x and the SiLU(z) gate are applied there;
+//   * y leaves through LDS too: one wavefront per tile (in turn) stores the
+//     block's 16 x 16 tile with 16-byte stores.
+// One barrier per tile; LDS buffers alternate between tiles.  Steps past the
+// end of the sequence (the last, partial tile) read the last step's values
+// with delta = 0, which leaves the state unchanged, and store nothing.
+#pragma once
+
+#include "mssm_internal.h"
+#include "scan_device.h"
+
+namespace mssm {
+namespace chain {
+
+constexpr int kWaves = 4;                // wavefronts per block
+constexpr int kBlock = 64 * kWaves;
+constexpr int kStates = 16;              // N handled by this design
+constexpr int kTile = 16;                // steps per tile = lanes per DPP row
+constexpr int kChannels = 4 * kWaves;    // channels per block
+// LDS row stride (floats) of the [16][16] tiles: rows stay 16-byte aligned
+// and the per-lane column reads (lane (c, n) reads row n, column 4w + c) fall
+// in distinct banks.
+constexpr int kRow = 20;
+
+template <int kCtrl>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(
+      __builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, 0xF, 0xF, false));
+}
+// Value of lane s of the lane's DPP row (row_newbcast).
+template <int s>
+__device__ __forceinline__ float row_bcast(float v) {
+  return __int_as_float(
+      __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x150 + s, 0xF, 0xF, true));
+}
+constexpr int kQuadXor2 = 0x4E, kQuadXor1 = 0xB1;
+
+// Row total of p[i], scattered: lane n of each DPP row returns the sum over
+// the row's 16 lanes of p[n].  Four halving levels.  The first two use the
+// DPP bank mask (a bank is 4 lanes of a row) to write each half of the row
+// from its own pair of sums, which saves the selects: lanes 0-7 take
+// p[i] + p[i] of lane n ^ 8 (row_ror:8), lanes 8-15 take p[i+8] + its
+// partner's; then within each half-row (row_half_mirror, partner 7 - n)
+// banks 0 and 2 keep the lower index, banks 1 and 3 the upper.  The last two
+// levels split lanes inside a bank, so they select.  The asm blocks start
+// with s_nop 1: a DPP read of a VGPR that the previous VALU instruction wrote
+// needs two wait states, and the compiler does not look inside asm.
+__device__ __forceinline__ float row_reduce_scatter16(const float (&p)[16], int n) {
+  float q8[8], q4[4], q2[2];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    asm volatile(
+        "s_nop 1\n\t"
+        "v_add_f32_dpp %0, %1, %1 row_ror:8 row_mask:0xf bank_mask:0x3\n\t"
+        "v_add_f32_dpp %0, %2, %2 row_ror:8 row_mask:0xf bank_mask:0xc"
+        : "=&v"(q8[i])
+        : "v"(p[i]), "v"(p[i + 8]));
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    asm volatile(
+        "s_nop 1\n\t"
+        "v_add_f32_dpp %0, %1, %1 row_half_mirror row_mask:0xf bank_mask:0x5\n\t"
+        "v_add_f32_dpp %0, %2, %2 row_half_mirror row_mask:0xf bank_mask:0xa"
+        : "=&v"(q4[i])
+        : "v"(q8[i]), "v"(q8[i + 4]));
+  bool up = (n & 2) != 0;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const float keep = up ? q4[i + 2] : q4[i], send = up ? q4[i] : q4[i + 2];
+    q2[i] = keep + dpp<kQuadXor2>(send);
+  }
+  up = (n & 1) != 0;
+  const float keep = up ? q2[1] : q2[0], send = up ? q2[0] : q2[1];
+  return keep + dpp<kQuadXor1>(send);
+}
+
+// Raw bits of 4 consecutive input values, as loaded.
+template <typename T> struct RawOf;
+template <> struct RawOf<float> { using type = float4; };
+template <> struct RawOf<uint16_t> { using type = uint2; };
+__device__ __forceinline__ void unpack(const float4& q, float (&v)[4]) {
+  v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
+}
+__device__ __forceinline__ void unpack(const uint2& q, float (&v)[4]) {   // bfloat16 -> float
+  v[0] = __uint_as_float(q.x << 16); v[1] = __uint_as_float(q.x & 0xFFFF0000u);
+  v[2] = __uint_as_float(q.y << 16); v[3] = __uint_as_float(q.y & 0xFFFF0000u);
+}
+
+// Block index -> logical block such that consecutive logical blocks (adjacent
+// channels, which share cache lines) run on one XCD: the hardware hands block
+// i to XCD i % 8.
+__device__ __forceinline__ int64_t xcd_local_block(int64_t bid, int64_t nblk) {
+  constexpr int kXcds = 8;
+  const int64_t per = nblk / kXcds, rem = nblk % kXcds;
+  const int64_t xcd = bid % kXcds, idx = bid / kXcds;
+  return xcd * per + (xcd < rem ? xcd : rem) + idx;
+}
+
+// grid: batch * D / 16 blocks of kBlock lanes.  Requirements (checked by the
+// launcher): N = 16, D % 16 == 0, x / delta / z aligned to 4 elements, y to
+// 16 bytes, 16 * D * 4 < 2^31.
+template <typename T, class V>
+__global__ __launch_bounds__(kBlock) void chain_scan_kernel(
+    const T* __restrict__ x, const T* __restrict__ delta, const float* __restrict__ A,
+    const T* __restrict__ Bm, const T* __restrict__ Cm, const float* __restrict__ Dskip,
+    const T* __restrict__ z, const float* __restrict__ h0, float* __restrict__ h_last,
+    float* __restrict__ y, int64_t L, int64_t D) {
+  constexpr int kTiles = V::kGate ? 5 : 4;     // x, delta, B^T, C^T (, z)
+  __shared__ __align__(16) float tin[2][kTiles][kTile][kRow];
+  __shared__ __align__(16) float tout[2][kTile][kRow];
+  using Raw = typename RawOf<T>::type;
+
+  const int64_t n_dgroups = D / kChannels;
+  const int64_t blk = xcd_local_block(blockIdx.x, gridDim.x);
+  const int64_t dg = blk % n_dgroups;
+  const int64_t b = blk / n_dgroups;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n = lane & 15;
+  const int ch = wave * 4 + (lane >> 4);       // channel within the block
+  const int64_t d0 = dg * kChannels;
+  const int64_t chain_idx = (b * D + d0 + ch) * kStates + n;   // [batch, D, N] index
+  const float a_dn = A[(d0 + ch) * kStates + n];
+  const float A2 = a_dn * kLog2e;
+  float Ainv = 0.0f;
+  if constexpr (V::kZoh) Ainv = 1.0f / a_dn;
+  float Dd = 0.0f;
+  if constexpr (V::kSkip) Dd = Dskip[d0 + ch];
+  float h = h0 ? h0[chain_idx] : 0.0f;
+
+  // Loader lane: step ls of the tile, 4 values from column lq.
+  const int ls = lane >> 2, lq = (lane & 3) * 4;
+  const T* src;
+  int64_t rs;
+  if (wave == 0) {
+    src = x + b * L * D + d0;
+    rs = D;
+  } else if (wave == 1) {
+    src = delta + b * L * D + d0;
+    rs = D;
+  } else if (wave == 2) {
+    src = Bm + b * L * kStates;
+    rs = kStates;
+  } else {
+    src = Cm + b * L * kStates;
+    rs = kStates;
+  }
+  const T* zsrc = V::kGate ? z + b * L * D + d0 : nullptr;   // loaded by wavefront 0
+  float* yb = y + b * L * D + d0;
+  const int64_t ntiles = (L + kTile - 1) / kTile;
+  const int64_t last = ntiles - 1;
+  const int tail_steps = static_cast<int>(L - last * kTile);   // steps of the last tile, 1..16
+  const int ls_tail = ls < tail_steps ? ls : tail_steps - 1;
+  const uint32_t off_full = static_cast<uint32_t>((ls * rs + lq) * sizeof(T));
+  const uint32_t off_tail = static_cast<uint32_t>((ls_tail * rs + lq) * sizeof(T));
+  const bool pad_lane = ls >= tail_steps;
+  const uint32_t yoff = static_cast<uint32_t>((ls * D + lq) * sizeof(float));
+
+  auto load1 = [&](const T* s, int64_t k) {
+    const T* base = s + k * kTile * rs;
+    return *reinterpret_cast<const Raw*>(reinterpret_cast<const char*>(base) +
+                                         (k == last ? off_tail : off_full));
+  };
+  struct Regs {
+    Raw v, zv;
+  };
+  auto load = [&](Regs& r, int64_t k) {
+    r.v = load1(src, k);
+    if constexpr (V::kGate) {
+      if (wave == 0) r.zv = load1(zsrc, k);
+    }
+  };
+  // Tile k's loaded values into LDS buffer `buf`.
+  auto put = [&](const Regs& r, int buf, int64_t k) {
+    float v[4];
+    unpack(r.v, v);
+    if (wave == 1 && k == last && pad_lane) v[0] = v[1] = v[2] = v[3] = 0.0f;   // delta
+    if (wave < 2) {
+      *reinterpret_cast<float4*>(&tin[buf][wave][ls][lq]) = make_float4(v[0], v[1], v[2], v[3]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) tin[buf][wave][lq + i][ls] = v[i];
+    }
+    if constexpr (V::kGate) {
+      if (wave == 0) {
+        unpack(r.zv, v);
+        *reinterpret_cast<float4*>(&tin[buf][4][ls][lq]) = make_float4(v[0], v[1], v[2], v[3]);
+      }
+    }
+  };
+  auto store_y = [&](int64_t k) {
+    const float4 v = *reinterpret_cast<const float4*>(&tout[k & 1][ls][lq]);
+    float* base = yb + k * kTile * D;
+    if (k != last || ls < tail_steps)
+      *reinterpret_cast<float4*>(reinterpret_cast<char*>(base) + yoff) = v;
+  };
+  auto compute = [&](int64_t k) {
+    const int buf = k & 1;
+    const float xv = tin[buf][0][n][ch];
+    const float dv = tin[buf][1][n][ch];
+    float Bt[kTile], Ct[kTile];
+#pragma unroll
+    for (int j = 0; j < kTile / 4; ++j) {
+      const float4 vb = *reinterpret_cast<const float4*>(&tin[buf][2][n][4 * j]);
+      const float4 vc = *reinterpret_cast<const float4*>(&tin[buf][3][n][4 * j]);
+      Bt[4 * j] = vb.x; Bt[4 * j + 1] = vb.y; Bt[4 * j + 2] = vb.z; Bt[4 * j + 3] = vb.w;
+      Ct[4 * j] = vc.x; Ct[4 * j + 1] = vc.y; Ct[4 * j + 2] = vc.z; Ct[4 * j + 3] = vc.w;
+    }
+    float p[kTile];
+    if constexpr (V::kZoh) {
+#pragma unroll
+      for (int s = 0; s < kTile; ++s) Bt[s] *= Ainv;
+    }
+    const float uv = V::kZoh ? xv : dv * xv;   // broadcast input factor of the step
+#define MSSM_CHAIN_STEP(S)                                                    \
+    {                                                                         \
+      const float a = fast_exp2(row_bcast<S>(dv) * A2);                       \
+      const float w = row_bcast<S>(uv) * Bt[S];                               \
+      h = __builtin_fmaf(a, h, V::kZoh ? __builtin_fmaf(a, w, -w) : w);       \
+      p[S] = Ct[S] * h;                                                       \
+    }
+    MSSM_CHAIN_STEP(0) MSSM_CHAIN_STEP(1) MSSM_CHAIN_STEP(2) MSSM_CHAIN_STEP(3)
+    MSSM_CHAIN_STEP(4) MSSM_CHAIN_STEP(5) MSSM_CHAIN_STEP(6) MSSM_CHAIN_STEP(7)
+    MSSM_CHAIN_STEP(8) MSSM_CHAIN_STEP(9) MSSM_CHAIN_STEP(10) MSSM_CHAIN_STEP(11)
+    MSSM_CHAIN_STEP(12) MSSM_CHAIN_STEP(13) MSSM_CHAIN_STEP(14) MSSM_CHAIN_STEP(15)
+#undef MSSM_CHAIN_STEP
+    float yv = row_reduce_scatter16(p, n);     // y of step n of this row's channel
+    if constexpr (V::kSkip) yv = __builtin_fmaf(Dd, xv, yv);
+    if constexpr (V::kGate) yv *= silu(tin[buf][4][n][ch]);
+    tout[buf][n][ch] = yv;
+  };
+
+  // Pipeline.  Iteration k: barrier; the y tile of k - 1 goes out; tile k + 1
+  // (loaded two iterations earlier) goes into LDS; tile k + 3 is loaded;
+  // tile k is computed.  Unrolled by two so the two register sets have fixed
+  // names.  Loads past the last tile repeat it and are never used.
+  Regs r0, r1;
+  load(r0, 0);
+  load(r1, 1 < last ? 1 : last);
+  put(r0, 0, 0);
+  load(r0, 2 < last ? 2 : last);
+  int64_t k = 0;
+  for (; k + 2 <= ntiles; k += 2) {
+    __syncthreads();
+    if (k >= 1 && wave == ((k - 1) & 3)) store_y(k - 1);
+    put(r1, 1, k + 1);
+    load(r1, k + 3 < last ? k + 3 : last);
+    compute(k);
+    __syncthreads();
+    if (wave == (k & 3)) store_y(k);
+    put(r0, 0, k + 2);
+    load(r0, k + 4 < last ? k + 4 : last);
+    compute(k + 1);
+  }
+  if (k < ntiles) {
+    __syncthreads();
+    if (k >= 1 && wave == ((k - 1) & 3)) store_y(k - 1);
+    compute(k);
+  }
+  __syncthreads();
+  if (wave == (last & 3)) store_y(last);
+  if constexpr (V::kState) h_last[chain_idx] = h;
+}
+
+template <class V>
+hipError_t launch_variant(const ScanArgs& a, hipStream_t stream);
+
+}  // namespace chain
+
+#define MSSM_DEFINE_CHAIN_VARIANT(ZOH, SKIP, GATE, STATE)                                     \
+  template <>                                                                                 \
+  hipError_t chain::launch_variant<Variant<ZOH, SKIP, GATE, STATE>>(const ScanArgs& a,        \
+                                                                    hipStream_t stream) {    \
+    using V = Variant<ZOH, SKIP, GATE, STATE>;                                                \
+    const dim3 grid(static_cast<unsigned>(a.batch * (a.D / chain::kChannels)));               \
+    if (a.dtype == MSSM_FLOAT32)                                                              \
+      hipLaunchKernelGGL((chain::chain_scan_kernel<float, V>), grid, dim3(chain::kBlock), 0,   \
+                         stream, static_cast<const float*>(a.x),                              \
+                         static_cast<const float*>(a.delta), a.A,                             \
+                         static_cast<const float*>(a.B), static_cast<const float*>(a.C),      \
+                         a.Dskip, static_cast<const float*>(a.z), a.h0, a.h_last,             \
+                         static_cast<float*>(a.y), a.L, a.D);                                 \
+    else                                                                                      \
+      hipLaunchKernelGGL((chain::chain_scan_kernel<uint16_t, V>), grid, dim3(chain::kBlock),  \
+                         0, stream, static_cast<const uint16_t*>(a.x),                        \
+                         static_cast<const uint16_t*>(a.delta), a.A,                          \
+                         static_cast<const uint16_t*>(a.B), static_cast<const uint16_t*>(a.C),\
+                         a.Dskip, static_cast<const uint16_t*>(a.z), a.h0, a.h_last,          \
+                         static_cast<float*>(a.y), a.L, a.D);                                 \
+    return hipGetLastError();                                                                 \
+  }
+
+}  // namespace mssm

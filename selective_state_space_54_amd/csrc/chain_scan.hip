@@ -1,0 +1,72 @@
+// Choice between the chunked scan and the single-pass (one lane per channel
+// and state) scan, and the single-pass kernel's variant dispatch.
+#include <cstdint>
+#include <cstdlib>
+#include <cstring>
+
+#include "chain_scan.h"
+
+namespace mssm {
+
+namespace {
+
+// Fewest batch * D channels for which the single-pass design is chosen by
+// itself.  Its lanes each carry one chain, so a SIMD needs about two of its
+// wavefronts (8192 channels on 1024 SIMDs) before the chain's latency is
+// hidden; below that the chunked design, which cuts time into chunks for
+// parallelism, is faster.
+constexpr int64_t kMinChannels = 8192;
+
+bool aligned(const void* p, size_t a) { return reinterpret_cast<uintptr_t>(p) % a == 0; }
+
+enum class Design { kAuto, kChunked, kChain };
+
+// MSSM_SCAN_DESIGN=chunked or =chain pins the design (tests and tuning run
+// both designs on the same shapes); =chain still needs a supported shape.
+Design design_setting() {
+  const char* e = std::getenv("MSSM_SCAN_DESIGN");
+  if (e == nullptr) return Design::kAuto;
+  if (std::strcmp(e, "chunked") == 0) return Design::kChunked;
+  if (std::strcmp(e, "chain") == 0) return Design::kChain;
+  return Design::kAuto;
+}
+
+template <bool kZoh, bool kSkip, bool kGate>
+hipError_t launch_state(const ScanArgs& a, hipStream_t stream) {
+  if (a.h_last) return chain::launch_variant<Variant<kZoh, kSkip, kGate, true>>(a, stream);
+  return chain::launch_variant<Variant<kZoh, kSkip, kGate, false>>(a, stream);
+}
+
+template <bool kZoh>
+hipError_t launch_parts(const ScanArgs& a, hipStream_t stream) {
+  const bool skip = a.Dskip != nullptr, gate = a.z != nullptr;
+  if (skip && gate) return launch_state<kZoh, true, true>(a, stream);
+  if (skip) return launch_state<kZoh, true, false>(a, stream);
+  if (gate) return launch_state<kZoh, false, true>(a, stream);
+  return launch_state<kZoh, false, false>(a, stream);
+}
+
+}  // namespace
+
+bool chain_scan_applies(const ScanArgs& a) {
+  const Design d = design_setting();
+  if (d == Design::kChunked) return false;
+  if (a.N != chain::kStates || a.D % chain::kChannels != 0 || a.L < 1 || a.batch < 1)
+    return false;
+  // 4-value loads of x, delta, z, B, C and 16-byte stores of y
+  const size_t in_align = a.dtype == MSSM_FLOAT32 ? 16 : 8;
+  if (!aligned(a.x, in_align) || !aligned(a.delta, in_align) || !aligned(a.B, in_align) ||
+      !aligned(a.C, in_align) || (a.z && !aligned(a.z, in_align)) || !aligned(a.y, 16))
+    return false;
+  // 32-bit lane offsets within a 16-step tile; grid size
+  if (a.D * chain::kTile * static_cast<int64_t>(sizeof(float)) >= (int64_t(1) << 31)) return false;
+  if (a.batch > (int64_t(1) << 31) / (a.D / chain::kChannels)) return false;
+  return d == Design::kChain || a.batch * a.D >= kMinChannels;
+}
+
+hipError_t launch_chain_scan(const ScanArgs& a, hipStream_t stream) {
+  return a.bbar == MSSM_BBAR_ZOH ? launch_parts<true>(a, stream)
+                                 : launch_parts<false>(a, stream);
+}
+
+}  // namespace mssm

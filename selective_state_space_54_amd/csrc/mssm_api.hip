@@ -40,6 +40,7 @@ mssm_status check_shape(int64_t batch, int64_t L, int64_t D, int64_t N, mssm_dty
 bool empty_problem(int64_t batch, int64_t L, int64_t D) { return batch == 0 || L == 0 || D == 0; }
 
 mssm_status check_grid(const mssm::ScanPlan& p, int64_t batch, int64_t D, int64_t N) {
+  if (p.chain) return MSSM_SUCCESS;   // sizes checked when the design was chosen
   // largest launch: chunk blocks (n_dtiles * K * batch) or carry blocks (n_dtiles * N * batch)
   const int64_t n_dtiles = (D + 255) / 256;
   int64_t blocks;
@@ -91,7 +92,7 @@ mssm_status mssm_selective_scan_fwd_ws(const void* x, const void* delta, const f
   if (empty_problem(batch, L, D)) return MSSM_SUCCESS;
   if (!x || !delta || !A || !B || !C || !y) return MSSM_ERROR_INVALID_VALUE;
   const mssm::ScanArgs a{x, delta, A, B, C, y, batch, L, D, N, dtype};
-  const mssm::ScanPlan plan = mssm::plan_scan(batch, L, D, N, mssm::choose_cpl(a));
+  const mssm::ScanPlan plan = mssm::plan_for(a);
   s = check_grid(plan, batch, D, N);
   if (s != MSSM_SUCCESS) return s;
   if (plan.workspace_bytes > 0 && (!workspace || workspace_bytes < plan.workspace_bytes))
@@ -113,7 +114,7 @@ mssm_status mssm_selective_scan_fwd(const void* x, const void* delta, const floa
   if (empty_problem(batch, L, D)) return MSSM_SUCCESS;
   if (!x || !delta || !A || !B || !C || !y) return MSSM_ERROR_INVALID_VALUE;
   const mssm::ScanArgs a{x, delta, A, B, C, y, batch, L, D, N, dtype};
-  const mssm::ScanPlan plan = mssm::plan_scan(batch, L, D, N, mssm::choose_cpl(a));
+  const mssm::ScanPlan plan = mssm::plan_for(a);
   s = check_grid(plan, batch, D, N);
   if (s != MSSM_SUCCESS) return s;
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -164,7 +165,7 @@ mssm_status mssm_selective_scan_fwd_ex(const void* x, const void* delta, const f
   a.h0 = h0;
   a.h_last = h_last;
   a.bbar = bbar;
-  const mssm::ScanPlan plan = mssm::plan_scan(batch, L, D, N, mssm::choose_cpl(a));
+  const mssm::ScanPlan plan = mssm::plan_for(a);
   s = check_grid(plan, batch, D, N);
   if (s != MSSM_SUCCESS) return s;
   if (plan.workspace_bytes > 0 && (!workspace || workspace_bytes < plan.workspace_bytes))

@@ -17,6 +17,7 @@ namespace mssm {
 // into its carry-in with the affine-pair operator and scans its own steps from
 // that carry.
 struct ScanPlan {
+  bool chain = false;         // single-pass design instead (no chunks, no workspace)
   int cpl = 1;                // chains (adjacent channels) per lane: 1 or 2
   int K = 1;
   int64_t chunk_len = 0;
@@ -46,6 +47,16 @@ struct ScanArgs {
 // Plan for `cpl` chains per lane.
 ScanPlan plan_scan(int64_t batch, int64_t L, int64_t D, int64_t N, int cpl);
 
+// Single-pass scan with one lane per (channel, state index), for N = 16 and
+// shapes with many channels: whether it is used for these arguments (shape,
+// alignment, channel count, MSSM_SCAN_DESIGN), and its launch.
+bool chain_scan_applies(const ScanArgs& a);
+hipError_t launch_chain_scan(const ScanArgs& a, hipStream_t stream);
+
+// The plan for these arguments: the single-pass design when it applies, else
+// the chunked plan with the chains-per-lane choice below.
+ScanPlan plan_for(const ScanArgs& a);
+
 // Workspace that covers the plan of every chains-per-lane choice the launcher
 // can make for this shape (the choice also depends on pointer alignment).
 size_t workspace_bound(int64_t batch, int64_t L, int64_t D, int64_t N);
@@ -61,6 +72,7 @@ hipError_t launch_scan(const ScanArgs& a, const ScanPlan& plan, void* workspace,
                        hipStream_t stream);
 
 bool state_size_supported(int64_t N);
+
 
 // The carry pass over chunk summaries (shared by the plain, fused and backward
 // paths): hloc [batch, K-1, N, D] is overwritten with the carries, sum_s

@@ -145,6 +145,15 @@ size_t workspace_bound(int64_t batch, int64_t L, int64_t D, int64_t N) {
   return w;
 }
 
+ScanPlan plan_for(const ScanArgs& a) {
+  if (chain_scan_applies(a)) {
+    ScanPlan p;
+    p.chain = true;
+    return p;
+  }
+  return plan_scan(a.batch, a.L, a.D, a.N, choose_cpl(a));
+}
+
 int choose_cpl(const ScanArgs& a) {
   int cpl = default_cpl(a.D, a.dtype);
   const size_t align = 2 * (a.dtype == MSSM_FLOAT32 ? 4 : 2);
@@ -181,6 +190,7 @@ static hipError_t launch_output(const ScanArgs& a, const ScanPlan& plan, const S
 }
 
 hipError_t launch_scan(const ScanArgs& a, const ScanPlan& plan, void* ws, hipStream_t stream) {
+  if (plan.chain) return launch_chain_scan(a, stream);
   ScanParams p{};
   p.x = a.x;
   p.delta = a.delta;

@@ -17,6 +17,11 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmssm.so")
 
 MSSM_SUCCESS = 0
+MSSM_ERROR_INVALID_VALUE = 1
+MSSM_ERROR_NOT_SUPPORTED = 2
+MSSM_ERROR_SIZE_OVERFLOW = 3
+MSSM_ERROR_WORKSPACE = 4
+MSSM_ERROR_HIP = 5
 MSSM_FLOAT32 = 0
 MSSM_BFLOAT16 = 1
 MSSM_BBAR_EULER = 0
@@ -195,6 +200,34 @@ def mssm_selective_scan_fwd_ws(x, delta, A, B, C, y, workspace, *, stream=None):
         _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(y), ws_ptr, ws_bytes,
         batch, L, D, N, _DTYPES[x.dtype], _stream_handle(stream)), "mssm_selective_scan_fwd_ws")
     return y
+
+
+class PreparedCall:
+    """One C-ABI call whose arguments were validated and converted once.
+    Calling it issues the same call again (same buffers, same stream) without
+    the per-call Python checks, for loops whose launches would otherwise wait
+    on the host.  It holds references to the tensors it was built from."""
+
+    __slots__ = ("_fn", "_args", "_where", "_keep")
+
+    def __init__(self, fn, args, where, keep):
+        self._fn, self._args, self._where, self._keep = fn, args, where, keep
+
+    def __call__(self):
+        status = self._fn(*self._args)
+        if status != MSSM_SUCCESS:
+            raise MssmError(status, self._where)
+
+
+def prepare_selective_scan_fwd_ws(x, delta, A, B, C, y, workspace, *, stream=None):
+    """mssm_selective_scan_fwd_ws as a PreparedCall."""
+    batch, L, D, N = _check_scan_args(x, delta, A, B, C, y)
+    ws_ptr = _ptr(workspace) if workspace is not None and workspace.numel() > 0 else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    args = (_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(y), ws_ptr, ws_bytes,
+            batch, L, D, N, _DTYPES[x.dtype], _stream_handle(stream))
+    return PreparedCall(load().mssm_selective_scan_fwd_ws, args, "mssm_selective_scan_fwd_ws",
+                        (x, delta, A, B, C, y, workspace))
 
 
 def selective_scan(x, delta, A, B, C, *, stream=None):

@@ -94,7 +94,10 @@ def test_zero_sizes_are_no_ops(lib):
         assert lib.mssm_selective_scan_fwd_ws(*nulls, None, 0, *shape, 16, 0, None) == 0
 
 
-def test_workspace_too_small_is_rejected(lib):
+def test_workspace_too_small_is_rejected(lib, monkeypatch):
+    # the chunked design's workspace (the single-pass design, which this shape
+    # would get by default, needs none)
+    monkeypatch.setenv("MSSM_SCAN_DESIGN", "chunked")
     st, nbytes = _ws(lib, 8, 2048, 1536, 16, 0)
     assert nbytes > 0
     r = lib.mssm_selective_scan_fwd_ws(*([FAKE] * 6), FAKE, nbytes - 1, 8, 2048, 1536, 16, 0, None)
@@ -142,7 +145,8 @@ def _ex(lib, ptrs, bbar, ws, wsb, batch, L, D, N, dtype=0):
     return lib.mssm_selective_scan_fwd_ex(*ptrs, bbar, ws, wsb, batch, L, D, N, dtype, None)
 
 
-def test_scan_ex_argument_errors(lib):
+def test_scan_ex_argument_errors(lib, monkeypatch):
+    monkeypatch.setenv("MSSM_SCAN_DESIGN", "chunked")   # the workspace cases below
     p10 = [FAKE] * 10          # x, delta, A, B, C, Dskip, z, h0, y, h_last
     assert _ex(lib, p10, 2, FAKE, 1 << 40, 1, 4, 4, 4) == 1        # bad bbar enum
     assert _ex(lib, p10, -1, FAKE, 1 << 40, 1, 4, 4, 4) == 1

@@ -1,0 +1,141 @@
+"""GPU parity of the single-pass scan design (one lane per channel and state,
+N = 16, D a multiple of 16) against the float64 oracle, through the C ABI.
+
+MSSM_SCAN_DESIGN=chain pins that design on shapes far below the channel count
+at which it is chosen by itself, so ragged and tiny sequences, every optional
+part, both input types and both input terms run through it; =chunked pins the
+other design on the full-size workloads, which now default to the single pass.
+"""
+import os
+
+import numpy as np
+import pytest
+
+import workloads
+from gpu_support import assert_parity, dev, host64, inputs_on_device, oracle_scan
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+from selective_state_space_54_amd import mssm  # noqa: E402
+from test_scan_ex_gpu import _opts, check  # noqa: E402
+
+
+@pytest.fixture
+def design(request):
+    old = os.environ.get("MSSM_SCAN_DESIGN")
+    os.environ["MSSM_SCAN_DESIGN"] = request.param
+    yield request.param
+    if old is None:
+        os.environ.pop("MSSM_SCAN_DESIGN", None)
+    else:
+        os.environ["MSSM_SCAN_DESIGN"] = old
+
+
+# (batch, L, D): one step, less than a tile, exactly one tile, one step past a
+# tile, many tiles with a ragged end, an odd tile count, wider blocks of channels
+SHAPES = [(1, 1, 16), (2, 15, 32), (1, 16, 16), (2, 17, 48), (3, 100, 64), (1, 257, 160),
+          (2, 48, 16), (1, 1000, 96)]
+
+
+@pytest.mark.parametrize("design", ["chain"], indirect=True)
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("kind", ["mamba130m_layer_fp32", "mid_bf16"])
+def test_plain_scan_shapes(kind, shape, design):
+    batch, L, D = shape
+    print(f"case chain plain {kind} {shape}", flush=True)
+    g = workloads.generate(kind, batch=batch, L=L, D=D, N=16, seed=500 + L + D)
+    t = inputs_on_device(g)
+    y = mssm.selective_scan(t["x"], t["delta"], t["A"], t["B"], t["C"])
+    torch.cuda.synchronize()
+    assert_parity(host64(y), oracle_scan(g), g["workload"].dtype, f"chain {kind} {shape}")
+
+
+@pytest.mark.parametrize("design", ["chain"], indirect=True)
+@pytest.mark.parametrize("init", [False, True], ids=["h0=0", "h0"])
+@pytest.mark.parametrize("gate", [False, True], ids=["nogate", "gate"])
+@pytest.mark.parametrize("skip", [False, True], ids=["noskip", "skip"])
+@pytest.mark.parametrize("bbar", ["euler", "zoh"])
+@pytest.mark.parametrize("kind", ["mamba130m_layer_fp32", "mid_bf16"])
+def test_each_combination_of_parts(kind, bbar, skip, gate, init, design):
+    print(f"case chain parts {kind} {bbar} skip={skip} gate={gate} h0={init}", flush=True)
+    g = workloads.generate(kind, batch=2, L=777, D=128, N=16, seed=61)
+    extras = workloads.generate_extras(g["workload"])
+    check(g, _opts(extras, skip, gate, init), bbar, f"chain {kind} {bbar} {skip} {gate} {init}")
+
+
+@pytest.mark.parametrize("design", ["chain"], indirect=True)
+@pytest.mark.parametrize("shape", [(1, 1, 16), (2, 31, 32), (1, 200, 80)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_all_parts_ragged_bf16(shape, design):
+    batch, L, D = shape
+    g = workloads.generate("mid_bf16", batch=batch, L=L, D=D, N=16, seed=71 + L)
+    extras = workloads.generate_extras(g["workload"])
+    check(g, _opts(extras, True, True, True), "zoh", f"chain all parts {shape}")
+
+
+@pytest.mark.parametrize("design", ["chain"], indirect=True)
+def test_runs_without_workspace(design):
+    """The single-pass design needs no workspace: a call with none succeeds at
+    a length where the chunked design needs chunk summaries."""
+    g = workloads.generate("mamba130m_layer_fp32", batch=2, L=4096, D=64, N=16, seed=73)
+    w = g["workload"]
+    t = inputs_on_device(g)
+    y = torch.empty((w.batch, w.L, w.D), dtype=torch.float32, device="cuda")
+    mssm.mssm_selective_scan_fwd_ws(t["x"], t["delta"], t["A"], t["B"], t["C"], y, None)
+    torch.cuda.synchronize()
+    assert_parity(host64(y), oracle_scan(g), "fp32", "chain without workspace")
+    os.environ["MSSM_SCAN_DESIGN"] = "chunked"
+    with pytest.raises(mssm.MssmError) as e:
+        mssm.mssm_selective_scan_fwd_ws(t["x"], t["delta"], t["A"], t["B"], t["C"], y, None)
+    assert e.value.status == mssm.MSSM_ERROR_WORKSPACE
+
+
+@pytest.mark.parametrize("design", ["chain"], indirect=True)
+def test_unsupported_shapes_fall_back(design):
+    """N != 16 or D not a multiple of 16 run the chunked kernels even when the
+    single pass is asked for."""
+    for (D, N) in ((24, 16), (32, 8)):
+        g = workloads.generate("mamba130m_layer_fp32", batch=1, L=300, D=D, N=N, seed=79)
+        t = inputs_on_device(g)
+        y = mssm.selective_scan(t["x"], t["delta"], t["A"], t["B"], t["C"])
+        torch.cuda.synchronize()
+        assert_parity(host64(y), oracle_scan(g), "fp32", f"fallback D={D} N={N}")
+
+
+@pytest.mark.parametrize("design", ["chain"], indirect=True)
+def test_sequence_in_pieces_equals_one_call(design):
+    g = workloads.generate("mid_bf16", batch=2, L=1000, D=64, N=16, seed=83)
+    extras = workloads.generate_extras(g["workload"])
+    t = inputs_on_device(g)
+    h = dev(extras["h0"])
+    pieces = []
+    for a, b in ((0, 33), (33, 48), (48, 49), (49, 1000)):
+        sl = {k: t[k][:, a:b].contiguous() for k in ("x", "delta", "B", "C")}
+        y, h = mssm.selective_scan_ex(sl["x"], sl["delta"], t["A"], sl["B"], sl["C"], h0=h,
+                                      return_last_state=True)
+        pieces.append(y)
+    torch.cuda.synchronize()
+    y = host64(torch.cat(pieces, dim=1))
+    from test_scan_ex_gpu import oracle_ex
+    y_ref, h_ref = oracle_ex(g, _opts(extras, False, False, True), "euler")
+    assert_parity(y, y_ref, "bf16", "chain pieces y")
+    assert_parity(host64(h), h_ref, "bf16", "chain pieces h_last")
+
+
+@pytest.mark.parametrize("name", ["mamba130m_layer_fp32", "mid_bf16"])
+@pytest.mark.parametrize("design", ["chain", "chunked"], indirect=True)
+def test_full_size_both_designs_sampled_channels(name, design):
+    print(f"case full size {name} design={design}", flush=True)
+    g = workloads.generate(name)
+    t = inputs_on_device(g)
+    y = mssm.selective_scan(t["x"], t["delta"], t["A"], t["B"], t["C"])
+    torch.cuda.synchronize()
+    ch = np.arange(3, g["workload"].D, 17)
+    y = host64(y)[:, :, ch]
+    r = assert_parity(y, oracle_scan(g, channels=ch), g["workload"].dtype,
+                      f"{name} {design}")
+    print(name, design, r, flush=True)
