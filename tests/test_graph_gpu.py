@@ -61,6 +61,26 @@ def test_scan_with_workspace_in_a_graph():
                                                                 to["B"], to["C"]))
 
 
+def test_single_pass_scan_with_all_parts_in_a_graph():
+    """8192 channels: the single-pass kernel, which uses no workspace."""
+    gw = workloads.generate("mid_bf16", batch=2, L=300, D=4096, N=16, seed=94)
+    ex = workloads.generate_extras(gw["workload"])
+    t = inputs_on_device(gw)
+    Dk, z, h0 = dev(ex["Dskip"]), dev(ex["z"]), dev(ex["h0"])
+    y = torch.empty((2, 300, 4096), dtype=torch.float32, device="cuda")
+    h = torch.empty((2, 4096, 16), dtype=torch.float32, device="cuda")
+    ref_y, ref_h = mssm.selective_scan_ex(t["x"], t["delta"], t["A"], t["B"], t["C"], Dskip=Dk,
+                                          z=z, h0=h0, bbar="zoh", return_last_state=True)
+    torch.cuda.synchronize()
+    g = capture(lambda: mssm.mssm_selective_scan_fwd_ex(
+        t["x"], t["delta"], t["A"], t["B"], t["C"], y, None, Dskip=Dk, z=z, h0=h0, h_last=h,
+        bbar="zoh"))
+    other = workloads.generate("mamba130m_layer_fp32", batch=1, L=300, D=64, N=16, seed=4)
+    to = inputs_on_device(other)
+    replay_and_check(g, [y, h], [ref_y, ref_h], lambda: mssm.selective_scan(
+        to["x"], to["delta"], to["A"], to["B"], to["C"]))
+
+
 def test_extended_scan_and_decode_steps_in_a_graph():
     gw = workloads.generate("mamba130m_layer_fp32", batch=2, L=700, D=192, N=16, seed=92)
     e = workloads.generate_extras(gw["workload"])
