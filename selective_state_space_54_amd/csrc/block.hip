@@ -135,12 +135,17 @@ hipError_t launch_conv1d_silu(const void* u, bool u_f32, const float* w, const f
 }
 
 BlockPlan plan_block(int64_t batch, int64_t L, int64_t Dm, int64_t Di, int64_t N, int64_t R,
-                     int cpl) {
+                     int cpl, bool chain) {
   BlockPlan b;
   const size_t M = static_cast<size_t>(batch * L);
   const size_t di = static_cast<size_t>(Di);
   (void)Dm;
-  b.scan = plan_scan(batch, L, Di, N, cpl);
+  if (chain) {
+    b.chain = true;
+    b.scan.chain = true;
+  } else {
+    b.scan = plan_scan(batch, L, Di, N, cpl);
+  }
   size_t off = 0;
   b.u_offset = off;      off += align256(sizeof(float) * M * di);
   b.z_offset = off;      off += align256(sizeof(float) * M * di);
@@ -160,8 +165,8 @@ BlockPlan plan_block(int64_t batch, int64_t L, int64_t Dm, int64_t Di, int64_t N
 
 size_t block_workspace_bound(int64_t batch, int64_t L, int64_t Dm, int64_t Di, int64_t N,
                              int64_t R) {
-  size_t w = plan_block(batch, L, Dm, Di, N, R, 1).workspace_bytes;
-  if (Di % 2 == 0) w = std::max(w, plan_block(batch, L, Dm, Di, N, R, 2).workspace_bytes);
+  size_t w = plan_block(batch, L, Dm, Di, N, R, 1, false).workspace_bytes;
+  if (Di % 2 == 0) w = std::max(w, plan_block(batch, L, Dm, Di, N, R, 2, false).workspace_bytes);
   return w;
 }
 
@@ -205,30 +210,53 @@ FusedStatus launch_block(const BlockArgs& a, const BlockPlan& bp, void* workspac
   }
   st.hip = launch_fused_prep(P, M, a.R, ldp, a.W_dt, Di, dtl, dtl_lo, wT, stream);
   if (st.hip != hipSuccess) return st;
-  FusedScanArgs sa{};
-  sa.x = X;
-  sa.x_f32 = true;
-  sa.z = Z;
-  sa.Dskip = a.Dskip;
-  sa.y = G;
-  sa.y_bf16 = true;
-  sa.y_lo = Gl;
-  sa.P = P;
-  sa.dtl = dtl;
-  sa.dtl_lo = dtl_lo;
-  sa.wT = wT;
-  sa.dt_bias = a.dt_bias;
-  sa.A = a.A;
-  if (bp.scan.K > 1) {
-    sa.sum_h = reinterpret_cast<float*>(ws + bp.scan_offset);
-    sa.sum_s = reinterpret_cast<double*>(ws + bp.scan_offset + bp.scan.sum_s_offset);
+  if (bp.chain) {
+    // the single pass: delta written out (into u, which the conv has consumed)
+    st.hip = launch_dtproj_softplus(dtl, dtl_lo, wT, a.dt_bias, U, M, Di, a.R, stream);
+    if (st.hip != hipSuccess) return st;
+    ChainFusedArgs ca;
+    ca.x = X;
+    ca.x_f32 = true;
+    ca.delta = U;
+    ca.P = P;
+    ca.ldp = ldp;
+    ca.R = a.R;
+    ca.A = a.A;
+    ca.Dskip = a.Dskip;
+    ca.z = Z;
+    ca.y = G;
+    ca.y_lo = Gl;
+    ca.y_bf16 = true;
+    ca.batch = a.batch;
+    ca.L = a.L;
+    ca.D = Di;
+    st.hip = launch_chain_fused(ca, stream);
+  } else {
+    FusedScanArgs sa{};
+    sa.x = X;
+    sa.x_f32 = true;
+    sa.z = Z;
+    sa.Dskip = a.Dskip;
+    sa.y = G;
+    sa.y_bf16 = true;
+    sa.y_lo = Gl;
+    sa.P = P;
+    sa.dtl = dtl;
+    sa.dtl_lo = dtl_lo;
+    sa.wT = wT;
+    sa.dt_bias = a.dt_bias;
+    sa.A = a.A;
+    if (bp.scan.K > 1) {
+      sa.sum_h = reinterpret_cast<float*>(ws + bp.scan_offset);
+      sa.sum_s = reinterpret_cast<double*>(ws + bp.scan_offset + bp.scan.sum_s_offset);
+    }
+    sa.batch = a.batch;
+    sa.L = a.L;
+    sa.D = Di;
+    sa.N = a.N;
+    sa.R = a.R;
+    st.hip = launch_fused_scan(sa, bp.scan, stream);
   }
-  sa.batch = a.batch;
-  sa.L = a.L;
-  sa.D = Di;
-  sa.N = a.N;
-  sa.R = a.R;
-  st.hip = launch_fused_scan(sa, bp.scan, stream);
   if (st.hip != hipSuccess) return st;
   // output projection of the gated result G = hi + lo
   if (!gemm_rm_bf16(hb, M, Dm, Di, G, Di, a.W_out, Dm, a.out, Dm, 0.0f) ||

@@ -104,16 +104,21 @@ __device__ __forceinline__ float row_reduce_scatter16(const float (&p)[16], int 
   return keep + dpp<kQuadXor1>(send);
 }
 
-// Raw bits of 4 consecutive input values, as loaded.
-template <typename T> struct RawOf;
-template <> struct RawOf<float> { using type = float4; };
-template <> struct RawOf<uint16_t> { using type = uint2; };
-__device__ __forceinline__ void unpack(const float4& q, float (&v)[4]) {
-  v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
+// Raw bits of 4 consecutive input values of `esz` bytes each (4: float32,
+// 2: bfloat16), as loaded: 16 or 8 bytes.
+__device__ __forceinline__ uint4 load_raw(const char* p, int esz) {
+  if (esz == 4) return *reinterpret_cast<const uint4*>(p);
+  const uint2 q = *reinterpret_cast<const uint2*>(p);
+  return make_uint4(q.x, q.y, 0u, 0u);
 }
-__device__ __forceinline__ void unpack(const uint2& q, float (&v)[4]) {   // bfloat16 -> float
-  v[0] = __uint_as_float(q.x << 16); v[1] = __uint_as_float(q.x & 0xFFFF0000u);
-  v[2] = __uint_as_float(q.y << 16); v[3] = __uint_as_float(q.y & 0xFFFF0000u);
+__device__ __forceinline__ void unpack_raw(const uint4& q, int esz, float (&v)[4]) {
+  if (esz == 4) {
+    v[0] = __uint_as_float(q.x); v[1] = __uint_as_float(q.y);
+    v[2] = __uint_as_float(q.z); v[3] = __uint_as_float(q.w);
+  } else {                                   // bfloat16 -> float32, exact
+    v[0] = __uint_as_float(q.x << 16); v[1] = __uint_as_float(q.x & 0xFFFF0000u);
+    v[2] = __uint_as_float(q.y << 16); v[3] = __uint_as_float(q.y & 0xFFFF0000u);
+  }
 }
 
 // Block index -> logical block such that consecutive logical blocks (adjacent
@@ -126,19 +131,50 @@ __device__ __forceinline__ int64_t xcd_local_block(int64_t bid, int64_t nblk) {
   return xcd * per + (xcd < rem ? xcd : rem) + idx;
 }
 
+// Element types of what the kernel reads and writes:
+//   TX : x and z            TD : delta            TBC : B and C
+//   TY : y; float, or uint16_t for a bfloat16 pair y = bf16(y), y_lo =
+//        bf16(y - bf16(y)) (round to nearest even), which carries y to about
+//        16 significant bits (the Mamba block's input to its output GEMM)
+template <typename TX_, typename TD_, typename TBC_, typename TY_>
+struct ChainIO {
+  using TX = TX_;
+  using TD = TD_;
+  using TBC = TBC_;
+  using TY = TY_;
+};
+
+// Pointers and sizes of one call.  B and C are rows of ld_bc elements (N for
+// the plain scan; R + 2N when they are columns of the selection projection's
+// output).  Dskip / z / h0 / h_last / y_lo are read or written only by the
+// variants that use them.
+struct ChainParams {
+  const void* x;
+  const void* delta;
+  const void* B;
+  const void* C;
+  const void* z;
+  const float* A;
+  const float* Dskip;
+  const float* h0;
+  float* h_last;
+  void* y;
+  void* y_lo;
+  int64_t L, D, ld_bc;
+};
+
 // grid: batch * D / 16 blocks of kBlock lanes.  Requirements (checked by the
-// launcher): N = 16, D % 16 == 0, x / delta / z aligned to 4 elements, y to
-// 16 bytes, 16 * D * 4 < 2^31.
-template <typename T, class V>
-__global__ __launch_bounds__(kBlock) void chain_scan_kernel(
-    const T* __restrict__ x, const T* __restrict__ delta, const float* __restrict__ A,
-    const T* __restrict__ Bm, const T* __restrict__ Cm, const float* __restrict__ Dskip,
-    const T* __restrict__ z, const float* __restrict__ h0, float* __restrict__ h_last,
-    float* __restrict__ y, int64_t L, int64_t D) {
+// launchers): N = 16, D % 16 == 0, float32 inputs 16-byte and bfloat16 inputs
+// 8-byte aligned (rows too: ld_bc a multiple of 4), y 16-byte aligned,
+// 16 * D * 4 < 2^31.
+template <class IO, class V>
+__global__ __launch_bounds__(kBlock) void chain_scan_kernel(ChainParams prm) {
+  using TX = typename IO::TX;
+  using TY = typename IO::TY;
   constexpr int kTiles = V::kGate ? 5 : 4;     // x, delta, B^T, C^T (, z)
   __shared__ __align__(16) float tin[2][kTiles][kTile][kRow];
   __shared__ __align__(16) float tout[2][kTile][kRow];
-  using Raw = typename RawOf<T>::type;
+  const int64_t L = prm.L, D = prm.D;
 
   const int64_t n_dgroups = D / kChannels;
   const int64_t blk = xcd_local_block(blockIdx.x, gridDim.x);
@@ -150,60 +186,67 @@ __global__ __launch_bounds__(kBlock) void chain_scan_kernel(
   const int ch = wave * 4 + (lane >> 4);       // channel within the block
   const int64_t d0 = dg * kChannels;
   const int64_t chain_idx = (b * D + d0 + ch) * kStates + n;   // [batch, D, N] index
-  const float a_dn = A[(d0 + ch) * kStates + n];
+  const float a_dn = prm.A[(d0 + ch) * kStates + n];
   const float A2 = a_dn * kLog2e;
   float Ainv = 0.0f;
   if constexpr (V::kZoh) Ainv = 1.0f / a_dn;
   float Dd = 0.0f;
-  if constexpr (V::kSkip) Dd = Dskip[d0 + ch];
-  float h = h0 ? h0[chain_idx] : 0.0f;
+  if constexpr (V::kSkip) Dd = prm.Dskip[d0 + ch];
+  float h = prm.h0 ? prm.h0[chain_idx] : 0.0f;
 
-  // Loader lane: step ls of the tile, 4 values from column lq.
+  // Loader lane: step ls of the tile, 4 values from column lq, of the tile
+  // this wavefront loads (0: x (and z), 1: delta, 2: B, 3: C).
   const int ls = lane >> 2, lq = (lane & 3) * 4;
-  const T* src;
-  int64_t rs;
+  const char* src;
+  int esz;              // bytes per element of this wavefront's tile
+  int64_t rs;           // elements between rows (steps)
   if (wave == 0) {
-    src = x + b * L * D + d0;
+    src = static_cast<const char*>(prm.x) + (b * L * D + d0) * sizeof(TX);
+    esz = sizeof(TX);
     rs = D;
   } else if (wave == 1) {
-    src = delta + b * L * D + d0;
+    src = static_cast<const char*>(prm.delta) + (b * L * D + d0) * sizeof(typename IO::TD);
+    esz = sizeof(typename IO::TD);
     rs = D;
-  } else if (wave == 2) {
-    src = Bm + b * L * kStates;
-    rs = kStates;
   } else {
-    src = Cm + b * L * kStates;
-    rs = kStates;
+    src = static_cast<const char*>(wave == 2 ? prm.B : prm.C) +
+          b * L * prm.ld_bc * sizeof(typename IO::TBC);
+    esz = sizeof(typename IO::TBC);
+    rs = prm.ld_bc;
   }
-  const T* zsrc = V::kGate ? z + b * L * D + d0 : nullptr;   // loaded by wavefront 0
-  float* yb = y + b * L * D + d0;
+  const char* zsrc = V::kGate ? static_cast<const char*>(prm.z) + (b * L * D + d0) * sizeof(TX)
+                              : nullptr;   // loaded by wavefront 0
+  char* yb = static_cast<char*>(prm.y) + (b * L * D + d0) * sizeof(TY);
+  char* yb_lo = sizeof(TY) == 2 ? static_cast<char*>(prm.y_lo) + (b * L * D + d0) * sizeof(TY)
+                                : nullptr;
   const int64_t ntiles = (L + kTile - 1) / kTile;
   const int64_t last = ntiles - 1;
   const int tail_steps = static_cast<int>(L - last * kTile);   // steps of the last tile, 1..16
   const int ls_tail = ls < tail_steps ? ls : tail_steps - 1;
-  const uint32_t off_full = static_cast<uint32_t>((ls * rs + lq) * sizeof(T));
-  const uint32_t off_tail = static_cast<uint32_t>((ls_tail * rs + lq) * sizeof(T));
+  const int64_t rs_bytes = rs * esz;
+  const uint32_t off_full = static_cast<uint32_t>(ls * rs_bytes + lq * esz);
+  const uint32_t off_tail = static_cast<uint32_t>(ls_tail * rs_bytes + lq * esz);
+  const uint32_t zoff_full = static_cast<uint32_t>((ls * D + lq) * sizeof(TX));
+  const uint32_t zoff_tail = static_cast<uint32_t>((ls_tail * D + lq) * sizeof(TX));
   const bool pad_lane = ls >= tail_steps;
-  const uint32_t yoff = static_cast<uint32_t>((ls * D + lq) * sizeof(float));
+  const uint32_t yoff = static_cast<uint32_t>((ls * D + lq) * sizeof(TY));
 
-  auto load1 = [&](const T* s, int64_t k) {
-    const T* base = s + k * kTile * rs;
-    return *reinterpret_cast<const Raw*>(reinterpret_cast<const char*>(base) +
-                                         (k == last ? off_tail : off_full));
-  };
   struct Regs {
-    Raw v, zv;
+    uint4 v, zv;
   };
   auto load = [&](Regs& r, int64_t k) {
-    r.v = load1(src, k);
+    r.v = load_raw(src + k * kTile * rs_bytes + (k == last ? off_tail : off_full), esz);
     if constexpr (V::kGate) {
-      if (wave == 0) r.zv = load1(zsrc, k);
+      if (wave == 0)
+        r.zv = load_raw(zsrc + k * kTile * D * static_cast<int64_t>(sizeof(TX)) +
+                            (k == last ? zoff_tail : zoff_full),
+                        sizeof(TX));
     }
   };
   // Tile k's loaded values into LDS buffer `buf`.
   auto put = [&](const Regs& r, int buf, int64_t k) {
     float v[4];
-    unpack(r.v, v);
+    unpack_raw(r.v, esz, v);
     if (wave == 1 && k == last && pad_lane) v[0] = v[1] = v[2] = v[3] = 0.0f;   // delta
     if (wave < 2) {
       *reinterpret_cast<float4*>(&tin[buf][wave][ls][lq]) = make_float4(v[0], v[1], v[2], v[3]);
@@ -213,16 +256,30 @@ __global__ __launch_bounds__(kBlock) void chain_scan_kernel(
     }
     if constexpr (V::kGate) {
       if (wave == 0) {
-        unpack(r.zv, v);
+        unpack_raw(r.zv, sizeof(TX), v);
         *reinterpret_cast<float4*>(&tin[buf][4][ls][lq]) = make_float4(v[0], v[1], v[2], v[3]);
       }
     }
   };
   auto store_y = [&](int64_t k) {
     const float4 v = *reinterpret_cast<const float4*>(&tout[k & 1][ls][lq]);
-    float* base = yb + k * kTile * D;
-    if (k != last || ls < tail_steps)
-      *reinterpret_cast<float4*>(reinterpret_cast<char*>(base) + yoff) = v;
+    if (k == last && ls >= tail_steps) return;
+    const int64_t step_bytes = k * kTile * D * static_cast<int64_t>(sizeof(TY));
+    if constexpr (sizeof(TY) == 4) {
+      *reinterpret_cast<float4*>(yb + step_bytes + yoff) = v;
+    } else {
+      const float w[4] = {v.x, v.y, v.z, v.w};
+      uint32_t hi[4], lo[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        hi[i] = bf16_rne_bits(w[i]);
+        lo[i] = bf16_rne_bits(w[i] - __uint_as_float(hi[i] << 16));
+      }
+      *reinterpret_cast<uint2*>(yb + step_bytes + yoff) =
+          make_uint2(hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16));
+      *reinterpret_cast<uint2*>(yb_lo + step_bytes + yoff) =
+          make_uint2(lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16));
+    }
   };
   auto compute = [&](int64_t k) {
     const int buf = k & 1;
@@ -289,7 +346,15 @@ __global__ __launch_bounds__(kBlock) void chain_scan_kernel(
   }
   __syncthreads();
   if (wave == (last & 3)) store_y(last);
-  if constexpr (V::kState) h_last[chain_idx] = h;
+  if constexpr (V::kState) prm.h_last[chain_idx] = h;
+}
+
+// Launch on `stream` for `batch` rows; returns the launch status.
+template <class IO, class V>
+hipError_t launch_io(const ChainParams& p, int64_t batch, hipStream_t stream) {
+  const dim3 grid(static_cast<unsigned>(batch * (p.D / kChannels)));
+  hipLaunchKernelGGL((chain_scan_kernel<IO, V>), grid, dim3(kBlock), 0, stream, p);
+  return hipGetLastError();
 }
 
 template <class V>
@@ -297,27 +362,20 @@ hipError_t launch_variant(const ScanArgs& a, hipStream_t stream);
 
 }  // namespace chain
 
+// The plain and extended scan: x, delta, B, C (and z) all of the call's dtype,
+// B and C rows of N = 16, y float32.
 #define MSSM_DEFINE_CHAIN_VARIANT(ZOH, SKIP, GATE, STATE)                                     \
   template <>                                                                                 \
   hipError_t chain::launch_variant<Variant<ZOH, SKIP, GATE, STATE>>(const ScanArgs& a,        \
                                                                     hipStream_t stream) {    \
     using V = Variant<ZOH, SKIP, GATE, STATE>;                                                \
-    const dim3 grid(static_cast<unsigned>(a.batch * (a.D / chain::kChannels)));               \
+    const chain::ChainParams p{a.x,      a.delta, a.B,      a.C, a.z, a.A, a.Dskip, a.h0,      \
+                               a.h_last, a.y,     nullptr,  a.L, a.D, chain::kStates};         \
     if (a.dtype == MSSM_FLOAT32)                                                              \
-      hipLaunchKernelGGL((chain::chain_scan_kernel<float, V>), grid, dim3(chain::kBlock), 0,   \
-                         stream, static_cast<const float*>(a.x),                              \
-                         static_cast<const float*>(a.delta), a.A,                             \
-                         static_cast<const float*>(a.B), static_cast<const float*>(a.C),      \
-                         a.Dskip, static_cast<const float*>(a.z), a.h0, a.h_last,             \
-                         static_cast<float*>(a.y), a.L, a.D);                                 \
-    else                                                                                      \
-      hipLaunchKernelGGL((chain::chain_scan_kernel<uint16_t, V>), grid, dim3(chain::kBlock),  \
-                         0, stream, static_cast<const uint16_t*>(a.x),                        \
-                         static_cast<const uint16_t*>(a.delta), a.A,                          \
-                         static_cast<const uint16_t*>(a.B), static_cast<const uint16_t*>(a.C),\
-                         a.Dskip, static_cast<const uint16_t*>(a.z), a.h0, a.h_last,          \
-                         static_cast<float*>(a.y), a.L, a.D);                                 \
-    return hipGetLastError();                                                                 \
+      return chain::launch_io<chain::ChainIO<float, float, float, float>, V>(p, a.batch,      \
+                                                                             stream);         \
+    return chain::launch_io<chain::ChainIO<uint16_t, uint16_t, uint16_t, float>, V>(          \
+        p, a.batch, stream);                                                                  \
   }
 
 }  // namespace mssm

@@ -64,6 +64,18 @@ bool chain_scan_applies(const ScanArgs& a) {
   return d == Design::kChain || a.batch * a.D >= kMinChannels;
 }
 
+bool chain_fused_applies(int64_t batch, int64_t D, int64_t N, int64_t R, const void* x,
+                         const void* y) {
+  const Design d = design_setting();
+  if (d == Design::kChunked) return false;
+  if (N != chain::kStates || D % chain::kChannels != 0 || batch < 1) return false;
+  if (R > 256) return false;   // the delta kernel keeps W_dt in registers for R <= 256
+  if (!aligned(x, 16) || !aligned(y, 16)) return false;
+  if (D * chain::kTile * static_cast<int64_t>(sizeof(float)) >= (int64_t(1) << 31)) return false;
+  if (batch > (int64_t(1) << 31) / (D / chain::kChannels)) return false;
+  return d == Design::kChain || batch * D >= kMinChannels;
+}
+
 hipError_t launch_chain_scan(const ScanArgs& a, hipStream_t stream) {
   return a.bbar == MSSM_BBAR_ZOH ? launch_parts<true>(a, stream)
                                  : launch_parts<false>(a, stream);

@@ -392,6 +392,99 @@ __global__ void dtlow_split_kernel(const float* __restrict__ P, uint16_t* __rest
   }
 }
 
+// Delta[m, d] = softplus(sum_r (hi[m, r] + lo[m, r]) wT[d, r] + bias[d]) for the
+// whole [M, D] matrix, float32: the step sizes of "Understanding Mamba",
+// section 5.1 eq. (6) written out once for the single-pass scan.  Same
+// arithmetic as delta_tile (v_mfma_f32_32x32x16_bf16, hi and lo parts
+// accumulated into one float32 result, bias, softplus).  KS = R / 16 K steps.
+// A block is 4 wavefronts over 128 channels (32 each) and kDtRowTiles tiles of
+// 32 rows.  Each wavefront keeps its channels' W_dt^T operands in registers;
+// each row tile's dt_low rows (one contiguous stretch of memory per part) are
+// copied into LDS with 16-byte loads shared by the four wavefronts, the next
+// tile's loads in flight while the current one computes.  Rows >= M and
+// channels >= D read clamped operands and store nothing.
+constexpr int kDtRowTiles = 8;               // 32-row tiles per block
+
+template <int KS>
+__global__ __launch_bounds__(kFBlock) void dtproj_softplus_kernel(
+    const uint16_t* __restrict__ dtl, const uint16_t* __restrict__ dtl_lo,
+    const uint16_t* __restrict__ wT, const float* __restrict__ bias, float* __restrict__ delta,
+    int64_t M, int64_t D, int64_t n_cblocks) {
+  constexpr int R = 16 * KS;
+  constexpr int kStride = R + 8;                    // LDS row stride (bf16): 16-byte rows, skewed banks
+  constexpr int kRowChunks = R / 8;                 // 16-byte pieces per row
+  constexpr int kChunks = 2 * 32 * kRowChunks;      // both parts of a 32-row tile
+  constexpr int kPerThread = (kChunks + kFBlock - 1) / kFBlock;
+  __shared__ __align__(16) uint16_t sa[2][32][kStride];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int64_t rb = blockIdx.x / n_cblocks;
+  const int64_t c0 = (blockIdx.x % n_cblocks) * 128 + wave * 32;
+  const int khalf = 8 * (lane / 32);
+  const int64_t ch = min(c0 + lane % 32, D - 1);
+  bf16x8 bw[KS];
+#pragma unroll
+  for (int k = 0; k < KS; ++k) bw[k] = load_bf16x8(wT + ch * R + 16 * k + khalf);
+  const float bias_c = bias[ch];
+  const bool col_ok = c0 + lane % 32 < D;
+
+  // this thread's pieces of every tile: part, row, column (compile-time divisors)
+  auto piece = [&](int q, int& arr, int& row, int& col) {
+    const int c = threadIdx.x + kFBlock * q;
+    arr = c / (32 * kRowChunks);
+    row = (c % (32 * kRowChunks)) / kRowChunks;
+    col = (c % kRowChunks) * 8;
+  };
+  u32x4 pre[kPerThread];
+  auto fetch = [&](int64_t m0) {
+#pragma unroll
+    for (int q = 0; q < kPerThread; ++q) {
+      int arr, row, col;
+      piece(q, arr, row, col);
+      if (threadIdx.x + kFBlock * q < kChunks) {
+        const int64_t m = min(m0 + row, M - 1);
+        pre[q] = *reinterpret_cast<const u32x4*>((arr ? dtl_lo : dtl) + m * R + col);
+      }
+    }
+  };
+  auto stash = [&]() {
+#pragma unroll
+    for (int q = 0; q < kPerThread; ++q) {
+      int arr, row, col;
+      piece(q, arr, row, col);
+      if (threadIdx.x + kFBlock * q < kChunks)
+        *reinterpret_cast<u32x4*>(&sa[arr][row][col]) = pre[q];
+    }
+  };
+
+  const int64_t first = rb * kDtRowTiles * 32;
+  fetch(first);
+  for (int t = 0; t < kDtRowTiles; ++t) {
+    const int64_t m0 = first + 32 * t;
+    if (m0 >= M) break;                        // uniform over the block
+    __syncthreads();                           // the previous tile's LDS reads are done
+    stash();
+    __syncthreads();
+    if (t + 1 < kDtRowTiles && m0 + 32 < M) fetch(m0 + 32);   // in flight during this tile
+    if (c0 >= D) continue;                     // a wavefront past the last channel only copies
+    f32x16 acc = f32x16{};
+#pragma unroll
+    for (int k = 0; k < KS; ++k) {
+      bf16x8 a, a_lo;
+      __builtin_memcpy(&a, &sa[0][lane % 32][16 * k + khalf], sizeof(a));
+      __builtin_memcpy(&a_lo, &sa[1][lane % 32][16 * k + khalf], sizeof(a_lo));
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bw[k], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_lo, bw[k], acc, 0, 0, 0);
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      // output element (row 8 (r / 4) + 4 (lane / 32) + r % 4, column lane % 32)
+      const int64_t m = m0 + 8 * (r / 4) + 4 * (lane / 32) + (r % 4);
+      if (col_ok && m < M) delta[m * D + c0 + lane % 32] = softplus_f(acc[r] + bias_c);
+    }
+  }
+}
+
 // wT[d, r] = W[r, d]
 __global__ void transpose_bf16_kernel(const uint16_t* __restrict__ W, uint16_t* __restrict__ wT,
                                       int R, int64_t D) {
@@ -496,6 +589,28 @@ hipError_t launch_fused_prep(const float* P, int64_t M, int64_t R, int64_t ldp, 
   return hipGetLastError();
 }
 
+hipError_t launch_dtproj_softplus(const uint16_t* dtl, const uint16_t* dtl_lo, const uint16_t* wT,
+                                  const float* bias, float* delta, int64_t M, int64_t D,
+                                  int64_t R, hipStream_t stream) {
+  const int64_t n_cblocks = (D + 127) / 128;
+  const dim3 grid(static_cast<unsigned>((M + 32 * kDtRowTiles - 1) / (32 * kDtRowTiles) *
+                                        n_cblocks));
+#define MSSM_DTPROJ_CASE(KS)                                                                    \
+  case KS:                                                                                     \
+    hipLaunchKernelGGL((dtproj_softplus_kernel<KS>), grid, dim3(kFBlock), 0, stream, dtl,      \
+                       dtl_lo, wT, bias, delta, M, D, n_cblocks);                              \
+    break;
+  switch (R / 16) {
+    MSSM_DTPROJ_CASE(1) MSSM_DTPROJ_CASE(2) MSSM_DTPROJ_CASE(3) MSSM_DTPROJ_CASE(4)
+    MSSM_DTPROJ_CASE(5) MSSM_DTPROJ_CASE(6) MSSM_DTPROJ_CASE(7) MSSM_DTPROJ_CASE(8)
+    MSSM_DTPROJ_CASE(9) MSSM_DTPROJ_CASE(10) MSSM_DTPROJ_CASE(11) MSSM_DTPROJ_CASE(12)
+    MSSM_DTPROJ_CASE(13) MSSM_DTPROJ_CASE(14) MSSM_DTPROJ_CASE(15) MSSM_DTPROJ_CASE(16)
+    default: return hipErrorInvalidValue;     // R a multiple of 16 up to 256
+  }
+#undef MSSM_DTPROJ_CASE
+  return hipGetLastError();
+}
+
 hipError_t launch_fused_scan(const FusedScanArgs& a, const ScanPlan& p, hipStream_t stream) {
   if (!a.x_f32) {
     if (a.z || a.Dskip || a.y_bf16) return hipErrorInvalidValue;
@@ -506,22 +621,35 @@ hipError_t launch_fused_scan(const FusedScanArgs& a, const ScanPlan& p, hipStrea
   return launch_fused_scan_v<FusedVariant<float, false, true, uint16_t>>(a, p, stream);
 }
 
-FusedPlan plan_fused(int64_t batch, int64_t L, int64_t D, int64_t N, int64_t R, int cpl) {
+FusedPlan plan_fused(int64_t batch, int64_t L, int64_t D, int64_t N, int64_t R, int cpl,
+                     bool chain) {
   FusedPlan f;
   const int64_t M = batch * L;
-  f.scan = plan_scan(batch, L, D, N, cpl);
+  if (chain) {
+    f.chain = true;
+    f.scan.chain = true;
+  } else {
+    f.scan = plan_scan(batch, L, D, N, cpl);
+  }
   f.p_bytes = align256(sizeof(float) * (size_t)M * (size_t)(R + 2 * N));
   f.dtl_offset = f.p_bytes;
   f.dtl_lo_offset = f.dtl_offset + align256(sizeof(uint16_t) * (size_t)M * (size_t)R);
   f.wt_offset = f.dtl_lo_offset + align256(sizeof(uint16_t) * (size_t)M * (size_t)R);
   f.scan_offset = f.wt_offset + align256(sizeof(uint16_t) * (size_t)D * (size_t)R);
-  f.workspace_bytes = f.scan_offset + f.scan.workspace_bytes;
+  if (chain) {
+    f.delta_offset = f.scan_offset;
+    f.workspace_bytes = f.delta_offset + align256(sizeof(float) * (size_t)M * (size_t)D);
+  } else {
+    f.workspace_bytes = f.scan_offset + f.scan.workspace_bytes;
+  }
   return f;
 }
 
 size_t fused_workspace_bound(int64_t batch, int64_t L, int64_t D, int64_t N, int64_t R) {
-  size_t w = plan_fused(batch, L, D, N, R, 1).workspace_bytes;
-  if (D % 2 == 0) w = std::max(w, plan_fused(batch, L, D, N, R, 2).workspace_bytes);
+  size_t w = plan_fused(batch, L, D, N, R, 1, false).workspace_bytes;
+  if (D % 2 == 0) w = std::max(w, plan_fused(batch, L, D, N, R, 2, false).workspace_bytes);
+  if (N == 16 && D % 16 == 0 && R <= 256)
+    w = std::max(w, plan_fused(batch, L, D, N, R, 1, true).workspace_bytes);
   return w;
 }
 
@@ -559,6 +687,24 @@ FusedStatus launch_fused(const FusedArgs& a, const FusedPlan& f, void* workspace
   uint16_t* wT = reinterpret_cast<uint16_t*>(ws + f.wt_offset);
   st.hip = launch_fused_prep(P, M, a.R, ldp, a.W_dt, a.D, dtl, dtl_lo, wT, stream);
   if (st.hip != hipSuccess) return st;
+  if (f.chain) {
+    float* delta = reinterpret_cast<float*>(ws + f.delta_offset);
+    st.hip = launch_dtproj_softplus(dtl, dtl_lo, wT, a.dt_bias, delta, M, a.D, a.R, stream);
+    if (st.hip != hipSuccess) return st;
+    ChainFusedArgs ca;
+    ca.x = a.x;
+    ca.delta = delta;
+    ca.P = P;
+    ca.ldp = ldp;
+    ca.R = a.R;
+    ca.A = a.A;
+    ca.y = a.y;
+    ca.batch = a.batch;
+    ca.L = a.L;
+    ca.D = a.D;
+    st.hip = launch_chain_fused(ca, stream);
+    return st;
+  }
   FusedScanArgs sa{};
   sa.x = a.x;
   sa.y = a.y;

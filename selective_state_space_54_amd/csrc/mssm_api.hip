@@ -252,7 +252,8 @@ mssm_status mssm_selective_ssm_fused_fwd(const void* x, const void* W_xproj, con
   if (s != MSSM_SUCCESS) return s;
   if (empty_problem(batch, L, D)) return MSSM_SUCCESS;
   if (!x || !W_xproj || !W_dtproj || !dt_bias || !A || !y) return MSSM_ERROR_INVALID_VALUE;
-  const mssm::FusedPlan plan = mssm::plan_fused(batch, L, D, N, R, mssm::choose_fused_cpl(D));
+  const mssm::FusedPlan plan = mssm::plan_fused(batch, L, D, N, R, mssm::choose_fused_cpl(D),
+                                                mssm::chain_fused_applies(batch, D, N, R, x, y));
   s = check_grid(plan.scan, batch, D, N);
   if (s != MSSM_SUCCESS) return s;
   if (!workspace || workspace_bytes < plan.workspace_bytes) return MSSM_ERROR_WORKSPACE;
@@ -377,8 +378,10 @@ mssm_status mssm_mamba_block_fwd(const void* u0, const void* W_in, const float* 
   }
   if (!u0 || !W_in || !conv_w || !W_x || !W_dt || !dt_bias || !A || !W_out)
     return MSSM_ERROR_INVALID_VALUE;
+  // the block's scan reads and writes its own workspace buffers (256-byte aligned)
   const mssm::BlockPlan plan =
-      mssm::plan_block(batch, L, Dm, Di, N, R, mssm::choose_fused_cpl(Di));
+      mssm::plan_block(batch, L, Dm, Di, N, R, mssm::choose_fused_cpl(Di),
+                       mssm::chain_fused_applies(batch, Di, N, R, workspace, workspace));
   s = check_grid(plan.scan, batch, Di, N);
   if (s != MSSM_SUCCESS) return s;
   if (!workspace || workspace_bytes < plan.workspace_bytes) return MSSM_ERROR_WORKSPACE;

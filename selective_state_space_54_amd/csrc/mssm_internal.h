@@ -53,6 +53,29 @@ ScanPlan plan_scan(int64_t batch, int64_t L, int64_t D, int64_t N, int cpl);
 bool chain_scan_applies(const ScanArgs& a);
 hipError_t launch_chain_scan(const ScanArgs& a, hipStream_t stream);
 
+// The single pass behind the selection projections (fused selective SSM and
+// Mamba block): delta is the float32 matrix softplus(dt_low W_dt + bias) and
+// B, C are the columns R .. R+2N-1 of P's rows.  Whether it applies (N = 16,
+// D % 16 == 0, R <= 256, enough channels, MSSM_SCAN_DESIGN; x and y as
+// given), and the launch.
+struct ChainFusedArgs {
+  const void* x = nullptr;        // [batch, L, D] bf16, or float32 with x_f32
+  bool x_f32 = false;
+  const float* delta = nullptr;   // [batch, L, D]
+  const float* P = nullptr;       // [batch*L, ldp]
+  int64_t ldp = 0, R = 0;
+  const float* A = nullptr;
+  const float* Dskip = nullptr;   // or null
+  const float* z = nullptr;       // [batch, L, D] float32, or null
+  void* y = nullptr;              // float32, or bf16 hi part with y_bf16
+  void* y_lo = nullptr;           // with y_bf16: bf16(y - hi)
+  bool y_bf16 = false;
+  int64_t batch = 0, L = 0, D = 0;
+};
+bool chain_fused_applies(int64_t batch, int64_t D, int64_t N, int64_t R, const void* x,
+                         const void* y);
+hipError_t launch_chain_fused(const ChainFusedArgs& a, hipStream_t stream);
+
 // The plan for these arguments: the single-pass design when it applies, else
 // the chunked plan with the chains-per-lane choice below.
 ScanPlan plan_for(const ScanArgs& a);
@@ -119,6 +142,8 @@ struct FusedArgs {
 // summaries.
 struct FusedPlan {
   ScanPlan scan;
+  bool chain = false;         // single-pass scan over a float32 delta matrix
+  size_t delta_offset = 0;    // with chain: float32 [batch*L, D]
   size_t p_bytes = 0;
   size_t dtl_offset = 0;
   size_t dtl_lo_offset = 0;
@@ -162,6 +187,12 @@ hipError_t launch_fused_prep(const float* P, int64_t M, int64_t R, int64_t ldp, 
                              int64_t D, uint16_t* dtl, uint16_t* dtl_lo, uint16_t* wT,
                              hipStream_t stream);
 
+// delta[m, d] = softplus(sum_r (dtl + dtl_lo)[m, r] wT[d, r] + bias[d]), float32
+// [M, D], on the matrix cores (R a multiple of 16).
+hipError_t launch_dtproj_softplus(const uint16_t* dtl, const uint16_t* dtl_lo, const uint16_t* wT,
+                                  const float* bias, float* delta, int64_t M, int64_t D,
+                                  int64_t R, hipStream_t stream);
+
 // The device's rocBLAS handle (created on first use, kept until exit), bound
 // to `stream`.  false: rocBLAS failed (hip_error == hipSuccess) or a HIP call
 // failed (hip_error set).
@@ -203,13 +234,14 @@ struct BlockArgs {
 // W_dt^T and chunk summaries.
 struct BlockPlan {
   ScanPlan scan;
+  bool chain = false;         // single pass; delta goes to the (by then unused) u buffer
   size_t u_offset = 0, z_offset = 0, x_offset = 0, xb_offset = 0, xl_offset = 0, g_offset = 0,
          gl_offset = 0;
   size_t p_offset = 0, dtl_offset = 0, dtl_lo_offset = 0, wt_offset = 0, scan_offset = 0;
   size_t workspace_bytes = 0;
 };
 BlockPlan plan_block(int64_t batch, int64_t L, int64_t Dm, int64_t Di, int64_t N, int64_t R,
-                     int cpl);
+                     int cpl, bool chain);
 size_t block_workspace_bound(int64_t batch, int64_t L, int64_t Dm, int64_t Di, int64_t N,
                              int64_t R);
 FusedStatus launch_block(const BlockArgs& a, const BlockPlan& plan, void* workspace,
@@ -254,7 +286,10 @@ struct BwdPlan {
 BwdPlan plan_bwd(int64_t batch, int64_t L, int64_t D, int64_t N);
 hipError_t launch_bwd(const BwdArgs& a, const BwdPlan& plan, void* workspace, hipStream_t stream);
 
-FusedPlan plan_fused(int64_t batch, int64_t L, int64_t D, int64_t N, int64_t R, int cpl);
+// chain: the single-pass order (plan_fused ignores cpl then); the bound
+// covers every order and layout.
+FusedPlan plan_fused(int64_t batch, int64_t L, int64_t D, int64_t N, int64_t R, int cpl,
+                     bool chain);
 size_t fused_workspace_bound(int64_t batch, int64_t L, int64_t D, int64_t N, int64_t R);
 int choose_fused_cpl(int64_t D);
 FusedStatus launch_fused(const FusedArgs& a, const FusedPlan& f, void* workspace,

@@ -18,3 +18,20 @@ def golden():
     import json
     with open(os.path.join(ROOT, "tests", "golden", "page_examples.json")) as f:
         return json.load(f)
+
+
+@pytest.fixture
+def design(request):
+    """Pins the scan order for one test (parametrize indirectly with "chain",
+    "chunked" or "auto"): sets MSSM_SCAN_DESIGN, which the library reads at
+    every call, and restores it afterwards."""
+    old = os.environ.get("MSSM_SCAN_DESIGN")
+    if request.param == "auto":
+        os.environ.pop("MSSM_SCAN_DESIGN", None)
+    else:
+        os.environ["MSSM_SCAN_DESIGN"] = request.param
+    yield request.param
+    if old is None:
+        os.environ.pop("MSSM_SCAN_DESIGN", None)
+    else:
+        os.environ["MSSM_SCAN_DESIGN"] = old

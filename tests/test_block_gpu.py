@@ -105,10 +105,11 @@ def test_block_is_deterministic():
     assert np.array_equal(a, b)
 
 
-def test_block_full_size_sampled_rows():
+@pytest.mark.parametrize("design", ["auto", "chunked"], indirect=True)
+def test_block_full_size_sampled_rows(design):
     """batch 16, L 2048, Dm 2560, Di 5120, N 16, R 160, k 4: rows 0 and 15
-    (batch rows are independent) against the oracle."""
-    print("case mamba_block_bf16 full size", flush=True)
+    (batch rows are independent) against the oracle, with either scan order."""
+    print(f"case mamba_block_bf16 full size design={design}", flush=True)
     g = workloads.generate_block()
     out = run_block(g)
     assert np.isfinite(out).all()

@@ -24,17 +24,6 @@ from selective_state_space_54_amd import mssm  # noqa: E402
 from test_scan_ex_gpu import _opts, check  # noqa: E402
 
 
-@pytest.fixture
-def design(request):
-    old = os.environ.get("MSSM_SCAN_DESIGN")
-    os.environ["MSSM_SCAN_DESIGN"] = request.param
-    yield request.param
-    if old is None:
-        os.environ.pop("MSSM_SCAN_DESIGN", None)
-    else:
-        os.environ["MSSM_SCAN_DESIGN"] = old
-
-
 # (batch, L, D): one step, less than a tile, exactly one tile, one step past a
 # tile, many tiles with a ragged end, an odd tile count, wider blocks of channels
 SHAPES = [(1, 1, 16), (2, 15, 32), (1, 16, 16), (2, 17, 48), (3, 100, 64), (1, 257, 160),

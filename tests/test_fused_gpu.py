@@ -96,9 +96,12 @@ def test_fused_zero_dt_proj_matches_plain_scan_on_gpu():
     assert_parity(y, oracle_fused(g), "bf16", "fused with W_dt = 0")
 
 
-def test_fused_full_size_workload_sampled_channels():
-    """batch 16, L 2048, D 5120, N 16, R 160: every 20th channel against the oracle."""
-    print("case fused_proj_bf16 full size", flush=True)
+@pytest.mark.parametrize("design", ["auto", "chunked"], indirect=True)
+def test_fused_full_size_workload_sampled_channels(design):
+    """batch 16, L 2048, D 5120, N 16, R 160: every 20th channel against the
+    oracle; by default this shape takes the single-pass scan over a written-out
+    delta, pinned "chunked" the chunked kernels with delta on the matrix cores."""
+    print(f"case fused_proj_bf16 full size design={design}", flush=True)
     g = workloads.generate("fused_proj_bf16")
     y = run_fused(g)
     assert np.isfinite(y).all()
