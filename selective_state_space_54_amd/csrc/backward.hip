@@ -27,6 +27,8 @@
 //      reduce-scatter across lanes and written as per-wavefront partials;
 //      dA/dD as per-chunk partials;
 //   4. small kernels add the partials up (a fixed order: deterministic).
+#include <algorithm>
+
 #include "mssm_internal.h"
 #include "scan_kernels.h"
 
@@ -480,8 +482,21 @@ hipError_t launch_bwd_n(const BwdArgs& a, const BwdPlan& bp, char* ws, hipStream
 
 }  // namespace
 
-BwdPlan plan_bwd(int64_t batch, int64_t L, int64_t D, int64_t N) {
+BwdPlan plan_bwd(int64_t batch, int64_t L, int64_t D, int64_t N, bool chain) {
   BwdPlan b;
+  if (chain) {
+    // checkpoints [batch, tiles, D, N]; dB/dC partials per 16-channel block
+    // [D/16, batch*L, 2N]; dA partials [batch, D, N]; dD partials [batch, D]
+    const size_t tiles = (size_t)((L + 15) / 16);
+    b.chain = true;
+    size_t off = 0;
+    b.ck_offset = off;      off += align256(sizeof(float) * (size_t)batch * tiles * (size_t)D * (size_t)N);
+    b.part_bc_offset = off; off += align256(sizeof(float) * (size_t)(D / 16) * (size_t)batch * (size_t)L * 2 * (size_t)N);
+    b.part_a_offset = off;  off += align256(sizeof(float) * (size_t)batch * (size_t)D * (size_t)N);
+    b.part_d_offset = off;  off += align256(sizeof(float) * (size_t)batch * (size_t)D);
+    b.workspace_bytes = off;
+    return b;
+  }
   b.chunk = kChunk;
   b.K = static_cast<int>((L + kChunk - 1) / kChunk);
   const size_t sums = b.K > 1 ? align256(sizeof(float) * (size_t)batch * (size_t)(b.K - 1) *
@@ -502,8 +517,33 @@ BwdPlan plan_bwd(int64_t batch, int64_t L, int64_t D, int64_t N) {
   return b;
 }
 
+size_t bwd_workspace_bound(int64_t batch, int64_t L, int64_t D, int64_t N) {
+  size_t w = plan_bwd(batch, L, D, N, false).workspace_bytes;
+  if (N == 16 && D % 16 == 0) w = std::max(w, plan_bwd(batch, L, D, N, true).workspace_bytes);
+  return w;
+}
+
 hipError_t launch_bwd(const BwdArgs& a, const BwdPlan& bp, void* workspace, hipStream_t stream) {
   char* ws = static_cast<char*>(workspace);
+  if (bp.chain) {
+    float* part_bc = reinterpret_cast<float*>(ws + bp.part_bc_offset);
+    float* part_a = reinterpret_cast<float*>(ws + bp.part_a_offset);
+    float* part_d = reinterpret_cast<float*>(ws + bp.part_d_offset);
+    hipError_t e = launch_chain_bwd(a, reinterpret_cast<float*>(ws + bp.ck_offset), part_bc,
+                                    part_a, part_d, stream);
+    if (e != hipSuccess) return e;
+    // per-block dB/dC partials, per-batch-row dA / dD partials, in a fixed order
+    hipLaunchKernelGGL(bwd_reduce_bc_kernel, dim3(2048), dim3(256), 0, stream, part_bc, a.dB,
+                       a.dC, a.batch * a.L, static_cast<int>(a.N), a.D / 16);
+    const int64_t da_count = a.D * a.N;
+    hipLaunchKernelGGL(bwd_reduce_rows_kernel,
+                       dim3((unsigned)((da_count + kRedCols - 1) / kRedCols)),
+                       dim3(kRedCols * kRedGroups), 0, stream, part_a, a.dA, da_count, a.batch);
+    if (a.Dskip)
+      hipLaunchKernelGGL(bwd_reduce_rows_kernel, dim3((unsigned)((a.D + kRedCols - 1) / kRedCols)),
+                         dim3(kRedCols * kRedGroups), 0, stream, part_d, a.dD, a.D, a.batch);
+    return hipGetLastError();
+  }
   switch (a.N) {
     case 1: return launch_bwd_n<1>(a, bp, ws, stream);
     case 2: return launch_bwd_n<2>(a, bp, ws, stream);

@@ -1,0 +1,374 @@
+// Backward pass of the selective scan in the single-pass layout (one lane per
+// channel and state index, N = 16, D % 16 == 0): the gradients of
+// "Understanding Mamba" eq. (2)-(3) with the first-order input term, the
+// feedthrough D x and the SiLU(z) gate, by recomputation ("State Space Models
+// and Mamba", hardware-aware scan: the backward recomputes the states).
+//
+// With g_t = dout_t SiLU(z_t), a_t = exp(delta_t A), u_t = delta_t x_t B_t:
+//   lam_t = C_t g_t + a_{t+1} lam_{t+1}            (the adjoint, lam_L = 0)
+//   dx_t = g_t D + delta_t sum_n lam_t B_t       ddelta_t = x_t sum_n lam_t B_t
+//                                                          + sum_n lam_t A a_t h_{t-1}
+//   dA += lam_t delta_t a_t h_{t-1}   dB_t += lam_t delta_t x_t   dC_t += g_t h_t
+//   dD += g_t x_t   dz_t = dout_t y_t SiLU'(z_t)   dh0 = a_0 lam_0
+//
+// A first pass (chain_scan_kernel in checkpoint mode) stores every lane's
+// state after each 16-step tile.  This kernel walks the tiles backwards: a
+// lane recomputes its tile's 16 states from the checkpoint into registers,
+// then sweeps the tile backwards carrying a_{t+1} lam_{t+1} across tiles.
+// Sums over n (dx, ddelta, and y for dz) are the row reduce-scatter of the
+// forward read-out, landing on the lane that owns the step.  Sums over
+// channels (dB, dC) fold the wavefront's four rows with permlane swaps, the
+// four wavefronts through LDS, and leave one partial per block of 16
+// channels for a separate reduction; dA and dD leave one partial per batch
+// row.  Inputs and outputs move through LDS in 16 x 16 tiles as in the
+// forward kernel.
+#pragma once
+
+#include "chain_scan.h"
+
+namespace mssm {
+namespace chain {
+
+struct ChainBwdParams {
+  const void* x;
+  const void* delta;
+  const void* B;
+  const void* C;
+  const void* z;            // or null
+  const float* A;
+  const float* Dskip;       // or null
+  const float* h0;          // or null
+  const float* dout;        // [batch, L, D]
+  const float* ck;          // [batch, tiles, D, N]: state after each tile (the last unused)
+  float* dx;                // [batch, L, D]
+  float* ddelta;
+  float* dz;                // with z
+  float* dh0;               // or null
+  float* part_bc;           // [D / 16, batch * L, 2N]: dB | dC per block
+  float* part_a;            // [batch, D, N]
+  float* part_d;            // [batch, D], with Dskip
+  int64_t L, D;
+};
+
+__device__ __forceinline__ float silu_grad(float v) {   // d/dv (v sigmoid(v))
+  const float s = __builtin_amdgcn_rcpf(1.0f + fast_exp2(-v * kLog2e));
+  return s * (1.0f + v * (1.0f - s));
+}
+
+// a + b after permlane32_swap: lanes 0..31 get a summed with a of lanes
+// 32..63, lanes 32..63 get b summed with b of lanes 0..31 (rows r and r + 2).
+__device__ __forceinline__ float fold_rows2(float a, float b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+// the same with permlane16_swap: rows 0 and 2 get a summed with the next row's
+// a, rows 1 and 3 get b summed with the previous row's b.
+__device__ __forceinline__ float fold_rows1(float a, float b) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// The row reduce-scatter of row_reduce_scatter16 in two parts, so that its
+// first level can run as soon as both of its operands exist: rs_first(p[i],
+// p[i + 8]) gives q8[i]; rs_rest(q8) finishes (lane n of the row returns the
+// row total of p[n]).
+__device__ __forceinline__ float rs_first(float lo, float hi) {
+  float q;
+  asm volatile(
+      "s_nop 1\n\t"
+      "v_add_f32_dpp %0, %1, %1 row_ror:8 row_mask:0xf bank_mask:0x3\n\t"
+      "v_add_f32_dpp %0, %2, %2 row_ror:8 row_mask:0xf bank_mask:0xc"
+      : "=&v"(q)
+      : "v"(lo), "v"(hi));
+  return q;
+}
+__device__ __forceinline__ float rs_rest(const float (&q8)[8], int n) {
+  float q4[4], q2[2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    asm volatile(
+        "s_nop 1\n\t"
+        "v_add_f32_dpp %0, %1, %1 row_half_mirror row_mask:0xf bank_mask:0x5\n\t"
+        "v_add_f32_dpp %0, %2, %2 row_half_mirror row_mask:0xf bank_mask:0xa"
+        : "=&v"(q4[i])
+        : "v"(q8[i]), "v"(q8[i + 4]));
+  bool up = (n & 2) != 0;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const float keep = up ? q4[i + 2] : q4[i], send = up ? q4[i] : q4[i + 2];
+    q2[i] = keep + dpp<kQuadXor2>(send);
+  }
+  up = (n & 1) != 0;
+  const float keep = up ? q2[1] : q2[0], send = up ? q2[0] : q2[1];
+  return keep + dpp<kQuadXor1>(send);
+}
+
+// grid: batch * D / 16 blocks of kBlock lanes.
+template <typename T, bool kSkip, bool kGate>
+__global__ __launch_bounds__(kBlock) void chain_bwd_kernel(ChainBwdParams prm) {
+  // inputs [buffer][x, delta, B^T, C^T, dout, z]; outputs [buffer][dx, ddelta, dz];
+  // dB/dC partials [buffer][wavefront][step][dB n | dC n]
+  __shared__ __align__(16) float tin[2][6][kTile][kRow];
+  __shared__ __align__(16) float tout[2][3][kTile][kRow];
+  __shared__ __align__(16) float tbc[2][kWaves][kTile][2 * kStates];
+  const int64_t L = prm.L, D = prm.D;
+  const int64_t n_dgroups = D / kChannels;
+  const int64_t blk = xcd_local_block(blockIdx.x, gridDim.x);
+  const int64_t dg = blk % n_dgroups;
+  const int64_t b = blk / n_dgroups;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n = lane & 15;
+  const int row = lane >> 4;
+  const int ch = wave * 4 + row;
+  const int64_t d0 = dg * kChannels;
+  const int64_t chain_idx = (b * D + d0 + ch) * kStates + n;
+  const float An = prm.A[(d0 + ch) * kStates + n];
+  const float A2 = An * kLog2e;
+  float Dd = 0.0f;
+  if constexpr (kSkip) Dd = prm.Dskip[d0 + ch];
+  const int64_t ntiles = (L + kTile - 1) / kTile;
+  const int64_t last = ntiles - 1;
+  const int tail_steps = static_cast<int>(L - last * kTile);
+
+  // Loads: wavefront 0 x (and z), 1 delta and dout, 2 B, 3 C; 4 values per lane.
+  const int ls = lane >> 2, lq = (lane & 3) * 4;
+  const int ls_tail = ls < tail_steps ? ls : tail_steps - 1;
+  const char* src;
+  const char* src2 = nullptr;
+  int esz = sizeof(T), esz2 = sizeof(T);
+  int64_t rs = D;
+  if (wave == 0) {
+    src = static_cast<const char*>(prm.x) + (b * L * D + d0) * sizeof(T);
+    if constexpr (kGate) src2 = static_cast<const char*>(prm.z) + (b * L * D + d0) * sizeof(T);
+  } else if (wave == 1) {
+    src = static_cast<const char*>(prm.delta) + (b * L * D + d0) * sizeof(T);
+    src2 = reinterpret_cast<const char*>(prm.dout + b * L * D + d0);
+    esz2 = 4;
+  } else {
+    src = static_cast<const char*>(wave == 2 ? prm.B : prm.C) + b * L * kStates * sizeof(T);
+    rs = kStates;
+  }
+  const int64_t rs_bytes = rs * esz;
+  const uint32_t off_full = static_cast<uint32_t>(ls * rs_bytes + lq * esz);
+  const uint32_t off_tail = static_cast<uint32_t>(ls_tail * rs_bytes + lq * esz);
+  const uint32_t off2_full = static_cast<uint32_t>((ls * D + lq) * esz2);
+  const uint32_t off2_tail = static_cast<uint32_t>((ls_tail * D + lq) * esz2);
+  const int64_t tile_bytes = kTile * rs_bytes, tile_bytes2 = kTile * D * esz2;
+  const bool has2 = wave == 1 || (kGate && wave == 0);
+
+  struct Regs {
+    uint4 v, v2;
+  };
+  auto tile_of = [&](int64_t i) {            // iteration i walks tile last - i (clamped at 0)
+    return i <= last ? last - i : int64_t(0);
+  };
+  auto load = [&](Regs& r, int64_t i) {
+    const int64_t kt = tile_of(i);
+    r.v = load_raw(src + kt * tile_bytes + (kt == last ? off_tail : off_full), esz);
+    if (has2) r.v2 = load_raw(src2 + kt * tile_bytes2 + (kt == last ? off2_tail : off2_full), esz2);
+  };
+  auto put = [&](const Regs& r, int buf, int64_t i) {
+    const bool pad = tile_of(i) == last && ls >= tail_steps;
+    float v[4], w[4];
+    unpack_raw(r.v, esz, v);
+    if (has2) unpack_raw(r.v2, esz2, w);
+    if (wave == 1 && pad) v[0] = v[1] = v[2] = v[3] = w[0] = w[1] = w[2] = w[3] = 0.0f;
+    if (wave < 2) {
+      *reinterpret_cast<float4*>(&tin[buf][wave][ls][lq]) = make_float4(v[0], v[1], v[2], v[3]);
+      if (has2)
+        *reinterpret_cast<float4*>(&tin[buf][wave == 1 ? 4 : 5][ls][lq]) =
+            make_float4(w[0], w[1], w[2], w[3]);
+    } else {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) tin[buf][wave][lq + q][ls] = v[q];
+    }
+  };
+
+  // Stores of a finished tile (iteration i, buffer buf): wavefront 0 dx,
+  // 1 ddelta, 2 dz, 3 the block's dB/dC partial.
+  auto store = [&](int64_t i) {
+    const int buf = i & 1;
+    const int64_t kt = tile_of(i);
+    const int64_t t0 = kt * kTile;
+    const int steps = kt == last ? tail_steps : kTile;
+    if (wave < 3) {
+      if (wave == 2 && !kGate) return;
+      float* dst = wave == 0 ? prm.dx : (wave == 1 ? prm.ddelta : prm.dz);
+      const float4 v = *reinterpret_cast<const float4*>(&tout[buf][wave][ls][lq]);
+      if (ls < steps) *reinterpret_cast<float4*>(dst + (b * L + t0 + ls) * D + d0 + lq) = v;
+    } else {
+      // 16 steps x 32 values; lane takes 8 consecutive ones of one step
+      const int e = lane * 8;
+      const int step = e / (2 * kStates);
+      float s[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) s[q] = 0.0f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const float4 p = *reinterpret_cast<const float4*>(&tbc[buf][w][0][0] + e);
+        const float4 q4 = *reinterpret_cast<const float4*>(&tbc[buf][w][0][0] + e + 4);
+        s[0] += p.x; s[1] += p.y; s[2] += p.z; s[3] += p.w;
+        s[4] += q4.x; s[5] += q4.y; s[6] += q4.z; s[7] += q4.w;
+      }
+      if (step < steps) {
+        float* dst = prm.part_bc + ((dg * (gridDim.x / n_dgroups) + b) * L + t0) * (2 * kStates) + e;
+        *reinterpret_cast<float4*>(dst) = make_float4(s[0], s[1], s[2], s[3]);
+        *reinterpret_cast<float4*>(dst + 4) = make_float4(s[4], s[5], s[6], s[7]);
+      }
+    }
+  };
+
+  // state entering a tile: h0 (or 0) for tile 0, else the checkpoint
+  auto state_in = [&](int64_t kt) {
+    if (kt == 0) return prm.h0 ? prm.h0[chain_idx] : 0.0f;
+    return prm.ck[((b * ntiles + kt - 1) * D + d0 + ch) * kStates + n];
+  };
+
+  float lamn = 0.0f;       // a_{t+1} lam_{t+1} entering the step being swept
+  float dA = 0.0f, dDacc = 0.0f;
+  auto compute = [&](int64_t i, float hin) {
+    const int buf = i & 1;
+    const int64_t kt = tile_of(i);
+    const float xv = tin[buf][0][n][ch];
+    const float dv = tin[buf][1][n][ch];
+    const float go = tin[buf][4][n][ch];
+    float zv = 0.0f;
+    if constexpr (kGate) zv = tin[buf][5][n][ch];
+    // B_t[n] and C_t[n] of the tile's steps, four at a time from LDS
+    auto b4 = [&](int j) { return *reinterpret_cast<const float4*>(&tin[buf][2][n][4 * j]); };
+    auto c4 = [&](int j) { return *reinterpret_cast<const float4*>(&tin[buf][3][n][4 * j]); };
+    auto el = [](const float4& v, int e) { return e == 0 ? v.x : e == 1 ? v.y : e == 2 ? v.z : v.w; };
+    const float gv = kGate ? go * silu(zv) : go;   // g of step n
+    const float uv = dv * xv;
+    // recompute: a_s and h_s
+    float a[kTile], hs[kTile];
+    float hp = hin;
+#pragma unroll
+    for (int j = 0; j < kTile / 4; ++j) {
+      const float4 bq = b4(j);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int s = 4 * j + e;
+        a[s] = fast_exp2(row_bcast_dyn(dv, s) * A2);
+        hs[s] = __builtin_fmaf(a[s], hp, row_bcast_dyn(uv, s) * el(bq, e));
+        hp = hs[s];
+      }
+    }
+    if constexpr (kGate) {   // dz = dout y SiLU'(z), y = C.h + D x, for step n
+      float py[kTile];
+#pragma unroll
+      for (int j = 0; j < kTile / 4; ++j) {
+        const float4 cq = c4(j);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) py[4 * j + e] = el(cq, e) * hs[4 * j + e];
+      }
+      float y = row_reduce_scatter16(py, n);
+      if constexpr (kSkip) y = __builtin_fmaf(Dd, xv, y);
+      tout[buf][2][n][ch] = go * y * silu_grad(zv);
+    }
+    // backwards through the tile; dB, dC over the wavefront's four channels
+    // per pair of steps: rows 0 / 1 / 2 / 3 end with dB of step 2j / dB of
+    // 2j + 1 / dC of 2j / dC of 2j + 1
+    // p1 = lam B and p2 = lam A a h_{s-1} enter the n-sums: steps 8..15 wait
+    // for their partners 0..7, then both go through the first reduce level
+    float p1h[kTile / 2], p2h[kTile / 2], q1[kTile / 2], q2[kTile / 2];
+    float vb_odd = 0.0f, vc_odd = 0.0f;
+    float4 bq = make_float4(0.0f, 0.0f, 0.0f, 0.0f), cq = bq;
+#pragma unroll
+    for (int s = kTile - 1; s >= 0; --s) {
+      if (s % 4 == 3) {
+        bq = b4(s / 4);
+        cq = c4(s / 4);
+      }
+      const float Bs = el(bq, s % 4), Cs = el(cq, s % 4);
+      const float gs = row_bcast_dyn(gv, s);
+      const float lam = __builtin_fmaf(Cs, gs, lamn);
+      lamn = a[s] * lam;
+      const float r = lam * (a[s] * (s > 0 ? hs[s > 0 ? s - 1 : 0] : hin));
+      dA = __builtin_fmaf(r, row_bcast_dyn(dv, s), dA);
+      const float p2 = r * An, p1 = lam * Bs;
+      if (s >= kTile / 2) {
+        p1h[s - kTile / 2] = p1;
+        p2h[s - kTile / 2] = p2;
+      } else {
+        q1[s] = rs_first(p1, p1h[s]);
+        q2[s] = rs_first(p2, p2h[s]);
+      }
+      const float vb = lam * row_bcast_dyn(uv, s);
+      const float vc = gs * hs[s];
+      if (s & 1) {
+        vb_odd = vb;
+        vc_odd = vc;
+      } else {
+        const float lo = fold_rows2(vb, vc);
+        const float hi = fold_rows2(vb_odd, vc_odd);
+        tbc[buf][wave][s + (row & 1)][(row >> 1) * kStates + n] = fold_rows1(lo, hi);
+      }
+    }
+    const float s1 = rs_rest(q1, n);   // sum_n lam B of step n
+    const float s2 = rs_rest(q2, n);   // sum_n lam A a h_{t-1} of step n
+    float dxv = dv * s1;
+    if constexpr (kSkip) {
+      dxv = __builtin_fmaf(gv, Dd, dxv);
+      if (kt != last || n < tail_steps) dDacc = __builtin_fmaf(gv, xv, dDacc);
+    }
+    tout[buf][0][n][ch] = dxv;
+    tout[buf][1][n][ch] = __builtin_fmaf(xv, s1, s2);
+  };
+
+  // Pipeline (iterations walk the tiles backwards): iteration i: barrier;
+  // stores of iteration i - 1; inputs of iteration i + 1 into LDS; loads for
+  // iteration i + 3; the checkpoint for iteration i + 1; compute iteration i.
+  Regs r0, r1;
+  load(r0, 0);
+  load(r1, 1);
+  put(r0, 0, 0);
+  load(r0, 2);
+  float hin = state_in(tile_of(0));
+  float hin_next = state_in(tile_of(1));
+  int64_t i = 0;
+  for (; i + 2 <= ntiles; i += 2) {
+    __syncthreads();
+    if (i >= 1) store(i - 1);
+    put(r1, 1, i + 1);
+    load(r1, i + 3);
+    compute(i, hin);
+    hin = hin_next;
+    hin_next = state_in(tile_of(i + 2));
+    __syncthreads();
+    store(i);
+    put(r0, 0, i + 2);
+    load(r0, i + 4);
+    compute(i + 1, hin);
+    hin = hin_next;
+    hin_next = state_in(tile_of(i + 3));
+  }
+  if (i < ntiles) {
+    __syncthreads();
+    if (i >= 1) store(i - 1);
+    compute(i, hin);
+  }
+  __syncthreads();
+  store(last);              // iteration last handles tile 0
+  prm.part_a[chain_idx] = dA;
+  if (prm.dh0) prm.dh0[chain_idx] = lamn;
+  if constexpr (kSkip) {
+    float t = dDacc;        // sum over the row's 16 lanes (one step each)
+#pragma unroll
+    for (int o = 8; o >= 1; o >>= 1) t += __shfl_xor(t, o, 16);
+    if (n == 0) prm.part_d[b * D + d0 + ch] = t;
+  }
+}
+
+template <typename T, bool kSkip, bool kGate>
+hipError_t launch_bwd_chain_t(const ChainBwdParams& p, int64_t batch, hipStream_t stream) {
+  const dim3 grid(static_cast<unsigned>(batch * (p.D / kChannels)));
+  hipLaunchKernelGGL((chain_bwd_kernel<T, kSkip, kGate>), grid, dim3(kBlock), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace chain
+}  // namespace mssm

@@ -65,6 +65,20 @@ __device__ __forceinline__ float row_bcast(float v) {
 }
 constexpr int kQuadXor2 = 0x4E, kQuadXor1 = 0xB1;
 
+// row_bcast for an index known after unrolling (s must fold to a constant)
+__device__ __forceinline__ float row_bcast_dyn(float v, int s) {
+  switch (s) {
+    case 0: return row_bcast<0>(v);   case 1: return row_bcast<1>(v);
+    case 2: return row_bcast<2>(v);   case 3: return row_bcast<3>(v);
+    case 4: return row_bcast<4>(v);   case 5: return row_bcast<5>(v);
+    case 6: return row_bcast<6>(v);   case 7: return row_bcast<7>(v);
+    case 8: return row_bcast<8>(v);   case 9: return row_bcast<9>(v);
+    case 10: return row_bcast<10>(v); case 11: return row_bcast<11>(v);
+    case 12: return row_bcast<12>(v); case 13: return row_bcast<13>(v);
+    case 14: return row_bcast<14>(v); default: return row_bcast<15>(v);
+  }
+}
+
 // Row total of p[i], scattered: lane n of each DPP row returns the sum over
 // the row's 16 lanes of p[n].  Four halving levels.  The first two use the
 // DPP bank mask (a bank is 4 lanes of a row) to write each half of the row
@@ -161,13 +175,16 @@ struct ChainParams {
   void* y;
   void* y_lo;
   int64_t L, D, ld_bc;
+  float* ck = nullptr;    // checkpoint mode: [batch, tiles, D, N] states (the last tile's unused)
 };
 
 // grid: batch * D / 16 blocks of kBlock lanes.  Requirements (checked by the
 // launchers): N = 16, D % 16 == 0, float32 inputs 16-byte and bfloat16 inputs
 // 8-byte aligned (rows too: ld_bc a multiple of 4), y 16-byte aligned,
 // 16 * D * 4 < 2^31.
-template <class IO, class V>
+// kCk (checkpoints for the backward pass): no read-out and no y; instead the
+// state after every tile but the last goes to ck[b, tile, d, n].
+template <class IO, class V, bool kCk = false>
 __global__ __launch_bounds__(kBlock) void chain_scan_kernel(ChainParams prm) {
   using TX = typename IO::TX;
   using TY = typename IO::TY;
@@ -262,6 +279,7 @@ __global__ __launch_bounds__(kBlock) void chain_scan_kernel(ChainParams prm) {
     }
   };
   auto store_y = [&](int64_t k) {
+    if constexpr (kCk) return;
     const float4 v = *reinterpret_cast<const float4*>(&tout[k & 1][ls][lq]);
     if (k == last && ls >= tail_steps) return;
     const int64_t step_bytes = k * kTile * D * static_cast<int64_t>(sizeof(TY));
@@ -281,7 +299,29 @@ __global__ __launch_bounds__(kBlock) void chain_scan_kernel(ChainParams prm) {
           make_uint2(lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16));
     }
   };
+  auto checkpoint = [&](int64_t k) {
+    const int buf = k & 1;
+    const float xv = tin[buf][0][n][ch];
+    const float dv = tin[buf][1][n][ch];
+    float Bt[kTile];
+#pragma unroll
+    for (int j = 0; j < kTile / 4; ++j) {
+      const float4 vb = *reinterpret_cast<const float4*>(&tin[buf][2][n][4 * j]);
+      Bt[4 * j] = vb.x; Bt[4 * j + 1] = vb.y; Bt[4 * j + 2] = vb.z; Bt[4 * j + 3] = vb.w;
+    }
+    const float uv = dv * xv;
+#pragma unroll
+    for (int s = 0; s < kTile; ++s) {
+      const float a = fast_exp2(row_bcast_dyn(dv, s) * A2);
+      h = __builtin_fmaf(a, h, row_bcast_dyn(uv, s) * Bt[s]);
+    }
+    if (k < last) prm.ck[((b * ntiles + k) * D + d0 + ch) * kStates + n] = h;
+  };
   auto compute = [&](int64_t k) {
+    if constexpr (kCk) {
+      checkpoint(k);
+      return;
+    }
     const int buf = k & 1;
     const float xv = tin[buf][0][n][ch];
     const float dv = tin[buf][1][n][ch];
@@ -350,10 +390,10 @@ __global__ __launch_bounds__(kBlock) void chain_scan_kernel(ChainParams prm) {
 }
 
 // Launch on `stream` for `batch` rows; returns the launch status.
-template <class IO, class V>
+template <class IO, class V, bool kCk = false>
 hipError_t launch_io(const ChainParams& p, int64_t batch, hipStream_t stream) {
   const dim3 grid(static_cast<unsigned>(batch * (p.D / kChannels)));
-  hipLaunchKernelGGL((chain_scan_kernel<IO, V>), grid, dim3(kBlock), 0, stream, p);
+  hipLaunchKernelGGL((chain_scan_kernel<IO, V, kCk>), grid, dim3(kBlock), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -48,9 +48,14 @@ hipError_t launch_parts(const ScanArgs& a, hipStream_t stream) {
 
 }  // namespace
 
-bool chain_scan_applies(const ScanArgs& a) {
+bool single_pass_chosen(int64_t channels) {
   const Design d = design_setting();
   if (d == Design::kChunked) return false;
+  return d == Design::kChain || channels >= kMinChannels;
+}
+
+bool chain_scan_applies(const ScanArgs& a) {
+  if (design_setting() == Design::kChunked) return false;
   if (a.N != chain::kStates || a.D % chain::kChannels != 0 || a.L < 1 || a.batch < 1)
     return false;
   // 4-value loads of x, delta, z, B, C and 16-byte stores of y
@@ -61,19 +66,18 @@ bool chain_scan_applies(const ScanArgs& a) {
   // 32-bit lane offsets within a 16-step tile; grid size
   if (a.D * chain::kTile * static_cast<int64_t>(sizeof(float)) >= (int64_t(1) << 31)) return false;
   if (a.batch > (int64_t(1) << 31) / (a.D / chain::kChannels)) return false;
-  return d == Design::kChain || a.batch * a.D >= kMinChannels;
+  return single_pass_chosen(a.batch * a.D);
 }
 
 bool chain_fused_applies(int64_t batch, int64_t D, int64_t N, int64_t R, const void* x,
                          const void* y) {
-  const Design d = design_setting();
-  if (d == Design::kChunked) return false;
+  if (design_setting() == Design::kChunked) return false;
   if (N != chain::kStates || D % chain::kChannels != 0 || batch < 1) return false;
   if (R > 256) return false;   // the delta kernel keeps W_dt in registers for R <= 256
   if (!aligned(x, 16) || !aligned(y, 16)) return false;
   if (D * chain::kTile * static_cast<int64_t>(sizeof(float)) >= (int64_t(1) << 31)) return false;
   if (batch > (int64_t(1) << 31) / (D / chain::kChannels)) return false;
-  return d == Design::kChain || batch * D >= kMinChannels;
+  return single_pass_chosen(batch * D);
 }
 
 hipError_t launch_chain_scan(const ScanArgs& a, hipStream_t stream) {

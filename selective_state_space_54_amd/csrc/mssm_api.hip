@@ -409,7 +409,7 @@ mssm_status mssm_selective_scan_bwd_workspace_size(int64_t batch, int64_t L, int
   if (!bytes) return MSSM_ERROR_INVALID_VALUE;
   const mssm_status s = check_shape(batch, L, D, N, dtype);
   if (s != MSSM_SUCCESS) return s;
-  *bytes = (batch == 0 || L == 0 || D == 0) ? 0 : mssm::plan_bwd(batch, L, D, N).workspace_bytes;
+  *bytes = (batch == 0 || L == 0 || D == 0) ? 0 : mssm::bwd_workspace_bound(batch, L, D, N);
   return MSSM_SUCCESS;
 }
 
@@ -446,8 +446,10 @@ mssm_status mssm_selective_scan_bwd(const void* x, const void* delta, const floa
   }
   if (!x || !delta || !A || !B || !C || !dout || !dx || !ddelta || !dB || !dC)
     return MSSM_ERROR_INVALID_VALUE;
-  const mssm::BwdPlan plan = mssm::plan_bwd(batch, L, D, N);
-  {
+  const mssm::BwdArgs a{x,  delta,  A,  B,  C,      Dskip, z,  h0,  dout,  dx,    ddelta, dA,
+                        dB, dC,     dDskip, dz, dh0, batch, L, D, N, dtype};
+  const mssm::BwdPlan plan = mssm::plan_bwd(batch, L, D, N, mssm::chain_bwd_applies(a));
+  if (!plan.chain) {
     const int64_t n_dtiles = (D + 255) / 256;
     int64_t blocks;
     if (!mul_ok(n_dtiles, plan.K, &blocks) || !mul_ok(blocks, batch, &blocks))
@@ -458,8 +460,6 @@ mssm_status mssm_selective_scan_bwd(const void* x, const void* delta, const floa
   }
   if (!workspace || workspace_bytes < plan.workspace_bytes) return MSSM_ERROR_WORKSPACE;
   if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return MSSM_ERROR_WORKSPACE;
-  const mssm::BwdArgs a{x,  delta,  A,  B,  C,      Dskip, z,  h0,  dout,  dx,    ddelta, dA,
-                        dB, dC,     dDskip, dz, dh0, batch, L, D, N, dtype};
   const hipError_t e = mssm::launch_bwd(a, plan, workspace, st);
   if (e != hipSuccess) {
     set_hip_error(e, "selective scan backward launch");

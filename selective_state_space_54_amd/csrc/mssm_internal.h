@@ -47,6 +47,11 @@ struct ScanArgs {
 // Plan for `cpl` chains per lane.
 ScanPlan plan_scan(int64_t batch, int64_t L, int64_t D, int64_t N, int cpl);
 
+// Whether a call over this many channels (batch * D) takes the single-pass
+// order when its shape and pointers allow it: MSSM_SCAN_DESIGN=chunked / chain
+// pins the answer, else at least 8192 channels.
+bool single_pass_chosen(int64_t channels);
+
 // Single-pass scan with one lane per (channel, state index), for N = 16 and
 // shapes with many channels: whether it is used for these arguments (shape,
 // alignment, channel count, MSSM_SCAN_DESIGN), and its launch.
@@ -277,14 +282,26 @@ struct BwdArgs {
 // [ceil(D/64), batch, L, 2N], per-chunk dA partials [batch*K, D, N] and dD
 // partials [batch*K, D].
 struct BwdPlan {
+  bool chain = false;         // single-pass order: checkpoints + one reverse kernel
+  size_t ck_offset = 0;       // with chain: states after each tile [batch, tiles, D, N]
   int64_t chunk = 0;
   int K = 1;
   size_t fwd_h_offset = 0, fwd_s_offset = 0, rev_h_offset = 0, rev_s_offset = 0;
   size_t part_bc_offset = 0, part_a_offset = 0, part_d_offset = 0;
   size_t workspace_bytes = 0;
 };
-BwdPlan plan_bwd(int64_t batch, int64_t L, int64_t D, int64_t N);
+// chain: the single-pass order (partials per 16-channel block and per batch
+// row); the bound covers both orders.
+BwdPlan plan_bwd(int64_t batch, int64_t L, int64_t D, int64_t N, bool chain);
+size_t bwd_workspace_bound(int64_t batch, int64_t L, int64_t D, int64_t N);
 hipError_t launch_bwd(const BwdArgs& a, const BwdPlan& plan, void* workspace, hipStream_t stream);
+
+// The single-pass backward (N = 16, D % 16 == 0, aligned pointers, enough
+// channels): whether it applies, and its two kernels (checkpoints, reverse
+// sweep) writing the partials that launch_bwd then reduces.
+bool chain_bwd_applies(const BwdArgs& a);
+hipError_t launch_chain_bwd(const BwdArgs& a, float* ck, float* part_bc, float* part_a,
+                            float* part_d, hipStream_t stream);
 
 // chain: the single-pass order (plan_fused ignores cpl then); the bound
 // covers every order and layout.

@@ -238,7 +238,10 @@ def test_block_support_and_argument_errors(lib):
     assert call([None] * 11, None, 0, 0, 8, 32, 64, 16, 16, 4) == 0
 
 
-def test_backward_argument_errors(lib):
+def test_backward_argument_errors(lib, monkeypatch):
+    # the chunked order, whose workspace the bound below covers exactly at
+    # this shape; a smaller buffer is refused before anything launches
+    monkeypatch.setenv("MSSM_SCAN_DESIGN", "chunked")
     out = ctypes.c_size_t(0)
     assert lib.mssm_selective_scan_bwd_workspace_size(8, 2048, 1536, 16, 0, ctypes.byref(out)) == 0
     assert out.value > 0
@@ -265,4 +268,7 @@ def test_backward_argument_errors(lib):
         ptrs[i] = None
         assert call(ptrs, FAKE, 1 << 40, 1, 4, 4, 4) == 1, f"null {i} accepted"
     assert call(p17, FAKE, nb - 1, 8, 2048, 1536, 16) == 4
+    assert call(p17, ctypes.c_void_p(0x1004), nb, 8, 2048, 1536, 16) == 4
+    monkeypatch.setenv("MSSM_SCAN_DESIGN", "chain")
+    assert call(p17, FAKE, 0, 8, 2048, 1536, 16) == 4
     assert call(p17, ctypes.c_void_p(0x1004), nb, 8, 2048, 1536, 16) == 4

@@ -69,17 +69,43 @@ def test_backward_all_parts(shape, dtype):
     grad_parity(grads, ref, dtype, f"bwd {shape} {dtype}")
 
 
+# N = 16 and D a multiple of 16: shapes the single-pass backward takes
+# (one, several and a ragged number of 16-step tiles; one to eight blocks of
+# 16 channels per batch row)
+CHAIN_SHAPES = [
+    (1, 1, 16, 16), (2, 15, 32, 16), (1, 16, 64, 16), (3, 17, 48, 16), (2, 33, 16, 16),
+    (1, 100, 128, 16), (2, 1000, 96, 16), (1, 4099, 32, 16),
+]
+
+
+@pytest.mark.parametrize("design", ["chain"], indirect=True)
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("shape", CHAIN_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_backward_single_pass_all_parts(shape, dtype, design):
+    batch, L, D, N = shape
+    print(f"case bwd single pass {shape} {dtype}", flush=True)
+    name = "mamba130m_layer_fp32" if dtype == "fp32" else "mid_bf16"
+    g = workloads.generate(name, batch=batch, L=L, D=D, N=N, seed=700 + L + D)
+    extras = workloads.generate_extras(g["workload"])
+    grads, ref = run_case(g, extras, ("Dskip", "z", "h0"), seed=L + 1)
+    grad_parity(grads, ref, dtype, f"bwd single pass {shape} {dtype}")
+
+
+@pytest.mark.parametrize("design", ["chain", "chunked"], indirect=True)
 @pytest.mark.parametrize("parts", [(), ("Dskip",), ("z",), ("h0",), ("Dskip", "z")],
                          ids=lambda p: "-".join(p) or "plain")
-def test_backward_each_combination(parts):
-    g = workloads.generate("mamba130m_layer_fp32", batch=2, L=333, D=100, N=16, seed=5)
-    extras = workloads.generate_extras(g["workload"])
-    grads, ref = run_case(g, extras, parts, seed=3)
-    assert set(grads) == set(ref)
-    grad_parity(grads, ref, "fp32", f"bwd {parts}")
+def test_backward_each_combination(parts, design):
+    # D = 100 only has the chunked order; D = 96 has both
+    for D in (100, 96):
+        g = workloads.generate("mamba130m_layer_fp32", batch=2, L=333, D=D, N=16, seed=5)
+        extras = workloads.generate_extras(g["workload"])
+        grads, ref = run_case(g, extras, parts, seed=3)
+        assert set(grads) == set(ref)
+        grad_parity(grads, ref, "fp32", f"bwd {parts} D={D} {design}")
 
 
-def test_backward_is_deterministic():
+@pytest.mark.parametrize("design", ["chain", "chunked"], indirect=True)
+def test_backward_is_deterministic(design):
     g = workloads.generate("mid_bf16", batch=2, L=500, D=256, N=16, seed=6)
     extras = workloads.generate_extras(g["workload"])
     a, _ = run_case(g, extras, ("Dskip", "z", "h0"), seed=4)
@@ -88,9 +114,10 @@ def test_backward_is_deterministic():
         assert torch.equal(a[k], b[k]), k
 
 
-def test_backward_full_size_headline():
+@pytest.mark.parametrize("design", ["auto", "chunked"], indirect=True)
+def test_backward_full_size_headline(design):
     """batch 8, L 2048, D 1536, N 16 with feedthrough, gate and initial state."""
-    print("case bwd mamba130m_layer_fp32 full size", flush=True)
+    print(f"case bwd mamba130m_layer_fp32 full size {design}", flush=True)
     g = workloads.generate("mamba130m_layer_fp32")
     extras = workloads.generate_extras(g["workload"])
     grads, ref = run_case(g, extras, ("Dskip", "z", "h0"), seed=11)
