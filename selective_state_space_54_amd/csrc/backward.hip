@@ -367,7 +367,7 @@ __global__ __launch_bounds__(kRedCols * kRedGroups) void bwd_reduce_rows_kernel(
     for (; r < nparts; r += kRedGroups) s += part[r * count + e];
   }
   acc[grp][col] = s;
-  __syncthreads();
+  block_sync();
   if (grp == 0 && e < count) {
     float t = 0.0f;
 #pragma unroll

@@ -105,6 +105,34 @@ __device__ __forceinline__ float rs_rest(const float (&q8)[8], int n) {
   return keep + dpp<kQuadXor1>(send);
 }
 
+// acc += (value of lane s of the DPP row of v) * m in one instruction
+// (v_fmac_f32 with a row_newbcast operand, which the compiler does not form by
+// itself).  The leading s_nop covers the two wait states a DPP read needs
+// after a VALU write of its source, which the compiler does not check inside
+// asm.
+template <int s>
+__device__ __forceinline__ void fmac_bcast(float& acc, float v, float m) {
+  asm volatile(
+      "s_nop 1\n\t"
+      "v_fmac_f32_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf bound_ctrl:1"
+      : "+v"(acc)
+      : "v"(v), "v"(m), "i"(s));
+}
+__device__ __forceinline__ void fmac_bcast_dyn(float& acc, float v, float m, int s) {
+  switch (s) {
+    case 0: fmac_bcast<0>(acc, v, m); break;   case 1: fmac_bcast<1>(acc, v, m); break;
+    case 2: fmac_bcast<2>(acc, v, m); break;   case 3: fmac_bcast<3>(acc, v, m); break;
+    case 4: fmac_bcast<4>(acc, v, m); break;   case 5: fmac_bcast<5>(acc, v, m); break;
+    case 6: fmac_bcast<6>(acc, v, m); break;   case 7: fmac_bcast<7>(acc, v, m); break;
+    case 8: fmac_bcast<8>(acc, v, m); break;   case 9: fmac_bcast<9>(acc, v, m); break;
+    case 10: fmac_bcast<10>(acc, v, m); break; case 11: fmac_bcast<11>(acc, v, m); break;
+    case 12: fmac_bcast<12>(acc, v, m); break; case 13: fmac_bcast<13>(acc, v, m); break;
+    case 14: fmac_bcast<14>(acc, v, m); break; default: fmac_bcast<15>(acc, v, m); break;
+  }
+}
+
+constexpr int kBcRow = 48;   // floats per step row of the dB | dC partial tile
+
 // grid: batch * D / 16 blocks of kBlock lanes.
 template <typename T, bool kSkip, bool kGate>
 __global__ __launch_bounds__(kBlock) void chain_bwd_kernel(ChainBwdParams prm) {
@@ -112,7 +140,9 @@ __global__ __launch_bounds__(kBlock) void chain_bwd_kernel(ChainBwdParams prm) {
   // dB/dC partials [buffer][wavefront][step][dB n | dC n]
   __shared__ __align__(16) float tin[2][6][kTile][kRow];
   __shared__ __align__(16) float tout[2][3][kTile][kRow];
-  __shared__ __align__(16) float tbc[2][kWaves][kTile][2 * kStates];
+  // (rows of kBcRow floats: the two steps a wavefront writes at once then
+  // land 16 banks apart)
+  __shared__ __align__(16) float tbc[2][kWaves][kTile][kBcRow];
   const int64_t L = prm.L, D = prm.D;
   const int64_t n_dgroups = D / kChannels;
   const int64_t blk = xcd_local_block(blockIdx.x, gridDim.x);
@@ -177,10 +207,9 @@ __global__ __launch_bounds__(kBlock) void chain_bwd_kernel(ChainBwdParams prm) {
     if (has2) unpack_raw(r.v2, esz2, w);
     if (wave == 1 && pad) v[0] = v[1] = v[2] = v[3] = w[0] = w[1] = w[2] = w[3] = 0.0f;
     if (wave < 2) {
-      *reinterpret_cast<float4*>(&tin[buf][wave][ls][lq]) = make_float4(v[0], v[1], v[2], v[3]);
+      lds_put4(&tin[buf][wave][ls][lq], v[0], v[1], v[2], v[3]);
       if (has2)
-        *reinterpret_cast<float4*>(&tin[buf][wave == 1 ? 4 : 5][ls][lq]) =
-            make_float4(w[0], w[1], w[2], w[3]);
+        lds_put4(&tin[buf][wave == 1 ? 4 : 5][ls][lq], w[0], w[1], w[2], w[3]);
     } else {
 #pragma unroll
       for (int q = 0; q < 4; ++q) tin[buf][wave][lq + q][ls] = v[q];
@@ -197,19 +226,19 @@ __global__ __launch_bounds__(kBlock) void chain_bwd_kernel(ChainBwdParams prm) {
     if (wave < 3) {
       if (wave == 2 && !kGate) return;
       float* dst = wave == 0 ? prm.dx : (wave == 1 ? prm.ddelta : prm.dz);
-      const float4 v = *reinterpret_cast<const float4*>(&tout[buf][wave][ls][lq]);
+      const float4 v = lds_get4(&tout[buf][wave][ls][lq]);
       if (ls < steps) *reinterpret_cast<float4*>(dst + (b * L + t0 + ls) * D + d0 + lq) = v;
     } else {
       // 16 steps x 32 values; lane takes 8 consecutive ones of one step
-      const int e = lane * 8;
-      const int step = e / (2 * kStates);
+      const int step = lane >> 2, col = (lane & 3) * 8;
+      const int e = step * (2 * kStates) + col;
       float s[8];
 #pragma unroll
       for (int q = 0; q < 8; ++q) s[q] = 0.0f;
 #pragma unroll
       for (int w = 0; w < kWaves; ++w) {
-        const float4 p = *reinterpret_cast<const float4*>(&tbc[buf][w][0][0] + e);
-        const float4 q4 = *reinterpret_cast<const float4*>(&tbc[buf][w][0][0] + e + 4);
+        const float4 p = *reinterpret_cast<const float4*>(&tbc[buf][w][step][col]);
+        const float4 q4 = *reinterpret_cast<const float4*>(&tbc[buf][w][step][col + 4]);
         s[0] += p.x; s[1] += p.y; s[2] += p.z; s[3] += p.w;
         s[4] += q4.x; s[5] += q4.y; s[6] += q4.z; s[7] += q4.w;
       }
@@ -238,11 +267,13 @@ __global__ __launch_bounds__(kBlock) void chain_bwd_kernel(ChainBwdParams prm) {
     float zv = 0.0f;
     if constexpr (kGate) zv = tin[buf][5][n][ch];
     // B_t[n] and C_t[n] of the tile's steps, four at a time from LDS
-    auto b4 = [&](int j) { return *reinterpret_cast<const float4*>(&tin[buf][2][n][4 * j]); };
-    auto c4 = [&](int j) { return *reinterpret_cast<const float4*>(&tin[buf][3][n][4 * j]); };
+    auto b4 = [&](int j) { return lds_get4(&tin[buf][2][n][4 * j]); };
+    auto c4 = [&](int j) { return lds_get4(&tin[buf][3][n][4 * j]); };
     auto el = [](const float4& v, int e) { return e == 0 ? v.x : e == 1 ? v.y : e == 2 ? v.z : v.w; };
     const float gv = kGate ? go * silu(zv) : go;   // g of step n
     const float uv = dv * xv;
+    // a separate copy for the reverse sweep's broadcasts of delta x (see opaque)
+    const float uv_r = opaque(uv);
     // recompute: a_s and h_s
     float a[kTile], hs[kTile];
     float hp = hin;
@@ -257,24 +288,15 @@ __global__ __launch_bounds__(kBlock) void chain_bwd_kernel(ChainBwdParams prm) {
         hp = hs[s];
       }
     }
-    if constexpr (kGate) {   // dz = dout y SiLU'(z), y = C.h + D x, for step n
-      float py[kTile];
-#pragma unroll
-      for (int j = 0; j < kTile / 4; ++j) {
-        const float4 cq = c4(j);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) py[4 * j + e] = el(cq, e) * hs[4 * j + e];
-      }
-      float y = row_reduce_scatter16(py, n);
-      if constexpr (kSkip) y = __builtin_fmaf(Dd, xv, y);
-      tout[buf][2][n][ch] = go * y * silu_grad(zv);
-    }
     // backwards through the tile; dB, dC over the wavefront's four channels
     // per pair of steps: rows 0 / 1 / 2 / 3 end with dB of step 2j / dB of
-    // 2j + 1 / dC of 2j / dC of 2j + 1
-    // p1 = lam B and p2 = lam A a h_{s-1} enter the n-sums: steps 8..15 wait
-    // for their partners 0..7, then both go through the first reduce level
-    float p1h[kTile / 2], p2h[kTile / 2], q1[kTile / 2], q2[kTile / 2];
+    // 2j + 1 / dC of 2j / dC of 2j + 1.
+    // p1 = lam B, p2 = lam A a h_{s-1} (and py = C h for the gate's y) enter
+    // sums over n: steps 8..15 wait for their partners 0..7, then both go
+    // through the first reduce level
+    constexpr int kH = kTile / 2;
+    float p1h[kH], p2h[kH], q1[kH], q2[kH];
+    float p3h[kGate ? kH : 1], q3[kGate ? kH : 1];
     float vb_odd = 0.0f, vc_odd = 0.0f;
     float4 bq = make_float4(0.0f, 0.0f, 0.0f, 0.0f), cq = bq;
 #pragma unroll
@@ -284,21 +306,23 @@ __global__ __launch_bounds__(kBlock) void chain_bwd_kernel(ChainBwdParams prm) {
         cq = c4(s / 4);
       }
       const float Bs = el(bq, s % 4), Cs = el(cq, s % 4);
-      const float gs = row_bcast_dyn(gv, s);
-      const float lam = __builtin_fmaf(Cs, gs, lamn);
+      float lam = lamn;
+      fmac_bcast_dyn(lam, gv, Cs, s);        // lam = C_s g_s + a_{s+1} lam_{s+1}
       lamn = a[s] * lam;
-      const float r = lam * (a[s] * (s > 0 ? hs[s > 0 ? s - 1 : 0] : hin));
-      dA = __builtin_fmaf(r, row_bcast_dyn(dv, s), dA);
+      const float r = lamn * (s > 0 ? hs[s > 0 ? s - 1 : 0] : hin);   // lam a h_{s-1}
+      fmac_bcast_dyn(dA, dv, r, s);
       const float p2 = r * An, p1 = lam * Bs;
-      if (s >= kTile / 2) {
-        p1h[s - kTile / 2] = p1;
-        p2h[s - kTile / 2] = p2;
+      if (s >= kH) {
+        p1h[s - kH] = p1;
+        p2h[s - kH] = p2;
+        if constexpr (kGate) p3h[s - kH] = Cs * hs[s];
       } else {
         q1[s] = rs_first(p1, p1h[s]);
         q2[s] = rs_first(p2, p2h[s]);
+        if constexpr (kGate) q3[s] = rs_first(Cs * hs[s], p3h[s]);
       }
-      const float vb = lam * row_bcast_dyn(uv, s);
-      const float vc = gs * hs[s];
+      const float vb = lam * row_bcast_dyn(uv_r, s);
+      const float vc = row_bcast_dyn(gv, s) * hs[s];
       if (s & 1) {
         vb_odd = vb;
         vc_odd = vc;
@@ -307,6 +331,11 @@ __global__ __launch_bounds__(kBlock) void chain_bwd_kernel(ChainBwdParams prm) {
         const float hi = fold_rows2(vb_odd, vc_odd);
         tbc[buf][wave][s + (row & 1)][(row >> 1) * kStates + n] = fold_rows1(lo, hi);
       }
+    }
+    if constexpr (kGate) {   // dz = dout y SiLU'(z), y = C.h + D x, for step n
+      float y = rs_rest(q3, n);
+      if constexpr (kSkip) y = __builtin_fmaf(Dd, xv, y);
+      tout[buf][2][n][ch] = go * y * silu_grad(zv);
     }
     const float s1 = rs_rest(q1, n);   // sum_n lam B of step n
     const float s2 = rs_rest(q2, n);   // sum_n lam A a h_{t-1} of step n
@@ -331,14 +360,14 @@ __global__ __launch_bounds__(kBlock) void chain_bwd_kernel(ChainBwdParams prm) {
   float hin_next = state_in(tile_of(1));
   int64_t i = 0;
   for (; i + 2 <= ntiles; i += 2) {
-    __syncthreads();
+    block_sync();
     if (i >= 1) store(i - 1);
     put(r1, 1, i + 1);
     load(r1, i + 3);
     compute(i, hin);
     hin = hin_next;
     hin_next = state_in(tile_of(i + 2));
-    __syncthreads();
+    block_sync();
     store(i);
     put(r0, 0, i + 2);
     load(r0, i + 4);
@@ -347,11 +376,11 @@ __global__ __launch_bounds__(kBlock) void chain_bwd_kernel(ChainBwdParams prm) {
     hin_next = state_in(tile_of(i + 3));
   }
   if (i < ntiles) {
-    __syncthreads();
+    block_sync();
     if (i >= 1) store(i - 1);
     compute(i, hin);
   }
-  __syncthreads();
+  block_sync();
   store(last);              // iteration last handles tile 0
   prm.part_a[chain_idx] = dA;
   if (prm.dh0) prm.dh0[chain_idx] = lamn;

@@ -47,10 +47,31 @@ constexpr int kBlock = 64 * kWaves;
 constexpr int kStates = 16;              // N handled by this design
 constexpr int kTile = 16;                // steps per tile = lanes per DPP row
 constexpr int kChannels = 4 * kWaves;    // channels per block
-// LDS row stride (floats) of the [16][16] tiles: rows stay 16-byte aligned
-// and the per-lane column reads (lane (c, n) reads row n, column 4w + c) fall
-// in distinct banks.
+// LDS row stride (floats) of the [16][16] tiles: rows stay 16-byte aligned,
+// so 4-value accesses along a row are single 16-byte ones.  The LDS serves
+// 32 banks of 4 bytes per half wavefront (measured: a stride of 32 words
+// costs as much as 64), so the per-lane column accesses (lane (c, n) at row
+// n, column 4w + c) meet each bank twice; a stride of 18 avoids that but
+// splits the row accesses, and measured slower.
 constexpr int kRow = 20;
+
+// 4 consecutive floats of an LDS tile row, starting at a multiple of 4
+// columns: one 16-byte access when rows are 16-byte aligned, else two 8-byte
+// ones.
+__device__ __forceinline__ float4 lds_get4(const float* p) {
+  if constexpr (kRow % 4 == 0) return *reinterpret_cast<const float4*>(p);
+  const float2 a = *reinterpret_cast<const float2*>(p);
+  const float2 b = *reinterpret_cast<const float2*>(p + 2);
+  return make_float4(a.x, a.y, b.x, b.y);
+}
+__device__ __forceinline__ void lds_put4(float* p, float a, float b, float c, float d) {
+  if constexpr (kRow % 4 == 0) {
+    *reinterpret_cast<float4*>(p) = make_float4(a, b, c, d);
+  } else {
+    *reinterpret_cast<float2*>(p) = make_float2(a, b);
+    *reinterpret_cast<float2*>(p + 2) = make_float2(c, d);
+  }
+}
 
 template <int kCtrl>
 __device__ __forceinline__ float dpp(float v) {
@@ -77,6 +98,16 @@ __device__ __forceinline__ float row_bcast_dyn(float v, int s) {
     case 12: return row_bcast<12>(v); case 13: return row_bcast<13>(v);
     case 14: return row_bcast<14>(v); default: return row_bcast<15>(v);
   }
+}
+
+// The same value under a name the compiler cannot see through (no
+// instruction).  A DPP move is folded into its consumer only when every use
+// of it can take the DPP operand; broadcasting separate copies for separate
+// consumers keeps each move single-use, where otherwise one shared move would
+// be kept in a register per step of the tile and cost an instruction.
+__device__ __forceinline__ float opaque(float v) {
+  asm volatile("" : "+v"(v));
+  return v;
 }
 
 // Row total of p[i], scattered: lane n of each DPP row returns the sum over
@@ -266,7 +297,7 @@ __global__ __launch_bounds__(kBlock) void chain_scan_kernel(ChainParams prm) {
     unpack_raw(r.v, esz, v);
     if (wave == 1 && k == last && pad_lane) v[0] = v[1] = v[2] = v[3] = 0.0f;   // delta
     if (wave < 2) {
-      *reinterpret_cast<float4*>(&tin[buf][wave][ls][lq]) = make_float4(v[0], v[1], v[2], v[3]);
+      lds_put4(&tin[buf][wave][ls][lq], v[0], v[1], v[2], v[3]);
     } else {
 #pragma unroll
       for (int i = 0; i < 4; ++i) tin[buf][wave][lq + i][ls] = v[i];
@@ -274,13 +305,13 @@ __global__ __launch_bounds__(kBlock) void chain_scan_kernel(ChainParams prm) {
     if constexpr (V::kGate) {
       if (wave == 0) {
         unpack_raw(r.zv, sizeof(TX), v);
-        *reinterpret_cast<float4*>(&tin[buf][4][ls][lq]) = make_float4(v[0], v[1], v[2], v[3]);
+        lds_put4(&tin[buf][4][ls][lq], v[0], v[1], v[2], v[3]);
       }
     }
   };
   auto store_y = [&](int64_t k) {
     if constexpr (kCk) return;
-    const float4 v = *reinterpret_cast<const float4*>(&tout[k & 1][ls][lq]);
+    const float4 v = lds_get4(&tout[k & 1][ls][lq]);
     if (k == last && ls >= tail_steps) return;
     const int64_t step_bytes = k * kTile * D * static_cast<int64_t>(sizeof(TY));
     if constexpr (sizeof(TY) == 4) {
@@ -306,7 +337,7 @@ __global__ __launch_bounds__(kBlock) void chain_scan_kernel(ChainParams prm) {
     float Bt[kTile];
 #pragma unroll
     for (int j = 0; j < kTile / 4; ++j) {
-      const float4 vb = *reinterpret_cast<const float4*>(&tin[buf][2][n][4 * j]);
+      const float4 vb = lds_get4(&tin[buf][2][n][4 * j]);
       Bt[4 * j] = vb.x; Bt[4 * j + 1] = vb.y; Bt[4 * j + 2] = vb.z; Bt[4 * j + 3] = vb.w;
     }
     const float uv = dv * xv;
@@ -328,8 +359,8 @@ __global__ __launch_bounds__(kBlock) void chain_scan_kernel(ChainParams prm) {
     float Bt[kTile], Ct[kTile];
 #pragma unroll
     for (int j = 0; j < kTile / 4; ++j) {
-      const float4 vb = *reinterpret_cast<const float4*>(&tin[buf][2][n][4 * j]);
-      const float4 vc = *reinterpret_cast<const float4*>(&tin[buf][3][n][4 * j]);
+      const float4 vb = lds_get4(&tin[buf][2][n][4 * j]);
+      const float4 vc = lds_get4(&tin[buf][3][n][4 * j]);
       Bt[4 * j] = vb.x; Bt[4 * j + 1] = vb.y; Bt[4 * j + 2] = vb.z; Bt[4 * j + 3] = vb.w;
       Ct[4 * j] = vc.x; Ct[4 * j + 1] = vc.y; Ct[4 * j + 2] = vc.z; Ct[4 * j + 3] = vc.w;
     }
@@ -368,23 +399,23 @@ __global__ __launch_bounds__(kBlock) void chain_scan_kernel(ChainParams prm) {
   load(r0, 2 < last ? 2 : last);
   int64_t k = 0;
   for (; k + 2 <= ntiles; k += 2) {
-    __syncthreads();
+    block_sync();
     if (k >= 1 && wave == ((k - 1) & 3)) store_y(k - 1);
     put(r1, 1, k + 1);
     load(r1, k + 3 < last ? k + 3 : last);
     compute(k);
-    __syncthreads();
+    block_sync();
     if (wave == (k & 3)) store_y(k);
     put(r0, 0, k + 2);
     load(r0, k + 4 < last ? k + 4 : last);
     compute(k + 1);
   }
   if (k < ntiles) {
-    __syncthreads();
+    block_sync();
     if (k >= 1 && wave == ((k - 1) & 3)) store_y(k - 1);
     compute(k);
   }
-  __syncthreads();
+  block_sync();
   if (wave == (last & 3)) store_y(last);
   if constexpr (V::kState) prm.h_last[chain_idx] = h;
 }

@@ -462,9 +462,9 @@ __global__ __launch_bounds__(kFBlock) void dtproj_softplus_kernel(
   for (int t = 0; t < kDtRowTiles; ++t) {
     const int64_t m0 = first + 32 * t;
     if (m0 >= M) break;                        // uniform over the block
-    __syncthreads();                           // the previous tile's LDS reads are done
+    block_sync();                           // the previous tile's LDS reads are done
     stash();
-    __syncthreads();
+    block_sync();
     if (t + 1 < kDtRowTiles && m0 + 32 < M) fetch(m0 + 32);   // in flight during this tile
     if (c0 >= D) continue;                     // a wavefront past the last channel only copies
     f32x16 acc = f32x16{};

@@ -19,6 +19,17 @@ namespace mssm {
 
 constexpr float kLog2e = 1.4426950408889634f;
 
+// Block-wide barrier that first waits until this wavefront's LDS operations
+// have completed.  The compiler's own lowering of __syncthreads can leave out
+// that wait on gfx950 (which can back off a barrier): in a loop whose body
+// ends with an LDS store and starts with a barrier, the store issued before
+// the back edge was still in flight when other wavefronts passed the barrier
+// and read the tile, which then held stale values now and then.
+__device__ __forceinline__ void block_sync() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __syncthreads();
+}
+
 // ---- element access: float32, or bfloat16 stored as uint16_t ----------------------------
 
 __device__ __forceinline__ float to_float(float v) { return v; }
