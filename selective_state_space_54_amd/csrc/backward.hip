@@ -324,21 +324,64 @@ __global__ __launch_bounds__(kBwdBlock) void bwd_chunk_kernel(
   if (kSkip && active) p.partD[(b * p.K + k) * D + d] = dD;
 }
 
-// dB[r, n] and dC[r, n] (r = b * L + t): the sum of the wavefront partials.
-__global__ void bwd_reduce_bc_kernel(const float* __restrict__ part, float* __restrict__ dB,
-                                     float* __restrict__ dC, int64_t rows, int N, int64_t n_wt) {
+// dB[r, n] and dC[r, n] (r = b * L + t): the sum of the n_wt partials
+// part[w * total + e], added in w order.  When total is a multiple of 4 a
+// thread takes 4 adjacent outputs (16-byte loads) and issues 8 partials'
+// loads before adding them, so enough reads are in flight to stream the
+// partials at HBM rate.
+constexpr int kBcUnroll = 8;
+__global__ __launch_bounds__(256) void bwd_reduce_bc_kernel(const float* __restrict__ part,
+                                                            float* __restrict__ dB,
+                                                            float* __restrict__ dC, int64_t rows,
+                                                            int N, int64_t n_wt) {
   const int64_t total = rows * 2 * N;
-  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total;
-       e += (int64_t)gridDim.x * blockDim.x) {
-    float s = 0.0f;
-    for (int64_t w = 0; w < n_wt; ++w) s += part[w * total + e];
+  const bool vec = total % 4 == 0;
+  const int64_t groups = vec ? total / 4 : total;
+  auto emit = [&](int64_t e, float v) {
     const int64_t r = e / (2 * N);
     const int c = static_cast<int>(e % (2 * N));
     if (c < N)
-      dB[r * N + c] = s;
+      dB[r * N + c] = v;
     else
-      dC[r * N + c - N] = s;
+      dC[r * N + c - N] = v;
+  };
+  for (int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; g < groups;
+       g += (int64_t)gridDim.x * blockDim.x) {
+    if (vec) {
+      const float4* p = reinterpret_cast<const float4*>(part) + g;
+      const int64_t stride = total / 4;
+      float4 s = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+      int64_t w = 0;
+      for (; w + kBcUnroll <= n_wt; w += kBcUnroll) {
+        float4 v[kBcUnroll];
+#pragma unroll
+        for (int u = 0; u < kBcUnroll; ++u) v[u] = p[(w + u) * stride];
+#pragma unroll
+        for (int u = 0; u < kBcUnroll; ++u) {
+          s.x += v[u].x; s.y += v[u].y; s.z += v[u].z; s.w += v[u].w;
+        }
+      }
+      for (; w < n_wt; ++w) {
+        const float4 v = p[w * stride];
+        s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
+      }
+      emit(4 * g, s.x);
+      emit(4 * g + 1, s.y);
+      emit(4 * g + 2, s.z);
+      emit(4 * g + 3, s.w);
+    } else {
+      float s = 0.0f;
+      for (int64_t w = 0; w < n_wt; ++w) s += part[w * total + g];
+      emit(g, s);
+    }
   }
+}
+
+// Grid of the kernel above for `rows` rows of 2N outputs.
+inline unsigned reduce_bc_grid(int64_t rows, int64_t N) {
+  const int64_t total = rows * 2 * N;
+  const int64_t groups = total % 4 == 0 ? total / 4 : total;
+  return static_cast<unsigned>(std::max<int64_t>(1, std::min<int64_t>((groups + 255) / 256, 8192)));
 }
 
 // out[e] = sum_r part[r * count + e], r < nparts.  A block takes 16 outputs;
@@ -453,8 +496,8 @@ hipError_t launch_bwd_t(const BwdArgs& a, const BwdPlan& bp, char* ws, hipStream
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   // 4. sums of the partials
-  hipLaunchKernelGGL(bwd_reduce_bc_kernel, dim3(2048), dim3(256), 0, stream, p.partBC, a.dB,
-                     a.dC, a.batch * a.L, static_cast<int>(a.N), p.n_wt);
+  hipLaunchKernelGGL(bwd_reduce_bc_kernel, dim3(reduce_bc_grid(a.batch * a.L, a.N)), dim3(256), 0,
+                     stream, p.partBC, a.dB, a.dC, a.batch * a.L, static_cast<int>(a.N), p.n_wt);
   const int64_t da_count = a.D * a.N;
   hipLaunchKernelGGL(bwd_reduce_rows_kernel, dim3((unsigned)((da_count + kRedCols - 1) / kRedCols)),
                      dim3(kRedCols * kRedGroups), 0, stream, p.partA, a.dA, da_count,
@@ -533,8 +576,8 @@ hipError_t launch_bwd(const BwdArgs& a, const BwdPlan& bp, void* workspace, hipS
                                     part_a, part_d, stream);
     if (e != hipSuccess) return e;
     // per-block dB/dC partials, per-batch-row dA / dD partials, in a fixed order
-    hipLaunchKernelGGL(bwd_reduce_bc_kernel, dim3(2048), dim3(256), 0, stream, part_bc, a.dB,
-                       a.dC, a.batch * a.L, static_cast<int>(a.N), a.D / 16);
+    hipLaunchKernelGGL(bwd_reduce_bc_kernel, dim3(reduce_bc_grid(a.batch * a.L, a.N)), dim3(256), 0,
+                       stream, part_bc, a.dB, a.dC, a.batch * a.L, static_cast<int>(a.N), a.D / 16);
     const int64_t da_count = a.D * a.N;
     hipLaunchKernelGGL(bwd_reduce_rows_kernel,
                        dim3((unsigned)((da_count + kRedCols - 1) / kRedCols)),

@@ -217,37 +217,30 @@ __global__ __launch_bounds__(kBlock) void chain_bwd_kernel(ChainBwdParams prm) {
   };
 
   // Stores of a finished tile (iteration i, buffer buf): wavefront 0 dx,
-  // 1 ddelta, 2 dz, 3 the block's dB/dC partial.
+  // 1 ddelta, 2 dz; and each wavefront sums the four wavefronts' dB/dC
+  // values of 4 of the tile's steps into the block's partial.
   auto store = [&](int64_t i) {
     const int buf = i & 1;
     const int64_t kt = tile_of(i);
     const int64_t t0 = kt * kTile;
     const int steps = kt == last ? tail_steps : kTile;
-    if (wave < 3) {
-      if (wave == 2 && !kGate) return;
+    if (wave < 2 || (kGate && wave == 2)) {
       float* dst = wave == 0 ? prm.dx : (wave == 1 ? prm.ddelta : prm.dz);
       const float4 v = lds_get4(&tout[buf][wave][ls][lq]);
       if (ls < steps) *reinterpret_cast<float4*>(dst + (b * L + t0 + ls) * D + d0 + lq) = v;
-    } else {
-      // 16 steps x 32 values; lane takes 8 consecutive ones of one step
-      const int step = lane >> 2, col = (lane & 3) * 8;
-      const int e = step * (2 * kStates) + col;
-      float s[8];
-#pragma unroll
-      for (int q = 0; q < 8; ++q) s[q] = 0.0f;
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        const float4 p = *reinterpret_cast<const float4*>(&tbc[buf][w][step][col]);
-        const float4 q4 = *reinterpret_cast<const float4*>(&tbc[buf][w][step][col + 4]);
-        s[0] += p.x; s[1] += p.y; s[2] += p.z; s[3] += p.w;
-        s[4] += q4.x; s[5] += q4.y; s[6] += q4.z; s[7] += q4.w;
-      }
-      if (step < steps) {
-        float* dst = prm.part_bc + ((dg * (gridDim.x / n_dgroups) + b) * L + t0) * (2 * kStates) + e;
-        *reinterpret_cast<float4*>(dst) = make_float4(s[0], s[1], s[2], s[3]);
-        *reinterpret_cast<float4*>(dst + 4) = make_float4(s[4], s[5], s[6], s[7]);
-      }
     }
+    const int step = wave * 4 + (lane >> 4), col = (lane & 15) * 2;
+    float2 sum = *reinterpret_cast<const float2*>(&tbc[buf][0][step][col]);
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) {
+      const float2 v = *reinterpret_cast<const float2*>(&tbc[buf][w][step][col]);
+      sum.x += v.x;
+      sum.y += v.y;
+    }
+    if (step < steps)
+      *reinterpret_cast<float2*>(prm.part_bc +
+                                 ((dg * (gridDim.x / n_dgroups) + b) * L + t0 + step) *
+                                     (2 * kStates) + col) = sum;
   };
 
   // state entering a tile: h0 (or 0) for tile 0, else the checkpoint
