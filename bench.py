@@ -382,9 +382,10 @@ def time_backward(name, steps, warmup, torch, mssm, workloads, parts=True):
     torch.cuda.empty_cache()
     return {"kernel_ms": round(kernel_ms, 4),
             "Gelem/s": round(elements(w) / (kernel_ms * 1e-3) / 1e9, 1),
-            "note": "backward of the scan with Dskip, z gate and h0: forward chunk summaries "
-                    "+ carries, reverse summaries + carries, per-chunk recompute and "
-                    "reverse sweep, partial-sum reductions"}
+            "note": "backward of the scan with Dskip, z gate and h0; at this shape the single-"
+                    "pass order: a forward pass storing the state after every 16-step tile, "
+                    "one reverse kernel recomputing each tile from its checkpoint, and the "
+                    "fixed-order partial-sum reductions"}
 
 
 def cpu_baseline(name, workloads, oracle, threads):

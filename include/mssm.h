@@ -292,9 +292,18 @@ mssm_status mssm_mamba_block_fwd(const void *u0, const void *W_in, const float *
  * A, B, C, Dskip, z, h0) with the first-order input term (MSSM_BBAR_EULER), by
  * the chain rule through the recurrence (the adjoint lam_t = C_t g_t +
  * a_{t+1} lam_{t+1} is a reverse scan).  The states are recomputed from the
- * inputs, never stored: the call re-runs the forward chunk summaries, runs the
- * adjoint's chunk summaries in reverse, then recomputes each 16-step chunk's
- * states in registers while sweeping it backwards.
+ * inputs, never stored in full ("State Space Models and Mamba", the
+ * hardware-aware scan recomputes them for the backward pass).  Two orders,
+ * chosen like the forward scan's (MSSM_SCAN_DESIGN, shape and alignment):
+ *   single pass (N = 16, D % 16 == 0, 16-byte aligned float32 / 8-byte
+ *     aligned bfloat16 inputs and float32 gradients, at least 8192 channels
+ *     batch * D): one forward pass stores the state after every 16-step tile
+ *     in the workspace, then one kernel walks the tiles backwards,
+ *     recomputing each tile's states from its checkpoint while sweeping the
+ *     adjoint;
+ *   chunked (every other case): re-runs the forward chunk summaries, runs the
+ *     adjoint's chunk summaries in reverse, then recomputes each 16-step
+ *     chunk's states in registers while sweeping it backwards.
  *
  *   dout            : [batch, L, D] float32 (the gradient of the float32 y)
  *   dx, ddelta, dz  : [batch, L, D] float32
@@ -306,7 +315,8 @@ mssm_status mssm_mamba_block_fwd(const void *u0, const void *W_in, const float *
  * dA and dDskip (sums over batch and time) and dB, dC (sums over channels)
  * are formed from partial sums in a fixed order: results are deterministic.
  * The workspace (256-byte aligned, mssm_selective_scan_bwd_workspace_size
- * bytes) holds the chunk summaries of both directions and the partial sums.
+ * bytes, enough for either order) holds the checkpoints or the chunk
+ * summaries of both directions, and the partial sums.
  * With batch, L or D equal to zero the gradients that still have elements are
  * set to zero.
  */
