@@ -388,6 +388,70 @@ def time_backward(name, steps, warmup, torch, mssm, workloads, parts=True):
                     "fixed-order partial-sum reductions"}
 
 
+def time_train_pair(name, steps, warmup, torch, mssm, workloads):
+    """One training pair on the workload with feedthrough, gate and initial
+    state: forward then backward, timed (a) as mssm_selective_scan_fwd_ex +
+    mssm_selective_scan_bwd (the backward recomputes its checkpoints and the
+    pre-gate output) and (b) as mssm_selective_scan_fwd_save +
+    mssm_selective_scan_bwd_saved (the forward saves them)."""
+    w = workloads.workload(name)
+    g = workloads.generate(name)
+    d = device_inputs(g, torch)
+    e = workloads.generate_extras(w)
+    opt = {k: _to_device(e[k], torch) for k in ("Dskip", "z", "h0")}
+    del g, e
+    dout = torch.randn((w.batch, w.L, w.D), device="cuda")
+    opts = dict(device="cuda", dtype=torch.float32)
+    y = torch.empty((w.batch, w.L, w.D), **opts)
+    grads = {"dx": torch.empty((w.batch, w.L, w.D), **opts),
+             "ddelta": torch.empty((w.batch, w.L, w.D), **opts),
+             "dA": torch.empty((w.D, w.N), **opts), "dB": torch.empty((w.batch, w.L, w.N), **opts),
+             "dC": torch.empty((w.batch, w.L, w.N), **opts), "dD": torch.empty((w.D,), **opts),
+             "dz": torch.empty((w.batch, w.L, w.D), **opts),
+             "dh0": torch.empty((w.batch, w.D, w.N), **opts)}
+    nb = mssm.mssm_selective_scan_bwd_workspace_size(w.batch, w.L, w.D, w.N, d["x"].dtype)
+    ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    nf = mssm.mssm_selective_scan_workspace_size(w.batch, w.L, w.D, w.N, d["x"].dtype)
+    wsf = torch.empty(max(nf, 1), dtype=torch.uint8, device="cuda")
+    ns = mssm.mssm_selective_scan_saved_size(w.batch, w.L, w.D, w.N, True)
+    saved = torch.empty(ns, dtype=torch.uint8, device="cuda")
+    args = (d["x"], d["delta"], d["A"], d["B"], d["C"])
+
+    def recompute():
+        mssm.mssm_selective_scan_fwd_ex(*args, y, wsf, **opt)
+        mssm.mssm_selective_scan_bwd(*args, dout, grads, ws, **opt)
+
+    def with_saved():
+        mssm.mssm_selective_scan_fwd_save(*args, y, saved, **opt)
+        mssm.mssm_selective_scan_bwd_saved(*args, saved, dout, grads, ws, **opt)
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        stream = torch.cuda.current_stream()
+        s_ev = torch.cuda.Event(enable_timing=True)
+        e_ev = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        s_ev.record(stream)
+        for _ in range(steps):
+            fn()
+        e_ev.record(stream)
+        torch.cuda.synchronize()
+        return s_ev.elapsed_time(e_ev) / steps
+
+    ms_re = timed(recompute)
+    ms_saved = timed(with_saved)
+    fwd_save_ms = timed(lambda: mssm.mssm_selective_scan_fwd_save(*args, y, saved, **opt))
+    del d, opt, dout, grads, ws, wsf, saved, y
+    torch.cuda.empty_cache()
+    return {"recompute_ms": round(ms_re, 4), "saved_ms": round(ms_saved, 4),
+            "fwd_save_ms": round(fwd_save_ms, 4),
+            "Gelem/s (saved)": round(elements(w) / (ms_saved * 1e-3) / 1e9, 1),
+            "note": "forward + backward with Dskip, z gate and h0; saved: the forward also "
+                    "writes the state after every 16-step tile and the output before the "
+                    "gate, which the backward reads instead of recomputing"}
+
+
 def cpu_baseline(name, workloads, oracle, threads):
     """The float64 oracle on the host cores, on the whole headline workload."""
     g = workloads.generate(name)
@@ -423,7 +487,7 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", default=None,
                     choices=["fused_proj_bf16", "scan_ex", "decode_step_bf16", "conv1d_silu_fp32",
-                             "mamba_block_bf16", "backward"],
+                             "mamba_block_bf16", "backward", "train_pair"],
                     help="time only this extra workload and print its record (for profiling)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (5 times) and exit; "
@@ -465,6 +529,8 @@ def main(argv=None):
             rec = time_conv(torch, mssm, steps=args.steps, warmup=args.warmup)
         elif args.only == "backward":
             rec = time_backward(HEADLINE, args.steps, args.warmup, torch, mssm, workloads)
+        elif args.only == "train_pair":
+            rec = time_train_pair(HEADLINE, args.steps, args.warmup, torch, mssm, workloads)
         else:
             rec = time_block(args.only, args.steps, args.warmup, torch, mssm, workloads)
         print(json.dumps({"only": args.only, **rec}), flush=True)
@@ -536,6 +602,8 @@ def main(argv=None):
         others["mamba_block_bf16"] = time_block("mamba_block_bf16", 5, 2, torch, mssm, workloads)
         others["backward mamba130m_layer_fp32"] = time_backward(HEADLINE, 5, 2, torch, mssm,
                                                                 workloads)
+        others["forward + backward mamba130m_layer_fp32"] = time_train_pair(
+            HEADLINE, 5, 2, torch, mssm, workloads)
         line["workloads"] = others
     if not args.no_cpu_baseline:
         import oracle

@@ -331,6 +331,59 @@ mssm_status mssm_selective_scan_bwd(const void *x, const void *delta, const floa
                                     int64_t batch, int64_t L, int64_t D, int64_t N,
                                     mssm_dtype dtype, void *stream);
 
+/*
+ * ---- forward and backward sharing saved states (training) -------------------------------
+ *
+ * The backward pass needs the states h_t, which it recomputes ("State Space
+ * Models and Mamba", hardware-aware scan: the backward recomputes the states
+ * rather than reading them from memory); the single-pass order restarts that
+ * recomputation from checkpoints, the state after every 16-step tile.
+ * mssm_selective_scan_bwd writes them with a forward pass of its own.  In
+ * training the forward call is made anyway, so mssm_selective_scan_fwd_save
+ * writes them there, together with, when z is given, the output before the
+ * gate (C . h + Dskip x, which the gate's gradient needs), and
+ * mssm_selective_scan_bwd_saved reads them instead of recomputing.
+ *
+ * Only the single-pass layout has this form: N = 16, D % 16 == 0, float32
+ * x / delta / B / C / z 16-byte aligned (bfloat16: 8-byte), y, dout and the
+ * float32 gradients dx, ddelta, dz 16-byte aligned; any channel count.  Other
+ * shapes give MSSM_ERROR_NOT_SUPPORTED (use mssm_selective_scan_fwd_ex and
+ * mssm_selective_scan_bwd), as do unaligned pointers.
+ *
+ * mssm_selective_scan_saved_size: bytes of the saved buffer for this shape,
+ *   with (gate != 0) or without the gate; 0 for shapes without this form.
+ * mssm_selective_scan_fwd_save: y (and h_last) exactly as
+ *   mssm_selective_scan_fwd_ex with MSSM_BBAR_EULER and the same optional
+ *   parts, and the saved tensors, in `saved` (float32, 256-byte aligned, at
+ *   least saved_size bytes, caller-owned): states [batch, ceil(L/16), D, N]
+ *   (the state after tile j, j < ceil(L/16) - 1; the last tile's slot is not
+ *   written), then with z the output before the gate [batch, L, D].  Needs
+ *   no workspace.  L == 0 only sets h_last = h0 (or zero).
+ * mssm_selective_scan_bwd_saved: the gradients of mssm_selective_scan_bwd
+ *   (same arguments, same workspace size query) from `saved` as written by
+ *   mssm_selective_scan_fwd_save for the same inputs, Dskip, z and h0.  A
+ *   buffer written for other inputs gives wrong gradients; one too small or
+ *   unaligned gives MSSM_ERROR_WORKSPACE.
+ */
+mssm_status mssm_selective_scan_saved_size(int64_t batch, int64_t L, int64_t D, int64_t N,
+                                           int gate, size_t *bytes);
+
+mssm_status mssm_selective_scan_fwd_save(const void *x, const void *delta, const float *A,
+                                         const void *B, const void *C, const float *Dskip,
+                                         const void *z, const float *h0, float *y,
+                                         float *h_last, float *saved, size_t saved_bytes,
+                                         int64_t batch, int64_t L, int64_t D, int64_t N,
+                                         mssm_dtype dtype, void *stream);
+
+mssm_status mssm_selective_scan_bwd_saved(const void *x, const void *delta, const float *A,
+                                          const void *B, const void *C, const float *Dskip,
+                                          const void *z, const float *h0, const float *saved,
+                                          size_t saved_bytes, const float *dout, float *dx,
+                                          float *ddelta, float *dA, float *dB, float *dC,
+                                          float *dDskip, float *dz, float *dh0, void *workspace,
+                                          size_t workspace_bytes, int64_t batch, int64_t L,
+                                          int64_t D, int64_t N, mssm_dtype dtype, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -560,6 +560,19 @@ BwdPlan plan_bwd(int64_t batch, int64_t L, int64_t D, int64_t N, bool chain) {
   return b;
 }
 
+SavedLayout saved_layout(int64_t batch, int64_t L, int64_t D, int64_t N, bool gate) {
+  SavedLayout s;
+  if (N != 16 || D % 16 != 0 || batch <= 0 || L <= 0 || D <= 0) return s;
+  const size_t tiles = (size_t)((L + 15) / 16);
+  s.ck_offset = 0;
+  s.bytes = align256(sizeof(float) * (size_t)batch * tiles * (size_t)D * (size_t)N);
+  if (gate) {
+    s.y_pre_offset = s.bytes;
+    s.bytes += align256(sizeof(float) * (size_t)batch * (size_t)L * (size_t)D);
+  }
+  return s;
+}
+
 size_t bwd_workspace_bound(int64_t batch, int64_t L, int64_t D, int64_t N) {
   size_t w = plan_bwd(batch, L, D, N, false).workspace_bytes;
   if (N == 16 && D % 16 == 0) w = std::max(w, plan_bwd(batch, L, D, N, true).workspace_bytes);
@@ -572,8 +585,9 @@ hipError_t launch_bwd(const BwdArgs& a, const BwdPlan& bp, void* workspace, hipS
     float* part_bc = reinterpret_cast<float*>(ws + bp.part_bc_offset);
     float* part_a = reinterpret_cast<float*>(ws + bp.part_a_offset);
     float* part_d = reinterpret_cast<float*>(ws + bp.part_d_offset);
-    hipError_t e = launch_chain_bwd(a, reinterpret_cast<float*>(ws + bp.ck_offset), part_bc,
-                                    part_a, part_d, stream);
+    const bool saved = a.saved_ck != nullptr;
+    float* ck = saved ? const_cast<float*>(a.saved_ck) : reinterpret_cast<float*>(ws + bp.ck_offset);
+    hipError_t e = launch_chain_bwd(a, ck, a.saved_y_pre, saved, part_bc, part_a, part_d, stream);
     if (e != hipSuccess) return e;
     // per-block dB/dC partials, per-batch-row dA / dD partials, in a fixed order
     hipLaunchKernelGGL(bwd_reduce_bc_kernel, dim3(reduce_bc_grid(a.batch * a.L, a.N)), dim3(256), 0,

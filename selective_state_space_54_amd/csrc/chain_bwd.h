@@ -40,6 +40,7 @@ struct ChainBwdParams {
   const float* h0;          // or null
   const float* dout;        // [batch, L, D]
   const float* ck;          // [batch, tiles, D, N]: state after each tile (the last unused)
+  const float* y_pre;       // [batch, L, D] output before the gate (saved forward), or null
   float* dx;                // [batch, L, D]
   float* ddelta;
   float* dz;                // with z
@@ -134,11 +135,14 @@ __device__ __forceinline__ void fmac_bcast_dyn(float& acc, float v, float m, int
 constexpr int kBcRow = 48;   // floats per step row of the dB | dC partial tile
 
 // grid: batch * D / 16 blocks of kBlock lanes.
-template <typename T, bool kSkip, bool kGate>
+// kSaved: the checkpoints come from the forward call, and with the gate so
+// does y_pre, which then replaces this kernel's own read-out of y.
+template <typename T, bool kSkip, bool kGate, bool kSaved>
 __global__ __launch_bounds__(kBlock) void chain_bwd_kernel(ChainBwdParams prm) {
+  constexpr bool kPre = kSaved && kGate;   // y_pre read, not recomputed
   // inputs [buffer][x, delta, B^T, C^T, dout, z]; outputs [buffer][dx, ddelta, dz];
   // dB/dC partials [buffer][wavefront][step][dB n | dC n]
-  __shared__ __align__(16) float tin[2][6][kTile][kRow];
+  __shared__ __align__(16) float tin[2][kPre ? 7 : 6][kTile][kRow];
   __shared__ __align__(16) float tout[2][3][kTile][kRow];
   // (rows of kBcRow floats: the two steps a wavefront writes at once then
   // land 16 banks apart)
@@ -163,7 +167,8 @@ __global__ __launch_bounds__(kBlock) void chain_bwd_kernel(ChainBwdParams prm) {
   const int64_t last = ntiles - 1;
   const int tail_steps = static_cast<int>(L - last * kTile);
 
-  // Loads: wavefront 0 x (and z), 1 delta and dout, 2 B, 3 C; 4 values per lane.
+  // Loads: wavefront 0 x (and z), 1 delta and dout, 2 B (and y_pre), 3 C; 4
+  // values per lane.
   const int ls = lane >> 2, lq = (lane & 3) * 4;
   const int ls_tail = ls < tail_steps ? ls : tail_steps - 1;
   const char* src;
@@ -180,6 +185,10 @@ __global__ __launch_bounds__(kBlock) void chain_bwd_kernel(ChainBwdParams prm) {
   } else {
     src = static_cast<const char*>(wave == 2 ? prm.B : prm.C) + b * L * kStates * sizeof(T);
     rs = kStates;
+    if (kPre && wave == 2) {
+      src2 = reinterpret_cast<const char*>(prm.y_pre + b * L * D + d0);
+      esz2 = 4;
+    }
   }
   const int64_t rs_bytes = rs * esz;
   const uint32_t off_full = static_cast<uint32_t>(ls * rs_bytes + lq * esz);
@@ -187,7 +196,7 @@ __global__ __launch_bounds__(kBlock) void chain_bwd_kernel(ChainBwdParams prm) {
   const uint32_t off2_full = static_cast<uint32_t>((ls * D + lq) * esz2);
   const uint32_t off2_tail = static_cast<uint32_t>((ls_tail * D + lq) * esz2);
   const int64_t tile_bytes = kTile * rs_bytes, tile_bytes2 = kTile * D * esz2;
-  const bool has2 = wave == 1 || (kGate && wave == 0);
+  const bool has2 = wave == 1 || (kGate && wave == 0) || (kPre && wave == 2);
 
   struct Regs {
     uint4 v, v2;
@@ -213,6 +222,7 @@ __global__ __launch_bounds__(kBlock) void chain_bwd_kernel(ChainBwdParams prm) {
     } else {
 #pragma unroll
       for (int q = 0; q < 4; ++q) tin[buf][wave][lq + q][ls] = v[q];
+      if (kPre && wave == 2) lds_put4(&tin[buf][6][ls][lq], w[0], w[1], w[2], w[3]);
     }
   };
 
@@ -308,11 +318,11 @@ __global__ __launch_bounds__(kBlock) void chain_bwd_kernel(ChainBwdParams prm) {
       if (s >= kH) {
         p1h[s - kH] = p1;
         p2h[s - kH] = p2;
-        if constexpr (kGate) p3h[s - kH] = Cs * hs[s];
+        if constexpr (kGate && !kPre) p3h[s - kH] = Cs * hs[s];
       } else {
         q1[s] = rs_first(p1, p1h[s]);
         q2[s] = rs_first(p2, p2h[s]);
-        if constexpr (kGate) q3[s] = rs_first(Cs * hs[s], p3h[s]);
+        if constexpr (kGate && !kPre) q3[s] = rs_first(Cs * hs[s], p3h[s]);
       }
       const float vb = lam * row_bcast_dyn(uv_r, s);
       const float vc = row_bcast_dyn(gv, s) * hs[s];
@@ -325,7 +335,9 @@ __global__ __launch_bounds__(kBlock) void chain_bwd_kernel(ChainBwdParams prm) {
         tbc[buf][wave][s + (row & 1)][(row >> 1) * kStates + n] = fold_rows1(lo, hi);
       }
     }
-    if constexpr (kGate) {   // dz = dout y SiLU'(z), y = C.h + D x, for step n
+    if constexpr (kPre) {    // dz = dout y SiLU'(z) with the forward's y = C.h + D x
+      tout[buf][2][n][ch] = go * tin[buf][6][n][ch] * silu_grad(zv);
+    } else if constexpr (kGate) {   // the same with y read out here
       float y = rs_rest(q3, n);
       if constexpr (kSkip) y = __builtin_fmaf(Dd, xv, y);
       tout[buf][2][n][ch] = go * y * silu_grad(zv);
@@ -385,10 +397,10 @@ __global__ __launch_bounds__(kBlock) void chain_bwd_kernel(ChainBwdParams prm) {
   }
 }
 
-template <typename T, bool kSkip, bool kGate>
+template <typename T, bool kSkip, bool kGate, bool kSaved>
 hipError_t launch_bwd_chain_t(const ChainBwdParams& p, int64_t batch, hipStream_t stream) {
   const dim3 grid(static_cast<unsigned>(batch * (p.D / kChannels)));
-  hipLaunchKernelGGL((chain_bwd_kernel<T, kSkip, kGate>), grid, dim3(kBlock), 0, stream, p);
+  hipLaunchKernelGGL((chain_bwd_kernel<T, kSkip, kGate, kSaved>), grid, dim3(kBlock), 0, stream, p);
   return hipGetLastError();
 }
 

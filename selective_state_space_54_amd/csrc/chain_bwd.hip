@@ -11,15 +11,29 @@ namespace {
 
 bool aligned(const void* p, size_t a) { return reinterpret_cast<uintptr_t>(p) % a == 0; }
 
+template <typename T, bool kSaved>
+hipError_t launch_parts(const chain::ChainBwdParams& p, const BwdArgs& a, hipStream_t stream) {
+  const bool skip = a.Dskip != nullptr, gate = a.z != nullptr;
+  if (skip && gate) return chain::launch_bwd_chain_t<T, true, true, kSaved>(p, a.batch, stream);
+  if (skip) return chain::launch_bwd_chain_t<T, true, false, kSaved>(p, a.batch, stream);
+  if (gate) return chain::launch_bwd_chain_t<T, false, true, kSaved>(p, a.batch, stream);
+  return chain::launch_bwd_chain_t<T, false, false, kSaved>(p, a.batch, stream);
+}
+
+// saved: the checkpoints in ck (and y_pre with the gate) come from the
+// forward call; else the checkpoint pass writes ck first.
 template <typename T>
-hipError_t launch_typed(const BwdArgs& a, float* ck, float* part_bc, float* part_a, float* part_d,
-                        hipStream_t stream) {
-  chain::ChainParams cp{a.x,     a.delta, a.B,     a.C,     nullptr, a.A, nullptr, a.h0,
-                        nullptr, nullptr, nullptr, a.L,     a.D,     chain::kStates};
-  cp.ck = ck;
-  hipError_t e = chain::launch_io<chain::ChainIO<T, T, T, float>, PlainVariant, true>(
-      cp, a.batch, stream);
-  if (e != hipSuccess) return e;
+hipError_t launch_typed(const BwdArgs& a, float* ck, const float* y_pre, bool saved,
+                        float* part_bc, float* part_a, float* part_d, hipStream_t stream) {
+  if (!saved) {
+    chain::ChainParams cp{a.x,     a.delta, a.B,     a.C,     nullptr, a.A, nullptr, a.h0,
+                          nullptr, nullptr, nullptr, a.L,     a.D,     chain::kStates};
+    cp.ck = ck;
+    const hipError_t e =
+        chain::launch_io<chain::ChainIO<T, T, T, float>, PlainVariant, chain::kCkOnly>(
+            cp, a.batch, stream);
+    if (e != hipSuccess) return e;
+  }
   chain::ChainBwdParams p{};
   p.x = a.x;
   p.delta = a.delta;
@@ -31,6 +45,7 @@ hipError_t launch_typed(const BwdArgs& a, float* ck, float* part_bc, float* part
   p.h0 = a.h0;
   p.dout = a.dout;
   p.ck = ck;
+  p.y_pre = y_pre;
   p.dx = a.dx;
   p.ddelta = a.ddelta;
   p.dz = a.dz;
@@ -40,16 +55,12 @@ hipError_t launch_typed(const BwdArgs& a, float* ck, float* part_bc, float* part
   p.part_d = part_d;
   p.L = a.L;
   p.D = a.D;
-  const bool skip = a.Dskip != nullptr, gate = a.z != nullptr;
-  if (skip && gate) return chain::launch_bwd_chain_t<T, true, true>(p, a.batch, stream);
-  if (skip) return chain::launch_bwd_chain_t<T, true, false>(p, a.batch, stream);
-  if (gate) return chain::launch_bwd_chain_t<T, false, true>(p, a.batch, stream);
-  return chain::launch_bwd_chain_t<T, false, false>(p, a.batch, stream);
+  return saved ? launch_parts<T, true>(p, a, stream) : launch_parts<T, false>(p, a, stream);
 }
 
 }  // namespace
 
-bool chain_bwd_applies(const BwdArgs& a) {
+bool chain_bwd_layout_ok(const BwdArgs& a) {
   if (a.N != chain::kStates || a.D % chain::kChannels != 0 || a.L < 1 || a.batch < 1)
     return false;
   const size_t in_align = a.dtype == MSSM_FLOAT32 ? 16 : 8;
@@ -59,13 +70,20 @@ bool chain_bwd_applies(const BwdArgs& a) {
     return false;
   if (a.D * chain::kTile * static_cast<int64_t>(sizeof(float)) >= (int64_t(1) << 31)) return false;
   if (a.batch > (int64_t(1) << 31) / (a.D / chain::kChannels)) return false;
-  return single_pass_chosen(a.batch * a.D);
+  if (a.saved_ck && !aligned(a.saved_ck, 16)) return false;
+  if (a.saved_y_pre && !aligned(a.saved_y_pre, 16)) return false;
+  return true;
 }
 
-hipError_t launch_chain_bwd(const BwdArgs& a, float* ck, float* part_bc, float* part_a,
-                            float* part_d, hipStream_t stream) {
-  if (a.dtype == MSSM_FLOAT32) return launch_typed<float>(a, ck, part_bc, part_a, part_d, stream);
-  return launch_typed<uint16_t>(a, ck, part_bc, part_a, part_d, stream);
+bool chain_bwd_applies(const BwdArgs& a) {
+  return chain_bwd_layout_ok(a) && single_pass_chosen(a.batch * a.D);
+}
+
+hipError_t launch_chain_bwd(const BwdArgs& a, float* ck, const float* y_pre, bool saved,
+                            float* part_bc, float* part_a, float* part_d, hipStream_t stream) {
+  if (a.dtype == MSSM_FLOAT32)
+    return launch_typed<float>(a, ck, y_pre, saved, part_bc, part_a, part_d, stream);
+  return launch_typed<uint16_t>(a, ck, y_pre, saved, part_bc, part_a, part_d, stream);
 }
 
 }  // namespace mssm

@@ -206,22 +206,32 @@ struct ChainParams {
   void* y;
   void* y_lo;
   int64_t L, D, ld_bc;
-  float* ck = nullptr;    // checkpoint mode: [batch, tiles, D, N] states (the last tile's unused)
+  float* ck = nullptr;    // [batch, tiles, D, N] states after each tile (the last tile's unused)
+  float* y_pre = nullptr; // [batch, L, D] float32 output before the gate
 };
 
 // grid: batch * D / 16 blocks of kBlock lanes.  Requirements (checked by the
 // launchers): N = 16, D % 16 == 0, float32 inputs 16-byte and bfloat16 inputs
 // 8-byte aligned (rows too: ld_bc a multiple of 4), y 16-byte aligned,
 // 16 * D * 4 < 2^31.
-// kCk (checkpoints for the backward pass): no read-out and no y; instead the
-// state after every tile but the last goes to ck[b, tile, d, n].
-template <class IO, class V, bool kCk = false>
+// kMode: what the launch produces (checkpoints are for the backward pass):
+//   kOut     y (and h_last);
+//   kCkOnly  no read-out and no y, only the state after every tile but the
+//            last, to ck[b, tile, d, n];
+//   kOutSave y, those states, and with the gate also y_pre, the output before
+//            the gate (which the gate's gradient needs).
+constexpr int kOut = 0, kCkOnly = 1, kOutSave = 2;
+template <class IO, class V, int kMode = kOut>
 __global__ __launch_bounds__(kBlock) void chain_scan_kernel(ChainParams prm) {
   using TX = typename IO::TX;
   using TY = typename IO::TY;
+  constexpr bool kCk = kMode == kCkOnly;
+  constexpr bool kSave = kMode == kOutSave;
+  constexpr bool kPre = kSave && V::kGate;
   constexpr int kTiles = V::kGate ? 5 : 4;     // x, delta, B^T, C^T (, z)
   __shared__ __align__(16) float tin[2][kTiles][kTile][kRow];
   __shared__ __align__(16) float tout[2][kTile][kRow];
+  __shared__ __align__(16) float tpre[kPre ? 2 : 1][kTile][kRow];   // y before the gate
   const int64_t L = prm.L, D = prm.D;
 
   const int64_t n_dgroups = D / kChannels;
@@ -312,7 +322,11 @@ __global__ __launch_bounds__(kBlock) void chain_scan_kernel(ChainParams prm) {
   auto store_y = [&](int64_t k) {
     if constexpr (kCk) return;
     const float4 v = lds_get4(&tout[k & 1][ls][lq]);
+    float4 u;
+    if constexpr (kPre) u = lds_get4(&tpre[k & 1][ls][lq]);
     if (k == last && ls >= tail_steps) return;
+    if constexpr (kPre)
+      *reinterpret_cast<float4*>(prm.y_pre + (b * L + k * kTile + ls) * D + d0 + lq) = u;
     const int64_t step_bytes = k * kTile * D * static_cast<int64_t>(sizeof(TY));
     if constexpr (sizeof(TY) == 4) {
       *reinterpret_cast<float4*>(yb + step_bytes + yoff) = v;
@@ -384,6 +398,10 @@ __global__ __launch_bounds__(kBlock) void chain_scan_kernel(ChainParams prm) {
 #undef MSSM_CHAIN_STEP
     float yv = row_reduce_scatter16(p, n);     // y of step n of this row's channel
     if constexpr (V::kSkip) yv = __builtin_fmaf(Dd, xv, yv);
+    if constexpr (kPre) tpre[buf][n][ch] = yv;
+    if constexpr (kSave) {
+      if (k < last) prm.ck[((b * ntiles + k) * D + d0 + ch) * kStates + n] = h;
+    }
     if constexpr (V::kGate) yv *= silu(tin[buf][4][n][ch]);
     tout[buf][n][ch] = yv;
   };
@@ -421,15 +439,18 @@ __global__ __launch_bounds__(kBlock) void chain_scan_kernel(ChainParams prm) {
 }
 
 // Launch on `stream` for `batch` rows; returns the launch status.
-template <class IO, class V, bool kCk = false>
+template <class IO, class V, int kMode = kOut>
 hipError_t launch_io(const ChainParams& p, int64_t batch, hipStream_t stream) {
   const dim3 grid(static_cast<unsigned>(batch * (p.D / kChannels)));
-  hipLaunchKernelGGL((chain_scan_kernel<IO, V, kCk>), grid, dim3(kBlock), 0, stream, p);
+  hipLaunchKernelGGL((chain_scan_kernel<IO, V, kMode>), grid, dim3(kBlock), 0, stream, p);
   return hipGetLastError();
 }
 
 template <class V>
 hipError_t launch_variant(const ScanArgs& a, hipStream_t stream);
+// y plus the saved states (and y_pre with the gate), first-order input term
+template <class V>
+hipError_t launch_save(const ScanArgs& a, float* ck, float* y_pre, hipStream_t stream);
 
 }  // namespace chain
 
@@ -447,6 +468,24 @@ hipError_t launch_variant(const ScanArgs& a, hipStream_t stream);
                                                                              stream);         \
     return chain::launch_io<chain::ChainIO<uint16_t, uint16_t, uint16_t, float>, V>(          \
         p, a.batch, stream);                                                                  \
+  }
+
+// The forward that also saves what the backward reads: y float32, first-order
+// input term, the optional parts of V.
+#define MSSM_DEFINE_CHAIN_SAVE(SKIP, GATE, STATE)                                              \
+  template <>                                                                                 \
+  hipError_t chain::launch_save<Variant<false, SKIP, GATE, STATE>>(                           \
+      const ScanArgs& a, float* ck, float* y_pre, hipStream_t stream) {                       \
+    using V = Variant<false, SKIP, GATE, STATE>;                                              \
+    chain::ChainParams p{a.x,      a.delta, a.B,      a.C, a.z, a.A, a.Dskip, a.h0,            \
+                         a.h_last, a.y,     nullptr,  a.L, a.D, chain::kStates};               \
+    p.ck = ck;                                                                                \
+    p.y_pre = y_pre;                                                                          \
+    if (a.dtype == MSSM_FLOAT32)                                                              \
+      return chain::launch_io<chain::ChainIO<float, float, float, float>, V, chain::kOutSave>( \
+          p, a.batch, stream);                                                                \
+    return chain::launch_io<chain::ChainIO<uint16_t, uint16_t, uint16_t, float>, V,           \
+                            chain::kOutSave>(p, a.batch, stream);                             \
   }
 
 }  // namespace mssm

@@ -80,6 +80,33 @@ bool chain_fused_applies(int64_t batch, int64_t D, int64_t N, int64_t R, const v
   return single_pass_chosen(batch * D);
 }
 
+bool chain_save_layout_ok(const ScanArgs& a) {
+  if (a.N != chain::kStates || a.D % chain::kChannels != 0 || a.L < 1 || a.batch < 1)
+    return false;
+  const size_t in_align = a.dtype == MSSM_FLOAT32 ? 16 : 8;
+  if (!aligned(a.x, in_align) || !aligned(a.delta, in_align) || !aligned(a.B, in_align) ||
+      !aligned(a.C, in_align) || (a.z && !aligned(a.z, in_align)) || !aligned(a.y, 16))
+    return false;
+  if (a.D * chain::kTile * static_cast<int64_t>(sizeof(float)) >= (int64_t(1) << 31)) return false;
+  return a.batch <= (int64_t(1) << 31) / (a.D / chain::kChannels);
+}
+
+namespace {
+template <bool kSkip, bool kGate>
+hipError_t launch_save_state(const ScanArgs& a, float* ck, float* y_pre, hipStream_t stream) {
+  if (a.h_last) return chain::launch_save<Variant<false, kSkip, kGate, true>>(a, ck, y_pre, stream);
+  return chain::launch_save<Variant<false, kSkip, kGate, false>>(a, ck, y_pre, stream);
+}
+}  // namespace
+
+hipError_t launch_chain_save(const ScanArgs& a, float* ck, float* y_pre, hipStream_t stream) {
+  const bool skip = a.Dskip != nullptr, gate = a.z != nullptr;
+  if (skip && gate) return launch_save_state<true, true>(a, ck, y_pre, stream);
+  if (skip) return launch_save_state<true, false>(a, ck, y_pre, stream);
+  if (gate) return launch_save_state<false, true>(a, ck, y_pre, stream);
+  return launch_save_state<false, false>(a, ck, y_pre, stream);
+}
+
 hipError_t launch_chain_scan(const ScanArgs& a, hipStream_t stream) {
   return a.bbar == MSSM_BBAR_ZOH ? launch_parts<true>(a, stream)
                                  : launch_parts<false>(a, stream);

@@ -402,24 +402,17 @@ mssm_status mssm_mamba_block_fwd(const void* u0, const void* W_in, const float* 
 
 }  // extern "C"
 
-extern "C" {
+namespace {
 
-mssm_status mssm_selective_scan_bwd_workspace_size(int64_t batch, int64_t L, int64_t D, int64_t N,
-                                                   mssm_dtype dtype, size_t* bytes) {
-  if (!bytes) return MSSM_ERROR_INVALID_VALUE;
-  const mssm_status s = check_shape(batch, L, D, N, dtype);
-  if (s != MSSM_SUCCESS) return s;
-  *bytes = (batch == 0 || L == 0 || D == 0) ? 0 : mssm::bwd_workspace_bound(batch, L, D, N);
-  return MSSM_SUCCESS;
-}
-
-mssm_status mssm_selective_scan_bwd(const void* x, const void* delta, const float* A,
-                                    const void* B, const void* C, const float* Dskip,
-                                    const void* z, const float* h0, const float* dout, float* dx,
-                                    float* ddelta, float* dA, float* dB, float* dC, float* dDskip,
-                                    float* dz, float* dh0, void* workspace, size_t workspace_bytes,
-                                    int64_t batch, int64_t L, int64_t D, int64_t N,
-                                    mssm_dtype dtype, void* stream) {
+// The backward call; with_saved: the checkpoints (and y_pre with the gate)
+// come from `saved`, written by mssm_selective_scan_fwd_save.
+mssm_status bwd_impl(const void* x, const void* delta, const float* A, const void* B,
+                     const void* C, const float* Dskip, const void* z, const float* h0,
+                     const float* dout, float* dx, float* ddelta, float* dA, float* dB,
+                     float* dC, float* dDskip, float* dz, float* dh0, const float* saved,
+                     size_t saved_bytes, bool with_saved, void* workspace,
+                     size_t workspace_bytes, int64_t batch, int64_t L, int64_t D, int64_t N,
+                     mssm_dtype dtype, void* stream) {
   mssm_status s = check_shape(batch, L, D, N, dtype);
   if (s != MSSM_SUCCESS) return s;
   if ((Dskip != nullptr) != (dDskip != nullptr) || (z != nullptr) != (dz != nullptr))
@@ -446,9 +439,24 @@ mssm_status mssm_selective_scan_bwd(const void* x, const void* delta, const floa
   }
   if (!x || !delta || !A || !B || !C || !dout || !dx || !ddelta || !dB || !dC)
     return MSSM_ERROR_INVALID_VALUE;
-  const mssm::BwdArgs a{x,  delta,  A,  B,  C,      Dskip, z,  h0,  dout,  dx,    ddelta, dA,
-                        dB, dC,     dDskip, dz, dh0, batch, L, D, N, dtype};
-  const mssm::BwdPlan plan = mssm::plan_bwd(batch, L, D, N, mssm::chain_bwd_applies(a));
+  mssm::BwdArgs a{x,  delta,  A,  B,  C,      Dskip, z,  h0,  dout,  dx,    ddelta, dA,
+                  dB, dC,     dDskip, dz, dh0, batch, L, D, N, dtype};
+  bool chain;
+  if (with_saved) {
+    if (N != 16 || D % 16 != 0) return MSSM_ERROR_NOT_SUPPORTED;
+    if (!saved) return MSSM_ERROR_INVALID_VALUE;
+    const mssm::SavedLayout lay = mssm::saved_layout(batch, L, D, N, z != nullptr);
+    if (saved_bytes < lay.bytes || reinterpret_cast<uintptr_t>(saved) % 256 != 0)
+      return MSSM_ERROR_WORKSPACE;
+    const char* base = reinterpret_cast<const char*>(saved);
+    a.saved_ck = reinterpret_cast<const float*>(base + lay.ck_offset);
+    a.saved_y_pre = z ? reinterpret_cast<const float*>(base + lay.y_pre_offset) : nullptr;
+    if (!mssm::chain_bwd_layout_ok(a)) return MSSM_ERROR_NOT_SUPPORTED;
+    chain = true;
+  } else {
+    chain = mssm::chain_bwd_applies(a);
+  }
+  const mssm::BwdPlan plan = mssm::plan_bwd(batch, L, D, N, chain);
   if (!plan.chain) {
     const int64_t n_dtiles = (D + 255) / 256;
     int64_t blocks;
@@ -466,6 +474,93 @@ mssm_status mssm_selective_scan_bwd(const void* x, const void* delta, const floa
     return MSSM_ERROR_HIP;
   }
   return MSSM_SUCCESS;
+}
+
+}  // namespace
+
+extern "C" {
+
+mssm_status mssm_selective_scan_bwd_workspace_size(int64_t batch, int64_t L, int64_t D, int64_t N,
+                                                   mssm_dtype dtype, size_t* bytes) {
+  if (!bytes) return MSSM_ERROR_INVALID_VALUE;
+  const mssm_status s = check_shape(batch, L, D, N, dtype);
+  if (s != MSSM_SUCCESS) return s;
+  *bytes = (batch == 0 || L == 0 || D == 0) ? 0 : mssm::bwd_workspace_bound(batch, L, D, N);
+  return MSSM_SUCCESS;
+}
+
+mssm_status mssm_selective_scan_bwd(const void* x, const void* delta, const float* A,
+                                    const void* B, const void* C, const float* Dskip,
+                                    const void* z, const float* h0, const float* dout, float* dx,
+                                    float* ddelta, float* dA, float* dB, float* dC, float* dDskip,
+                                    float* dz, float* dh0, void* workspace, size_t workspace_bytes,
+                                    int64_t batch, int64_t L, int64_t D, int64_t N,
+                                    mssm_dtype dtype, void* stream) {
+  return bwd_impl(x, delta, A, B, C, Dskip, z, h0, dout, dx, ddelta, dA, dB, dC, dDskip, dz, dh0,
+                  nullptr, 0, false, workspace, workspace_bytes, batch, L, D, N, dtype, stream);
+}
+
+mssm_status mssm_selective_scan_saved_size(int64_t batch, int64_t L, int64_t D, int64_t N,
+                                           int gate, size_t* bytes) {
+  if (!bytes) return MSSM_ERROR_INVALID_VALUE;
+  const mssm_status s = check_shape(batch, L, D, N, MSSM_FLOAT32);
+  if (s != MSSM_SUCCESS) return s;
+  *bytes = mssm::saved_layout(batch, L, D, N, gate != 0).bytes;
+  return MSSM_SUCCESS;
+}
+
+mssm_status mssm_selective_scan_fwd_save(const void* x, const void* delta, const float* A,
+                                         const void* B, const void* C, const float* Dskip,
+                                         const void* z, const float* h0, float* y,
+                                         float* h_last, float* saved, size_t saved_bytes,
+                                         int64_t batch, int64_t L, int64_t D, int64_t N,
+                                         mssm_dtype dtype, void* stream) {
+  mssm_status s = check_shape(batch, L, D, N, dtype);
+  if (s != MSSM_SUCCESS) return s;
+  if (batch == 0 || D == 0) return MSSM_SUCCESS;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (L == 0) {   // nothing to save; the state passes through
+    if (!h_last) return MSSM_SUCCESS;
+    const hipError_t e = mssm::launch_state_init(h_last, h0, batch * D * N, st);
+    if (e != hipSuccess) {
+      set_hip_error(e, "state copy launch");
+      return MSSM_ERROR_HIP;
+    }
+    return MSSM_SUCCESS;
+  }
+  if (N != 16 || D % 16 != 0) return MSSM_ERROR_NOT_SUPPORTED;
+  if (!x || !delta || !A || !B || !C || !y || !saved) return MSSM_ERROR_INVALID_VALUE;
+  const mssm::SavedLayout lay = mssm::saved_layout(batch, L, D, N, z != nullptr);
+  if (saved_bytes < lay.bytes || reinterpret_cast<uintptr_t>(saved) % 256 != 0)
+    return MSSM_ERROR_WORKSPACE;
+  mssm::ScanArgs a{x, delta, A, B, C, y, batch, L, D, N, dtype};
+  a.Dskip = Dskip;
+  a.z = z;
+  a.h0 = h0;
+  a.h_last = h_last;
+  if (!mssm::chain_save_layout_ok(a)) return MSSM_ERROR_NOT_SUPPORTED;
+  char* base = reinterpret_cast<char*>(saved);
+  float* ck = reinterpret_cast<float*>(base + lay.ck_offset);
+  float* y_pre = z ? reinterpret_cast<float*>(base + lay.y_pre_offset) : nullptr;
+  const hipError_t e = mssm::launch_chain_save(a, ck, y_pre, st);
+  if (e != hipSuccess) {
+    set_hip_error(e, "selective scan (saving) launch");
+    return MSSM_ERROR_HIP;
+  }
+  return MSSM_SUCCESS;
+}
+
+mssm_status mssm_selective_scan_bwd_saved(const void* x, const void* delta, const float* A,
+                                          const void* B, const void* C, const float* Dskip,
+                                          const void* z, const float* h0, const float* saved,
+                                          size_t saved_bytes, const float* dout, float* dx,
+                                          float* ddelta, float* dA, float* dB, float* dC,
+                                          float* dDskip, float* dz, float* dh0, void* workspace,
+                                          size_t workspace_bytes, int64_t batch, int64_t L,
+                                          int64_t D, int64_t N, mssm_dtype dtype, void* stream) {
+  return bwd_impl(x, delta, A, B, C, Dskip, z, h0, dout, dx, ddelta, dA, dB, dC, dDskip, dz, dh0,
+                  saved, saved_bytes, true, workspace, workspace_bytes, batch, L, D, N, dtype,
+                  stream);
 }
 
 }  // extern "C"

@@ -58,6 +58,20 @@ bool single_pass_chosen(int64_t channels);
 bool chain_scan_applies(const ScanArgs& a);
 hipError_t launch_chain_scan(const ScanArgs& a, hipStream_t stream);
 
+// Forward that also saves the backward pass's inputs (first-order input term):
+// the state after every 16-step tile into ck [batch, tiles, D, N] and, with
+// the gate, the output before the gate into y_pre [batch, L, D].  Needs the
+// single-pass layout (shape and alignment), whatever the channel count.
+bool chain_save_layout_ok(const ScanArgs& a);
+hipError_t launch_chain_save(const ScanArgs& a, float* ck, float* y_pre, hipStream_t stream);
+
+// Where the saved tensors sit in the caller's buffer (256-byte aligned
+// offsets); bytes == 0 when the shape has no saved form.
+struct SavedLayout {
+  size_t ck_offset = 0, y_pre_offset = 0, bytes = 0;
+};
+SavedLayout saved_layout(int64_t batch, int64_t L, int64_t D, int64_t N, bool gate);
+
 // The single pass behind the selection projections (fused selective SSM and
 // Mamba block): delta is the float32 matrix softplus(dt_low W_dt + bias) and
 // B, C are the columns R .. R+2N-1 of P's rows.  Whether it applies (N = 16,
@@ -274,6 +288,10 @@ struct BwdArgs {
   float* dh0;           // or null
   int64_t batch, L, D, N;
   mssm_dtype dtype;
+  // from a saving forward call (single pass only): the states after each
+  // tile, and with the gate the output before it; null: recomputed
+  const float* saved_ck = nullptr;
+  const float* saved_y_pre = nullptr;
 };
 
 // Chunks of `chunk` steps; workspace: forward and reverse chunk summaries
@@ -299,9 +317,10 @@ hipError_t launch_bwd(const BwdArgs& a, const BwdPlan& plan, void* workspace, hi
 // The single-pass backward (N = 16, D % 16 == 0, aligned pointers, enough
 // channels): whether it applies, and its two kernels (checkpoints, reverse
 // sweep) writing the partials that launch_bwd then reduces.
-bool chain_bwd_applies(const BwdArgs& a);
-hipError_t launch_chain_bwd(const BwdArgs& a, float* ck, float* part_bc, float* part_a,
-                            float* part_d, hipStream_t stream);
+bool chain_bwd_layout_ok(const BwdArgs& a);   // shape and alignment only
+bool chain_bwd_applies(const BwdArgs& a);     // and the order is chosen
+hipError_t launch_chain_bwd(const BwdArgs& a, float* ck, const float* y_pre, bool saved,
+                            float* part_bc, float* part_a, float* part_d, hipStream_t stream);
 
 // chain: the single-pass order (plan_fused ignores cpl then); the bound
 // covers every order and layout.

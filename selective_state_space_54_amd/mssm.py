@@ -60,6 +60,12 @@ _SIGNATURES = {
                                                               ctypes.POINTER(ctypes.c_size_t)]),
     "mssm_selective_scan_bwd": (ctypes.c_int, [_vp] * 17 + [_vp, ctypes.c_size_t] + [_i64] * 4 +
                                 [ctypes.c_int, _vp]),
+    "mssm_selective_scan_saved_size": (ctypes.c_int, [_i64, _i64, _i64, _i64, ctypes.c_int,
+                                                      ctypes.POINTER(ctypes.c_size_t)]),
+    "mssm_selective_scan_fwd_save": (ctypes.c_int, [_vp] * 11 + [ctypes.c_size_t] + [_i64] * 4 +
+                                     [ctypes.c_int, _vp]),
+    "mssm_selective_scan_bwd_saved": (ctypes.c_int, [_vp] * 9 + [ctypes.c_size_t] + [_vp] * 10 +
+                                      [ctypes.c_size_t] + [_i64] * 4 + [ctypes.c_int, _vp]),
     "mssm_causal_conv1d_silu": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64,
                                                ctypes.c_int, _vp]),
     "mssm_mamba_block_supports": (ctypes.c_int, [_i64, _i64, _i64]),
@@ -476,13 +482,8 @@ def mssm_selective_scan_bwd_workspace_size(batch, L, D, N, dtype) -> int:
     return out.value
 
 
-def mssm_selective_scan_bwd(x, delta, A, B, C, dout, grads, workspace, *, Dskip=None, z=None,
-                            h0=None, stream=None):
-    """Gradients of sum(dout * y) for y = selective_scan_ex(x, delta, A, B, C, Dskip=Dskip,
-    z=z, h0=h0) (first-order input term).  ``grads`` maps dx, ddelta, dA, dB, dC (and dD,
-    dz, dh0 for the parts given) to float32 tensors that are overwritten."""
+def _check_bwd_args(x, delta, A, B, C, dout, grads, Dskip, z, h0):
     batch, L, D, N = _scan_shapes(x, A)
-    y_like = torch.empty(0)
     dev = x.device
     _dtype_code(x.dtype)
     if dev.type != "cuda":
@@ -502,21 +503,76 @@ def mssm_selective_scan_bwd(x, delta, A, B, C, dout, grads, workspace, *, Dskip=
         if k not in shapes:
             raise ValueError(f"unknown gradient {k}")
         _dense(v, k, torch.float32, shapes[k], dev)
-    del y_like
+    return batch, L, D, N
+
+
+def _bytes_of(t):
+    return t.numel() * t.element_size() if t is not None else 0
+
+
+def mssm_selective_scan_bwd(x, delta, A, B, C, dout, grads, workspace, *, Dskip=None, z=None,
+                            h0=None, stream=None):
+    """Gradients of sum(dout * y) for y = selective_scan_ex(x, delta, A, B, C, Dskip=Dskip,
+    z=z, h0=h0) (first-order input term).  ``grads`` maps dx, ddelta, dA, dB, dC (and dD,
+    dz, dh0 for the parts given) to float32 tensors that are overwritten."""
+    batch, L, D, N = _check_bwd_args(x, delta, A, B, C, dout, grads, Dskip, z, h0)
     g = lambda k: _ptr(grads.get(k))
     ws_ptr = _ptr(workspace) if workspace is not None and workspace.numel() > 0 else None
-    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(load().mssm_selective_scan_bwd(
         _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(Dskip), _ptr(z), _ptr(h0),
         _ptr(dout), g("dx"), g("ddelta"), g("dA"), g("dB"), g("dC"), g("dD"), g("dz"), g("dh0"),
-        ws_ptr, ws_bytes, batch, L, D, N, _DTYPES[x.dtype], _stream_handle(stream)),
+        ws_ptr, _bytes_of(workspace), batch, L, D, N, _DTYPES[x.dtype], _stream_handle(stream)),
         "mssm_selective_scan_bwd")
     return grads
 
 
-def selective_scan_bwd(x, delta, A, B, C, dout, *, Dskip=None, z=None, h0=None, stream=None):
-    """Allocate the gradients and the workspace with torch, then run
-    mssm_selective_scan_bwd; returns the dict of gradients."""
+def mssm_selective_scan_saved_size(batch, L, D, N, gate) -> int:
+    """Bytes of the buffer mssm_selective_scan_fwd_save fills (0: no saved form)."""
+    out = ctypes.c_size_t(0)
+    _check(load().mssm_selective_scan_saved_size(batch, L, D, N, 1 if gate else 0,
+                                                 ctypes.byref(out)),
+           "mssm_selective_scan_saved_size")
+    return out.value
+
+
+def mssm_selective_scan_fwd_save(x, delta, A, B, C, y, saved, *, Dskip=None, z=None, h0=None,
+                                 h_last=None, stream=None):
+    """y (and h_last) as mssm_selective_scan_fwd_ex (first-order term), and into ``saved``
+    (a uint8 or float32 GPU tensor of mssm_selective_scan_saved_size bytes) the states the
+    backward pass restarts from (and with z the output before the gate)."""
+    batch, L, D, N = _check_scan_args(x, delta, A, B, C, y)
+    dev = x.device
+    _check_optional(Dskip, "Dskip", torch.float32, (D,), dev)
+    _check_optional(z, "z", x.dtype, (batch, L, D), dev)
+    _check_optional(h0, "h0", torch.float32, (batch, D, N), dev)
+    _check_optional(h_last, "h_last", torch.float32, (batch, D, N), dev)
+    if saved is not None and (saved.device != dev or not saved.is_contiguous()):
+        raise ValueError("saved must be a contiguous tensor on the inputs' device")
+    _check(load().mssm_selective_scan_fwd_save(
+        _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(Dskip), _ptr(z), _ptr(h0), _ptr(y),
+        _ptr(h_last), _ptr(saved), _bytes_of(saved), batch, L, D, N, _DTYPES[x.dtype],
+        _stream_handle(stream)), "mssm_selective_scan_fwd_save")
+    return y
+
+
+def mssm_selective_scan_bwd_saved(x, delta, A, B, C, saved, dout, grads, workspace, *,
+                                  Dskip=None, z=None, h0=None, stream=None):
+    """mssm_selective_scan_bwd reading the states (and y before the gate) that
+    mssm_selective_scan_fwd_save wrote into ``saved`` for the same inputs."""
+    batch, L, D, N = _check_bwd_args(x, delta, A, B, C, dout, grads, Dskip, z, h0)
+    if saved is not None and (saved.device != x.device or not saved.is_contiguous()):
+        raise ValueError("saved must be a contiguous tensor on the inputs' device")
+    g = lambda k: _ptr(grads.get(k))
+    ws_ptr = _ptr(workspace) if workspace is not None and workspace.numel() > 0 else None
+    _check(load().mssm_selective_scan_bwd_saved(
+        _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(Dskip), _ptr(z), _ptr(h0),
+        _ptr(saved), _bytes_of(saved), _ptr(dout), g("dx"), g("ddelta"), g("dA"), g("dB"),
+        g("dC"), g("dD"), g("dz"), g("dh0"), ws_ptr, _bytes_of(workspace), batch, L, D, N,
+        _DTYPES[x.dtype], _stream_handle(stream)), "mssm_selective_scan_bwd_saved")
+    return grads
+
+
+def _alloc_grads(x, A, Dskip, z, h0):
     batch, L, D, N = _scan_shapes(x, A)
     opts = dict(device=x.device, dtype=torch.float32)
     grads = {"dx": torch.empty((batch, L, D), **opts), "ddelta": torch.empty((batch, L, D), **opts),
@@ -530,5 +586,36 @@ def selective_scan_bwd(x, delta, A, B, C, dout, *, Dskip=None, z=None, h0=None, 
         grads["dh0"] = torch.empty((batch, D, N), **opts)
     nbytes = mssm_selective_scan_bwd_workspace_size(batch, L, D, N, x.dtype)
     ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=x.device)
+    return grads, ws
+
+
+def selective_scan_fwd_save(x, delta, A, B, C, *, Dskip=None, z=None, h0=None,
+                            return_last_state=False, stream=None):
+    """Allocate y, the saved buffer (and the final state) with torch, then run
+    mssm_selective_scan_fwd_save.  Returns (y, saved) or (y, saved, h_last)."""
+    batch, L, D, N = _scan_shapes(x, A)
+    y = torch.empty(x.shape, dtype=torch.float32, device=x.device)
+    nbytes = mssm_selective_scan_saved_size(batch, L, D, N, z is not None)
+    saved = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=x.device)
+    h_last = (torch.empty((batch, D, N), dtype=torch.float32, device=x.device)
+              if return_last_state else None)
+    mssm_selective_scan_fwd_save(x, delta, A, B, C, y, saved, Dskip=Dskip, z=z, h0=h0,
+                                 h_last=h_last, stream=stream)
+    return (y, saved, h_last) if return_last_state else (y, saved)
+
+
+def selective_scan_bwd_saved(x, delta, A, B, C, saved, dout, *, Dskip=None, z=None, h0=None,
+                             stream=None):
+    """Allocate the gradients and the workspace with torch, then run
+    mssm_selective_scan_bwd_saved; returns the dict of gradients."""
+    grads, ws = _alloc_grads(x, A, Dskip, z, h0)
+    return mssm_selective_scan_bwd_saved(x, delta, A, B, C, saved, dout, grads, ws, Dskip=Dskip,
+                                         z=z, h0=h0, stream=stream)
+
+
+def selective_scan_bwd(x, delta, A, B, C, dout, *, Dskip=None, z=None, h0=None, stream=None):
+    """Allocate the gradients and the workspace with torch, then run
+    mssm_selective_scan_bwd; returns the dict of gradients."""
+    grads, ws = _alloc_grads(x, A, Dskip, z, h0)
     return mssm_selective_scan_bwd(x, delta, A, B, C, dout, grads, ws, Dskip=Dskip, z=z, h0=h0,
                                    stream=stream)

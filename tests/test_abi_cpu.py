@@ -272,3 +272,57 @@ def test_backward_argument_errors(lib, monkeypatch):
     monkeypatch.setenv("MSSM_SCAN_DESIGN", "chain")
     assert call(p17, FAKE, 0, 8, 2048, 1536, 16) == 4
     assert call(p17, ctypes.c_void_p(0x1004), nb, 8, 2048, 1536, 16) == 4
+
+
+def test_saved_forward_and_backward_argument_errors(lib):
+    out = ctypes.c_size_t(0)
+    assert lib.mssm_selective_scan_saved_size(8, 2048, 1536, 16, 1, None) == 1
+    assert lib.mssm_selective_scan_saved_size(8, 2048, 1536, 16, 0, ctypes.byref(out)) == 0
+    ck_bytes = out.value
+    assert ck_bytes == 8 * 128 * 1536 * 16 * 4      # states after each 16-step tile
+    assert lib.mssm_selective_scan_saved_size(8, 2048, 1536, 16, 1, ctypes.byref(out)) == 0
+    assert out.value == ck_bytes + 8 * 2048 * 1536 * 4   # + the output before the gate
+    nb = out.value
+    for shape in ((8, 2048, 1530, 16), (8, 2048, 1536, 8)):   # no saved form
+        assert lib.mssm_selective_scan_saved_size(*shape, 1, ctypes.byref(out)) == 0
+        assert out.value == 0
+    assert lib.mssm_selective_scan_saved_size(-1, 4, 16, 16, 0, ctypes.byref(out)) == 1
+
+    def fwd(ptrs, saved, sbytes, batch, L, D, N, dtype=0):
+        return lib.mssm_selective_scan_fwd_save(*ptrs, saved, sbytes, batch, L, D, N, dtype, None)
+    # x delta A B C Dskip z h0 y h_last
+    p10 = [FAKE] * 10
+    assert fwd(p10, FAKE, nb, 8, 2048, 1536, 8) == 2          # N != 16
+    assert fwd(p10, FAKE, nb, 8, 2048, 1530, 16) == 2         # D % 16 != 0
+    assert fwd(p10, FAKE, nb, 0, 2048, 1536, 16) == 0         # empty
+    for i in (0, 1, 2, 3, 4, 8):
+        ptrs = list(p10)
+        ptrs[i] = None
+        assert fwd(ptrs, FAKE, nb, 8, 2048, 1536, 16) == 1, f"null {i} accepted"
+    assert fwd(p10, None, nb, 8, 2048, 1536, 16) == 1
+    assert fwd(p10, FAKE, nb - 1, 8, 2048, 1536, 16) == 4     # buffer too small
+    assert fwd(p10, ctypes.c_void_p(0x1010), nb, 8, 2048, 1536, 16) == 4   # not 256-aligned
+    ptrs = list(p10)
+    ptrs[0] = ctypes.c_void_p(0x1004)                          # x not 16-byte aligned
+    assert fwd(ptrs, FAKE, nb, 8, 2048, 1536, 16) == 2
+
+    wsb = ctypes.c_size_t(0)
+    assert lib.mssm_selective_scan_bwd_workspace_size(8, 2048, 1536, 16, 0, ctypes.byref(wsb)) == 0
+
+    def bwd(head, saved, sbytes, tail, ws, wbytes, batch, L, D, N, dtype=0):
+        return lib.mssm_selective_scan_bwd_saved(*head, saved, sbytes, *tail, ws, wbytes, batch, L,
+                                                 D, N, dtype, None)
+    head = [FAKE] * 8            # x delta A B C Dskip z h0
+    tail = [FAKE] * 9            # dout dx ddelta dA dB dC dD dz dh0
+    big = 1 << 40
+    assert bwd(head, FAKE, nb, tail, FAKE, big, 8, 2048, 1536, 8) == 2
+    assert bwd(head, None, nb, tail, FAKE, big, 8, 2048, 1536, 16) == 1
+    assert bwd(head, FAKE, nb - 1, tail, FAKE, big, 8, 2048, 1536, 16) == 4
+    assert bwd(head, ctypes.c_void_p(0x1010), nb, tail, FAKE, big, 8, 2048, 1536, 16) == 4
+    h = list(head)
+    h[3] = ctypes.c_void_p(0x1008)                             # B not 16-byte aligned
+    assert bwd(h, FAKE, nb, tail, FAKE, big, 8, 2048, 1536, 16) == 2
+    assert bwd(head, FAKE, nb, tail, FAKE, 0, 8, 2048, 1536, 16) == 4    # no workspace
+    t = list(tail)
+    t[7] = None                                                # z without dz
+    assert bwd(head, FAKE, nb, t, FAKE, big, 8, 2048, 1536, 16) == 1
