@@ -86,38 +86,29 @@ __device__ __forceinline__ float rs_first(float lo, float hi) {
   return q;
 }
 __device__ __forceinline__ float rs_rest(const float (&q8)[8], int n) {
-  float q4[4], q2[2];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    asm volatile(
-        "s_nop 1\n\t"
-        "v_add_f32_dpp %0, %1, %1 row_half_mirror row_mask:0xf bank_mask:0x5\n\t"
-        "v_add_f32_dpp %0, %2, %2 row_half_mirror row_mask:0xf bank_mask:0xa"
-        : "=&v"(q4[i])
-        : "v"(q8[i]), "v"(q8[i + 4]));
-  bool up = (n & 2) != 0;
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const float keep = up ? q4[i + 2] : q4[i], send = up ? q4[i] : q4[i + 2];
-    q2[i] = keep + dpp<kQuadXor2>(send);
-  }
-  up = (n & 1) != 0;
-  const float keep = up ? q2[1] : q2[0], send = up ? q2[0] : q2[1];
-  return keep + dpp<kQuadXor1>(send);
+  float q4[4];
+  reduce_level2(q8, q4);
+  return reduce_levels34(q4, n);
 }
 
 // acc += (value of lane s of the DPP row of v) * m in one instruction
 // (v_fmac_f32 with a row_newbcast operand, which the compiler does not form by
-// itself).  The leading s_nop covers the two wait states a DPP read needs
-// after a VALU write of its source, which the compiler does not check inside
-// asm.
+// itself).  A DPP read needs two wait states after a VALU write of its
+// source, which the compiler does not check inside asm: v must have been made
+// ready with dpp_sources_ready (tests/test_isa_checks_cpu.py checks the built
+// code for such hazards).
 template <int s>
 __device__ __forceinline__ void fmac_bcast(float& acc, float v, float m) {
   asm volatile(
-      "s_nop 1\n\t"
       "v_fmac_f32_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf bound_ctrl:1"
       : "+v"(acc)
       : "v"(v), "v"(m), "i"(s));
+}
+// Two wait states after v and w are final, before fmac_bcast reads them
+// through DPP: a tile's broadcast sources are computed once, so one s_nop
+// before its sweep replaces one per instruction.
+__device__ __forceinline__ void dpp_sources_ready(float v, float w) {
+  asm volatile("s_nop 1" ::"v"(v), "v"(w));
 }
 __device__ __forceinline__ void fmac_bcast_dyn(float& acc, float v, float m, int s) {
   switch (s) {
@@ -302,6 +293,7 @@ __global__ __launch_bounds__(kBlock) void chain_bwd_kernel(ChainBwdParams prm) {
     float p3h[kGate ? kH : 1], q3[kGate ? kH : 1];
     float vb_odd = 0.0f, vc_odd = 0.0f;
     float4 bq = make_float4(0.0f, 0.0f, 0.0f, 0.0f), cq = bq;
+    dpp_sources_ready(gv, dv);
 #pragma unroll
     for (int s = kTile - 1; s >= 0; --s) {
       if (s % 4 == 3) {

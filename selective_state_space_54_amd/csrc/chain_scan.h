@@ -110,34 +110,46 @@ __device__ __forceinline__ float opaque(float v) {
   return v;
 }
 
-// Row total of p[i], scattered: lane n of each DPP row returns the sum over
-// the row's 16 lanes of p[n].  Four halving levels.  The first two use the
-// DPP bank mask (a bank is 4 lanes of a row) to write each half of the row
-// from its own pair of sums, which saves the selects: lanes 0-7 take
-// p[i] + p[i] of lane n ^ 8 (row_ror:8), lanes 8-15 take p[i+8] + its
-// partner's; then within each half-row (row_half_mirror, partner 7 - n)
-// banks 0 and 2 keep the lower index, banks 1 and 3 the upper.  The last two
-// levels split lanes inside a bank, so they select.  The asm blocks start
-// with s_nop 1: a DPP read of a VGPR that the previous VALU instruction wrote
-// needs two wait states, and the compiler does not look inside asm.
-__device__ __forceinline__ float row_reduce_scatter16(const float (&p)[16], int n) {
-  float q8[8], q4[4], q2[2];
-#pragma unroll
-  for (int i = 0; i < 8; ++i)
-    asm volatile(
-        "s_nop 1\n\t"
-        "v_add_f32_dpp %0, %1, %1 row_ror:8 row_mask:0xf bank_mask:0x3\n\t"
-        "v_add_f32_dpp %0, %2, %2 row_ror:8 row_mask:0xf bank_mask:0xc"
-        : "=&v"(q8[i])
-        : "v"(p[i]), "v"(p[i + 8]));
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    asm volatile(
-        "s_nop 1\n\t"
-        "v_add_f32_dpp %0, %1, %1 row_half_mirror row_mask:0xf bank_mask:0x5\n\t"
-        "v_add_f32_dpp %0, %2, %2 row_half_mirror row_mask:0xf bank_mask:0xa"
-        : "=&v"(q4[i])
-        : "v"(q8[i]), "v"(q8[i + 4]));
+// The first two reduce levels below, for 16 values, as one asm block: one
+// s_nop 1 covers the two wait states a DPP read needs after a VALU write of
+// its source (for the inputs, written by compiler code the asm cannot see);
+// inside the block every DPP source was written at least 6 instructions
+// earlier.
+#define MSSM_L1(I, J)                                                              \
+  "v_add_f32_dpp %[q" #I "], %[p" #I "], %[p" #I "] row_ror:8 row_mask:0xf bank_mask:0x3\n\t" \
+  "v_add_f32_dpp %[q" #I "], %[p" #J "], %[p" #J "] row_ror:8 row_mask:0xf bank_mask:0xc\n\t"
+#define MSSM_L2(I, A, B)                                                                     \
+  "v_add_f32_dpp %[r" #I "], %[q" #A "], %[q" #A "] row_half_mirror row_mask:0xf bank_mask:0x5\n\t" \
+  "v_add_f32_dpp %[r" #I "], %[q" #B "], %[q" #B "] row_half_mirror row_mask:0xf bank_mask:0xa\n\t"
+__device__ __forceinline__ void reduce_levels12(const float (&p)[16], float (&q4)[4]) {
+  float q8[8];
+  asm volatile("s_nop 1\n\t"
+               MSSM_L1(0, 8) MSSM_L1(1, 9) MSSM_L1(2, 10) MSSM_L1(3, 11)
+               MSSM_L1(4, 12) MSSM_L1(5, 13) MSSM_L1(6, 14) MSSM_L1(7, 15)
+               MSSM_L2(0, 0, 4) MSSM_L2(1, 1, 5) MSSM_L2(2, 2, 6) MSSM_L2(3, 3, 7)
+               : [q0] "=&v"(q8[0]), [q1] "=&v"(q8[1]), [q2] "=&v"(q8[2]), [q3] "=&v"(q8[3]),
+                 [q4] "=&v"(q8[4]), [q5] "=&v"(q8[5]), [q6] "=&v"(q8[6]), [q7] "=&v"(q8[7]),
+                 [r0] "=&v"(q4[0]), [r1] "=&v"(q4[1]), [r2] "=&v"(q4[2]), [r3] "=&v"(q4[3])
+               : [p0] "v"(p[0]), [p1] "v"(p[1]), [p2] "v"(p[2]), [p3] "v"(p[3]),
+                 [p4] "v"(p[4]), [p5] "v"(p[5]), [p6] "v"(p[6]), [p7] "v"(p[7]),
+                 [p8] "v"(p[8]), [p9] "v"(p[9]), [p10] "v"(p[10]), [p11] "v"(p[11]),
+                 [p12] "v"(p[12]), [p13] "v"(p[13]), [p14] "v"(p[14]), [p15] "v"(p[15]));
+}
+// Level 2 alone (for sums whose first level ran step by step).
+__device__ __forceinline__ void reduce_level2(const float (&q8)[8], float (&q4)[4]) {
+  asm volatile("s_nop 1\n\t"
+               MSSM_L2(0, 0, 4) MSSM_L2(1, 1, 5) MSSM_L2(2, 2, 6) MSSM_L2(3, 3, 7)
+               : [r0] "=&v"(q4[0]), [r1] "=&v"(q4[1]), [r2] "=&v"(q4[2]), [r3] "=&v"(q4[3])
+               : [q0] "v"(q8[0]), [q1] "v"(q8[1]), [q2] "v"(q8[2]), [q3] "v"(q8[3]),
+                 [q4] "v"(q8[4]), [q5] "v"(q8[5]), [q6] "v"(q8[6]), [q7] "v"(q8[7]));
+}
+#undef MSSM_L1
+#undef MSSM_L2
+
+// Levels 3 and 4: within each bank of 4 lanes (quad_perm partners n ^ 2,
+// then n ^ 1), selecting which value a lane keeps and which it sends.
+__device__ __forceinline__ float reduce_levels34(const float (&q4)[4], int n) {
+  float q2[2];
   bool up = (n & 2) != 0;
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
@@ -147,6 +159,20 @@ __device__ __forceinline__ float row_reduce_scatter16(const float (&p)[16], int 
   up = (n & 1) != 0;
   const float keep = up ? q2[1] : q2[0], send = up ? q2[0] : q2[1];
   return keep + dpp<kQuadXor1>(send);
+}
+
+// Row total of p[i], scattered: lane n of each DPP row returns the sum over
+// the row's 16 lanes of p[n].  Four halving levels.  The first two use the
+// DPP bank mask (a bank is 4 lanes of a row) to write each half of the row
+// from its own pair of sums, which saves the selects: lanes 0-7 take
+// p[i] + p[i] of lane n ^ 8 (row_ror:8), lanes 8-15 take p[i+8] + its
+// partner's; then within each half-row (row_half_mirror, partner 7 - n)
+// banks 0 and 2 keep the lower index, banks 1 and 3 the upper.  The last two
+// levels split lanes inside a bank, so they select.
+__device__ __forceinline__ float row_reduce_scatter16(const float (&p)[16], int n) {
+  float q4[4];
+  reduce_levels12(p, q4);
+  return reduce_levels34(q4, n);
 }
 
 // Raw bits of 4 consecutive input values of `esz` bytes each (4: float32,
