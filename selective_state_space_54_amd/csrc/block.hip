@@ -139,7 +139,6 @@ BlockPlan plan_block(int64_t batch, int64_t L, int64_t Dm, int64_t Di, int64_t N
   BlockPlan b;
   const size_t M = static_cast<size_t>(batch * L);
   const size_t di = static_cast<size_t>(Di);
-  (void)Dm;
   if (chain) {
     b.chain = true;
     b.scan.chain = true;
@@ -158,6 +157,9 @@ BlockPlan plan_block(int64_t batch, int64_t L, int64_t Dm, int64_t Di, int64_t N
   b.dtl_offset = off;    off += align256(sizeof(uint16_t) * M * (size_t)R);
   b.dtl_lo_offset = off; off += align256(sizeof(uint16_t) * M * (size_t)R);
   b.wt_offset = off;     off += align256(sizeof(uint16_t) * di * (size_t)R);
+  b.win_t_offset = off;  off += align256(sizeof(uint16_t) * 2 * di * (size_t)Dm);
+  b.wx_t_offset = off;   off += align256(sizeof(uint16_t) * (size_t)(R + 2 * N) * di);
+  b.wout_t_offset = off; off += align256(sizeof(uint16_t) * (size_t)Dm * di);
   b.scan_offset = off;   off += b.scan.workspace_bytes;
   b.workspace_bytes = off;
   return b;
@@ -192,10 +194,18 @@ FusedStatus launch_block(const BlockArgs& a, const BlockPlan& bp, void* workspac
     st.blas_failed = st.hip == hipSuccess;
     return st;
   }
-  const uint16_t* W_in = static_cast<const uint16_t*>(a.W_in);
+  // the weights transposed once per call, so every GEMM reads both operands
+  // along k (W_in^T rows 0..Di-1 are u's columns, Di..2Di-1 z's)
+  uint16_t* WinT = reinterpret_cast<uint16_t*>(ws + bp.win_t_offset);
+  uint16_t* WxT = reinterpret_cast<uint16_t*>(ws + bp.wx_t_offset);
+  uint16_t* WoutT = reinterpret_cast<uint16_t*>(ws + bp.wout_t_offset);
+  st.hip = launch_transpose_bf16(a.W_in, WinT, Dm, 2 * Di, stream);
+  if (st.hip == hipSuccess) st.hip = launch_transpose_bf16(a.W_x, WxT, Di, ldp, stream);
+  if (st.hip == hipSuccess) st.hip = launch_transpose_bf16(a.W_out, WoutT, Di, Dm, stream);
+  if (st.hip != hipSuccess) return st;
   // input projection: u = u0 W_in[:, :Di], z = u0 W_in[:, Di:]
-  if (!gemm_rm_bf16(hb, M, Di, Dm, a.u0, Dm, W_in, 2 * Di, U, Di, 0.0f) ||
-      !gemm_rm_bf16(hb, M, Di, Dm, a.u0, Dm, W_in + Di, 2 * Di, Z, Di, 0.0f)) {
+  if (!gemm_rm_bf16_bt(hb, M, Di, Dm, a.u0, Dm, WinT, Dm, U, Di, 0.0f) ||
+      !gemm_rm_bf16_bt(hb, M, Di, Dm, a.u0, Dm, WinT + Di * Dm, Dm, Z, Di, 0.0f)) {
     st.blas_failed = true;
     return st;
   }
@@ -203,8 +213,8 @@ FusedStatus launch_block(const BlockArgs& a, const BlockPlan& bp, void* workspac
                               stream);
   if (st.hip != hipSuccess) return st;
   // selection projection of x = hi + lo
-  if (!gemm_rm_bf16(hb, M, ldp, Di, Xb, Di, a.W_x, ldp, P, ldp, 0.0f) ||
-      !gemm_rm_bf16(hb, M, ldp, Di, Xl, Di, a.W_x, ldp, P, ldp, 1.0f)) {
+  if (!gemm_rm_bf16_bt(hb, M, ldp, Di, Xb, Di, WxT, Di, P, ldp, 0.0f) ||
+      !gemm_rm_bf16_bt(hb, M, ldp, Di, Xl, Di, WxT, Di, P, ldp, 1.0f)) {
     st.blas_failed = true;
     return st;
   }
@@ -259,8 +269,8 @@ FusedStatus launch_block(const BlockArgs& a, const BlockPlan& bp, void* workspac
   }
   if (st.hip != hipSuccess) return st;
   // output projection of the gated result G = hi + lo
-  if (!gemm_rm_bf16(hb, M, Dm, Di, G, Di, a.W_out, Dm, a.out, Dm, 0.0f) ||
-      !gemm_rm_bf16(hb, M, Dm, Di, Gl, Di, a.W_out, Dm, a.out, Dm, 1.0f))
+  if (!gemm_rm_bf16_bt(hb, M, Dm, Di, G, Di, WoutT, Di, a.out, Dm, 0.0f) ||
+      !gemm_rm_bf16_bt(hb, M, Dm, Di, Gl, Di, WoutT, Di, a.out, Dm, 1.0f))
     st.blas_failed = true;
   return st;
 }

@@ -567,16 +567,86 @@ bool blas_handle(hipStream_t stream, rocblas_handle* out, hipError_t* hip_error)
   return true;
 }
 
-bool gemm_rm_bf16(rocblas_handle h, int64_t M, int64_t n, int64_t k, const void* A, int64_t lda,
-                  const void* B, int64_t ldb, float* C, int64_t ldc, float beta) {
-  // row-major C = A B is column-major C^T = B^T A^T: (n x M) = (n x k)(k x M)
+bool gemm_rm_bf16_bt(rocblas_handle h, int64_t M, int64_t n, int64_t k, const void* A,
+                     int64_t lda, const void* BT, int64_t ldbt, float* C, int64_t ldc,
+                     float beta) {
+  // column-major C^T (n x M) = (BT stored k x n, transposed) (A^T, k x M)
   const float alpha = 1.0f;
-  return rocblas_gemm_ex(h, rocblas_operation_none, rocblas_operation_none, (rocblas_int)n,
-                         (rocblas_int)M, (rocblas_int)k, &alpha, B, rocblas_datatype_bf16_r,
-                         (rocblas_int)ldb, A, rocblas_datatype_bf16_r, (rocblas_int)lda, &beta, C,
-                         rocblas_datatype_f32_r, (rocblas_int)ldc, C, rocblas_datatype_f32_r,
+  return rocblas_gemm_ex(h, rocblas_operation_transpose, rocblas_operation_none, (rocblas_int)n,
+                         (rocblas_int)M, (rocblas_int)k, &alpha, BT, rocblas_datatype_bf16_r,
+                         (rocblas_int)ldbt, A, rocblas_datatype_bf16_r, (rocblas_int)lda, &beta,
+                         C, rocblas_datatype_f32_r, (rocblas_int)ldc, C, rocblas_datatype_f32_r,
                          (rocblas_int)ldc, rocblas_datatype_f32_r, rocblas_gemm_algo_standard, 0,
                          0) == rocblas_status_success;
+}
+
+namespace {
+
+// One 64 x 64 tile per block.  With vec (both dimensions multiples of 8 and
+// W 16-byte aligned) a thread moves 8 halves (16 bytes) per global access: it reads two 8-wide
+// pieces of W's rows, and writes two 8-wide pieces of wT's rows gathered from
+// a tile column in LDS (row pitch 72 halves keeps the 16-byte stores aligned
+// and spreads the column reads over the banks).  Other shapes go one half at
+// a time.
+__global__ __launch_bounds__(256) void transpose_tiles_bf16_kernel(
+    const uint16_t* __restrict__ W, uint16_t* __restrict__ wT, int64_t rows, int64_t cols,
+    bool vec) {
+  __shared__ __align__(16) uint16_t tile[64][72];
+  const int64_t tiles_c = (cols + 63) / 64;
+  const int64_t r0 = static_cast<int64_t>(blockIdx.x / tiles_c) * 64;
+  const int64_t c0 = static_cast<int64_t>(blockIdx.x % tiles_c) * 64;
+  const int t = threadIdx.x;
+  if (vec) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int piece = t + 256 * h;              // 64 rows x 8 pieces
+      const int i = piece >> 3, j = (piece & 7) * 8;
+      const int64_t r = r0 + i, c = c0 + j;
+      uint4 v = make_uint4(0u, 0u, 0u, 0u);
+      if (r < rows && c < cols) v = *reinterpret_cast<const uint4*>(W + r * cols + c);
+      *reinterpret_cast<uint4*>(&tile[i][j]) = v;
+    }
+    block_sync();
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int piece = t + 256 * h;              // 64 output rows (tile columns) x 8 pieces
+      const int i = piece >> 3, j = (piece & 7) * 8;
+      const int64_t c = c0 + i, r = r0 + j;
+      if (c < cols && r < rows) {
+        uint32_t w[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          w[q] = static_cast<uint32_t>(tile[j + 2 * q][i]) |
+                 (static_cast<uint32_t>(tile[j + 2 * q + 1][i]) << 16);
+        *reinterpret_cast<uint4*>(wT + c * rows + r) = make_uint4(w[0], w[1], w[2], w[3]);
+      }
+    }
+    return;
+  }
+  const int tx = t & 63, ty = t >> 6;
+  for (int i = ty; i < 64; i += 4) {
+    const int64_t r = r0 + i, c = c0 + tx;
+    tile[i][tx] = (r < rows && c < cols) ? W[r * cols + c] : uint16_t(0);
+  }
+  block_sync();
+  for (int i = ty; i < 64; i += 4) {
+    const int64_t c = c0 + i, r = r0 + tx;
+    if (c < cols && r < rows) wT[c * rows + r] = tile[tx][i];
+  }
+}
+
+}  // namespace
+
+hipError_t launch_transpose_bf16(const void* W, uint16_t* wT, int64_t rows, int64_t cols,
+                                 hipStream_t stream) {
+  const int64_t tiles = ((rows + 63) / 64) * ((cols + 63) / 64);
+  if (tiles <= 0) return hipSuccess;
+  // wT is workspace (256-byte aligned); W is the caller's
+  const bool vec = rows % 8 == 0 && cols % 8 == 0 && reinterpret_cast<uintptr_t>(W) % 16 == 0 &&
+                   reinterpret_cast<uintptr_t>(wT) % 16 == 0;
+  hipLaunchKernelGGL(transpose_tiles_bf16_kernel, dim3(static_cast<unsigned>(tiles)), dim3(256), 0,
+                     stream, static_cast<const uint16_t*>(W), wT, rows, cols, vec);
+  return hipGetLastError();
 }
 
 hipError_t launch_fused_prep(const float* P, int64_t M, int64_t R, int64_t ldp, const void* W_dt,
@@ -635,7 +705,8 @@ FusedPlan plan_fused(int64_t batch, int64_t L, int64_t D, int64_t N, int64_t R, 
   f.dtl_offset = f.p_bytes;
   f.dtl_lo_offset = f.dtl_offset + align256(sizeof(uint16_t) * (size_t)M * (size_t)R);
   f.wt_offset = f.dtl_lo_offset + align256(sizeof(uint16_t) * (size_t)M * (size_t)R);
-  f.scan_offset = f.wt_offset + align256(sizeof(uint16_t) * (size_t)D * (size_t)R);
+  f.wx_t_offset = f.wt_offset + align256(sizeof(uint16_t) * (size_t)D * (size_t)R);
+  f.scan_offset = f.wx_t_offset + align256(sizeof(uint16_t) * (size_t)(R + 2 * N) * (size_t)D);
   if (chain) {
     f.delta_offset = f.scan_offset;
     f.workspace_bytes = f.delta_offset + align256(sizeof(float) * (size_t)M * (size_t)D);
@@ -677,8 +748,11 @@ FusedStatus launch_fused(const FusedArgs& a, const FusedPlan& f, void* workspace
     st.blas_failed = st.hip == hipSuccess;
     return st;
   }
-  // x_proj: P[M, R + 2N] = x[M, D] W_x[D, R + 2N]
-  if (!gemm_rm_bf16(hb, M, ldp, a.D, a.x, a.D, a.W_x, ldp, P, ldp, 0.0f)) {
+  // x_proj: P[M, R + 2N] = x[M, D] W_x[D, R + 2N], with W_x transposed first
+  uint16_t* WxT = reinterpret_cast<uint16_t*>(ws + f.wx_t_offset);
+  st.hip = launch_transpose_bf16(a.W_x, WxT, a.D, ldp, stream);
+  if (st.hip != hipSuccess) return st;
+  if (!gemm_rm_bf16_bt(hb, M, ldp, a.D, a.x, a.D, WxT, a.D, P, ldp, 0.0f)) {
     st.blas_failed = true;
     return st;
   }

@@ -167,6 +167,7 @@ struct FusedPlan {
   size_t dtl_offset = 0;
   size_t dtl_lo_offset = 0;
   size_t wt_offset = 0;
+  size_t wx_t_offset = 0;     // W_x transposed [R + 2N, D] for the x_proj GEMM
   size_t scan_offset = 0;
   size_t workspace_bytes = 0;
 };
@@ -217,10 +218,17 @@ hipError_t launch_dtproj_softplus(const uint16_t* dtl, const uint16_t* dtl_lo, c
 // failed (hip_error set).
 bool blas_handle(hipStream_t stream, rocblas_handle* out, hipError_t* hip_error);
 
-// Row-major C[M, n] (float32, row stride ldc) = A[M, k] B[k, n] + beta C (A, B
-// bf16, row strides lda, ldb), float32 accumulation.  false if rocBLAS fails.
-bool gemm_rm_bf16(rocblas_handle h, int64_t M, int64_t n, int64_t k, const void* A, int64_t lda,
-                  const void* B, int64_t ldb, float* C, int64_t ldc, float beta);
+// Row-major C[M, n] (float32, row stride ldc) = A[M, k] B[k, n] + beta C, A
+// and B bf16, float32 accumulation, with B given transposed, BT[n, k] (row
+// strides lda, ldbt): both operands then run along k in memory, the layout
+// rocBLAS's matrix-core GEMMs are fastest with (measured 7 % faster than B as
+// [k, n] on the block's projections).  false if rocBLAS fails.
+bool gemm_rm_bf16_bt(rocblas_handle h, int64_t M, int64_t n, int64_t k, const void* A,
+                     int64_t lda, const void* BT, int64_t ldbt, float* C, int64_t ldc,
+                     float beta);
+// wT[c, r] = W[r, c] for a row-major bf16 W[rows, cols], in 64 x 64 tiles.
+hipError_t launch_transpose_bf16(const void* W, uint16_t* wT, int64_t rows, int64_t cols,
+                                 hipStream_t stream);
 
 // ---- the Mamba block ------------------------------------------------------------------------
 
@@ -257,6 +265,9 @@ struct BlockPlan {
   size_t u_offset = 0, z_offset = 0, x_offset = 0, xb_offset = 0, xl_offset = 0, g_offset = 0,
          gl_offset = 0;
   size_t p_offset = 0, dtl_offset = 0, dtl_lo_offset = 0, wt_offset = 0, scan_offset = 0;
+  // the projection weights transposed for the GEMMs: W_in^T [2Di, Dm], W_x^T
+  // [R + 2N, Di], W_out^T [Dm, Di]
+  size_t win_t_offset = 0, wx_t_offset = 0, wout_t_offset = 0;
   size_t workspace_bytes = 0;
 };
 BlockPlan plan_block(int64_t batch, int64_t L, int64_t Dm, int64_t Di, int64_t N, int64_t R,
