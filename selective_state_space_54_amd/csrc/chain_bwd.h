@@ -12,7 +12,9 @@
 //   dD += g_t x_t   dz_t = dout_t y_t SiLU'(z_t)   dh0 = a_0 lam_0
 //
 // A first pass (chain_scan_kernel in checkpoint mode) stores every lane's
-// state after each 16-step tile.  This kernel walks the tiles backwards: a
+// state after each 16-step tile, unless the forward call saved them (kOutSave,
+// which also keeps y before the gate: then dz reads it instead of reading y
+// out here).  This kernel walks the tiles backwards: a
 // lane recomputes its tile's 16 states from the checkpoint into registers,
 // then sweeps the tile backwards carrying a_{t+1} lam_{t+1} across tiles.
 // Sums over n (dx, ddelta, and y for dz) are the row reduce-scatter of the
