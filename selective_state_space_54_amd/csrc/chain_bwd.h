@@ -192,7 +192,7 @@ __global__ __launch_bounds__(kBlock) void chain_bwd_kernel(ChainBwdParams prm) {
   const bool has2 = wave == 1 || (kGate && wave == 0) || (kPre && wave == 2);
 
   struct Regs {
-    uint4 v, v2;
+    uint4 v, v2 = make_uint4(0u, 0u, 0u, 0u);
   };
   auto tile_of = [&](int64_t i) {            // iteration i walks tile last - i (clamped at 0)
     return i <= last ? last - i : int64_t(0);
@@ -203,11 +203,14 @@ __global__ __launch_bounds__(kBlock) void chain_bwd_kernel(ChainBwdParams prm) {
     if (has2) r.v2 = load_raw(src2 + kt * tile_bytes2 + (kt == last ? off2_tail : off2_full), esz2);
   };
   auto put = [&](const Regs& r, int buf, int64_t i) {
-    const bool pad = tile_of(i) == last && ls >= tail_steps;
     float v[4], w[4];
     unpack_raw(r.v, esz, v);
-    if (has2) unpack_raw(r.v2, esz2, w);
-    if (wave == 1 && pad) v[0] = v[1] = v[2] = v[3] = w[0] = w[1] = w[2] = w[3] = 0.0f;
+    unpack_raw(r.v2, esz2, w);   // unused by the wavefronts without a second tile
+    // steps past the end: delta and dout zero (the last tile only; a uniform
+    // branch, so the other tiles pay nothing for it)
+    if (wave == 1 && tile_of(i) == last) {
+      if (ls >= tail_steps) v[0] = v[1] = v[2] = v[3] = w[0] = w[1] = w[2] = w[3] = 0.0f;
+    }
     if (wave < 2) {
       lds_put4(&tin[buf][wave][ls][lq], v[0], v[1], v[2], v[3]);
       if (has2)

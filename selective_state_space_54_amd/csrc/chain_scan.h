@@ -331,7 +331,9 @@ __global__ __launch_bounds__(kBlock) void chain_scan_kernel(ChainParams prm) {
   auto put = [&](const Regs& r, int buf, int64_t k) {
     float v[4];
     unpack_raw(r.v, esz, v);
-    if (wave == 1 && k == last && pad_lane) v[0] = v[1] = v[2] = v[3] = 0.0f;   // delta
+    if (wave == 1 && k == last) {   // a uniform branch: the other tiles pay nothing
+      if (pad_lane) v[0] = v[1] = v[2] = v[3] = 0.0f;   // delta of steps past the end
+    }
     if (wave < 2) {
       lds_put4(&tin[buf][wave][ls][lq], v[0], v[1], v[2], v[3]);
     } else {
