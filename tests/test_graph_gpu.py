@@ -130,3 +130,37 @@ def test_backward_in_a_graph():
     keys = sorted(ref)
     replay_and_check(g, [grads[k] for k in keys], [ref[k] for k in keys],
                      lambda: mssm.selective_scan(t["x"], t["delta"], t["A"], t["B"], t["C"]))
+
+
+@pytest.mark.parametrize("design", ["chain"], indirect=True)
+def test_single_pass_training_pair_in_a_graph(design):
+    """The saving forward, the backward from saved states and the recomputing
+    backward (checkpoint pass + reverse kernel), captured together."""
+    gw = workloads.generate("mamba130m_layer_fp32", batch=2, L=333, D=256, N=16, seed=95)
+    ex = workloads.generate_extras(gw["workload"])
+    t = inputs_on_device(gw)
+    args = (t["x"], t["delta"], t["A"], t["B"], t["C"])
+    kw = dict(Dskip=dev(ex["Dskip"]), z=dev(ex["z"]), h0=dev(ex["h0"]))
+    dout = torch.from_numpy(np.random.default_rng(2).standard_normal((2, 333, 256))
+                            .astype(np.float32)).cuda()
+    y_ref, saved_ref = mssm.selective_scan_fwd_save(*args, **kw)
+    g_saved_ref = mssm.selective_scan_bwd_saved(*args, saved_ref, dout, **kw)
+    g_re_ref = mssm.selective_scan_bwd(*args, dout, **kw)
+    torch.cuda.synchronize()
+    y = torch.empty_like(y_ref)
+    saved = torch.empty_like(saved_ref)
+    g_saved = {k: torch.empty_like(v) for k, v in g_saved_ref.items()}
+    g_re = {k: torch.empty_like(v) for k, v in g_re_ref.items()}
+    nb = mssm.mssm_selective_scan_bwd_workspace_size(2, 333, 256, 16, torch.float32)
+    ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+
+    def work():
+        mssm.mssm_selective_scan_fwd_save(*args, y, saved, **kw)
+        mssm.mssm_selective_scan_bwd_saved(*args, saved, dout, g_saved, ws, **kw)
+        mssm.mssm_selective_scan_bwd(*args, dout, g_re, ws, **kw)
+
+    g = capture(work)
+    keys = sorted(g_saved_ref)
+    replay_and_check(g, [y] + [g_saved[k] for k in keys] + [g_re[k] for k in keys],
+                     [y_ref] + [g_saved_ref[k] for k in keys] + [g_re_ref[k] for k in keys],
+                     lambda: mssm.selective_scan(*args))
