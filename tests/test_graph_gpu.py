@@ -61,7 +61,8 @@ def test_scan_with_workspace_in_a_graph():
                                                                 to["B"], to["C"]))
 
 
-def test_single_pass_scan_with_all_parts_in_a_graph():
+@pytest.mark.parametrize("design", ["chain"], indirect=True)
+def test_single_pass_scan_with_all_parts_in_a_graph(design):
     """8192 channels: the single-pass kernel, which uses no workspace."""
     gw = workloads.generate("mid_bf16", batch=2, L=300, D=4096, N=16, seed=94)
     ex = workloads.generate_extras(gw["workload"])
