@@ -69,7 +69,7 @@
 extern "C" {
 #endif
 
-#define MSSM_ABI_VERSION 4
+#define MSSM_ABI_VERSION 5
 
 typedef enum {
     MSSM_SUCCESS = 0,
