@@ -189,11 +189,13 @@ FusedStatus launch_block(const BlockArgs& a, const BlockPlan& bp, void* workspac
   uint16_t* dtl = reinterpret_cast<uint16_t*>(ws + bp.dtl_offset);
   uint16_t* dtl_lo = reinterpret_cast<uint16_t*>(ws + bp.dtl_lo_offset);
   uint16_t* wT = reinterpret_cast<uint16_t*>(ws + bp.wt_offset);
-  rocblas_handle hb;
-  if (!blas_handle(stream, &hb, &st.hip)) {
+  BlasLease blas(stream);
+  if (!blas.ok()) {
+    st.hip = blas.hip_error();
     st.blas_failed = st.hip == hipSuccess;
     return st;
   }
+  const rocblas_handle hb = blas.get();
   // the weights transposed once per call, so every GEMM reads both operands
   // along k (W_in^T rows 0..Di-1 are u's columns, Di..2Di-1 z's)
   uint16_t* WinT = reinterpret_cast<uint16_t*>(ws + bp.win_t_offset);

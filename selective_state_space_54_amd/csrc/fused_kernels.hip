@@ -549,22 +549,23 @@ hipError_t launch_fused_scan_v(const FusedScanArgs& a, const ScanPlan& p, hipStr
 
 }  // namespace
 
-bool blas_handle(hipStream_t stream, rocblas_handle* out, hipError_t* hip_error) {
-  *hip_error = hipSuccess;
+BlasLease::BlasLease(hipStream_t stream) : lock_(g_blas_mutex) {
   int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) { *hip_error = e; return false; }
-  if (dev < 0 || dev >= 64) { *hip_error = hipErrorInvalidDevice; return false; }
-  std::lock_guard<std::mutex> lock(g_blas_mutex);
+  hip_ = hipGetDevice(&dev);
+  if (hip_ != hipSuccess) return;
+  if (dev < 0 || dev >= 64) {
+    hip_ = hipErrorInvalidDevice;
+    return;
+  }
   if (!g_blas[dev]) {
     if (rocblas_create_handle(&g_blas[dev]) != rocblas_status_success) {
       g_blas[dev] = nullptr;
-      return false;
+      return;
     }
   }
-  if (rocblas_set_stream(g_blas[dev], stream) != rocblas_status_success) return false;
-  *out = g_blas[dev];
-  return true;
+  if (rocblas_set_stream(g_blas[dev], stream) != rocblas_status_success) return;
+  handle_ = g_blas[dev];
+  ok_ = true;
 }
 
 bool gemm_rm_bf16_bt(rocblas_handle h, int64_t M, int64_t n, int64_t k, const void* A,
@@ -743,11 +744,13 @@ FusedStatus launch_fused(const FusedArgs& a, const FusedPlan& f, void* workspace
   float* P = reinterpret_cast<float*>(ws);
   const int64_t M = a.batch * a.L;
   const int64_t ldp = a.R + 2 * a.N;
-  rocblas_handle hb;
-  if (!blas_handle(stream, &hb, &st.hip)) {
+  BlasLease blas(stream);
+  if (!blas.ok()) {
+    st.hip = blas.hip_error();
     st.blas_failed = st.hip == hipSuccess;
     return st;
   }
+  const rocblas_handle hb = blas.get();
   // x_proj: P[M, R + 2N] = x[M, D] W_x[D, R + 2N], with W_x transposed first
   uint16_t* WxT = reinterpret_cast<uint16_t*>(ws + f.wx_t_offset);
   st.hip = launch_transpose_bf16(a.W_x, WxT, a.D, ldp, stream);

@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "mssm.h"
 
 namespace mssm {
@@ -213,10 +215,25 @@ hipError_t launch_dtproj_softplus(const uint16_t* dtl, const uint16_t* dtl_lo, c
                                   const float* bias, float* delta, int64_t M, int64_t D,
                                   int64_t R, hipStream_t stream);
 
-// The device's rocBLAS handle (created on first use, kept until exit), bound
-// to `stream`.  false: rocBLAS failed (hip_error == hipSuccess) or a HIP call
-// failed (hip_error set).
-bool blas_handle(hipStream_t stream, rocblas_handle* out, hipError_t* hip_error);
+// The current device's rocBLAS handle (created on first use, kept until exit),
+// bound to `stream` and held by this object until it goes out of scope: the
+// handle is shared by every call on the device, so a call keeps it, and the
+// stream it is bound to, to itself until its last GEMM is enqueued (calls
+// from several host threads then enqueue their GEMMs one call at a time).
+// ok() false: rocBLAS failed (hip_error() == hipSuccess) or a HIP call failed.
+class BlasLease {
+ public:
+  explicit BlasLease(hipStream_t stream);
+  bool ok() const { return ok_; }
+  rocblas_handle get() const { return handle_; }
+  hipError_t hip_error() const { return hip_; }
+
+ private:
+  std::unique_lock<std::mutex> lock_;
+  rocblas_handle handle_ = nullptr;
+  hipError_t hip_ = hipSuccess;
+  bool ok_ = false;
+};
 
 // Row-major C[M, n] (float32, row stride ldc) = A[M, k] B[k, n] + beta C, A
 // and B bf16, float32 accumulation, with B given transposed, BT[n, k] (row

@@ -116,3 +116,38 @@ def test_block_full_size_sampled_rows(design):
     rows = [0, 15]
     r = assert_parity(out[rows], oracle_block(g, rows=rows), "bf16", "mamba_block_bf16")
     print("mamba_block_bf16", r, flush=True)
+
+
+def test_block_from_two_host_threads_on_two_streams():
+    """The library shares one rocBLAS handle per device; two host threads
+    calling the block at once on their own streams must each get their own
+    result (the handle and its stream are held for a whole call)."""
+    import threading
+    gs = [workloads.generate_block(batch=2, L=200, Dm=64, D=128, N=16, R=32, seed=s)
+          for s in (81, 82)]
+    ts = [{k: dev(g[k]) for k in BLOCK_KEYS} for g in gs]
+    refs = [mssm.mamba_block(*(t[k] for k in BLOCK_KEYS)) for t in ts]
+    torch.cuda.synchronize()
+    outs = [[None] * 6, [None] * 6]
+    errors = []
+
+    def work(i):
+        try:
+            s = torch.cuda.Stream()
+            with torch.cuda.stream(s):
+                for r in range(6):
+                    outs[i][r] = mssm.mamba_block(*(ts[i][k] for k in BLOCK_KEYS), stream=s)
+            s.synchronize()
+        except Exception as e:   # reported below, in the main thread
+            errors.append(e)
+
+    threads = [threading.Thread(target=work, args=(i,)) for i in (0, 1)]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join()
+    assert not errors, errors
+    torch.cuda.synchronize()
+    for i in (0, 1):
+        for r in range(6):
+            assert torch.equal(outs[i][r], refs[i]), f"thread {i} call {r}"
