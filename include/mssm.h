@@ -51,6 +51,10 @@
  *
  * Streams: `stream` is a hipStream_t passed as void*; NULL means the null
  * stream.  Work is enqueued asynchronously; the call does not synchronise.
+ * Calls may come from several host threads at once, each with its own
+ * stream and buffers (the GEMMs of the fused path and the block share one
+ * rocBLAS handle per device, which a call holds until its GEMMs are
+ * enqueued).
  *
  * Errors: every entry point returns an mssm_status.  Arguments are checked
  * before any HIP call is made, so argument errors are reported on machines
