@@ -54,8 +54,7 @@ bool single_pass_chosen(int64_t channels) {
   return d == Design::kChain || channels >= kMinChannels;
 }
 
-bool chain_scan_applies(const ScanArgs& a) {
-  if (design_setting() == Design::kChunked) return false;
+bool chain_layout_ok(const ScanArgs& a) {
   if (a.N != chain::kStates || a.D % chain::kChannels != 0 || a.L < 1 || a.batch < 1)
     return false;
   // 4-value loads of x, delta, z, B, C and 16-byte stores of y
@@ -65,8 +64,12 @@ bool chain_scan_applies(const ScanArgs& a) {
     return false;
   // 32-bit lane offsets within a 16-step tile; grid size
   if (a.D * chain::kTile * static_cast<int64_t>(sizeof(float)) >= (int64_t(1) << 31)) return false;
-  if (a.batch > (int64_t(1) << 31) / (a.D / chain::kChannels)) return false;
-  return single_pass_chosen(a.batch * a.D);
+  return a.batch <= (int64_t(1) << 31) / (a.D / chain::kChannels);
+}
+
+bool chain_scan_applies(const ScanArgs& a) {
+  return design_setting() != Design::kChunked && chain_layout_ok(a) &&
+         single_pass_chosen(a.batch * a.D);
 }
 
 bool chain_fused_applies(int64_t batch, int64_t D, int64_t N, int64_t R, const void* x,
@@ -78,17 +81,6 @@ bool chain_fused_applies(int64_t batch, int64_t D, int64_t N, int64_t R, const v
   if (D * chain::kTile * static_cast<int64_t>(sizeof(float)) >= (int64_t(1) << 31)) return false;
   if (batch > (int64_t(1) << 31) / (D / chain::kChannels)) return false;
   return single_pass_chosen(batch * D);
-}
-
-bool chain_save_layout_ok(const ScanArgs& a) {
-  if (a.N != chain::kStates || a.D % chain::kChannels != 0 || a.L < 1 || a.batch < 1)
-    return false;
-  const size_t in_align = a.dtype == MSSM_FLOAT32 ? 16 : 8;
-  if (!aligned(a.x, in_align) || !aligned(a.delta, in_align) || !aligned(a.B, in_align) ||
-      !aligned(a.C, in_align) || (a.z && !aligned(a.z, in_align)) || !aligned(a.y, 16))
-    return false;
-  if (a.D * chain::kTile * static_cast<int64_t>(sizeof(float)) >= (int64_t(1) << 31)) return false;
-  return a.batch <= (int64_t(1) << 31) / (a.D / chain::kChannels);
 }
 
 namespace {

@@ -538,7 +538,7 @@ mssm_status mssm_selective_scan_fwd_save(const void* x, const void* delta, const
   a.z = z;
   a.h0 = h0;
   a.h_last = h_last;
-  if (!mssm::chain_save_layout_ok(a)) return MSSM_ERROR_NOT_SUPPORTED;
+  if (!mssm::chain_layout_ok(a)) return MSSM_ERROR_NOT_SUPPORTED;
   char* base = reinterpret_cast<char*>(saved);
   float* ck = reinterpret_cast<float*>(base + lay.ck_offset);
   float* y_pre = z ? reinterpret_cast<float*>(base + lay.y_pre_offset) : nullptr;

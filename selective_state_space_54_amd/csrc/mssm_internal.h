@@ -60,11 +60,13 @@ bool single_pass_chosen(int64_t channels);
 bool chain_scan_applies(const ScanArgs& a);
 hipError_t launch_chain_scan(const ScanArgs& a, hipStream_t stream);
 
+// Whether the arguments fit the single-pass layout (N = 16, D % 16 == 0,
+// alignment, sizes), whatever the channel count or MSSM_SCAN_DESIGN.
+bool chain_layout_ok(const ScanArgs& a);
 // Forward that also saves the backward pass's inputs (first-order input term):
 // the state after every 16-step tile into ck [batch, tiles, D, N] and, with
 // the gate, the output before the gate into y_pre [batch, L, D].  Needs the
-// single-pass layout (shape and alignment), whatever the channel count.
-bool chain_save_layout_ok(const ScanArgs& a);
+// single-pass layout.
 hipError_t launch_chain_save(const ScanArgs& a, float* ck, float* y_pre, hipStream_t stream);
 
 // Where the saved tensors sit in the caller's buffer (256-byte aligned
