@@ -92,9 +92,26 @@ def test_block_small_shapes(shape, chunk_len):
     assert_parity(run_block(g), oracle_block(g), "bf16", f"block {shape}")
 
 
+CHAIN_SHAPES = [  # batch, L, Dm, Di (a multiple of 16), N = 16, R, k
+    (1, 1, 32, 64, 16, 16, 4), (2, 100, 48, 96, 16, 48, 4), (1, 257, 128, 256, 16, 160, 4),
+    (1, 65, 16, 32, 16, 256, 1),
+]
+
+
+@pytest.mark.parametrize("design", ["chain"], indirect=True)
+@pytest.mark.parametrize("shape", CHAIN_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_block_single_pass_shapes(shape, design):
+    batch, L, Dm, Di, N, R, k = shape
+    print(f"case block single pass {shape}", flush=True)
+    g = workloads.generate_block(batch=batch, L=L, Dm=Dm, D=Di, N=N, R=R, conv_k=k,
+                                 seed=750 + L + R)
+    assert_parity(run_block(g), oracle_block(g), "bf16", f"block single pass {shape}")
+
+
+@pytest.mark.parametrize("design", ["auto", "chain"], indirect=True)
 @pytest.mark.parametrize("drop", [("conv_b",), ("Dskip",), ("conv_b", "Dskip")],
                          ids=lambda d: "-".join(d))
-def test_block_optional_parts_absent(drop):
+def test_block_optional_parts_absent(drop, design):
     g = workloads.generate_block(batch=2, L=150, Dm=64, D=128, N=16, R=32, seed=77)
     assert_parity(run_block(g, drop), oracle_block(g, drop), "bf16", f"block without {drop}")
 

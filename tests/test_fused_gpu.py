@@ -72,6 +72,22 @@ def test_fused_small_shapes(shape, chunk_len):
     assert_parity(run_fused(g), oracle_fused(g), "bf16", f"fused {shape}")
 
 
+CHAIN_SHAPES = [  # batch, L, D, N = 16, R from 16 to 256: one step, ragged tails
+    (1, 1, 16, 16, 16), (2, 17, 32, 16, 48), (1, 100, 64, 16, 64), (2, 33, 48, 16, 128),
+    (1, 257, 96, 16, 160), (2, 64, 32, 16, 208), (1, 31, 128, 16, 256),
+]
+
+
+@pytest.mark.parametrize("design", ["chain"], indirect=True)
+@pytest.mark.parametrize("shape", CHAIN_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_fused_single_pass_shapes(shape, design):
+    """The single pass (delta from the dt_proj + softplus kernel) at small sizes."""
+    batch, L, D, N, R = shape
+    print(f"case fused single pass {shape}", flush=True)
+    g = workloads.generate("fused_proj_bf16", batch=batch, L=L, D=D, N=N, R=R, seed=950 + L + R)
+    assert_parity(run_fused(g), oracle_fused(g), "bf16", f"fused single pass {shape}")
+
+
 @pytest.mark.parametrize("cpl", ["1", "2"])
 def test_fused_both_chain_per_lane_variants(cpl):
     old = os.environ.get("MSSM_CPL")
@@ -87,7 +103,8 @@ def test_fused_both_chain_per_lane_variants(cpl):
     assert_parity(y, oracle_fused(g), "bf16", f"fused cpl={cpl}")
 
 
-def test_fused_zero_dt_proj_matches_plain_scan_on_gpu():
+@pytest.mark.parametrize("design", ["auto", "chain"], indirect=True)
+def test_fused_zero_dt_proj_matches_plain_scan_on_gpu(design):
     """W_dt = 0: Delta = softplus(bias) for every token; the fused result must
     equal the plain scan run on that Delta and on B, C taken from x @ W_x."""
     g = workloads.generate("fused_proj_bf16", batch=2, L=150, D=128, N=16, R=32, seed=41)
