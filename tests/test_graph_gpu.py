@@ -165,3 +165,23 @@ def test_single_pass_training_pair_in_a_graph(design):
     replay_and_check(g, [y] + [g_saved[k] for k in keys] + [g_re[k] for k in keys],
                      [y_ref] + [g_saved_ref[k] for k in keys] + [g_re_ref[k] for k in keys],
                      lambda: mssm.selective_scan(*args))
+
+
+@pytest.mark.parametrize("design", ["chain"], indirect=True)
+def test_fused_single_pass_in_a_graph(design):
+    """The fused SSM through the single pass (the x_proj GEMM on rocBLAS, the
+    dt low-rank split, W_dt's transpose, dt_proj + softplus, the scan)."""
+    g = workloads.generate("fused_proj_bf16", batch=5, L=300, D=64, N=16, R=32, seed=92)
+    t = {k: dev(g[k]) for k in ("x", "W_x", "W_dt", "dt_bias", "A")}
+    w = g["workload"]
+    nb = mssm.mssm_selective_ssm_fused_workspace_size(w.batch, w.L, w.D, w.N, w.R, torch.bfloat16)
+    ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    y = torch.empty((w.batch, w.L, w.D), dtype=torch.float32, device="cuda")
+    ref = mssm.selective_ssm_fused(t["x"], t["W_x"], t["W_dt"], t["dt_bias"], t["A"])
+    torch.cuda.synchronize()
+    graph = capture(lambda: mssm.mssm_selective_ssm_fused_fwd(t["x"], t["W_x"], t["W_dt"],
+                                                              t["dt_bias"], t["A"], y, ws))
+    other = workloads.generate("fused_proj_bf16", batch=4, L=100, D=32, N=16, R=16, seed=93)
+    to = {k: dev(other[k]) for k in ("x", "W_x", "W_dt", "dt_bias", "A")}
+    replay_and_check(graph, [y], [ref], lambda: mssm.selective_ssm_fused(
+        to["x"], to["W_x"], to["W_dt"], to["dt_bias"], to["A"]))
