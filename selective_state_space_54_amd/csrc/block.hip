@@ -151,15 +151,14 @@ BlockPlan plan_block(int64_t batch, int64_t L, int64_t Dm, int64_t Di, int64_t N
   b.x_offset = off;      off += align256(sizeof(float) * M * di);
   b.xb_offset = off;     off += align256(sizeof(uint16_t) * M * di);
   b.xl_offset = off;     off += align256(sizeof(uint16_t) * M * di);
-  b.g_offset = off;      off += align256(sizeof(uint16_t) * M * di);
-  b.gl_offset = off;     off += align256(sizeof(uint16_t) * M * di);
+  b.g_offset = off;      off += align256(sizeof(uint16_t) * M * 2 * di);
   b.p_offset = off;      off += align256(sizeof(float) * M * (size_t)(R + 2 * N));
   b.dtl_offset = off;    off += align256(sizeof(uint16_t) * M * (size_t)R);
   b.dtl_lo_offset = off; off += align256(sizeof(uint16_t) * M * (size_t)R);
   b.wt_offset = off;     off += align256(sizeof(uint16_t) * di * (size_t)R);
   b.win_t_offset = off;  off += align256(sizeof(uint16_t) * 2 * di * (size_t)Dm);
   b.wx_t_offset = off;   off += align256(sizeof(uint16_t) * (size_t)(R + 2 * N) * di);
-  b.wout_t_offset = off; off += align256(sizeof(uint16_t) * (size_t)Dm * di);
+  b.wout_t_offset = off; off += align256(sizeof(uint16_t) * (size_t)Dm * 2 * di);
   b.scan_offset = off;   off += b.scan.workspace_bytes;
   b.workspace_bytes = off;
   return b;
@@ -183,8 +182,11 @@ FusedStatus launch_block(const BlockArgs& a, const BlockPlan& bp, void* workspac
   float* X = reinterpret_cast<float*>(ws + bp.x_offset);
   uint16_t* Xb = reinterpret_cast<uint16_t*>(ws + bp.xb_offset);
   uint16_t* Xl = reinterpret_cast<uint16_t*>(ws + bp.xl_offset);
+  // the gated SSM output as a bf16 hi + lo pair: with the single pass the two
+  // column halves of one [M, 2 Di] matrix (out_proj is then one GEMM over
+  // k = 2 Di against W_out^T stacked twice), else two [M, Di] matrices
   uint16_t* G = reinterpret_cast<uint16_t*>(ws + bp.g_offset);
-  uint16_t* Gl = reinterpret_cast<uint16_t*>(ws + bp.gl_offset);
+  uint16_t* Gl = bp.chain ? G + Di : G + M * Di;
   float* P = reinterpret_cast<float*>(ws + bp.p_offset);
   uint16_t* dtl = reinterpret_cast<uint16_t*>(ws + bp.dtl_offset);
   uint16_t* dtl_lo = reinterpret_cast<uint16_t*>(ws + bp.dtl_lo_offset);
@@ -203,7 +205,10 @@ FusedStatus launch_block(const BlockArgs& a, const BlockPlan& bp, void* workspac
   uint16_t* WoutT = reinterpret_cast<uint16_t*>(ws + bp.wout_t_offset);
   st.hip = launch_transpose_bf16(a.W_in, WinT, Dm, 2 * Di, stream);
   if (st.hip == hipSuccess) st.hip = launch_transpose_bf16(a.W_x, WxT, Di, ldp, stream);
-  if (st.hip == hipSuccess) st.hip = launch_transpose_bf16(a.W_out, WoutT, Di, Dm, stream);
+  // W_out^T [Dm, 2 Di]: columns Di.. repeat columns 0..Di-1
+  if (st.hip == hipSuccess) st.hip = launch_transpose_bf16(a.W_out, WoutT, Di, Dm, stream, 2 * Di);
+  if (st.hip == hipSuccess)
+    st.hip = launch_transpose_bf16(a.W_out, WoutT + Di, Di, Dm, stream, 2 * Di);
   if (st.hip != hipSuccess) return st;
   // input projection: u = u0 W_in[:, :Di], z = u0 W_in[:, Di:]
   if (!gemm_rm_bf16_bt(hb, M, Di, Dm, a.u0, Dm, WinT, Dm, U, Di, 0.0f) ||
@@ -238,6 +243,7 @@ FusedStatus launch_block(const BlockArgs& a, const BlockPlan& bp, void* workspac
     ca.z = Z;
     ca.y = G;
     ca.y_lo = Gl;
+    ca.ld_y = 2 * Di;
     ca.y_bf16 = true;
     ca.batch = a.batch;
     ca.L = a.L;
@@ -271,8 +277,11 @@ FusedStatus launch_block(const BlockArgs& a, const BlockPlan& bp, void* workspac
   }
   if (st.hip != hipSuccess) return st;
   // output projection of the gated result G = hi + lo
-  if (!gemm_rm_bf16_bt(hb, M, Dm, Di, G, Di, WoutT, Di, a.out, Dm, 0.0f) ||
-      !gemm_rm_bf16_bt(hb, M, Dm, Di, Gl, Di, WoutT, Di, a.out, Dm, 1.0f))
+  const bool out_ok =
+      bp.chain ? gemm_rm_bf16_bt(hb, M, Dm, 2 * Di, G, 2 * Di, WoutT, 2 * Di, a.out, Dm, 0.0f)
+               : gemm_rm_bf16_bt(hb, M, Dm, Di, G, Di, WoutT, 2 * Di, a.out, Dm, 0.0f) &&
+                     gemm_rm_bf16_bt(hb, M, Dm, Di, Gl, Di, WoutT, 2 * Di, a.out, Dm, 1.0f);
+  if (!out_ok)
     st.blas_failed = true;
   return st;
 }

@@ -9,16 +9,18 @@
 namespace mssm {
 
 hipError_t launch_chain_fused(const ChainFusedArgs& a, hipStream_t stream) {
-  const chain::ChainParams p{a.x,    a.delta,     a.P + a.R, a.P + a.R + chain::kStates,
-                             a.z,    a.A,         a.Dskip,   nullptr,
-                             nullptr, a.y,        a.y_lo,    a.L,
-                             a.D,    a.ldp};
+  chain::ChainParams p{a.x,     a.delta, a.P + a.R, a.P + a.R + chain::kStates,
+                       a.z,     a.A,     a.Dskip,   nullptr,
+                       nullptr, a.y,     a.y_lo,    a.L,
+                       a.D,     a.ldp};
   if (!a.x_f32) {
     if (a.z || a.Dskip || a.y_bf16) return hipErrorInvalidValue;   // the fused SSM's form only
     return chain::launch_io<chain::ChainIO<uint16_t, float, float, float>, PlainVariant>(
         p, a.batch, stream);
   }
   if (!a.z || !a.y_bf16 || !a.y_lo) return hipErrorInvalidValue;   // the block's form only
+  p.ld_y = a.ld_y ? a.ld_y : a.D;
+  if (p.ld_y < a.D || p.ld_y % 8 != 0) return hipErrorInvalidValue;   // 16-byte rows
   using IO = chain::ChainIO<float, float, float, uint16_t>;
   if (a.Dskip) return chain::launch_io<IO, Variant<false, true, true>>(p, a.batch, stream);
   return chain::launch_io<IO, Variant<false, false, true>>(p, a.batch, stream);

@@ -234,6 +234,7 @@ struct ChainParams {
   int64_t L, D, ld_bc;
   float* ck = nullptr;    // [batch, tiles, D, N] states after each tile (the last tile's unused)
   float* y_pre = nullptr; // [batch, L, D] float32 output before the gate
+  int64_t ld_y = 0;       // bfloat16 pair output (TY = uint16_t): row stride of y and y_lo
 };
 
 // grid: batch * D / 16 blocks of kBlock lanes.  Requirements (checked by the
@@ -300,8 +301,12 @@ __global__ __launch_bounds__(kBlock) void chain_scan_kernel(ChainParams prm) {
   }
   const char* zsrc = V::kGate ? static_cast<const char*>(prm.z) + (b * L * D + d0) * sizeof(TX)
                               : nullptr;   // loaded by wavefront 0
-  char* yb = static_cast<char*>(prm.y) + (b * L * D + d0) * sizeof(TY);
-  char* yb_lo = sizeof(TY) == 2 ? static_cast<char*>(prm.y_lo) + (b * L * D + d0) * sizeof(TY)
+  // y rows: D apart, or ld_y apart for the bfloat16 pair (y and y_lo may then
+  // be the two column halves of one [batch * L, 2 D] matrix)
+  int64_t ldy = D;
+  if constexpr (sizeof(TY) == 2) ldy = prm.ld_y;
+  char* yb = static_cast<char*>(prm.y) + (b * L * ldy + d0) * sizeof(TY);
+  char* yb_lo = sizeof(TY) == 2 ? static_cast<char*>(prm.y_lo) + (b * L * ldy + d0) * sizeof(TY)
                                 : nullptr;
   const int64_t ntiles = (L + kTile - 1) / kTile;
   const int64_t last = ntiles - 1;
@@ -313,7 +318,7 @@ __global__ __launch_bounds__(kBlock) void chain_scan_kernel(ChainParams prm) {
   const uint32_t zoff_full = static_cast<uint32_t>((ls * D + lq) * sizeof(TX));
   const uint32_t zoff_tail = static_cast<uint32_t>((ls_tail * D + lq) * sizeof(TX));
   const bool pad_lane = ls >= tail_steps;
-  const uint32_t yoff = static_cast<uint32_t>((ls * D + lq) * sizeof(TY));
+  const uint32_t yoff = static_cast<uint32_t>((ls * ldy + lq) * sizeof(TY));
 
   struct Regs {
     uint4 v, zv;
@@ -355,7 +360,7 @@ __global__ __launch_bounds__(kBlock) void chain_scan_kernel(ChainParams prm) {
     if (k == last && ls >= tail_steps) return;
     if constexpr (kPre)
       *reinterpret_cast<float4*>(prm.y_pre + (b * L + k * kTile + ls) * D + d0 + lq) = u;
-    const int64_t step_bytes = k * kTile * D * static_cast<int64_t>(sizeof(TY));
+    const int64_t step_bytes = k * kTile * ldy * static_cast<int64_t>(sizeof(TY));
     if constexpr (sizeof(TY) == 4) {
       *reinterpret_cast<float4*>(yb + step_bytes + yoff) = v;
     } else {

@@ -591,7 +591,7 @@ namespace {
 // a time.
 __global__ __launch_bounds__(256) void transpose_tiles_bf16_kernel(
     const uint16_t* __restrict__ W, uint16_t* __restrict__ wT, int64_t rows, int64_t cols,
-    bool vec) {
+    int64_t ldt, bool vec) {
   __shared__ __align__(16) uint16_t tile[64][72];
   const int64_t tiles_c = (cols + 63) / 64;
   const int64_t r0 = static_cast<int64_t>(blockIdx.x / tiles_c) * 64;
@@ -619,7 +619,7 @@ __global__ __launch_bounds__(256) void transpose_tiles_bf16_kernel(
         for (int q = 0; q < 4; ++q)
           w[q] = static_cast<uint32_t>(tile[j + 2 * q][i]) |
                  (static_cast<uint32_t>(tile[j + 2 * q + 1][i]) << 16);
-        *reinterpret_cast<uint4*>(wT + c * rows + r) = make_uint4(w[0], w[1], w[2], w[3]);
+        *reinterpret_cast<uint4*>(wT + c * ldt + r) = make_uint4(w[0], w[1], w[2], w[3]);
       }
     }
     return;
@@ -632,21 +632,24 @@ __global__ __launch_bounds__(256) void transpose_tiles_bf16_kernel(
   block_sync();
   for (int i = ty; i < 64; i += 4) {
     const int64_t c = c0 + i, r = r0 + tx;
-    if (c < cols && r < rows) wT[c * rows + r] = tile[tx][i];
+    if (c < cols && r < rows) wT[c * ldt + r] = tile[tx][i];
   }
 }
 
 }  // namespace
 
 hipError_t launch_transpose_bf16(const void* W, uint16_t* wT, int64_t rows, int64_t cols,
-                                 hipStream_t stream) {
+                                 hipStream_t stream, int64_t ldt) {
   const int64_t tiles = ((rows + 63) / 64) * ((cols + 63) / 64);
   if (tiles <= 0) return hipSuccess;
-  // wT is workspace (256-byte aligned); W is the caller's
-  const bool vec = rows % 8 == 0 && cols % 8 == 0 && reinterpret_cast<uintptr_t>(W) % 16 == 0 &&
+  if (ldt == 0) ldt = rows;
+  if (ldt < rows) return hipErrorInvalidValue;
+  // wT is workspace; W is the caller's
+  const bool vec = rows % 8 == 0 && cols % 8 == 0 && ldt % 8 == 0 &&
+                   reinterpret_cast<uintptr_t>(W) % 16 == 0 &&
                    reinterpret_cast<uintptr_t>(wT) % 16 == 0;
   hipLaunchKernelGGL(transpose_tiles_bf16_kernel, dim3(static_cast<unsigned>(tiles)), dim3(256), 0,
-                     stream, static_cast<const uint16_t*>(W), wT, rows, cols, vec);
+                     stream, static_cast<const uint16_t*>(W), wT, rows, cols, ldt, vec);
   return hipGetLastError();
 }
 

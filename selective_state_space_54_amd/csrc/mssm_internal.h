@@ -93,6 +93,7 @@ struct ChainFusedArgs {
   void* y = nullptr;              // float32, or bf16 hi part with y_bf16
   void* y_lo = nullptr;           // with y_bf16: bf16(y - hi)
   bool y_bf16 = false;
+  int64_t ld_y = 0;               // with y_bf16: row stride of y and y_lo (0: D)
   int64_t batch = 0, L = 0, D = 0;
 };
 bool chain_fused_applies(int64_t batch, int64_t D, int64_t N, int64_t R, const void* x,
@@ -245,9 +246,10 @@ class BlasLease {
 bool gemm_rm_bf16_bt(rocblas_handle h, int64_t M, int64_t n, int64_t k, const void* A,
                      int64_t lda, const void* BT, int64_t ldbt, float* C, int64_t ldc,
                      float beta);
-// wT[c, r] = W[r, c] for a row-major bf16 W[rows, cols], in 64 x 64 tiles.
+// wT[c * ldt + r] = W[r, c] for a row-major bf16 W[rows, cols], in 64 x 64
+// tiles; ldt >= rows, 0 meaning rows.
 hipError_t launch_transpose_bf16(const void* W, uint16_t* wT, int64_t rows, int64_t cols,
-                                 hipStream_t stream);
+                                 hipStream_t stream, int64_t ldt = 0);
 
 // ---- the Mamba block ------------------------------------------------------------------------
 
@@ -281,11 +283,11 @@ struct BlockArgs {
 struct BlockPlan {
   ScanPlan scan;
   bool chain = false;         // single pass; delta goes to the (by then unused) u buffer
-  size_t u_offset = 0, z_offset = 0, x_offset = 0, xb_offset = 0, xl_offset = 0, g_offset = 0,
-         gl_offset = 0;
+  // g_offset: the gated output's bf16 hi + lo pair, 2 * M * Di values
+  size_t u_offset = 0, z_offset = 0, x_offset = 0, xb_offset = 0, xl_offset = 0, g_offset = 0;
   size_t p_offset = 0, dtl_offset = 0, dtl_lo_offset = 0, wt_offset = 0, scan_offset = 0;
   // the projection weights transposed for the GEMMs: W_in^T [2Di, Dm], W_x^T
-  // [R + 2N, Di], W_out^T [Dm, Di]
+  // [R + 2N, Di], W_out^T twice side by side [Dm, 2Di]
   size_t win_t_offset = 0, wx_t_offset = 0, wout_t_offset = 0;
   size_t workspace_bytes = 0;
 };
