@@ -251,48 +251,52 @@ __device__ __forceinline__ void scan_steps(const T* __restrict__ xb, const T* __
       buf_load_vals<T, CPL>(dr, in_lane, soff, dn[j]);
       if constexpr (kGate) buf_load_vals<T, CPL>(zr, in_lane, soff, zn[j]);
     }
+    // No branch around a step: steps past the chunk (the last tile's tail) run
+    // with delta = 0, which gives Abar = 1 and a zero input term, so the state
+    // is left exactly as it was, and store nothing.  (A branch made the
+    // compiler merge every state register at its end: a copy per state and
+    // step.)
 #pragma unroll
     for (int j = 0; j < kTile; ++j) {
       const int s = base + j;
-      if (s < nsteps) {
-        const int cur = j & 1;
-        wait_scalar_loads();
-        if (s + 1 < nsteps) {
-          load_row_any<N, kPairs>(Bb + (int64_t)(s + 1) * N, Bv[cur ^ 1]);
-          if constexpr (kWithY) load_row_any<N, kPairs>(Cb + (int64_t)(s + 1) * N, Cv[cur ^ 1]);
-        }
-        float dx[CPL], yv[CPL];
+      const bool live = s < nsteps;              // uniform
+      const int cur = j & 1;
+      wait_scalar_loads();
+      const int64_t nxt = s + 1 < nsteps ? s + 1 : last;
+      load_row_any<N, kPairs>(Bb + nxt * N, Bv[cur ^ 1]);
+      if constexpr (kWithY) load_row_any<N, kPairs>(Cb + nxt * N, Cv[cur ^ 1]);
+      float dl[CPL], dx[CPL], yv[CPL];
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) {
+        dl[c] = live ? dc[j][c] : 0.0f;
+        dx[c] = dl[c] * xc[j][c];
+        yv[c] = 0.0f;
+      }
+#pragma unroll
+      for (int n = 0; n < N; ++n) {
 #pragma unroll
         for (int c = 0; c < CPL; ++c) {
-          dx[c] = dc[j][c] * xc[j][c];
-          yv[c] = 0.0f;
-        }
-#pragma unroll
-        for (int n = 0; n < N; ++n) {
-#pragma unroll
-          for (int c = 0; c < CPL; ++c) {
-            const float a = fast_exp2(dc[j][c] * k.A2[c][n]);          // Abar = exp(delta A)
-            if constexpr (V::kZoh) {
-              // (Abar - 1) / A * B * x: u = x B / A, then a u - u in one rounding
-              const float u = (xc[j][c] * k.Ainv[c][n]) * Bv[cur][n];
-              h[c][n] = __builtin_fmaf(a, h[c][n], __builtin_fmaf(a, u, -u));
-            } else {
-              h[c][n] = __builtin_fmaf(a, h[c][n], dx[c] * Bv[cur][n]);  // h = Abar h + (delta B) x
-            }
-            if constexpr (kWithY) yv[c] = __builtin_fmaf(Cv[cur][n], h[c][n], yv[c]);  // C . h
+          const float a = fast_exp2(dl[c] * k.A2[c][n]);               // Abar = exp(delta A)
+          if constexpr (V::kZoh) {
+            // (Abar - 1) / A * B * x: u = x B / A, then a u - u in one rounding
+            const float u = (xc[j][c] * k.Ainv[c][n]) * Bv[cur][n];
+            h[c][n] = __builtin_fmaf(a, h[c][n], __builtin_fmaf(a, u, -u));
+          } else {
+            h[c][n] = __builtin_fmaf(a, h[c][n], dx[c] * Bv[cur][n]);  // h = Abar h + (delta B) x
           }
+          if constexpr (kWithY) yv[c] = __builtin_fmaf(Cv[cur][n], h[c][n], yv[c]);  // C . h
         }
-        if constexpr (kWithY) {
+      }
+      if constexpr (kWithY) {
 #pragma unroll
-          for (int c = 0; c < CPL; ++c) {
-            if constexpr (V::kSkip) yv[c] = __builtin_fmaf(k.Dd[c], xc[j][c], yv[c]);
-            if constexpr (kGate) yv[c] *= silu(zc[j][c]);
-          }
-          buf_store_vals<CPL>(yr, out_lane, s * out_row, yv);
-        } else {
-#pragma unroll
-          for (int c = 0; c < CPL; ++c) S[c] += static_cast<double>(dc[j][c]);
+        for (int c = 0; c < CPL; ++c) {
+          if constexpr (V::kSkip) yv[c] = __builtin_fmaf(k.Dd[c], xc[j][c], yv[c]);
+          if constexpr (kGate) yv[c] *= silu(zc[j][c]);
         }
+        if (live) buf_store_vals<CPL>(yr, out_lane, s * out_row, yv);
+      } else {
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) S[c] += static_cast<double>(dl[c]);
       }
     }
 #pragma unroll
