@@ -67,9 +67,23 @@ bool chain_layout_ok(const ScanArgs& a) {
   return a.batch <= (int64_t(1) << 31) / (a.D / chain::kChannels);
 }
 
+// Forward only: from this many steps on the chunked order is taken even with
+// enough channels for the single pass.  Measured on MI355X at 8192-16384
+// channels with two input sets alternating (so the Infinity Cache cannot keep
+// the second read of x and delta that the chunked order makes), chunked time /
+// single-pass time: bfloat16 1.00-1.02 at L = 8192, 0.96 at 16384, 0.86 at
+// 32768; float32 1.03 at L = 16384, 0.93 at 32768 (and about 1.4 at L = 2048).
+// The backward keeps the single pass, which beats its chunked order at every
+// length.
+static int64_t long_sequence_steps(mssm_dtype dtype) {
+  return dtype == MSSM_BFLOAT16 ? 16384 : 32768;
+}
+
 bool chain_scan_applies(const ScanArgs& a) {
-  return design_setting() != Design::kChunked && chain_layout_ok(a) &&
-         single_pass_chosen(a.batch * a.D);
+  const Design d = design_setting();
+  if (d == Design::kChunked || !chain_layout_ok(a)) return false;
+  if (d == Design::kAuto && a.L >= long_sequence_steps(a.dtype)) return false;
+  return single_pass_chosen(a.batch * a.D);
 }
 
 bool chain_fused_applies(int64_t batch, int64_t D, int64_t N, int64_t R, const void* x,

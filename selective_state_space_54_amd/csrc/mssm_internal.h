@@ -55,8 +55,9 @@ ScanPlan plan_scan(int64_t batch, int64_t L, int64_t D, int64_t N, int cpl);
 bool single_pass_chosen(int64_t channels);
 
 // Single-pass scan with one lane per (channel, state index), for N = 16 and
-// shapes with many channels: whether it is used for these arguments (shape,
-// alignment, channel count, MSSM_SCAN_DESIGN), and its launch.
+// shapes with many channels: whether the forward uses it for these arguments
+// (shape, alignment, channel count, sequence length: bfloat16 from 16384 steps
+// and float32 from 32768 go chunked, MSSM_SCAN_DESIGN), and its launch.
 bool chain_scan_applies(const ScanArgs& a);
 hipError_t launch_chain_scan(const ScanArgs& a, hipStream_t stream);
 
