@@ -2,21 +2,30 @@
 """Selective-scan benchmark on one MI355X; prints ONE JSON line.
 
 A step is one full pass of the hot path (discretise, recurrence, read-out,
-store) over one batch of the workload, inputs already in HBM.  With at least
-8192 channels (batch * D) and N = 16 the library runs the single-pass kernel
-(one lane per channel and state); otherwise the chunked kernels (summaries,
-carries, output).  The headline workload is the Mamba-130M-layer-shaped float32 scan
-(batch 8, L 2048, D 1536, N 16); the other synthetic workloads are measured
-the same way with fewer steps and reported under "workloads".
+store; for the fused workload also the selection projections) over one batch
+of the workload, inputs already in HBM.  The headline workload is the largest
+single-GPU configuration, the long-sequence bfloat16 scan (batch 1, L 131072,
+D 2560, N 16): with 2560 channels it takes the chunked order (chunk summaries,
+carries, output).  The other synthetic workloads are measured the same way and
+reported under "workloads"; every scan workload rotates two input sets so no
+step finds its inputs in the 256 MB last-level cache left by the step before.
 
 value    = algorithmic bytes per step * steps / wall time of the timed region
-           (bytes = (x + delta + y) over batch*L*D plus (B + C) over batch*L*N)
-roofline = the scan kernel against its binding roof.  The scan is bound by
-           vector-ALU issue: each (b, t, d, n) element needs 4 single-rate fp32
-           VALU operations and one half-rate v_exp_f32 = 6 lane-issue slots; the
-           chip issues 256 CU * 4 SIMD * 16 lanes * 2.4 GHz = 39.32e12 slots/s,
-           so the element roof is 6553.6 Gelem/s.  Kernel time comes from HIP
-           events recorded on the stream the kernels are launched on.
+           (bytes = (x + delta + y) over batch*L*D plus (B + C) over batch*L*N,
+           input element size for all five, as the metric defines them)
+roofline = the scan call against the roof that binds it.  Each (b, t, d, n)
+           element needs 4 single-rate fp32 VALU operations and one half-rate
+           v_exp_f32 = 6 lane-issue slots; the chip issues 256 CU * 4 SIMD * 16
+           lanes * 2.4 GHz = 39.32e12 slots/s, so the element roof is
+           6553.6 Gelem/s ("alu").  The same call is also reported against HBM
+           (algorithmic bytes / call time vs 8 TB/s and vs a device copy
+           measured in the same run), with the HBM bytes the rocprofv3 counters
+           measured for the current kernel sources ("traffic").  Call time
+           comes from HIP events recorded on the stream the kernels run on.
+cpu_baseline = the float64 oracle on the host cores: passes over the headline
+           workload for about 10 s, plus one oracle pass per workload (and one
+           on a single thread for the two smallest), with the core count and
+           CPU model.
 """
 from __future__ import annotations
 
@@ -25,6 +34,7 @@ import glob
 import hashlib
 import json
 import os
+import platform
 import sys
 import time
 
@@ -35,8 +45,11 @@ HBM_PEAK_GBS = 8000.0
 VALU_LANE_SLOTS_PER_S = 256 * 4 * 16 * 2.4e9
 SLOTS_PER_ELEMENT = 6
 ELEM_PEAK_GPS = VALU_LANE_SLOTS_PER_S / SLOTS_PER_ELEMENT / 1e9
-HEADLINE = "mamba130m_layer_fp32"
-OTHERS = ["tiny_fp32", "mid_bf16", "long_seq_bf16", "fused_proj_bf16"]
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+HEADLINE = "long_seq_bf16"
+CONFIGS = ("tiny_fp32", "mamba130m_layer_fp32", "mid_bf16", "long_seq_bf16", "fused_proj_bf16")
+TRAFFIC_PATH = os.path.join(ROOT, "profiles", "traffic.json")
+CSRC = os.path.join(ROOT, "selective_state_space_54_amd", "csrc")
 
 
 def algorithmic_bytes(w) -> int:
@@ -48,71 +61,154 @@ def elements(w) -> int:
     return w.batch * w.L * w.D * w.N
 
 
-# The sources the headline scan's kernel (the single pass: first-order input
-# term, no optional parts) is built from; the traffic record is tied to their
-# hash.
-HEADLINE_SOURCES = ("scan_device.h", "chain_scan.h", "chain_scan.hip", "chain_euler_plain.hip",
-                    "scan_kernels.hip", "mssm_internal.h")
+def projection_flops(w) -> int:
+    return 2 * w.batch * w.L * (w.D * (w.R + 2 * w.N) + w.R * w.D)
 
 
 def kernel_sources_digest() -> str:
+    """Hash of every kernel source: a traffic record taken on other sources is stale."""
     h = hashlib.sha256()
-    for name in HEADLINE_SOURCES:
-        with open(os.path.join(ROOT, "selective_state_space_54_amd", "csrc", name), "rb") as f:
-            h.update(name.encode())
+    for path in sorted(glob.glob(os.path.join(CSRC, "*"))):
+        with open(path, "rb") as f:
+            h.update(os.path.basename(path).encode())
             h.update(f.read())
     return h.hexdigest()
 
 
 def load_traffic(workload: str):
-    """HBM bytes per step measured with rocprofv3 counters, if they were taken
-    on the current kernel sources (else None)."""
-    path = os.path.join(ROOT, "profiles", "traffic.json")
-    if not os.path.exists(path):
+    """The counter record of this workload if it was taken on the current
+    kernel sources, else None."""
+    if not os.path.exists(TRAFFIC_PATH):
         return None
-    with open(path) as f:
+    with open(TRAFFIC_PATH) as f:
         rec = json.load(f).get(workload)
     if not rec or rec.get("kernel_sources_sha256") != kernel_sources_digest():
         return None
-    return rec.get("hbm_bytes_per_step")
+    return rec
 
 
-def device_inputs(g, torch):
-    import numpy as np
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
+
+
+# ---- rocprofv3 counter ingestion (CPU only) ----------------------------------------------
+
+def _counter_rows(directory):
+    import csv
+    rows = []
+    for path in glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True):
+        with open(path, newline="") as f:
+            rows.extend(csv.DictReader(f))
+    if not rows:
+        raise SystemExit(f"no counter_collection.csv under {directory}")
+    return rows
+
+
+def _per_kernel(directory, counter):
+    """{kernel name: (dispatches, total counter value)} for one counter."""
     out = {}
-    for k in ("x", "delta", "A", "B", "C"):
-        a = np.ascontiguousarray(g[k])
-        t = torch.from_numpy(a.view(np.int16)).view(torch.bfloat16) if a.dtype == np.uint16 \
-            else torch.from_numpy(a)
-        out[k] = t.cuda()
-    return out
+    for r in _counter_rows(directory):
+        if r.get("Counter_Name") != counter:
+            continue
+        name = r.get("Kernel_Name", "")
+        n, v = out.get(name, (0, 0.0))
+        disp = r.get("Dispatch_Id")
+        out[name] = (n, v + float(r["Counter_Value"]))
+        out.setdefault("__dispatches__", {}).setdefault(name, set()).add(disp)
+    disp = out.pop("__dispatches__", {})
+    return {k: (len(disp.get(k, ())), v) for k, (_, v) in out.items()}
 
 
-def time_workload(name, steps, warmup, rotate, torch, mssm, workloads):
-    w = workloads.workload(name)
-    sets = []
-    for r in range(rotate):
-        g = workloads.generate(name, seed=w.seed + 1000 * r)
-        d = device_inputs(g, torch)
-        d["y"] = torch.empty(d["x"].shape, dtype=torch.float32, device="cuda")
-        sets.append(d)
-        del g
-    nbytes = mssm.mssm_selective_scan_workspace_size(w.batch, w.L, w.D, w.N, sets[0]["x"].dtype)
-    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device="cuda")
+def ingest_counters(args):
+    """Turn rocprofv3 FETCH_SIZE / WRITE_SIZE runs of `--only-config WORKLOAD`
+    and of `--calibrate-copy MIB` into the workload's traffic record."""
+    copy_bytes = args.calibrate_mib * (1 << 20)
+    scales = {}
+    for counter, d in (("FETCH_SIZE", args.copy_fetch_dir), ("WRITE_SIZE", args.copy_write_dir)):
+        per = _per_kernel(d, counter)
+        # the copy kernel is the dispatch with the largest count per launch
+        best = max(v / n for n, v in per.values() if n)
+        scales[counter] = copy_bytes / (best * 1024.0)
+    fetch = _per_kernel(args.fetch_dir, "FETCH_SIZE")
+    write = _per_kernel(args.write_dir, "WRITE_SIZE")
+    kernels = {}
+    read_b = write_b = 0.0
+    for name in sorted(set(fetch) | set(write)):
+        if "mssm" not in name:
+            continue
+        nf, vf = fetch.get(name, (0, 0.0))
+        nw, vw = write.get(name, (0, 0.0))
+        rb = vf * 1024.0 * scales["FETCH_SIZE"] / args.calls
+        wb = vw * 1024.0 * scales["WRITE_SIZE"] / args.calls
+        kernels[name] = {"dispatches_per_call": round(max(nf, nw) / args.calls, 3),
+                         "fetch_KiB_per_dispatch": round(vf / max(nf, 1), 1),
+                         "write_KiB_per_dispatch": round(vw / max(nw, 1), 1),
+                         "read_bytes_per_call": int(rb), "write_bytes_per_call": int(wb)}
+        read_b += rb
+        write_b += wb
+    db = {}
+    if os.path.exists(TRAFFIC_PATH):
+        with open(TRAFFIC_PATH) as f:
+            db = json.load(f)
+    db[args.workload] = {
+        "kernel_sources_sha256": kernel_sources_digest(),
+        "hbm_bytes_per_step": int(read_b + write_b),
+        "read_bytes": int(read_b), "write_bytes": int(write_b),
+        "fetch_scale": round(scales["FETCH_SIZE"], 4),
+        "write_scale": round(scales["WRITE_SIZE"], 4),
+        "calls": args.calls, "kernels": kernels,
+        "summary": args.summary,
+    }
+    with open(TRAFFIC_PATH, "w") as f:
+        json.dump(db, f, indent=1, sort_keys=True)
+        f.write("\n")
+    print(json.dumps(db[args.workload], indent=1))
+    return 0
 
-    # validated once; each step issues the C call directly
-    calls = [mssm.prepare_selective_scan_fwd_ws(d["x"], d["delta"], d["A"], d["B"], d["C"],
-                                                d["y"], ws) for d in sets]
 
-    def step(i):
-        calls[i % rotate]()
+# ---- GPU timing -----------------------------------------------------------------------------
 
+def _to_dev_array(a, torch):
+    import numpy as np
+    a = np.ascontiguousarray(a)
+    t = torch.from_numpy(a.view(np.int16)).view(torch.bfloat16) if a.dtype == np.uint16 \
+        else torch.from_numpy(a)
+    return t.cuda()
+
+
+def measure_copy_bandwidth(torch, mib=1024, reps=10):
+    """GB/s (bytes read + bytes written) of a plain device-to-device copy."""
+    n = mib * (1 << 20) // 4
+    src = [torch.ones(n, dtype=torch.float32, device="cuda") for _ in range(2)]
+    dst = torch.empty_like(src[0])
+    for i in range(3):
+        dst.copy_(src[i % 2])
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    s.record()
+    for i in range(reps):
+        dst.copy_(src[i % 2])
+    e.record()
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e) / reps
+    del src, dst
+    torch.cuda.empty_cache()
+    return 2 * n * 4 / (ms * 1e-3) / 1e9
+
+
+def _timed(fn, steps, warmup, torch):
+    """Warm up, then time `steps` calls: one event pair around the region on the
+    stream the library launches on (launches queue back to back, so this is
+    call time plus the gaps between calls), and the host wall clock."""
     for i in range(warmup):
-        step(i)
-    # One event pair around the whole timed region, on the stream the library
-    # launches on: the average launch duration is its elapsed time / steps
-    # (launches queue back to back, so this is kernel time plus the gaps
-    # between launches, not the cost of per-step event records).
+        fn(i)
     stream = torch.cuda.current_stream()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
@@ -120,54 +216,101 @@ def time_workload(name, steps, warmup, rotate, torch, mssm, workloads):
     t0 = time.perf_counter()
     start.record(stream)
     for i in range(steps):
-        step(i)
+        fn(i)
     end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    kernel_ms = start.elapsed_time(end) / steps
+    return wall, start.elapsed_time(end) / steps
+
+
+def time_scan(name, steps, warmup, rotate, torch, mssm, workloads, keep_host=False):
+    """The plain scan (mssm_selective_scan_fwd_ws) on `rotate` input sets drawn
+    with seeds seed + 1000 r, used in turn.  Returns (workload, wall s, call ms,
+    host arrays of set 0 when keep_host)."""
+    w = workloads.workload(name)
+    sets, host0 = [], None
+    for r in range(rotate):
+        g = workloads.generate(name, seed=w.seed + 1000 * r)
+        d = {k: _to_dev_array(g[k], torch) for k in ("x", "delta", "A", "B", "C")}
+        d["y"] = torch.empty(d["x"].shape, dtype=torch.float32, device="cuda")
+        sets.append(d)
+        if r == 0 and keep_host:
+            host0 = g
+        del g
+    nbytes = mssm.mssm_selective_scan_workspace_size(w.batch, w.L, w.D, w.N, sets[0]["x"].dtype)
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device="cuda")
+    # validated once; each step issues the C call directly
+    calls = [mssm.prepare_selective_scan_fwd_ws(d["x"], d["delta"], d["A"], d["B"], d["C"],
+                                                d["y"], ws) for d in sets]
+    wall, call_ms = _timed(lambda i: calls[i % rotate](), steps, warmup, torch)
     del sets, ws, calls
     torch.cuda.empty_cache()
-    return w, wall, kernel_ms
+    return w, wall, call_ms, host0
 
 
-def time_fused(name, steps, warmup, torch, mssm, workloads):
-    """The fused path per step: W_x transpose, x_proj GEMM, dt_low split, W_dt
-    transpose, then (>= 8192 channels) the Delta kernel and the single-pass
-    scan, or the chunked fused summary / carry / output kernels."""
-    import numpy as np
+def time_fused(name, steps, warmup, rotate, torch, mssm, workloads, keep_host=False):
+    """The fused selective SSM per step (W_x transpose, x_proj GEMM with the
+    dt_low split in its epilogue, W_dt transpose, the Delta kernel and the
+    single-pass scan at this shape) on `rotate` input sets used in turn."""
     w = workloads.workload(name)
-    g = workloads.generate(name)
-    d = {}
-    for k in ("x", "W_x", "W_dt", "dt_bias", "A"):
-        a = np.ascontiguousarray(g[k])
-        t = torch.from_numpy(a.view(np.int16)).view(torch.bfloat16) if a.dtype == np.uint16 \
-            else torch.from_numpy(a)
-        d[k] = t.cuda()
-    del g
-    y = torch.empty(d["x"].shape, dtype=torch.float32, device="cuda")
+    sets, host0 = [], None
+    for r in range(rotate):
+        g = workloads.generate(name, seed=w.seed + 1000 * r)
+        sets.append({k: _to_dev_array(g[k], torch) for k in ("x", "W_x", "W_dt", "dt_bias", "A")})
+        if r == 0 and keep_host:
+            host0 = g
+        del g
+    y = torch.empty(sets[0]["x"].shape, dtype=torch.float32, device="cuda")
     nb = mssm.mssm_selective_ssm_fused_workspace_size(w.batch, w.L, w.D, w.N, w.R, torch.bfloat16)
     ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
 
-    def step():
+    def step(i):
+        d = sets[i % rotate]
         mssm.mssm_selective_ssm_fused_fwd(d["x"], d["W_x"], d["W_dt"], d["dt_bias"], d["A"], y, ws)
 
-    for _ in range(warmup):
-        step()
-    stream = torch.cuda.current_stream()
-    s_ev = torch.cuda.Event(enable_timing=True)
-    e_ev = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    s_ev.record(stream)
-    for _ in range(steps):
-        step()
-    e_ev.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    kernel_ms = s_ev.elapsed_time(e_ev) / steps
-    del d, y, ws
+    wall, call_ms = _timed(step, steps, warmup, torch)
+    del sets, y, ws
     torch.cuda.empty_cache()
-    return w, wall, kernel_ms
+    return w, wall, call_ms, host0
+
+
+def config_record(w, wall, call_ms, steps, rotate, copy_gbs):
+    """Throughput and roofline figures of one workload."""
+    nb = algorithmic_bytes(w)
+    gbs_call = nb / (call_ms * 1e-3) / 1e9
+    elem_rate = elements(w) / (call_ms * 1e-3) / 1e9
+    tr = load_traffic(w.name)
+    rec = {
+        "steps": steps, "input_sets_rotated": rotate,
+        "ms_per_step": round(wall * 1e3 / steps, 4),
+        "kernel_ms": round(call_ms, 4),
+        "GB/s": round(nb * steps / wall / 1e9, 2),
+        "tokens_channels_per_s": round(w.batch * w.L * w.D / (call_ms * 1e-3), 1),
+        "roofline": {
+            "bound": "alu", "achieved": round(elem_rate, 1), "peak": round(ELEM_PEAK_GPS, 1),
+            "unit": "Gelem/s", "frac": round(elem_rate / ELEM_PEAK_GPS, 4),
+            "traffic": tr["hbm_bytes_per_step"] if tr else None,
+            "hbm": {"achieved": round(gbs_call, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(gbs_call / HBM_PEAK_GBS, 4),
+                    "measured_copy_GBps": round(copy_gbs, 1),
+                    "frac_of_measured_copy": round(gbs_call / copy_gbs, 4),
+                    "algorithmic_bytes": nb,
+                    "traffic_over_algorithmic": (round(tr["hbm_bytes_per_step"] / nb, 3)
+                                                 if tr else None)},
+        },
+    }
+    if w.fused:
+        fl = projection_flops(w)
+        rec["roofline"]["projection_mfma"] = {
+            "flops": fl, "achieved_TFLOPs_over_call": round(fl / (call_ms * 1e-3) / 1e12, 2),
+            "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s"}
+        rec["note"] = ("bytes by the scan formula (x + Delta + y, B + C); Delta, B, C are formed "
+                       "from x and the weights inside the call")
+    return rec
+
+
+def device_inputs(g, torch):
+    return {k: _to_dev_array(g[k], torch) for k in ("x", "delta", "A", "B", "C")}
 
 
 def _to_device(a, torch):
@@ -453,29 +596,112 @@ def time_train_pair(name, steps, warmup, torch, mssm, workloads):
                     "gate, which the backward reads instead of recomputing"}
 
 
-def cpu_baseline(name, workloads, oracle, threads):
-    """The float64 oracle on the host cores, on the whole headline workload."""
-    g = workloads.generate(name)
+def probe_rates(torch, iters=4000, blocks=2048, reps=5):
+    """Issue rates of the VALU instructions the scan is made of, the scan's
+    per-element sequence as a whole, and plain read and copy bandwidth, from
+    the probes in libmssm_probe.so (built next to libmssm.so)."""
+    import ctypes
+    from selective_state_space_54_amd import build as hb
+    lib = ctypes.CDLL(hb.PROBE_LIB_PATH)
+    lib.mssm_probe_launch.restype = ctypes.c_int
+    lib.mssm_probe_launch.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.c_int64,
+                                      ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                      ctypes.c_void_p]
+    stream = torch.cuda.current_stream()
+    sh = ctypes.c_void_p(stream.cuda_stream)
+    out = torch.empty(4096 * 256, dtype=torch.float32, device="cuda")
+    bc = torch.linspace(-1.0, 1.0, 32, device="cuda", dtype=torch.float32)
+    n16 = (2 << 30) // 16
+    buf = torch.ones(n16 * 4, dtype=torch.int32, device="cuda")
+
+    def timed(which, nblk, it, arg=None, n=0):
+        def go():
+            rc = lib.mssm_probe_launch(which, nblk, it, ctypes.c_void_p(out.data_ptr()),
+                                       ctypes.c_void_p(arg) if arg else None, n, sh)
+            if rc != 0:
+                raise RuntimeError(f"probe {which} launch failed: {rc}")
+        go()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        s.record(stream)
+        for _ in range(reps):
+            go()
+        e.record(stream)
+        torch.cuda.synchronize()
+        return s.elapsed_time(e) / reps * 1e-3
+
+    res = {"lane_slots_per_s_nominal": VALU_LANE_SLOTS_PER_S, "blocks": blocks,
+           "threads_per_block": 256, "iterations": iters}
+    lanes = blocks * 256
+    for which, name in ((0, "v_exp_f32"), (1, "v_fma_f32"), (2, "v_mul_f32"),
+                        (3, "v_mul_f32 with DPP row_newbcast operand")):
+        t = timed(which, blocks, iters)
+        rate = lanes * iters * 16 / t
+        res[name] = {"lane_instructions_per_s": rate,
+                     "lane_slots_per_instruction": round(VALU_LANE_SLOTS_PER_S / rate, 3),
+                     "seconds": t}
+    t = timed(4, blocks, iters, bc.data_ptr())
+    rate = lanes * iters * 16 / t
+    res["scan element (mul, v_exp_f32, mul, fma, fma)"] = {
+        "Gelem_per_s": round(rate / 1e9, 1),
+        "lane_slots_per_element": round(VALU_LANE_SLOTS_PER_S / rate, 3), "seconds": t}
+    t = timed(5, 4096, 0, buf.data_ptr(), n16)
+    res["read_GBps"] = round(n16 * 16 / t / 1e9, 1)
+    del buf
+    torch.cuda.empty_cache()
+    res["copy_GBps (read + write)"] = round(measure_copy_bandwidth(torch), 1)
+    return res
+
+
+def _oracle_pass(g, oracle, workloads, threads):
+    """One float64 oracle pass over the workload's inputs (the fused workload:
+    its projections, then the scan); returns the seconds it took."""
+    import numpy as np
     w = g["workload"]
-    x = workloads.to_float64(g["x"])
-    dl = workloads.to_float64(g["delta"])
-    A = g["A"].astype("float64")
-    B = workloads.to_float64(g["B"])
-    C = workloads.to_float64(g["C"])
-    oracle.selective_scan(x[:, :64], dl[:, :64], A, B[:, :64], C[:, :64], nthreads=threads)
-    # repeat whole passes until about 10 s of wall time (bounded to 1000 passes)
-    passes, t0 = 0, time.perf_counter()
-    while True:
-        oracle.selective_scan(x, dl, A, B, C, nthreads=threads)
+    f64 = workloads.to_float64
+    t0 = time.perf_counter()
+    if w.fused:
+        oracle.selective_ssm_fused(f64(g["x"]), f64(g["W_x"]), f64(g["W_dt"]),
+                                   g["dt_bias"].astype(np.float64), g["A"].astype(np.float64),
+                                   R=w.R, nthreads=threads)
+    else:
+        oracle.selective_scan(f64(g["x"]), f64(g["delta"]), g["A"].astype(np.float64),
+                              f64(g["B"]), f64(g["C"]), nthreads=threads)
+    return time.perf_counter() - t0
+
+
+def cpu_baseline(hosts, oracle, workloads, threads, seconds=10.0):
+    """The oracle on the host: whole passes over the headline workload until
+    about `seconds` have passed (at least one), one pass over every other
+    workload, and single-thread passes over the two smallest."""
+    import numpy as np  # noqa: F401
+    g = hosts[HEADLINE]
+    w = g["workload"]
+    passes, spent = 0, 0.0
+    while passes == 0 or spent < seconds:
+        spent += _oracle_pass(g, oracle, workloads, threads)
         passes += 1
-        dt = time.perf_counter() - t0
-        if dt >= 10.0 or passes >= 1000:
+        if passes >= 100:
             break
-    return {"value": round(algorithmic_bytes(w) * passes / dt / 1e9, 4), "unit": "GB/s",
-            "cores": threads, "kind": "oracle", "seconds": round(dt, 3),
-            "sample": f"{passes} pass(es) over the whole {name} workload "
-                      f"({w.batch}x{w.L}x{w.D}x{w.N}), float64, {threads} threads over "
-                      f"independent (batch, channel) chains"}
+    per = {}
+    for name, gg in hosts.items():
+        if name == HEADLINE:
+            per[name] = {"threads": threads, "seconds_per_pass": round(spent / passes, 3)}
+            continue
+        ww = gg["workload"]
+        s = _oracle_pass(gg, oracle, workloads, threads)
+        per[name] = {"threads": threads, "seconds_per_pass": round(s, 3),
+                     "GB/s": round(algorithmic_bytes(ww) / s / 1e9, 4)}
+        if name in ("tiny_fp32", "mamba130m_layer_fp32"):
+            s1 = _oracle_pass(gg, oracle, workloads, 1)
+            per[name]["one_thread"] = {"seconds_per_pass": round(s1, 3),
+                                       "GB/s": round(algorithmic_bytes(ww) / s1 / 1e9, 4)}
+    return {"value": round(algorithmic_bytes(w) * passes / spent / 1e9, 4), "unit": "GB/s",
+            "cores": threads, "kind": "oracle", "seconds": round(spent, 3),
+            "os_cpu_count": os.cpu_count(), "cpu_model": cpu_model(),
+            "sample": f"{passes} whole pass(es) over {HEADLINE} ({w.batch}x{w.L}x{w.D}x{w.N}), "
+                      f"float64, {threads} threads over independent (batch, channel) chains",
+            "per_workload": per}
 
 
 def main(argv=None):
@@ -483,17 +709,38 @@ def main(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default=HEADLINE)
     ap.add_argument("--headline-only", action="store_true", help="skip the other workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only-config", default=None, choices=list(CONFIGS),
+                    help="time only this workload (two rotated input sets) and print its "
+                         "record; used for profiling")
     ap.add_argument("--only", default=None,
-                    choices=["fused_proj_bf16", "scan_ex", "decode_step_bf16", "conv1d_silu_fp32",
+                    choices=["scan_ex", "decode_step_bf16", "conv1d_silu_fp32",
                              "mamba_block_bf16", "backward", "train_pair"],
                     help="time only this extra workload and print its record (for profiling)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (5 times) and exit; "
                          "used to scale rocprofv3 FETCH_SIZE/WRITE_SIZE counters")
+    ap.add_argument("--probe-rates", action="store_true",
+                    help="only run the VALU issue-rate and bandwidth probes and print them")
+    ap.add_argument("--ingest-counters", action="store_true",
+                    help="(CPU only) turn rocprofv3 counter runs into profiles/traffic.json: "
+                         "needs --workload, --calls, --fetch-dir, --write-dir, --copy-fetch-dir, "
+                         "--copy-write-dir, --calibrate-mib, --summary")
+    ap.add_argument("--workload", default=None)
+    ap.add_argument("--calls", type=int, default=0)
+    ap.add_argument("--fetch-dir")
+    ap.add_argument("--write-dir")
+    ap.add_argument("--copy-fetch-dir")
+    ap.add_argument("--copy-write-dir")
+    ap.add_argument("--calibrate-mib", type=int, default=1024)
+    ap.add_argument("--summary", default="")
     args = ap.parse_args(argv)
+    if args.ingest_counters:
+        if not (args.workload and args.calls > 0 and args.fetch_dir and args.write_dir
+                and args.copy_fetch_dir and args.copy_write_dir):
+            ap.error("--ingest-counters needs --workload, --calls and the four run directories")
+        return ingest_counters(args)
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the scan does not shard across GPUs in this build "
               f"(asked for --gpus {args.gpus}).", file=sys.stderr)
@@ -517,31 +764,49 @@ def main(argv=None):
         torch.cuda.synchronize()
         print(json.dumps({"calibrate_copy_bytes_read": n * 4, "bytes_written": n * 4}))
         return 0
+    if args.probe_rates:
+        print(json.dumps({"probe_rates": probe_rates(torch)}), flush=True)
+        return 0
     mssm.load()
     if args.only:
-        if args.only == "fused_proj_bf16":
-            wo, _, kms = time_fused(args.only, args.steps, args.warmup, torch, mssm, workloads)
-            rec = {"kernel_ms": round(kms, 4)}
-        elif args.only == "scan_ex":
-            rec = time_scan_ex(HEADLINE, args.steps, args.warmup, torch, mssm, workloads)
+        HL = "mamba130m_layer_fp32"
+        if args.only == "scan_ex":
+            rec = time_scan_ex(HL, args.steps, args.warmup, torch, mssm, workloads)
         elif args.only == "decode_step_bf16":
             rec = time_decode(args.only, args.steps, args.warmup, torch, mssm, workloads)
         elif args.only == "conv1d_silu_fp32":
             rec = time_conv(torch, mssm, steps=args.steps, warmup=args.warmup)
         elif args.only == "backward":
-            rec = time_backward(HEADLINE, args.steps, args.warmup, torch, mssm, workloads)
+            rec = time_backward(HL, args.steps, args.warmup, torch, mssm, workloads)
         elif args.only == "train_pair":
-            rec = time_train_pair(HEADLINE, args.steps, args.warmup, torch, mssm, workloads)
+            rec = time_train_pair(HL, args.steps, args.warmup, torch, mssm, workloads)
         else:
             rec = time_block(args.only, args.steps, args.warmup, torch, mssm, workloads)
         print(json.dumps({"only": args.only, **rec}), flush=True)
         return 0
 
-    w, wall, kernel_ms = time_workload(args.workload, args.steps, args.warmup, 2, torch, mssm,
-                                       workloads)
+    copy_gbs = measure_copy_bandwidth(torch)
+    timer = lambda name, keep: (time_fused if workloads.workload(name).fused else time_scan)(
+        name, args.steps, args.warmup, 2, torch, mssm, workloads, keep_host=keep)
+    if args.only_config:
+        w, wall, call_ms, _ = timer(args.only_config, False)
+        print(json.dumps({"only_config": w.name,
+                          **config_record(w, wall, call_ms, args.steps, 2, copy_gbs)}), flush=True)
+        return 0
+
+    want_cpu = not args.no_cpu_baseline
+    hosts = {}
+    w, wall, call_ms, h0 = timer(HEADLINE, want_cpu)
+    if want_cpu:
+        hosts[HEADLINE] = h0
+    head = config_record(w, wall, call_ms, args.steps, 2, copy_gbs)
     nb = algorithmic_bytes(w)
     gbs = nb * args.steps / wall / 1e9
-    elem_rate = elements(w) / (kernel_ms * 1e-3) / 1e9
+    roof = dict(head["roofline"])
+    roof["kernel"] = ("one scan call: chunk_summary_kernel, chunk_carry_kernel, "
+                      "chunk_output_kernel launched back to back (2560 channels: the chunked "
+                      "order)")
+    roof["kernel_ms"] = head["kernel_ms"]
     line = {
         "metric": "selective-scan GB/s achieved (% of HBM peak) and B·L·D tokens-channels/sec",
         "value": round(gbs, 2),
@@ -556,20 +821,12 @@ def main(argv=None):
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": w.name, "batch": w.batch, "L": w.L, "D": w.D, "N": w.N,
-                   "storage": w.dtype, "parallelism": "single GPU"},
+                   "storage": w.dtype, "parallelism": "single GPU",
+                   "input_sets_rotated": 2},
         "hbm_peak_frac": round(gbs / HBM_PEAK_GBS, 4),
+        "measured_copy_GBps": round(copy_gbs, 1),
         "tokens_channels_per_s": round(w.batch * w.L * w.D * args.steps / wall, 1),
-        "roofline": {
-            "bound": "alu",
-            "kernel": "chain_scan_kernel (the whole scan call is this one kernel)",
-            "achieved": round(elem_rate, 1),
-            "peak": round(ELEM_PEAK_GPS, 1),
-            "unit": "Gelem/s",
-            "frac": round(elem_rate / ELEM_PEAK_GPS, 4),
-            "kernel_ms": round(kernel_ms, 4),
-            "hbm_GBps_at_kernel_time": round(nb / (kernel_ms * 1e-3) / 1e9, 1),
-            "traffic": load_traffic(w.name),
-        },
+        "roofline": roof,
     }
     if not args.headline_only:
         others = {}
@@ -582,47 +839,32 @@ def main(argv=None):
             except Exception as e:   # noqa: BLE001 - reported, not hidden
                 others[name] = {"error": f"{type(e).__name__}: {e}"[:300]}
 
-        def config_record(name):
-            if workloads.workload(name).fused:
-                wo, wall_o, kms_o = time_fused(name, 5, 2, torch, mssm, workloads)
-            else:
-                wo, wall_o, kms_o = time_workload(name, 5, 2, 1, torch, mssm, workloads)
-            nbo = algorithmic_bytes(wo)
-            rec = {
-                "ms_per_step": round(wall_o * 1e3 / 5, 4),
-                "kernel_ms": round(kms_o, 4),
-                "GB/s": round(nbo / (kms_o * 1e-3) / 1e9, 1),
-                "hbm_peak_frac": round(nbo / (kms_o * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                "tokens_channels_per_s": round(wo.batch * wo.L * wo.D / (kms_o * 1e-3), 1),
-                "Gelem/s": round(elements(wo) / (kms_o * 1e-3) / 1e9, 1),
-                "alu_frac": round(elements(wo) / (kms_o * 1e-3) / 1e9 / ELEM_PEAK_GPS, 4),
-            }
-            if wo.fused:
-                flops = 2 * wo.batch * wo.L * (wo.D * (wo.R + 2 * wo.N) + wo.R * wo.D)
-                rec["projection_TFLOPs"] = round(flops / 1e12, 2)
-                rec["note"] = ("bytes by the scan formula (x + Delta + y, B + C); Delta, B, "
-                               "C are formed on chip from x and the weights")
-            return rec
+        def scan_config(name):
+            wo, wall_o, ms_o, g0 = timer(name, want_cpu)
+            if want_cpu:
+                hosts[name] = g0
+            return config_record(wo, wall_o, ms_o, args.steps, 2, copy_gbs)
 
-        for name in OTHERS:
-            if name != w.name:
-                extra(name, lambda name=name: config_record(name))
+        for name in CONFIGS:
+            if name != HEADLINE:
+                extra(name, lambda name=name: scan_config(name))
+        HL = "mamba130m_layer_fp32"
         extra("mamba130m_layer_fp32 zoh+skip+gate+state",
-              lambda: time_scan_ex(HEADLINE, 10, 2, torch, mssm, workloads))
+              lambda: time_scan_ex(HL, 10, 2, torch, mssm, workloads))
         extra("decode_step_bf16",
               lambda: time_decode("decode_step_bf16", 200, 10, torch, mssm, workloads))
         extra("conv1d_silu_fp32", lambda: time_conv(torch, mssm))
         extra("mamba_block_bf16",
               lambda: time_block("mamba_block_bf16", 5, 2, torch, mssm, workloads))
         extra("backward mamba130m_layer_fp32",
-              lambda: time_backward(HEADLINE, 5, 2, torch, mssm, workloads))
+              lambda: time_backward(HL, 5, 2, torch, mssm, workloads))
         extra("forward + backward mamba130m_layer_fp32",
-              lambda: time_train_pair(HEADLINE, 5, 2, torch, mssm, workloads))
+              lambda: time_train_pair(HL, 5, 2, torch, mssm, workloads))
         line["workloads"] = others
-    if not args.no_cpu_baseline:
+    if want_cpu:
         import oracle
         threads = min(os.cpu_count() or 1, 16)
-        line["cpu_baseline"] = cpu_baseline(w.name, workloads, oracle, threads)
+        line["cpu_baseline"] = cpu_baseline(hosts, oracle, workloads, threads)
     print(json.dumps(line), flush=True)
     return 0
 

@@ -28,10 +28,10 @@
  *     sequence in time order; no chunks, no workspace.  Used for N = 16, D a
  *     multiple of 16, inputs aligned to 4 elements and y to 16 bytes, and at
  *     least 8192 channels (batch * D), where it fills the GPU on its own.
- *   The library picks one per call from the shape and the pointers.  The
- *   environment variable MSSM_SCAN_DESIGN=chunked or =chain, read at every
- *   call, pins the choice (=chain still needs a shape the single pass
- *   supports); the two agree to within float32 rounding.
+ *   The library picks one per call from the shape and the pointers;
+ *   mssm_set_tuning(MSSM_TUNE_SCAN_ORDER, ...) pins the choice (the single
+ *   pass still needs a shape it supports).  The two orders agree to within
+ *   float32 rounding.
  *
  * Layouts: dense, row-major, contiguous.
  *   x, delta    : [batch, L, D]   (d fastest)
@@ -52,9 +52,8 @@
  * Streams: `stream` is a hipStream_t passed as void*; NULL means the null
  * stream.  Work is enqueued asynchronously; the call does not synchronise.
  * Calls may come from several host threads at once, each with its own
- * stream and buffers (the GEMMs of the fused path and the block share one
- * rocBLAS handle per device, which a call holds until its GEMMs are
- * enqueued).
+ * stream and buffers (the block's rocBLAS GEMMs share one rocBLAS handle
+ * per device, which a call holds until its GEMMs are enqueued).
  *
  * Errors: every entry point returns an mssm_status.  Arguments are checked
  * before any HIP call is made, so argument errors are reported on machines
@@ -73,7 +72,7 @@
 extern "C" {
 #endif
 
-#define MSSM_ABI_VERSION 5
+#define MSSM_ABI_VERSION 6
 
 typedef enum {
     MSSM_SUCCESS = 0,
@@ -97,6 +96,37 @@ typedef enum {
                               Needs every A[d, n] nonzero (a zero entry gives NaN
                               in that channel); stable A is negative anyway.    */
 } mssm_bbar;
+
+/*
+ * Tuning settings, process-wide, for tests and performance sweeps.  They
+ * start from the environment, read once when the first setting is needed
+ * (MSSM_SCAN_DESIGN=chunked|chain, MSSM_CHUNK_LEN=<steps>,
+ * MSSM_CPL=1|2); calls never read the environment.  mssm_set_tuning takes
+ * effect for calls made after it returns.  A workspace size queried under
+ * one setting may be too small under another (the call then returns
+ * MSSM_ERROR_WORKSPACE), so set them before sizing buffers.
+ *   MSSM_TUNE_SCAN_ORDER      : MSSM_ORDER_AUTO (the default choice by shape,
+ *                               pointers and length), MSSM_ORDER_CHUNKED, or
+ *                               MSSM_ORDER_SINGLE_PASS where supported.
+ *                               Applies to the scan, its backward pass, the
+ *                               fused selective SSM and the block.
+ *   MSSM_TUNE_CHUNK_LEN       : steps per chunk of the chunked order; 0 picks
+ *                               it from the shape.
+ *   MSSM_TUNE_CHAINS_PER_LANE : channels per lane of the chunked kernels, 1
+ *                               or 2; 0 picks it from the dtype.
+ * mssm_set_tuning: MSSM_ERROR_INVALID_VALUE for an unknown key or a value
+ * out of range.  mssm_get_tuning writes the current value.
+ */
+typedef enum {
+    MSSM_TUNE_SCAN_ORDER = 0,
+    MSSM_TUNE_CHUNK_LEN = 1,
+    MSSM_TUNE_CHAINS_PER_LANE = 2
+} mssm_tuning;
+
+enum { MSSM_ORDER_AUTO = 0, MSSM_ORDER_CHUNKED = 1, MSSM_ORDER_SINGLE_PASS = 2 };
+
+mssm_status mssm_set_tuning(mssm_tuning key, int64_t value);
+mssm_status mssm_get_tuning(mssm_tuning key, int64_t *value);
 
 /* ABI version of the loaded library (MSSM_ABI_VERSION it was built with). */
 int mssm_abi_version(void);
@@ -208,18 +238,27 @@ mssm_status mssm_selective_scan_step(const void *x, const void *delta, const flo
  * W_dtproj + dt_bias) with W_dtproj [R, D] and one bias per channel
  * (softplus as in section 5.1); then the scan above runs on (x, Delta, A, B,
  * C).  x, W_xproj, W_dtproj are bfloat16; dt_bias, A and y are float32.
- * The projection is accumulated in float32; dt_proj runs on the bf16 matrix
- * cores with dt_low split into two bfloat16 parts (hi = bf16(dt_low),
- * lo = bf16(dt_low - hi)), i.e. dt_low kept to about 16 significant bits, and
- * float32 accumulation; B, C and the pre-softplus values stay float32.  Delta
- * is formed on chip and never written to memory.
+ * x_proj runs on the bf16 matrix cores (the library's own kernel, one pass
+ * over x) with float32 accumulation; dt_low leaves it as two bfloat16 parts
+ * (hi = bf16(dt_low), lo = bf16(dt_low - hi)), i.e. kept to about 16
+ * significant bits, for dt_proj, which also runs on the bf16 matrix cores
+ * with float32 accumulation; B, C and the pre-softplus values stay float32.
+ *
+ * Where Delta lives follows the scan order (see the top of this file):
+ *   - chunked order: Delta is made per 32-step tile on the matrix cores
+ *     inside the scan kernels and never written to memory;
+ *   - single pass (N = 16, D a multiple of 16, R <= 256, x and y 16-byte
+ *     aligned, at least 8192 channels batch * D, unless the chunked order is
+ *     pinned): one matrix-core kernel writes Delta once, as float32
+ *     [batch * L, D] (4 bytes per element) into the workspace, and the scan
+ *     reads it back.  The workspace size covers it.
  *
  * Supported: dtype MSSM_BFLOAT16 only (MSSM_FLOAT32 -> NOT_SUPPORTED); N in
  * the scan's set; R a multiple of 16 in [16, 1024]; batch*L and D below 2^31.
  * The workspace must be 256-byte aligned and at least
  * mssm_selective_ssm_fused_workspace_size bytes; it is always required (the
- * projection lands there).  The first call on a device creates a rocBLAS
- * handle for that device, kept until the process exits.
+ * projection lands there).  The fused path makes no library calls (no
+ * rocBLAS).
  */
 
 /* 1 if the fused path is built for state size N and rank R, else 0. */
@@ -264,8 +303,11 @@ mssm_status mssm_selective_ssm_fused_fwd(const void *x, const void *W_xproj,
  * dt_bias [Di], A [Di, N], Dskip [Di] (may be NULL) float32; out [batch, L, Dm]
  * float32.  Precision: the projections accumulate in float32; x stays float32
  * for the scan and the feedthrough; x_proj and W_out take their float32 inputs
- * (x, and the gated result) as bf16 hi + lo pairs, about 16 significant bits,
- * one accumulating GEMM per part.  The workspace (256-byte aligned,
+ * (x, and the gated result) as bf16 hi + lo pairs, about 16 significant bits
+ * (x_proj: both parts multiplied into the same sums by the library's own
+ * matrix-core kernel; in_proj and out_proj: rocBLAS GEMMs, one per part, on
+ * a rocBLAS handle the first call on a device creates and keeps until the
+ * process exits).  The workspace (256-byte aligned,
  * mssm_mamba_block_workspace_size bytes) holds u, z, x (float32
  * [batch*L, Di]), the two bf16 pairs and the fused scan's buffers.  batch, L or Dm equal to zero is a no-op; Di equal to zero writes
  * zeros to out.

@@ -11,6 +11,9 @@ ROOT = os.path.dirname(PKG_DIR)
 CSRC = os.path.join(PKG_DIR, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(PKG_DIR, "libmssm.so")
+# issue-rate and bandwidth probes behind the roofline figures (bench.py --probe-rates)
+PROBE_SRC = os.path.join(PKG_DIR, "probe", "issue_rates.hip")
+PROBE_LIB_PATH = os.path.join(PKG_DIR, "libmssm_probe.so")
 OBJ_DIR = os.path.join(PKG_DIR, "_build")
 
 # -packed-fp32-ops: no v_pk_{add,mul,fma}_f32 in the generated code.
@@ -60,7 +63,21 @@ def build(verbose: bool = False) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed ({r.returncode}):\n{r.stderr[-8000:]}")
     os.replace(tmp, LIB_PATH)
+    build_probe(hipcc, verbose)
     return LIB_PATH
+
+
+def build_probe(hipcc: str, verbose: bool = False) -> str:
+    """The measurement probes, a library of their own (not part of libmssm)."""
+    tmp = PROBE_LIB_PATH + ".tmp"
+    cmd = [hipcc, *HIPCC_FLAGS, "-shared", PROBE_SRC, "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed on {PROBE_SRC} ({r.returncode}):\n{r.stderr[-8000:]}")
+    os.replace(tmp, PROBE_LIB_PATH)
+    return PROBE_LIB_PATH
 
 
 if __name__ == "__main__":

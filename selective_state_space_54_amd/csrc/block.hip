@@ -157,7 +157,7 @@ BlockPlan plan_block(int64_t batch, int64_t L, int64_t Dm, int64_t Di, int64_t N
   b.dtl_lo_offset = off; off += align256(sizeof(uint16_t) * M * (size_t)R);
   b.wt_offset = off;     off += align256(sizeof(uint16_t) * di * (size_t)R);
   b.win_t_offset = off;  off += align256(sizeof(uint16_t) * 2 * di * (size_t)Dm);
-  b.wx_t_offset = off;   off += align256(sizeof(uint16_t) * (size_t)(R + 2 * N) * di);
+  b.wx_t_offset = off;   off += align256(sizeof(uint16_t) * (size_t)(R + 2 * N) * xproj_padded_k(Di));
   b.wout_t_offset = off; off += align256(sizeof(uint16_t) * (size_t)Dm * 2 * di);
   b.scan_offset = off;   off += b.scan.workspace_bytes;
   b.workspace_bytes = off;
@@ -204,7 +204,6 @@ FusedStatus launch_block(const BlockArgs& a, const BlockPlan& bp, void* workspac
   uint16_t* WxT = reinterpret_cast<uint16_t*>(ws + bp.wx_t_offset);
   uint16_t* WoutT = reinterpret_cast<uint16_t*>(ws + bp.wout_t_offset);
   st.hip = launch_transpose_bf16(a.W_in, WinT, Dm, 2 * Di, stream);
-  if (st.hip == hipSuccess) st.hip = launch_transpose_bf16(a.W_x, WxT, Di, ldp, stream);
   // W_out^T [Dm, 2 Di]: columns Di.. repeat columns 0..Di-1
   if (st.hip == hipSuccess) st.hip = launch_transpose_bf16(a.W_out, WoutT, Di, Dm, stream, 2 * Di);
   if (st.hip == hipSuccess)
@@ -219,13 +218,9 @@ FusedStatus launch_block(const BlockArgs& a, const BlockPlan& bp, void* workspac
   st.hip = launch_conv1d_silu(U, true, a.conv_w, a.conv_b, X, Xb, Xl, a.batch, a.L, Di, a.k,
                               stream);
   if (st.hip != hipSuccess) return st;
-  // selection projection of x = hi + lo
-  if (!gemm_rm_bf16_bt(hb, M, ldp, Di, Xb, Di, WxT, Di, P, ldp, 0.0f) ||
-      !gemm_rm_bf16_bt(hb, M, ldp, Di, Xl, Di, WxT, Di, P, ldp, 1.0f)) {
-    st.blas_failed = true;
-    return st;
-  }
-  st.hip = launch_fused_prep(P, M, a.R, ldp, a.W_dt, Di, dtl, dtl_lo, wT, stream);
+  // selection projection of x = hi + lo (dt_low as its bf16 pair, B and C in P)
+  st.hip = launch_xproj(Xb, Xl, Di, M, Di, a.W_x, ldp, a.R, WxT, dtl, dtl_lo, P, ldp, stream);
+  if (st.hip == hipSuccess) st.hip = launch_wdt_transpose(a.W_dt, a.R, Di, wT, stream);
   if (st.hip != hipSuccess) return st;
   if (bp.chain) {
     // the single pass: delta written out (into u, which the conv has consumed)

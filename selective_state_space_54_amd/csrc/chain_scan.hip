@@ -1,8 +1,6 @@
 // Choice between the chunked scan and the single-pass (one lane per channel
 // and state) scan, and the single-pass kernel's variant dispatch.
 #include <cstdint>
-#include <cstdlib>
-#include <cstring>
 
 #include "chain_scan.h"
 
@@ -21,14 +19,14 @@ bool aligned(const void* p, size_t a) { return reinterpret_cast<uintptr_t>(p) % 
 
 enum class Design { kAuto, kChunked, kChain };
 
-// MSSM_SCAN_DESIGN=chunked or =chain pins the design (tests and tuning run
-// both designs on the same shapes); =chain still needs a supported shape.
+// The scan-order setting (mssm_set_tuning) pins the design for tests and
+// tuning runs; the single pass still needs a supported shape.
 Design design_setting() {
-  const char* e = std::getenv("MSSM_SCAN_DESIGN");
-  if (e == nullptr) return Design::kAuto;
-  if (std::strcmp(e, "chunked") == 0) return Design::kChunked;
-  if (std::strcmp(e, "chain") == 0) return Design::kChain;
-  return Design::kAuto;
+  switch (tuning(MSSM_TUNE_SCAN_ORDER)) {
+    case MSSM_ORDER_CHUNKED: return Design::kChunked;
+    case MSSM_ORDER_SINGLE_PASS: return Design::kChain;
+    default: return Design::kAuto;
+  }
 }
 
 template <bool kZoh, bool kSkip, bool kGate>

@@ -6,12 +6,12 @@
 // maps dt_low back to D channels, a per-channel bias is added and softplus
 // keeps the step size positive.  Here:
 //
-//   x_proj  : one plain GEMM P = x @ W_x ([batch*L, D] x [D, R+2N], bf16 in,
-//             float32 out) through rocBLAS;
-//   prep    : dt_low split into two bfloat16 parts, hi = bf16(P[:, :R]) and
-//             lo = bf16(P[:, :R] - hi) (round to nearest even), so the matrix
-//             cores see dt_low to about 16 significant bits; W_dt transposed
-//             to [D, R];
+//   x_proj  : P = x @ W_x ([batch*L, D] x [D, R+2N], bf16 in, float32
+//             accumulation) on the matrix cores (xproj.hip); its epilogue
+//             stores dt_low as two bfloat16 parts, hi = bf16(dt_low) and
+//             lo = bf16(dt_low - hi) (round to nearest even), so dt_proj's
+//             matrix cores see dt_low to about 16 significant bits, and B, C
+//             as float32 rows of P; W_dt is transposed to [D, R];
 //   scan    : the same chunked two-pass scan as the plain path, except that
 //             Delta never exists in memory: every 32-step tile of a wavefront's
 //             channels is computed on the matrix cores (v_mfma_f32_32x32x16_bf16,
@@ -376,22 +376,6 @@ __global__ __launch_bounds__(kFBlock) void fused_output_kernel(
                                 c.wave_ch0, c.ch_valid, D, nsteps, lds, lds_stride<CPL>());
 }
 
-// hi[m, r] = bf16(P[m, r]), lo[m, r] = bf16(P[m, r] - hi[m, r]) (round to nearest
-// even), m < M, r < R: hi + lo carries P to about 16 significant bits.
-__global__ void dtlow_split_kernel(const float* __restrict__ P, uint16_t* __restrict__ hi,
-                                   uint16_t* __restrict__ lo, int64_t M, int R, int64_t ldp) {
-  const int64_t total = M * R;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
-       i += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t m = i / R;
-    const int r = static_cast<int>(i % R);
-    const float v = P[m * ldp + r];
-    const uint32_t h = bf16_rne_bits(v);
-    hi[i] = static_cast<uint16_t>(h);
-    lo[i] = static_cast<uint16_t>(bf16_rne_bits(v - __uint_as_float(h << 16)));
-  }
-}
-
 // Delta[m, d] = softplus(sum_r (hi[m, r] + lo[m, r]) wT[d, r] + bias[d]) for the
 // whole [M, D] matrix, float32: the step sizes of "Understanding Mamba",
 // section 5.1 eq. (6) written out once for the single-pass scan.  Same
@@ -653,11 +637,8 @@ hipError_t launch_transpose_bf16(const void* W, uint16_t* wT, int64_t rows, int6
   return hipGetLastError();
 }
 
-hipError_t launch_fused_prep(const float* P, int64_t M, int64_t R, int64_t ldp, const void* W_dt,
-                             int64_t D, uint16_t* dtl, uint16_t* dtl_lo, uint16_t* wT,
-                             hipStream_t stream) {
-  hipLaunchKernelGGL(dtlow_split_kernel, dim3(2048), dim3(256), 0, stream, P, dtl, dtl_lo, M,
-                     static_cast<int>(R), ldp);
+hipError_t launch_wdt_transpose(const void* W_dt, int64_t R, int64_t D, uint16_t* wT,
+                                hipStream_t stream) {
   hipLaunchKernelGGL(transpose_bf16_kernel, dim3(1024), dim3(256), 0, stream,
                      static_cast<const uint16_t*>(W_dt), wT, static_cast<int>(R), D);
   return hipGetLastError();
@@ -710,7 +691,8 @@ FusedPlan plan_fused(int64_t batch, int64_t L, int64_t D, int64_t N, int64_t R, 
   f.dtl_lo_offset = f.dtl_offset + align256(sizeof(uint16_t) * (size_t)M * (size_t)R);
   f.wt_offset = f.dtl_lo_offset + align256(sizeof(uint16_t) * (size_t)M * (size_t)R);
   f.wx_t_offset = f.wt_offset + align256(sizeof(uint16_t) * (size_t)D * (size_t)R);
-  f.scan_offset = f.wx_t_offset + align256(sizeof(uint16_t) * (size_t)(R + 2 * N) * (size_t)D);
+  f.scan_offset = f.wx_t_offset +
+                  align256(sizeof(uint16_t) * (size_t)(R + 2 * N) * (size_t)xproj_padded_k(D));
   if (chain) {
     f.delta_offset = f.scan_offset;
     f.workspace_bytes = f.delta_offset + align256(sizeof(float) * (size_t)M * (size_t)D);
@@ -731,12 +713,10 @@ size_t fused_workspace_bound(int64_t batch, int64_t L, int64_t D, int64_t N, int
 // One chain per lane: the Delta tile's matrix-core accumulators and operands
 // already take many registers, and two chains per lane leave one wavefront
 // per SIMD (218 VGPRs + 64 AGPRs); one chain keeps three, which measured 35%
-// faster on MI355X for the fused workload (1.91 vs 2.94 ms).  MSSM_CPL=2
-// selects the other layout for tuning runs.
+// faster on MI355X for the fused workload (1.91 vs 2.94 ms).  The
+// chains-per-lane setting 2 selects the other layout for tuning runs.
 int choose_fused_cpl(int64_t D) {
-  if (const char* env = std::getenv("MSSM_CPL")) {       // tuning experiments only
-    if (std::atoi(env) == 2 && D % 2 == 0) return 2;
-  }
+  if (tuning(MSSM_TUNE_CHAINS_PER_LANE) == 2 && D % 2 == 0) return 2;   // tuning runs only
   return 1;
 }
 
@@ -747,25 +727,15 @@ FusedStatus launch_fused(const FusedArgs& a, const FusedPlan& f, void* workspace
   float* P = reinterpret_cast<float*>(ws);
   const int64_t M = a.batch * a.L;
   const int64_t ldp = a.R + 2 * a.N;
-  BlasLease blas(stream);
-  if (!blas.ok()) {
-    st.hip = blas.hip_error();
-    st.blas_failed = st.hip == hipSuccess;
-    return st;
-  }
-  const rocblas_handle hb = blas.get();
-  // x_proj: P[M, R + 2N] = x[M, D] W_x[D, R + 2N], with W_x transposed first
-  uint16_t* WxT = reinterpret_cast<uint16_t*>(ws + f.wx_t_offset);
-  st.hip = launch_transpose_bf16(a.W_x, WxT, a.D, ldp, stream);
-  if (st.hip != hipSuccess) return st;
-  if (!gemm_rm_bf16_bt(hb, M, ldp, a.D, a.x, a.D, WxT, a.D, P, ldp, 0.0f)) {
-    st.blas_failed = true;
-    return st;
-  }
   uint16_t* dtl = reinterpret_cast<uint16_t*>(ws + f.dtl_offset);
   uint16_t* dtl_lo = reinterpret_cast<uint16_t*>(ws + f.dtl_lo_offset);
   uint16_t* wT = reinterpret_cast<uint16_t*>(ws + f.wt_offset);
-  st.hip = launch_fused_prep(P, M, a.R, ldp, a.W_dt, a.D, dtl, dtl_lo, wT, stream);
+  // x_proj: dt_low (as its bf16 hi + lo pair) and the B, C columns of P
+  uint16_t* WxT = reinterpret_cast<uint16_t*>(ws + f.wx_t_offset);
+  st.hip = launch_xproj(static_cast<const uint16_t*>(a.x), nullptr, a.D, M, a.D, a.W_x, ldp,
+                        a.R, WxT, dtl, dtl_lo, P, ldp, stream);
+  if (st.hip != hipSuccess) return st;
+  st.hip = launch_wdt_transpose(a.W_dt, a.R, a.D, wT, stream);
   if (st.hip != hipSuccess) return st;
   if (f.chain) {
     float* delta = reinterpret_cast<float*>(ws + f.delta_offset);

@@ -12,6 +12,10 @@
 
 namespace mssm {
 
+// Current value of a tuning setting (settings.hip): from the environment,
+// read once, or from mssm_set_tuning.
+int64_t tuning(mssm_tuning key);
+
 // How one scan call is cut along time.  The sequence is split into K chunks
 // of chunk_len steps (the last may be shorter).  Chunks 0..K-2 first produce
 // summaries (their local end state from a zero start, and their decay
@@ -50,19 +54,19 @@ struct ScanArgs {
 ScanPlan plan_scan(int64_t batch, int64_t L, int64_t D, int64_t N, int cpl);
 
 // Whether a call over this many channels (batch * D) takes the single-pass
-// order when its shape and pointers allow it: MSSM_SCAN_DESIGN=chunked / chain
-// pins the answer, else at least 8192 channels.
+// order when its shape and pointers allow it: the scan-order setting pins the
+// answer, else at least 8192 channels.
 bool single_pass_chosen(int64_t channels);
 
 // Single-pass scan with one lane per (channel, state index), for N = 16 and
 // shapes with many channels: whether the forward uses it for these arguments
 // (shape, alignment, channel count, sequence length: bfloat16 from 16384 steps
-// and float32 from 32768 go chunked, MSSM_SCAN_DESIGN), and its launch.
+// and float32 from 32768 go chunked, the scan-order setting), and its launch.
 bool chain_scan_applies(const ScanArgs& a);
 hipError_t launch_chain_scan(const ScanArgs& a, hipStream_t stream);
 
 // Whether the arguments fit the single-pass layout (N = 16, D % 16 == 0,
-// alignment, sizes), whatever the channel count or MSSM_SCAN_DESIGN.
+// alignment, sizes), whatever the channel count or the scan-order setting.
 bool chain_layout_ok(const ScanArgs& a);
 // Forward that also saves the backward pass's inputs (first-order input term):
 // the state after every 16-step tile into ck [batch, tiles, D, N] and, with
@@ -80,7 +84,7 @@ SavedLayout saved_layout(int64_t batch, int64_t L, int64_t D, int64_t N, bool ga
 // The single pass behind the selection projections (fused selective SSM and
 // Mamba block): delta is the float32 matrix softplus(dt_low W_dt + bias) and
 // B, C are the columns R .. R+2N-1 of P's rows.  Whether it applies (N = 16,
-// D % 16 == 0, R <= 256, enough channels, MSSM_SCAN_DESIGN; x and y as
+// D % 16 == 0, R <= 256, enough channels, the scan-order setting; x and y as
 // given), and the launch.
 struct ChainFusedArgs {
   const void* x = nullptr;        // [batch, L, D] bf16, or float32 with x_f32
@@ -173,7 +177,7 @@ struct FusedPlan {
   size_t dtl_offset = 0;
   size_t dtl_lo_offset = 0;
   size_t wt_offset = 0;
-  size_t wx_t_offset = 0;     // W_x transposed [R + 2N, D] for the x_proj GEMM
+  size_t wx_t_offset = 0;     // W_x transposed [R + 2N, D padded to 64] for x_proj
   size_t scan_offset = 0;
   size_t workspace_bytes = 0;
 };
@@ -208,10 +212,22 @@ struct FusedScanArgs {
 };
 hipError_t launch_fused_scan(const FusedScanArgs& a, const ScanPlan& plan, hipStream_t stream);
 
-// dt_low split into bf16 hi + lo parts and W_dt transposed, for the fused scan.
-hipError_t launch_fused_prep(const float* P, int64_t M, int64_t R, int64_t ldp, const void* W_dt,
-                             int64_t D, uint16_t* dtl, uint16_t* dtl_lo, uint16_t* wT,
-                             hipStream_t stream);
+// x_proj on the matrix cores (xproj.hip): P = x W_x for x [M, K] bf16 (row
+// stride lda; with x_lo, x = x + x_lo as a bf16 pair, both multiplied into
+// the same float32 sums) and W_x [K, ncol] bf16 (ncol = R + 2N).  Columns
+// below R (dt_low) are stored as the bf16 pair dtl = bf16(v), dtl_lo =
+// bf16(v - dtl) ([M, R] each); columns R.. to P[m * ldp + c] as float32.
+// WxT is workspace for W_x transposed and zero-padded along k:
+// ncol * xproj_padded_k(K) bf16.
+int64_t xproj_padded_k(int64_t K);
+hipError_t launch_xproj(const uint16_t* x, const uint16_t* x_lo, int64_t lda, int64_t M,
+                        int64_t K, const void* W_x, int64_t ncol, int64_t R, uint16_t* WxT,
+                        uint16_t* dtl, uint16_t* dtl_lo, float* P, int64_t ldp,
+                        hipStream_t stream);
+
+// wT [D, R] = W_dt^T for the dt_proj kernels.
+hipError_t launch_wdt_transpose(const void* W_dt, int64_t R, int64_t D, uint16_t* wT,
+                                hipStream_t stream);
 
 // delta[m, d] = softplus(sum_r (dtl + dtl_lo)[m, r] wT[d, r] + bias[d]), float32
 // [M, D], on the matrix cores (R a multiple of 16).

@@ -4,7 +4,6 @@
 // scan_summary_*.hip and scan_out_*.hip launchers.
 #include "scan_kernels.h"
 
-#include <cstdlib>
 
 namespace mssm {
 
@@ -92,10 +91,8 @@ hipError_t launch_state_init(float* h_last, const float* h0, int64_t count, hipS
 // channels' x and delta; MI355X sweeps: about 10-13% faster), not for float32
 // (register pressure lowers occupancy more than the extra ILP gains).
 int default_cpl(int64_t D, mssm_dtype dtype) {
-  if (const char* env = std::getenv("MSSM_CPL")) {       // tuning experiments only
-    const int v = std::atoi(env);
-    if (v == 1 || v == 2) return (v == 2 && D % 2 == 0) ? 2 : 1;
-  }
+  const int64_t v = tuning(MSSM_TUNE_CHAINS_PER_LANE);   // tuning experiments only
+  if (v == 1 || v == 2) return (v == 2 && D % 2 == 0) ? 2 : 1;
   return (dtype == MSSM_BFLOAT16 && D % 2 == 0) ? 2 : 1;
 }
 
@@ -107,18 +104,15 @@ ScanPlan plan_scan(int64_t batch, int64_t L, int64_t D, int64_t N, int cpl) {
   // wavefronts per SIMD over the kernel's life), with chunks of at least 64
   // steps (128 with two chains per lane).  Measured on MI355X with chunk-length sweeps of the synthetic
   // workloads (the per-chunk cost after the carry pass is small, so more
-  // chunks help until chunks get short).  MSSM_CHUNK_LEN overrides the chunk
-  // length (tuning sweeps and chunk-boundary tests).
+  // chunks help until chunks get short).  The chunk-length setting overrides
+  // it (tuning sweeps and chunk-boundary tests).
   const int64_t blocks_per_chunk = batch * ((D + kBlock * cpl - 1) / (kBlock * cpl));
   const int64_t target_blocks = 2048;
   int64_t K = (target_blocks + blocks_per_chunk / 2) / blocks_per_chunk;
   const int64_t min_chunk = cpl == 1 ? 64 : 128;
   K = std::max<int64_t>(1, std::min<int64_t>(K, L / min_chunk));
   int64_t chunk = (L + K - 1) / K;
-  if (const char* env = std::getenv("MSSM_CHUNK_LEN")) {
-    const long long v = std::atoll(env);
-    if (v > 0) chunk = v;
-  }
+  if (const int64_t v = tuning(MSSM_TUNE_CHUNK_LEN); v > 0) chunk = v;
   // buffer offsets inside one chunk are 32-bit: keep chunk * D * 4 < 2^31
   const int64_t max_chunk = std::max<int64_t>(1, ((int64_t(1) << 31) - 1) / (D * 4));
   chunk = std::min<int64_t>(chunk, max_chunk);

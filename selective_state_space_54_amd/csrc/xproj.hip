@@ -1,0 +1,273 @@
+// The selection projection x_proj on the matrix cores (gfx950), one pass
+// over x.
+//
+// Each token x_t (K = D values) is projected to [dt_low (R) | B_t (N) | C_t
+// (N)] = x_t W_x ("Understanding Mamba", section 5.1, eq. (6), in the low-rank
+// Mamba shape).  With batch * L = M tokens that is P[M, R + 2N] = x[M, K]
+// W_x[K, R + 2N]: a tall, thin GEMM whose cost is reading x once (335 MB for
+// the fused workload against 2 MB of weights), so the kernel is laid out for
+// streaming x:
+//
+//   * a block owns 64 rows of x and all (up to 192) output columns, so every
+//     element of x is read from memory exactly once;
+//   * the block's 64-row x tile comes into LDS 64 k-values at a time (16-byte
+//     loads, two buffers, the next tile's loads in flight during the current
+//     tile's products), and every wavefront reads its A fragments from there;
+//   * wavefront w owns output columns 48w .. 48w + 47 (three 16-column
+//     fragments) for all 64 rows: 4 x 3 accumulator tiles of
+//     v_mfma_f32_16x16x32_bf16, fp32 accumulation; its W fragments are its
+//     own, read straight from the transposed weights (W_x^T rows, zero-padded
+//     along k to a multiple of 64, so the k tail needs no test);
+//   * epilogue: columns below R (dt_low) are stored as the bf16 pair
+//     hi = bf16(v), lo = bf16(v - hi) that dt_proj's matrix cores read (R is a
+//     multiple of 16, so a 16-column fragment is all dt_low or all B/C); the
+//     B and C columns are stored as float32 into P's rows.
+//
+// With two A operands (the Mamba block: x kept as a bf16 hi + lo pair) both
+// tiles are multiplied into the same accumulators.
+//
+// MFMA operand layout (v_mfma_f32_16x16x32_bf16): A fragment, lane l holds row
+// l % 16 and 8 consecutive k values starting at 8 (l / 16); B fragment, lane l
+// holds column l % 16 and the same 8 k values; both operands use the same k
+// assignment, so the products pair up whatever order the hardware sums them
+// in.  Result: lane l holds rows 4 (l / 16) + i, i = 0..3, of column l % 16.
+#include <type_traits>
+
+#include "mssm_internal.h"
+#include "scan_device.h"
+
+namespace mssm {
+
+namespace {
+
+constexpr int kXBlock = 256;          // 4 wavefronts
+constexpr int kXRows = 64;            // rows of x per block
+constexpr int kXK = 64;               // k values per LDS tile
+constexpr int kXPitch = kXK + 8;      // LDS row pitch (bf16): 144 bytes, conflict-free 16-byte reads
+constexpr int kXColsPerWave = 48;     // three 16-column fragments
+constexpr int kXCols = 4 * kXColsPerWave;   // output columns per block
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ bf16x8 as_bf16x8(const uint4& u) {
+  bf16x8 v;
+  __builtin_memcpy(&v, &u, sizeof(v));
+  return v;
+}
+
+// W^T[c, r] = W[r, c] for r < K, 0 for K <= r < Kp; W is [K, ncol] row-major,
+// W^T [ncol, Kp].
+__global__ __launch_bounds__(256) void transpose_pad_kernel(const uint16_t* __restrict__ W,
+                                                            uint16_t* __restrict__ wT, int64_t K,
+                                                            int64_t ncol, int64_t Kp) {
+  __shared__ uint16_t tile[64][65];
+  const int64_t tiles_c = (ncol + 63) / 64;
+  const int64_t r0 = static_cast<int64_t>(blockIdx.x / tiles_c) * 64;
+  const int64_t c0 = static_cast<int64_t>(blockIdx.x % tiles_c) * 64;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  for (int i = ty; i < 64; i += 4) {
+    const int64_t r = r0 + i, c = c0 + tx;
+    tile[i][tx] = (r < K && c < ncol) ? W[r * ncol + c] : uint16_t(0);
+  }
+  __syncthreads();
+  for (int i = ty; i < 64; i += 4) {
+    const int64_t c = c0 + i, r = r0 + tx;
+    if (c < ncol && r < Kp) wT[c * Kp + r] = tile[tx][i];
+  }
+}
+
+// One 16-byte piece (8 bf16) of row m of an A operand at k0.  kVec: the row
+// stride and base allow a 16-byte load, and K is a multiple of 8, so a piece
+// is wholly inside or wholly past K.  Otherwise element loads, each tested.
+template <bool kVec>
+__device__ __forceinline__ uint4 load_piece(const uint16_t* __restrict__ A, int64_t lda,
+                                            int64_t m, int64_t k0, int64_t K) {
+  const uint16_t* p = A + m * lda + k0;
+  if constexpr (kVec) {
+    if (k0 >= K) return make_uint4(0u, 0u, 0u, 0u);
+    return *reinterpret_cast<const uint4*>(p);
+  } else {
+    uint32_t w[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t lo = k0 + 2 * j < K ? p[2 * j] : 0u;
+      const uint32_t hi = k0 + 2 * j + 1 < K ? p[2 * j + 1] : 0u;
+      w[j] = lo | (hi << 16);
+    }
+    return make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
+
+// grid: (ceil(M / 64), ceil(ncol / 192)).  A0 (and A1 with kTwo) [M, K] bf16
+// with row stride lda; wT [ncol, Kp] bf16, Kp a multiple of 64, zero for
+// k >= K.  Outputs: columns c < R to dtl / dtl_lo [M, R] (bf16 pair), columns
+// R <= c < ncol to P[m * ldp + c] (float32).
+template <bool kTwo, bool kVec>
+__global__ __launch_bounds__(kXBlock) void xproj_kernel(
+    const uint16_t* __restrict__ A0, const uint16_t* __restrict__ A1, int64_t lda,
+    const uint16_t* __restrict__ wT, int64_t Kp, int64_t K, int64_t M, int ncol, int R,
+    uint16_t* __restrict__ dtl, uint16_t* __restrict__ dtl_lo, float* __restrict__ P,
+    int64_t ldp) {
+  constexpr int kOps = kTwo ? 2 : 1;
+  __shared__ __align__(16) uint16_t sa[2][kOps][kXRows][kXPitch];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t m0 = static_cast<int64_t>(blockIdx.x) * kXRows;
+  const int c_wave = static_cast<int>(blockIdx.y) * kXCols + wave * kXColsPerWave;
+  // fragments of this wavefront that hold any column < ncol (wave-uniform)
+  int nfrag = (ncol - c_wave + 15) / 16;
+  nfrag = nfrag < 0 ? 0 : (nfrag > 3 ? 3 : nfrag);
+
+  // x tile pieces of this thread: 64 rows x 8 pieces of 8 k = 512 per operand
+  int prow[2], pk[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int p = threadIdx.x + kXBlock * h;
+    prow[h] = p >> 3;
+    pk[h] = (p & 7) * 8;
+  }
+  uint4 xa[kOps][2];
+  auto fetch_x = [&](int64_t k0) {
+#pragma unroll
+    for (int o = 0; o < kOps; ++o) {
+      const uint16_t* A = o == 0 ? A0 : A1;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int64_t m = min(m0 + prow[h], M - 1);
+        xa[o][h] = load_piece<kVec>(A, lda, m, k0 + pk[h], K);
+      }
+    }
+  };
+  auto stash_x = [&](int buf) {
+#pragma unroll
+    for (int o = 0; o < kOps; ++o)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        *reinterpret_cast<uint4*>(&sa[buf][o][prow[h]][pk[h]]) = xa[o][h];
+  };
+  // W fragments of this wavefront: (fragment, k step of 32) -> 8 bf16
+  const int bk = 8 * (lane >> 4);
+  const uint16_t* wrow[3];
+#pragma unroll
+  for (int f = 0; f < 3; ++f) {
+    const int c = min(c_wave + 16 * f + (lane & 15), ncol - 1);
+    wrow[f] = wT + static_cast<int64_t>(c) * Kp + bk;
+  }
+  uint4 wb[2][3][2];
+  auto fetch_w = [&](int slot, int64_t k0) {
+#pragma unroll
+    for (int f = 0; f < 3; ++f)
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+        if (f < nfrag) wb[slot][f][s] = *reinterpret_cast<const uint4*>(wrow[f] + k0 + 32 * s);
+  };
+
+  f32x4 acc[4][3];
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int f = 0; f < 3; ++f) acc[r][f] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+  const int64_t ntiles = Kp / kXK;
+  const int arow = lane & 15;
+  // Tile t: its x pieces (fetched one tile earlier) go into LDS buffer B, the
+  // next tile's x and W are fetched into the other register set, then the
+  // products.  B is a compile-time constant (the loop is unrolled by two), so
+  // the register sets keep fixed names.
+  auto tile = [&](int64_t t, auto Bc) {
+    constexpr int B = decltype(Bc)::value;
+    stash_x(B);
+    block_sync();
+    if (t + 1 < ntiles) {
+      fetch_x((t + 1) * kXK);            // in flight during this tile's products
+      fetch_w(B ^ 1, (t + 1) * kXK);
+    }
+    if (nfrag > 0) {
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+#pragma unroll
+          for (int o = 0; o < kOps; ++o) {
+            const bf16x8 a = as_bf16x8(
+                *reinterpret_cast<const uint4*>(&sa[B][o][16 * r + arow][32 * s + bk]));
+#pragma unroll
+            for (int f = 0; f < 3; ++f)
+              if (f < nfrag)
+                acc[r][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    a, as_bf16x8(wb[B][f][s]), acc[r][f], 0, 0, 0);
+          }
+        }
+      }
+    }
+  };
+  fetch_x(0);
+  fetch_w(0, 0);
+  int64_t t = 0;
+  for (; t + 2 <= ntiles; t += 2) {
+    tile(t, std::integral_constant<int, 0>{});
+    tile(t + 1, std::integral_constant<int, 1>{});
+  }
+  if (t < ntiles) tile(t, std::integral_constant<int, 0>{});
+
+  // epilogue
+  const int col_in = lane & 15;
+  const int row_in = 4 * (lane >> 4);
+#pragma unroll
+  for (int f = 0; f < 3; ++f) {
+    if (f >= nfrag) continue;
+    const int c = c_wave + 16 * f + col_in;
+    const bool dt_frag = c_wave + 16 * f < R;       // uniform: R is a multiple of 16
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t m = m0 + 16 * r + row_in + i;
+        if (m >= M) continue;
+        const float v = acc[r][f][i];
+        if (dt_frag) {
+          const uint32_t hi = bf16_rne_bits(v);
+          dtl[m * R + c] = static_cast<uint16_t>(hi);
+          dtl_lo[m * R + c] = static_cast<uint16_t>(bf16_rne_bits(v - __uint_as_float(hi << 16)));
+        } else if (c < ncol) {
+          P[m * ldp + c] = v;
+        }
+      }
+    }
+  }
+}
+
+}  // namespace
+
+int64_t xproj_padded_k(int64_t K) { return (K + kXK - 1) / kXK * kXK; }
+
+hipError_t launch_xproj(const uint16_t* x, const uint16_t* x_lo, int64_t lda, int64_t M,
+                        int64_t K, const void* W_x, int64_t ncol, int64_t R, uint16_t* WxT,
+                        uint16_t* dtl, uint16_t* dtl_lo, float* P, int64_t ldp,
+                        hipStream_t stream) {
+  if (M <= 0 || ncol <= 0) return hipSuccess;
+  const int64_t Kp = xproj_padded_k(K);
+  const int64_t tiles = ((Kp + 63) / 64) * ((ncol + 63) / 64);
+  hipLaunchKernelGGL(transpose_pad_kernel, dim3(static_cast<unsigned>(tiles)), dim3(256), 0,
+                     stream, static_cast<const uint16_t*>(W_x), WxT, K, ncol, Kp);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const dim3 grid(static_cast<unsigned>((M + kXRows - 1) / kXRows),
+                  static_cast<unsigned>((ncol + kXCols - 1) / kXCols));
+  const bool vec = K % 8 == 0 && lda % 8 == 0 && reinterpret_cast<uintptr_t>(x) % 16 == 0 &&
+                   (x_lo == nullptr || reinterpret_cast<uintptr_t>(x_lo) % 16 == 0);
+  const int nc = static_cast<int>(ncol), r = static_cast<int>(R);
+#define MSSM_XPROJ(TWO, VEC)                                                                    \
+  hipLaunchKernelGGL((xproj_kernel<TWO, VEC>), grid, dim3(kXBlock), 0, stream, x, x_lo, lda,   \
+                     WxT, Kp, K, M, nc, r, dtl, dtl_lo, P, ldp)
+  if (x_lo) {
+    if (vec) MSSM_XPROJ(true, true); else MSSM_XPROJ(true, false);
+  } else {
+    if (vec) MSSM_XPROJ(false, true); else MSSM_XPROJ(false, false);
+  }
+#undef MSSM_XPROJ
+  return hipGetLastError();
+}
+
+}  // namespace mssm

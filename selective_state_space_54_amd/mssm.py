@@ -8,6 +8,7 @@ There is no fallback: if the library is missing, loading fails loudly.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 
@@ -27,6 +28,14 @@ MSSM_BFLOAT16 = 1
 MSSM_BBAR_EULER = 0
 MSSM_BBAR_ZOH = 1
 _BBAR = {"euler": MSSM_BBAR_EULER, "zoh": MSSM_BBAR_ZOH}
+MSSM_TUNE_SCAN_ORDER = 0
+MSSM_TUNE_CHUNK_LEN = 1
+MSSM_TUNE_CHAINS_PER_LANE = 2
+MSSM_ORDER_AUTO = 0
+MSSM_ORDER_CHUNKED = 1
+MSSM_ORDER_SINGLE_PASS = 2
+_ORDERS = {"auto": MSSM_ORDER_AUTO, "chunked": MSSM_ORDER_CHUNKED,
+           "chain": MSSM_ORDER_SINGLE_PASS, "single_pass": MSSM_ORDER_SINGLE_PASS}
 _DTYPES = {torch.float32: MSSM_FLOAT32, torch.bfloat16: MSSM_BFLOAT16}
 _STATUS_NAMES = {0: "MSSM_SUCCESS", 1: "MSSM_ERROR_INVALID_VALUE", 2: "MSSM_ERROR_NOT_SUPPORTED",
                  3: "MSSM_ERROR_SIZE_OVERFLOW", 4: "MSSM_ERROR_WORKSPACE", 5: "MSSM_ERROR_HIP"}
@@ -38,6 +47,8 @@ _vp = ctypes.c_void_p
 _i64 = ctypes.c_int64
 _SIGNATURES = {
     "mssm_abi_version": (ctypes.c_int, []),
+    "mssm_set_tuning": (ctypes.c_int, [ctypes.c_int, _i64]),
+    "mssm_get_tuning": (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(ctypes.c_int64)]),
     "mssm_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "mssm_last_error_string": (ctypes.c_char_p, []),
     "mssm_supports_state_size": (ctypes.c_int, [_i64]),
@@ -150,6 +161,47 @@ def mssm_abi_version() -> int:
     return load().mssm_abi_version()
 
 
+def mssm_set_tuning(key: int, value: int) -> None:
+    """Set one process-wide tuning value (MSSM_TUNE_*)."""
+    _check(load().mssm_set_tuning(key, value), "mssm_set_tuning")
+
+
+def mssm_get_tuning(key: int) -> int:
+    out = ctypes.c_int64(0)
+    _check(load().mssm_get_tuning(key, ctypes.byref(out)), "mssm_get_tuning")
+    return out.value
+
+
+@contextlib.contextmanager
+def tuning(scan_order=None, chunk_len=None, chains_per_lane=None):
+    """Pin tuning settings for the calls made inside the block and restore the
+    previous values afterwards.  scan_order: "auto", "chunked" or "chain";
+    chunk_len: steps per chunk (0: automatic); chains_per_lane: 0, 1 or 2."""
+    wanted = {}
+    if scan_order is not None:
+        if scan_order not in _ORDERS:
+            raise ValueError(f"scan_order must be one of {sorted(_ORDERS)}")
+        wanted[MSSM_TUNE_SCAN_ORDER] = _ORDERS[scan_order]
+    if chunk_len is not None:
+        wanted[MSSM_TUNE_CHUNK_LEN] = int(chunk_len)
+    if chains_per_lane is not None:
+        wanted[MSSM_TUNE_CHAINS_PER_LANE] = int(chains_per_lane)
+    old = {k: mssm_get_tuning(k) for k in wanted}
+    try:
+        for k, v in wanted.items():
+            mssm_set_tuning(k, v)
+        yield
+    finally:
+        for k, v in old.items():
+            mssm_set_tuning(k, v)
+
+
+def _on(stream):
+    """Allocations for a call launched on `stream` are made on that stream, so
+    the caching allocator orders their reuse after the call's kernels."""
+    return torch.cuda.stream(stream) if stream is not None else contextlib.nullcontext()
+
+
 def mssm_supports_state_size(N: int) -> bool:
     return bool(load().mssm_supports_state_size(N))
 
@@ -239,9 +291,10 @@ def prepare_selective_scan_fwd_ws(x, delta, A, B, C, y, workspace, *, stream=Non
 def selective_scan(x, delta, A, B, C, *, stream=None):
     """Allocate y and the workspace with torch, then run mssm_selective_scan_fwd_ws."""
     batch, L, D, N = _scan_shapes(x, A)
-    y = torch.empty(x.shape, dtype=torch.float32, device=x.device)
     nbytes = mssm_selective_scan_workspace_size(batch, L, D, N, x.dtype)
-    ws = torch.empty(nbytes, dtype=torch.uint8, device=x.device) if nbytes else None
+    with _on(stream):
+        y = torch.empty(x.shape, dtype=torch.float32, device=x.device)
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=x.device) if nbytes else None
     return mssm_selective_scan_fwd_ws(x, delta, A, B, C, y, ws, stream=stream)
 
 
@@ -281,11 +334,12 @@ def selective_scan_ex(x, delta, A, B, C, *, Dskip=None, z=None, h0=None,
     """Allocate y (and the final state) with torch, then run
     mssm_selective_scan_fwd_ex.  Returns y, or (y, h_last)."""
     batch, L, D, N = _scan_shapes(x, A)
-    y = torch.empty(x.shape, dtype=torch.float32, device=x.device)
-    h_last = (torch.empty((batch, D, N), dtype=torch.float32, device=x.device)
-              if return_last_state else None)
     nbytes = mssm_selective_scan_workspace_size(batch, L, D, N, x.dtype)
-    ws = torch.empty(nbytes, dtype=torch.uint8, device=x.device) if nbytes else None
+    with _on(stream):
+        y = torch.empty(x.shape, dtype=torch.float32, device=x.device)
+        h_last = (torch.empty((batch, D, N), dtype=torch.float32, device=x.device)
+                  if return_last_state else None)
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=x.device) if nbytes else None
     mssm_selective_scan_fwd_ex(x, delta, A, B, C, y, ws, Dskip=Dskip, z=z, h0=h0, h_last=h_last,
                                bbar=bbar, stream=stream)
     return (y, h_last) if return_last_state else y
@@ -322,7 +376,8 @@ def mssm_selective_scan_step(x, delta, A, B, C, h, y, *, Dskip=None, z=None, bba
 
 def selective_scan_step(x, delta, A, B, C, h, *, Dskip=None, z=None, bbar="euler", stream=None):
     """Allocate y, run mssm_selective_scan_step (h updated in place), return y."""
-    y = torch.empty(x.shape, dtype=torch.float32, device=x.device)
+    with _on(stream):
+        y = torch.empty(x.shape, dtype=torch.float32, device=x.device)
     return mssm_selective_scan_step(x, delta, A, B, C, h, y, Dskip=Dskip, z=z, bbar=bbar,
                                     stream=stream)
 
@@ -377,9 +432,10 @@ def selective_ssm_fused(x, W_x, W_dt, dt_bias, A, *, stream=None):
     """Allocate y and the workspace with torch, then run mssm_selective_ssm_fused_fwd."""
     batch, L, D, N = _scan_shapes(x, A)
     R = W_dt.shape[0]
-    y = torch.empty(x.shape, dtype=torch.float32, device=x.device)
     nbytes = mssm_selective_ssm_fused_workspace_size(batch, L, D, N, R, x.dtype)
-    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=x.device)
+    with _on(stream):
+        y = torch.empty(x.shape, dtype=torch.float32, device=x.device)
+        ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=x.device)
     return mssm_selective_ssm_fused_fwd(x, W_x, W_dt, dt_bias, A, y, ws, stream=stream)
 
 
@@ -407,7 +463,8 @@ def mssm_causal_conv1d_silu(u, conv_w, conv_b, out, *, stream=None):
 
 
 def causal_conv1d_silu(u, conv_w, conv_b=None, *, stream=None):
-    out = torch.empty(u.shape, dtype=torch.float32, device=u.device)
+    with _on(stream):
+        out = torch.empty(u.shape, dtype=torch.float32, device=u.device)
     return mssm_causal_conv1d_silu(u, conv_w, conv_b, out, stream=stream)
 
 
@@ -464,10 +521,11 @@ def mamba_block(u0, W_in, conv_w, conv_b, W_x, W_dt, dt_bias, A, Dskip, W_out, *
     """Allocate out and the workspace with torch, then run mssm_mamba_block_fwd."""
     batch, L, Dm = u0.shape
     Di = W_in.shape[1] // 2
-    out = torch.empty((batch, L, Dm), dtype=torch.float32, device=u0.device)
     nbytes = mssm_mamba_block_workspace_size(batch, L, Dm, Di, A.shape[1], W_dt.shape[0],
                                              conv_w.shape[1], u0.dtype)
-    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=u0.device)
+    with _on(stream):
+        out = torch.empty((batch, L, Dm), dtype=torch.float32, device=u0.device)
+        ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=u0.device)
     return mssm_mamba_block_fwd(u0, W_in, conv_w, conv_b, W_x, W_dt, dt_bias, A, Dskip, W_out,
                                 out, ws, stream=stream)
 
@@ -572,7 +630,12 @@ def mssm_selective_scan_bwd_saved(x, delta, A, B, C, saved, dout, grads, workspa
     return grads
 
 
-def _alloc_grads(x, A, Dskip, z, h0):
+def _alloc_grads(x, A, Dskip, z, h0, stream=None):
+    with _on(stream):
+        return _alloc_grads_here(x, A, Dskip, z, h0)
+
+
+def _alloc_grads_here(x, A, Dskip, z, h0):
     batch, L, D, N = _scan_shapes(x, A)
     opts = dict(device=x.device, dtype=torch.float32)
     grads = {"dx": torch.empty((batch, L, D), **opts), "ddelta": torch.empty((batch, L, D), **opts),
@@ -594,11 +657,12 @@ def selective_scan_fwd_save(x, delta, A, B, C, *, Dskip=None, z=None, h0=None,
     """Allocate y, the saved buffer (and the final state) with torch, then run
     mssm_selective_scan_fwd_save.  Returns (y, saved) or (y, saved, h_last)."""
     batch, L, D, N = _scan_shapes(x, A)
-    y = torch.empty(x.shape, dtype=torch.float32, device=x.device)
     nbytes = mssm_selective_scan_saved_size(batch, L, D, N, z is not None)
-    saved = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=x.device)
-    h_last = (torch.empty((batch, D, N), dtype=torch.float32, device=x.device)
-              if return_last_state else None)
+    with _on(stream):
+        y = torch.empty(x.shape, dtype=torch.float32, device=x.device)
+        saved = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=x.device)
+        h_last = (torch.empty((batch, D, N), dtype=torch.float32, device=x.device)
+                  if return_last_state else None)
     mssm_selective_scan_fwd_save(x, delta, A, B, C, y, saved, Dskip=Dskip, z=z, h0=h0,
                                  h_last=h_last, stream=stream)
     return (y, saved, h_last) if return_last_state else (y, saved)
@@ -608,7 +672,7 @@ def selective_scan_bwd_saved(x, delta, A, B, C, saved, dout, *, Dskip=None, z=No
                              stream=None):
     """Allocate the gradients and the workspace with torch, then run
     mssm_selective_scan_bwd_saved; returns the dict of gradients."""
-    grads, ws = _alloc_grads(x, A, Dskip, z, h0)
+    grads, ws = _alloc_grads(x, A, Dskip, z, h0, stream)
     return mssm_selective_scan_bwd_saved(x, delta, A, B, C, saved, dout, grads, ws, Dskip=Dskip,
                                          z=z, h0=h0, stream=stream)
 
@@ -616,6 +680,6 @@ def selective_scan_bwd_saved(x, delta, A, B, C, saved, dout, *, Dskip=None, z=No
 def selective_scan_bwd(x, delta, A, B, C, dout, *, Dskip=None, z=None, h0=None, stream=None):
     """Allocate the gradients and the workspace with torch, then run
     mssm_selective_scan_bwd; returns the dict of gradients."""
-    grads, ws = _alloc_grads(x, A, Dskip, z, h0)
+    grads, ws = _alloc_grads(x, A, Dskip, z, h0, stream)
     return mssm_selective_scan_bwd(x, delta, A, B, C, dout, grads, ws, Dskip=Dskip, z=z, h0=h0,
                                    stream=stream)

@@ -24,6 +24,30 @@ def lib():
     return mssm.load()
 
 
+class _Order:
+    """Pins the scan order through the library's tuning setting for the rest of
+    a test; restore() puts the previous value back."""
+
+    def __init__(self):
+        self.old = None
+
+    def set(self, order):
+        if self.old is None:
+            self.old = mssm.mssm_get_tuning(mssm.MSSM_TUNE_SCAN_ORDER)
+        mssm.mssm_set_tuning(mssm.MSSM_TUNE_SCAN_ORDER, mssm._ORDERS[order])
+
+    def restore(self):
+        if self.old is not None:
+            mssm.mssm_set_tuning(mssm.MSSM_TUNE_SCAN_ORDER, self.old)
+
+
+@pytest.fixture
+def order(lib):
+    o = _Order()
+    yield o
+    o.restore()
+
+
 def test_exports_every_declared_symbol(lib):
     declared = _declared()
     assert declared, "no declarations found in include/mssm.h"
@@ -94,10 +118,10 @@ def test_zero_sizes_are_no_ops(lib):
         assert lib.mssm_selective_scan_fwd_ws(*nulls, None, 0, *shape, 16, 0, None) == 0
 
 
-def test_workspace_too_small_is_rejected(lib, monkeypatch):
+def test_workspace_too_small_is_rejected(lib, order):
     # the chunked design's workspace (the single-pass design, which this shape
     # would get by default, needs none)
-    monkeypatch.setenv("MSSM_SCAN_DESIGN", "chunked")
+    order.set("chunked")
     st, nbytes = _ws(lib, 8, 2048, 1536, 16, 0)
     assert nbytes > 0
     r = lib.mssm_selective_scan_fwd_ws(*([FAKE] * 6), FAKE, nbytes - 1, 8, 2048, 1536, 16, 0, None)
@@ -124,10 +148,10 @@ def test_fused_support_and_workspace_queries(lib):
     assert _fws(lib, 0, 64, 64, 16, 16, 1) == (0, 0)
 
 
-def test_fused_argument_errors(lib, monkeypatch):
+def test_fused_argument_errors(lib, order):
     # the workspace query covers both scan orders; the single pass (pinned here)
     # is the one whose plan needs all of it at this shape
-    monkeypatch.setenv("MSSM_SCAN_DESIGN", "chain")
+    order.set("chain")
     def call(ptrs, ws, wsb, batch, L, D, N, R, dtype=1):
         return lib.mssm_selective_ssm_fused_fwd(*ptrs, ws, wsb, batch, L, D, N, R, dtype, None)
     p6 = [FAKE] * 6
@@ -148,8 +172,8 @@ def _ex(lib, ptrs, bbar, ws, wsb, batch, L, D, N, dtype=0):
     return lib.mssm_selective_scan_fwd_ex(*ptrs, bbar, ws, wsb, batch, L, D, N, dtype, None)
 
 
-def test_scan_ex_argument_errors(lib, monkeypatch):
-    monkeypatch.setenv("MSSM_SCAN_DESIGN", "chunked")   # the workspace cases below
+def test_scan_ex_argument_errors(lib, order):
+    order.set("chunked")   # the workspace cases below
     p10 = [FAKE] * 10          # x, delta, A, B, C, Dskip, z, h0, y, h_last
     assert _ex(lib, p10, 2, FAKE, 1 << 40, 1, 4, 4, 4) == 1        # bad bbar enum
     assert _ex(lib, p10, -1, FAKE, 1 << 40, 1, 4, 4, 4) == 1
@@ -238,10 +262,10 @@ def test_block_support_and_argument_errors(lib):
     assert call([None] * 11, None, 0, 0, 8, 32, 64, 16, 16, 4) == 0
 
 
-def test_backward_argument_errors(lib, monkeypatch):
+def test_backward_argument_errors(lib, order):
     # the chunked order, whose workspace the bound below covers exactly at
     # this shape; a smaller buffer is refused before anything launches
-    monkeypatch.setenv("MSSM_SCAN_DESIGN", "chunked")
+    order.set("chunked")
     out = ctypes.c_size_t(0)
     assert lib.mssm_selective_scan_bwd_workspace_size(8, 2048, 1536, 16, 0, ctypes.byref(out)) == 0
     assert out.value > 0
@@ -269,7 +293,7 @@ def test_backward_argument_errors(lib, monkeypatch):
         assert call(ptrs, FAKE, 1 << 40, 1, 4, 4, 4) == 1, f"null {i} accepted"
     assert call(p17, FAKE, nb - 1, 8, 2048, 1536, 16) == 4
     assert call(p17, ctypes.c_void_p(0x1004), nb, 8, 2048, 1536, 16) == 4
-    monkeypatch.setenv("MSSM_SCAN_DESIGN", "chain")
+    order.set("chain")
     assert call(p17, FAKE, 0, 8, 2048, 1536, 16) == 4
     assert call(p17, ctypes.c_void_p(0x1004), nb, 8, 2048, 1536, 16) == 4
 
@@ -326,3 +350,81 @@ def test_saved_forward_and_backward_argument_errors(lib):
     t = list(tail)
     t[7] = None                                                # z without dz
     assert bwd(head, FAKE, nb, t, FAKE, big, 8, 2048, 1536, 16) == 1
+
+
+def test_tuning_settings_round_trip(lib):
+    keys = (mssm.MSSM_TUNE_SCAN_ORDER, mssm.MSSM_TUNE_CHUNK_LEN, mssm.MSSM_TUNE_CHAINS_PER_LANE)
+    old = [mssm.mssm_get_tuning(k) for k in keys]
+    try:
+        with mssm.tuning(scan_order="chunked", chunk_len=77, chains_per_lane=1):
+            assert [mssm.mssm_get_tuning(k) for k in keys] == [1, 77, 1]
+        assert [mssm.mssm_get_tuning(k) for k in keys] == old
+        assert lib.mssm_set_tuning(0, 3) == 1          # no such scan order
+        assert lib.mssm_set_tuning(1, -1) == 1         # negative chunk length
+        assert lib.mssm_set_tuning(2, 3) == 1          # 1 or 2 chains per lane (0: automatic)
+        assert lib.mssm_set_tuning(7, 0) == 1          # no such key
+        assert lib.mssm_get_tuning(0, None) == 1
+        v = ctypes.c_int64(0)
+        assert lib.mssm_get_tuning(9, ctypes.byref(v)) == 1
+    finally:
+        for k, v in zip(keys, old):
+            mssm.mssm_set_tuning(k, v)
+
+
+def _round256(v):
+    return (v + 255) // 256 * 256
+
+
+def _chunked_ws(k_minus_1, N, D):
+    """Chunked-order workspace: an end state per chunk but the last (float32
+    [K-1, N, D]) and its step-size total (float64 [K-1, D]), for batch 1."""
+    return _round256(4 * k_minus_1 * N * D) + _round256(8 * k_minus_1 * D)
+
+
+def test_chunk_length_setting_drives_the_plan(lib, order):
+    """The chunk length decides the chunked order's workspace, so the size
+    query shows which chunk length a call uses."""
+    order.set("chunked")
+    with mssm.tuning(chunk_len=100, chains_per_lane=1):
+        st, nbytes = _ws(lib, 1, 1000, 64, 4, 0)
+    assert st == 0 and nbytes == _chunked_ws(9, 4, 64)
+
+
+def test_environment_is_read_once_at_first_use():
+    """A process that starts with MSSM_CHUNK_LEN / MSSM_SCAN_DESIGN / MSSM_CPL set
+    gets them as its initial settings; changing the environment afterwards
+    changes nothing (calls do not read it), while mssm_set_tuning does."""
+    import subprocess
+    import sys
+    if not os.path.exists(mssm.LIB_PATH):
+        pytest.skip("libmssm.so not built")
+    code = f"""
+import ctypes, json, os, sys
+sys.path.insert(0, {ROOT!r})
+from selective_state_space_54_amd import mssm
+lib = mssm.load()
+def ws(L):
+    out = ctypes.c_size_t(0)
+    assert lib.mssm_selective_scan_workspace_size(1, L, 64, 4, 0, ctypes.byref(out)) == 0
+    return out.value
+first = [mssm.mssm_get_tuning(k) for k in (0, 1, 2)]
+size_first = ws(1000)
+os.environ["MSSM_CHUNK_LEN"] = "250"
+os.environ["MSSM_SCAN_DESIGN"] = "chain"
+os.environ["MSSM_CPL"] = "2"
+after_env = [mssm.mssm_get_tuning(k) for k in (0, 1, 2)]
+size_after_env = ws(1000)
+mssm.mssm_set_tuning(1, 250)
+size_after_set = ws(1000)
+print(json.dumps([first, after_env, size_first, size_after_env, size_after_set]))
+"""
+    env = dict(os.environ, MSSM_CHUNK_LEN="100", MSSM_SCAN_DESIGN="chunked", MSSM_CPL="1")
+    r = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True,
+                       timeout=120)
+    assert r.returncode == 0, r.stderr
+    import json
+    first, after_env, s1, s2, s3 = json.loads(r.stdout.strip().splitlines()[-1])
+    assert first == [1, 100, 1]
+    assert after_env == first
+    assert s1 == s2 == _chunked_ws(9, 4, 64)
+    assert s3 == _chunked_ws(3, 4, 64)

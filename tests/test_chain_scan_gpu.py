@@ -1,13 +1,12 @@
 """GPU parity of the single-pass scan design (one lane per channel and state,
 N = 16, D a multiple of 16) against the float64 oracle, through the C ABI.
 
-MSSM_SCAN_DESIGN=chain pins that design on shapes far below the channel count
-at which it is chosen by itself, so ragged and tiny sequences, every optional
-part, both input types and both input terms run through it; =chunked pins the
-other design on the full-size workloads, which now default to the single pass.
+The scan-order setting "chain" pins that design on shapes far below the
+channel count at which it is chosen by itself, so ragged and tiny sequences,
+every optional part, both input types and both input terms run through it;
+"chunked" pins the other design on the full-size workloads, which default to
+the single pass.
 """
-import os
-
 import numpy as np
 import pytest
 
@@ -77,8 +76,7 @@ def test_runs_without_workspace(design):
     mssm.mssm_selective_scan_fwd_ws(t["x"], t["delta"], t["A"], t["B"], t["C"], y, None)
     torch.cuda.synchronize()
     assert_parity(host64(y), oracle_scan(g), "fp32", "chain without workspace")
-    os.environ["MSSM_SCAN_DESIGN"] = "chunked"
-    with pytest.raises(mssm.MssmError) as e:
+    with mssm.tuning(scan_order="chunked"), pytest.raises(mssm.MssmError) as e:
         mssm.mssm_selective_scan_fwd_ws(t["x"], t["delta"], t["A"], t["B"], t["C"], y, None)
     assert e.value.status == mssm.MSSM_ERROR_WORKSPACE
 

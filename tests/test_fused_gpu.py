@@ -2,8 +2,6 @@
 scan) through the C ABI against the float64 oracle on the same bf16 inputs.
 The GPU keeps dt_low to about 16 significant bits (a bf16 hi + lo pair on the
 matrix cores); the oracle keeps it in float64."""
-import os
-
 import numpy as np
 import pytest
 
@@ -43,20 +41,6 @@ def oracle_fused(g, channels=None):
     return oracle.selective_scan(x, delta, A, B, C, nthreads=ORACLE_THREADS)
 
 
-@pytest.fixture
-def chunk_len(request):
-    old = os.environ.get("MSSM_CHUNK_LEN")
-    if request.param is None:
-        os.environ.pop("MSSM_CHUNK_LEN", None)
-    else:
-        os.environ["MSSM_CHUNK_LEN"] = str(request.param)
-    yield request.param
-    if old is None:
-        os.environ.pop("MSSM_CHUNK_LEN", None)
-    else:
-        os.environ["MSSM_CHUNK_LEN"] = old
-
-
 SHAPES = [  # batch, L, D, N, R
     (1, 1, 64, 16, 16), (1, 31, 64, 16, 32), (2, 33, 100, 16, 16), (1, 100, 130, 4, 48),
     (2, 300, 257, 16, 160), (1, 257, 512, 8, 160), (3, 129, 96, 16, 64),
@@ -90,16 +74,9 @@ def test_fused_single_pass_shapes(shape, design):
 
 @pytest.mark.parametrize("cpl", ["1", "2"])
 def test_fused_both_chain_per_lane_variants(cpl):
-    old = os.environ.get("MSSM_CPL")
-    os.environ["MSSM_CPL"] = cpl
-    try:
+    with mssm.tuning(chains_per_lane=int(cpl)):
         g = workloads.generate("fused_proj_bf16", batch=2, L=200, D=320, N=16, R=160, seed=31)
         y = run_fused(g)
-    finally:
-        if old is None:
-            os.environ.pop("MSSM_CPL", None)
-        else:
-            os.environ["MSSM_CPL"] = old
     assert_parity(y, oracle_fused(g), "bf16", f"fused cpl={cpl}")
 
 
@@ -114,16 +91,14 @@ def test_fused_zero_dt_proj_matches_plain_scan_on_gpu(design):
 
 
 @pytest.mark.parametrize("design", ["auto", "chunked"], indirect=True)
-def test_fused_full_size_workload_sampled_channels(design):
-    """batch 16, L 2048, D 5120, N 16, R 160: every 20th channel against the
-    oracle; by default this shape takes the single-pass scan over a written-out
-    delta, pinned "chunked" the chunked kernels with delta on the matrix cores."""
+def test_fused_full_size_workload_every_output(design):
+    """batch 16, L 2048, D 5120, N 16, R 160: every output against the oracle;
+    by default this shape takes the single-pass scan over a written-out delta,
+    pinned "chunked" the chunked kernels with delta on the matrix cores."""
     print(f"case fused_proj_bf16 full size design={design}", flush=True)
     g = workloads.generate("fused_proj_bf16")
     y = run_fused(g)
-    assert np.isfinite(y).all()
-    ch = np.arange(0, g["workload"].D, 20)
-    r = assert_parity(y[:, :, ch], oracle_fused(g, channels=ch), "bf16", "fused_proj_bf16")
+    r = assert_parity(y, oracle_fused(g), "bf16", "fused_proj_bf16")
     print("fused_proj_bf16", r, flush=True)
 
 

@@ -3,8 +3,6 @@ the C ABI) against the float64 oracle: the exact zero-order-hold input term,
 the feedthrough D x, the SiLU(z) gate, an initial state h0 and the final state
 h_last, across chunk boundaries, both chains-per-lane layouts, the workloads'
 full sizes, and a long sequence processed in pieces."""
-import os
-
 import numpy as np
 import pytest
 
@@ -19,20 +17,6 @@ if not torch.cuda.is_available():
     pytest.skip("no GPU", allow_module_level=True)
 
 from selective_state_space_54_amd import mssm  # noqa: E402
-
-
-@pytest.fixture
-def chunk_len(request):
-    old = os.environ.get("MSSM_CHUNK_LEN")
-    if request.param is None:
-        os.environ.pop("MSSM_CHUNK_LEN", None)
-    else:
-        os.environ["MSSM_CHUNK_LEN"] = str(request.param)
-    yield request.param
-    if old is None:
-        os.environ.pop("MSSM_CHUNK_LEN", None)
-    else:
-        os.environ["MSSM_CHUNK_LEN"] = old
 
 
 def _opts(extras, skip, gate, init):
@@ -110,17 +94,10 @@ def test_each_combination_of_parts(kind, bbar, skip, gate, init):
 
 @pytest.mark.parametrize("cpl", ["1", "2"])
 def test_both_chain_per_lane_variants(cpl):
-    old = os.environ.get("MSSM_CPL")
-    os.environ["MSSM_CPL"] = cpl
-    try:
+    with mssm.tuning(chains_per_lane=int(cpl)):
         g = workloads.generate("mid_bf16", batch=2, L=900, D=320, N=16, seed=23)
         extras = workloads.generate_extras(g["workload"])
         check(g, _opts(extras, True, True, True), "zoh", f"cpl={cpl}")
-    finally:
-        if old is None:
-            os.environ.pop("MSSM_CPL", None)
-        else:
-            os.environ["MSSM_CPL"] = old
 
 
 def test_zoh_on_small_steps_of_the_long_sequence_workload():
