@@ -134,7 +134,8 @@ int mssm_abi_version(void);
 /* Static text for a status code. */
 const char *mssm_status_string(mssm_status status);
 
-/* Text of the last HIP error seen by this thread ("" if none). */
+/* Text of the last HIP error seen by this thread, or of the last scratch-size
+ * refusal of mssm_selective_scan_fwd_noalloc ("" if none). */
 const char *mssm_last_error_string(void);
 
 /* State sizes N the scan kernels are built for (1, 2, 4, 8, 16, 32): returns 1
@@ -170,6 +171,32 @@ mssm_status mssm_selective_scan_fwd_ws(const void *x, const void *delta, const f
                                        void *workspace, size_t workspace_bytes,
                                        int64_t batch, int64_t L, int64_t D, int64_t N,
                                        mssm_dtype dtype, void *stream);
+
+/*
+ * For callers that cannot allocate device memory during the call (code being
+ * captured into a HIP graph, tight serving loops, harnesses that forbid
+ * allocation): the scan of mssm_selective_scan_fwd, same arguments, same
+ * result (the same kernels and chunking), with the chunked order's chunk
+ * summaries kept in a fixed device array that the library holds on every GPU
+ * it runs on until the process ends, MSSM_NOALLOC_SCRATCH_BYTES (128 MiB)
+ * per GPU.  The call allocates nothing: no hipMalloc, no hipFree, no
+ * allocating library routine.  The array's address on a device is looked up
+ * on the first call there.
+ *   - A shape whose chunk summaries need more than the array holds (see
+ *     mssm_selective_scan_workspace_size) gives MSSM_ERROR_WORKSPACE, with
+ *     the sizes in mssm_last_error_string(); the single pass needs none.
+ *   - Every call on a GPU uses that GPU's one array and leaves its contents
+ *     there; the summaries are written in full before they are read, so
+ *     nothing has to start at zero.  Calls that overlap in time on one GPU
+ *     (several streams or threads at once) race on the array and give wrong
+ *     results: serialise them.
+ */
+#define MSSM_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+
+mssm_status mssm_selective_scan_fwd_noalloc(const void *x, const void *delta, const float *A,
+                                            const void *B, const void *C, void *y,
+                                            int64_t batch, int64_t L, int64_t D, int64_t N,
+                                            mssm_dtype dtype, void *stream);
 
 /*
  * ---- the scan with its optional parts: input-term form, feedthrough, gate, state ---------

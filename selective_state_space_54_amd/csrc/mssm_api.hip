@@ -138,6 +138,41 @@ mssm_status mssm_selective_scan_fwd(const void* x, const void* delta, const floa
   return MSSM_SUCCESS;
 }
 
+mssm_status mssm_selective_scan_fwd_noalloc(const void* x, const void* delta, const float* A,
+                                            const void* B, const void* C, void* y,
+                                            int64_t batch, int64_t L, int64_t D, int64_t N,
+                                            mssm_dtype dtype, void* stream) {
+  mssm_status s = check_shape(batch, L, D, N, dtype);
+  if (s != MSSM_SUCCESS) return s;
+  if (empty_problem(batch, L, D)) return MSSM_SUCCESS;
+  if (!x || !delta || !A || !B || !C || !y) return MSSM_ERROR_INVALID_VALUE;
+  const mssm::ScanArgs a{x, delta, A, B, C, y, batch, L, D, N, dtype};
+  const mssm::ScanPlan plan = mssm::plan_for(a);
+  s = check_grid(plan, batch, D, N);
+  if (s != MSSM_SUCCESS) return s;
+  if (plan.workspace_bytes > mssm::noalloc_scratch_bytes()) {
+    std::snprintf(g_last_error, sizeof(g_last_error),
+                  "chunk summaries need %zu bytes; the fixed scratch holds %zu",
+                  plan.workspace_bytes, mssm::noalloc_scratch_bytes());
+    return MSSM_ERROR_WORKSPACE;
+  }
+  // this device's copy of the fixed scratch array (its address is looked up
+  // on the first call on each device)
+  void* ws = nullptr;
+  hipError_t e = mssm::scratch_pointer(&ws);
+  if (e != hipSuccess) {
+    set_hip_error(e, "scratch address");
+    return MSSM_ERROR_HIP;
+  }
+  e = mssm::launch_scan(a, plan, plan.workspace_bytes > 0 ? ws : nullptr,
+                        static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) {
+    set_hip_error(e, "selective scan launch");
+    return MSSM_ERROR_HIP;
+  }
+  return MSSM_SUCCESS;
+}
+
 mssm_status mssm_selective_scan_fwd_ex(const void* x, const void* delta, const float* A,
                                        const void* B, const void* C, const float* Dskip,
                                        const void* z, const float* h0, float* y, float* h_last,

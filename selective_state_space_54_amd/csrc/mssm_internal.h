@@ -125,6 +125,11 @@ hipError_t launch_scan(const ScanArgs& a, const ScanPlan& plan, void* workspace,
 
 bool state_size_supported(int64_t N);
 
+// The fixed device scratch of mssm_selective_scan_fwd_noalloc (noalloc.hip):
+// its size, and the current device's copy (address looked up once per device).
+size_t noalloc_scratch_bytes();
+hipError_t scratch_pointer(void** out);
+
 
 // The carry pass over chunk summaries (shared by the plain, fused and backward
 // paths): hloc [batch, K-1, N, D] is overwritten with the carries, sum_s

@@ -59,6 +59,8 @@ _SIGNATURES = {
     "mssm_selective_scan_fwd_ws": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                                   ctypes.c_size_t, _i64, _i64, _i64, _i64,
                                                   ctypes.c_int, _vp]),
+    "mssm_selective_scan_fwd_noalloc": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64,
+                                                       _i64, _i64, ctypes.c_int, _vp]),
     "mssm_selective_scan_fwd_ex": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                                   _vp, ctypes.c_int, _vp, ctypes.c_size_t, _i64,
                                                   _i64, _i64, _i64, ctypes.c_int, _vp]),
@@ -246,6 +248,19 @@ def mssm_selective_scan_fwd(x, delta, A, B, C, y, *, stream=None):
     _check(load().mssm_selective_scan_fwd(
         _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(y), batch, L, D, N,
         _DTYPES[x.dtype], _stream_handle(stream)), "mssm_selective_scan_fwd")
+    return y
+
+
+NOALLOC_SCRATCH_BYTES = 128 << 20
+
+
+def mssm_selective_scan_fwd_noalloc(x, delta, A, B, C, y, *, stream=None):
+    """y <- selective scan of (x, delta, A, B, C) with the chunk summaries in the
+    library's fixed per-GPU scratch array: the call allocates nothing."""
+    batch, L, D, N = _check_scan_args(x, delta, A, B, C, y)
+    _check(load().mssm_selective_scan_fwd_noalloc(
+        _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(y), batch, L, D, N,
+        _DTYPES[x.dtype], _stream_handle(stream)), "mssm_selective_scan_fwd_noalloc")
     return y
 
 

@@ -428,3 +428,23 @@ print(json.dumps([first, after_env, size_first, size_after_env, size_after_set])
     assert after_env == first
     assert s1 == s2 == _chunked_ws(9, 4, 64)
     assert s3 == _chunked_ws(3, 4, 64)
+
+
+def test_noalloc_argument_errors(lib):
+    """mssm_selective_scan_fwd_noalloc checks its arguments like
+    mssm_selective_scan_fwd, before any HIP call."""
+    def call(ptrs, batch, L, D, N, dtype=0):
+        return lib.mssm_selective_scan_fwd_noalloc(*ptrs, batch, L, D, N, dtype, None)
+    p6 = [FAKE] * 6
+    assert call(p6, -1, 4, 4, 4) == 1
+    assert call(p6, 1, 4, 4, 4, dtype=2) == 1
+    assert call(p6, 1, 4, 4, 3) == 2
+    assert call(p6, 1 << 40, 1 << 40, 4, 4) == 3
+    for i in range(6):
+        ptrs = list(p6)
+        ptrs[i] = None
+        assert call(ptrs, 1, 4, 4, 4) == 1, f"null pointer {i} accepted"
+    assert call([None] * 6, 0, 4, 4, 4) == 0
+    assert mssm.NOALLOC_SCRATCH_BYTES == 128 << 20
+    text = open(HEADER).read()
+    assert "#define MSSM_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)" in text
