@@ -160,6 +160,9 @@ BlockPlan plan_block(int64_t batch, int64_t L, int64_t Dm, int64_t Di, int64_t N
   b.wx_t_offset = off;   off += align256(sizeof(uint16_t) * (size_t)(R + 2 * N) * xproj_padded_k(Di));
   b.wout_t_offset = off; off += align256(sizeof(uint16_t) * (size_t)Dm * 2 * di);
   b.scan_offset = off;   off += b.scan.workspace_bytes;
+  if (chain && N == 16) {
+    b.bcg_offset = off;  off += align256(sizeof(float) * 4 * 8 * (size_t)xproj_bcg_rows(M));
+  }
   b.workspace_bytes = off;
   return b;
 }
@@ -168,6 +171,8 @@ size_t block_workspace_bound(int64_t batch, int64_t L, int64_t Dm, int64_t Di, i
                              int64_t R) {
   size_t w = plan_block(batch, L, Dm, Di, N, R, 1, false).workspace_bytes;
   if (Di % 2 == 0) w = std::max(w, plan_block(batch, L, Dm, Di, N, R, 2, false).workspace_bytes);
+  if (N == 16 && Di % 16 == 0 && R <= 256)
+    w = std::max(w, plan_block(batch, L, Dm, Di, N, R, 1, true).workspace_bytes);
   return w;
 }
 
@@ -219,7 +224,11 @@ FusedStatus launch_block(const BlockArgs& a, const BlockPlan& bp, void* workspac
                               stream);
   if (st.hip != hipSuccess) return st;
   // selection projection of x = hi + lo (dt_low as its bf16 pair, B and C in P)
-  st.hip = launch_xproj(Xb, Xl, Di, M, Di, a.W_x, ldp, a.R, WxT, dtl, dtl_lo, P, ldp, stream);
+  float* bcg = (bp.chain && split_fused_applies(a.batch, Di, a.N))
+                   ? reinterpret_cast<float*>(ws + bp.bcg_offset)
+                   : nullptr;
+  st.hip = launch_xproj(Xb, Xl, Di, M, Di, a.W_x, ldp, a.R, WxT, dtl, dtl_lo, P, ldp, bcg,
+                        stream);
   if (st.hip == hipSuccess) st.hip = launch_wdt_transpose(a.W_dt, a.R, Di, wT, stream);
   if (st.hip != hipSuccess) return st;
   if (bp.chain) {
@@ -243,6 +252,7 @@ FusedStatus launch_block(const BlockArgs& a, const BlockPlan& bp, void* workspac
     ca.batch = a.batch;
     ca.L = a.L;
     ca.D = Di;
+    ca.bcg = bcg;
     st.hip = launch_chain_fused(ca, stream);
   } else {
     FusedScanArgs sa{};

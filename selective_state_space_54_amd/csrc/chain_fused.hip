@@ -1,4 +1,5 @@
-// Single-pass scan launchers behind the selection projections: the fused
+// Single-pass scan launchers behind the selection projections (one lane per
+// channel and state; from 32768 channels on, the split-state kernel): the fused
 // selective SSM (bfloat16 x, float32 y) and the Mamba block (float32 x, the
 // feedthrough D x, the SiLU(z) gate, y stored as a bfloat16 hi + lo pair for
 // the output projection).  delta is the float32 matrix written by the
@@ -9,6 +10,9 @@
 namespace mssm {
 
 hipError_t launch_chain_fused(const ChainFusedArgs& a, hipStream_t stream) {
+  // with enough channels the state is split over the wavefronts of a block
+  // instead (split_scan.hip): no cross-lane operands in the step
+  if (split_fused_applies(a.batch, a.D, chain::kStates)) return launch_split_fused(a, stream);
   chain::ChainParams p{a.x,     a.delta, a.P + a.R, a.P + a.R + chain::kStates,
                        a.z,     a.A,     a.Dskip,   nullptr,
                        nullptr, a.y,     a.y_lo,    a.L,

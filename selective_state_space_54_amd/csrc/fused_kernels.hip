@@ -696,6 +696,10 @@ FusedPlan plan_fused(int64_t batch, int64_t L, int64_t D, int64_t N, int64_t R, 
   if (chain) {
     f.delta_offset = f.scan_offset;
     f.workspace_bytes = f.delta_offset + align256(sizeof(float) * (size_t)M * (size_t)D);
+    if (N == 16) {
+      f.bcg_offset = f.workspace_bytes;
+      f.workspace_bytes += align256(sizeof(float) * 4 * 8 * (size_t)xproj_bcg_rows(M));
+    }
   } else {
     f.workspace_bytes = f.scan_offset + f.scan.workspace_bytes;
   }
@@ -730,10 +734,14 @@ FusedStatus launch_fused(const FusedArgs& a, const FusedPlan& f, void* workspace
   uint16_t* dtl = reinterpret_cast<uint16_t*>(ws + f.dtl_offset);
   uint16_t* dtl_lo = reinterpret_cast<uint16_t*>(ws + f.dtl_lo_offset);
   uint16_t* wT = reinterpret_cast<uint16_t*>(ws + f.wt_offset);
-  // x_proj: dt_low (as its bf16 hi + lo pair) and the B, C columns of P
+  // x_proj: dt_low (as its bf16 hi + lo pair) and the B, C columns of P (and
+  // for the split-state scan B, C grouped by four state indices)
   uint16_t* WxT = reinterpret_cast<uint16_t*>(ws + f.wx_t_offset);
+  float* bcg = (f.chain && split_fused_applies(a.batch, a.D, a.N))
+                   ? reinterpret_cast<float*>(ws + f.bcg_offset)
+                   : nullptr;
   st.hip = launch_xproj(static_cast<const uint16_t*>(a.x), nullptr, a.D, M, a.D, a.W_x, ldp,
-                        a.R, WxT, dtl, dtl_lo, P, ldp, stream);
+                        a.R, WxT, dtl, dtl_lo, P, ldp, bcg, stream);
   if (st.hip != hipSuccess) return st;
   st.hip = launch_wdt_transpose(a.W_dt, a.R, a.D, wT, stream);
   if (st.hip != hipSuccess) return st;
@@ -752,6 +760,7 @@ FusedStatus launch_fused(const FusedArgs& a, const FusedPlan& f, void* workspace
     ca.batch = a.batch;
     ca.L = a.L;
     ca.D = a.D;
+    ca.bcg = bcg;
     st.hip = launch_chain_fused(ca, stream);
     return st;
   }

@@ -100,10 +100,16 @@ struct ChainFusedArgs {
   bool y_bf16 = false;
   int64_t ld_y = 0;               // with y_bf16: row stride of y and y_lo (0: D)
   int64_t batch = 0, L = 0, D = 0;
+  const float* bcg = nullptr;     // B, C grouped by four state indices (launch_xproj), or null
 };
 bool chain_fused_applies(int64_t batch, int64_t D, int64_t N, int64_t R, const void* x,
                          const void* y);
 hipError_t launch_chain_fused(const ChainFusedArgs& a, hipStream_t stream);
+// The split-state single pass (split_scan.hip): lane = channel, each of a
+// block's four wavefronts owns 4 of the N = 16 state indices; used by
+// launch_chain_fused from 32768 channels (batch * D) on, D a multiple of 64.
+bool split_fused_applies(int64_t batch, int64_t D, int64_t N);
+hipError_t launch_split_fused(const ChainFusedArgs& a, hipStream_t stream);
 
 // The plan for these arguments: the single-pass design when it applies, else
 // the chunked plan with the chains-per-lane choice below.
@@ -178,6 +184,7 @@ struct FusedPlan {
   ScanPlan scan;
   bool chain = false;         // single-pass scan over a float32 delta matrix
   size_t delta_offset = 0;    // with chain: float32 [batch*L, D]
+  size_t bcg_offset = 0;      // with chain and N = 16: B, C grouped (xproj_bcg_rows(M) rows)
   size_t p_bytes = 0;
   size_t dtl_offset = 0;
   size_t dtl_lo_offset = 0;
@@ -223,11 +230,15 @@ hipError_t launch_fused_scan(const FusedScanArgs& a, const ScanPlan& plan, hipSt
 // below R (dt_low) are stored as the bf16 pair dtl = bf16(v), dtl_lo =
 // bf16(v - dtl) ([M, R] each); columns R.. to P[m * ldp + c] as float32.
 // WxT is workspace for W_x transposed and zero-padded along k:
-// ncol * xproj_padded_k(K) bf16.
+// ncol * xproj_padded_k(K) bf16.  With bcg (N = 16 only) B and C are also
+// stored grouped by four state indices: bcg[(g * xproj_bcg_rows(M) + m) * 8 +
+// j] = B[m][4g + j] for j < 4 and C[m][4g + j - 4] for j >= 4; the 8 rows
+// past M are set to zero.
 int64_t xproj_padded_k(int64_t K);
+int64_t xproj_bcg_rows(int64_t M);
 hipError_t launch_xproj(const uint16_t* x, const uint16_t* x_lo, int64_t lda, int64_t M,
                         int64_t K, const void* W_x, int64_t ncol, int64_t R, uint16_t* WxT,
-                        uint16_t* dtl, uint16_t* dtl_lo, float* P, int64_t ldp,
+                        uint16_t* dtl, uint16_t* dtl_lo, float* P, int64_t ldp, float* bcg,
                         hipStream_t stream);
 
 // wT [D, R] = W_dt^T for the dt_proj kernels.
@@ -308,6 +319,7 @@ struct BlockPlan {
   // g_offset: the gated output's bf16 hi + lo pair, 2 * M * Di values
   size_t u_offset = 0, z_offset = 0, x_offset = 0, xb_offset = 0, xl_offset = 0, g_offset = 0;
   size_t p_offset = 0, dtl_offset = 0, dtl_lo_offset = 0, wt_offset = 0, scan_offset = 0;
+  size_t bcg_offset = 0;      // with chain and N = 16: B, C grouped for the split-state scan
   // the projection weights transposed for the GEMMs: W_in^T [2Di, Dm], W_x^T
   // [R + 2N, Di], W_out^T twice side by side [Dm, 2Di]
   size_t win_t_offset = 0, wx_t_offset = 0, wout_t_offset = 0;

@@ -100,14 +100,15 @@ ScanPlan plan_scan(int64_t batch, int64_t L, int64_t D, int64_t N, int cpl) {
   ScanPlan p;
   p.cpl = cpl;
   if (batch <= 0 || L <= 0 || D <= 0) return p;
-  // Chunk count: enough blocks to give every compute unit about eight (two
-  // wavefronts per SIMD over the kernel's life), with chunks of at least 64
-  // steps (128 with two chains per lane).  Measured on MI355X with chunk-length sweeps of the synthetic
-  // workloads (the per-chunk cost after the carry pass is small, so more
-  // chunks help until chunks get short).  The chunk-length setting overrides
-  // it (tuning sweeps and chunk-boundary tests).
+  // Chunk count: about 2560 blocks (ten per compute unit over the kernel's
+  // life), with chunks of at least 64 steps (128 with two chains per lane).
+  // Chunk-length sweeps of the long-sequence bf16 workload on MI355X (K
+  // from 100 to 1024 chunks): 256 steps (2560 blocks) fastest, 1.57 ms against
+  // 1.66 at 320 steps (2050 blocks) and 1.70 at 128 (the per-chunk cost after
+  // the carry pass is small, so more chunks help until chunks get short).  The
+  // chunk-length setting overrides it (tuning sweeps and chunk-boundary tests).
   const int64_t blocks_per_chunk = batch * ((D + kBlock * cpl - 1) / (kBlock * cpl));
-  const int64_t target_blocks = 2048;
+  const int64_t target_blocks = 2560;
   int64_t K = (target_blocks + blocks_per_chunk / 2) / blocks_per_chunk;
   const int64_t min_chunk = cpl == 1 ? 64 : 128;
   K = std::max<int64_t>(1, std::min<int64_t>(K, L / min_chunk));

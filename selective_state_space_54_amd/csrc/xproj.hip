@@ -11,8 +11,9 @@
 //   * a block owns 64 rows of x and all (up to 192) output columns, so every
 //     element of x is read from memory exactly once;
 //   * the block's 64-row x tile comes into LDS 64 k-values at a time (16-byte
-//     loads, two buffers, the next tile's loads in flight during the current
-//     tile's products), and every wavefront reads its A fragments from there;
+//     loads through a ring of three register sets and three LDS buffers, so
+//     loads run two tiles ahead of the products), and every wavefront reads
+//     its A fragments from there;
 //   * wavefront w owns output columns 48w .. 48w + 47 (three 16-column
 //     fragments) for all 64 rows: 4 x 3 accumulator tiles of
 //     v_mfma_f32_16x16x32_bf16, fp32 accumulation; its W fragments are its
@@ -21,7 +22,10 @@
 //   * epilogue: columns below R (dt_low) are stored as the bf16 pair
 //     hi = bf16(v), lo = bf16(v - hi) that dt_proj's matrix cores read (R is a
 //     multiple of 16, so a 16-column fragment is all dt_low or all B/C); the
-//     B and C columns are stored as float32 into P's rows.
+//     B and C columns are stored as float32 into P's rows (for N = 16 also,
+//     on request, in four groups of four state indices: [4][M + 8][B 4 | C 4],
+//     so that a wavefront owning four state indices finds consecutive steps'
+//     B and C side by side, the layout the split-state scan reads).
 //
 // With two A operands (the Mamba block: x kept as a bf16 hi + lo pair) both
 // tiles are multiplied into the same accumulators.
@@ -44,6 +48,7 @@ constexpr int kXBlock = 256;          // 4 wavefronts
 constexpr int kXRows = 64;            // rows of x per block
 constexpr int kXK = 64;               // k values per LDS tile
 constexpr int kXPitch = kXK + 8;      // LDS row pitch (bf16): 144 bytes, conflict-free 16-byte reads
+constexpr int kXStages = 3;           // tiles in LDS / register sets in the load ring
 constexpr int kXColsPerWave = 48;     // three 16-column fragments
 constexpr int kXCols = 4 * kXColsPerWave;   // output columns per block
 
@@ -60,7 +65,15 @@ __device__ __forceinline__ bf16x8 as_bf16x8(const uint4& u) {
 // W^T [ncol, Kp].
 __global__ __launch_bounds__(256) void transpose_pad_kernel(const uint16_t* __restrict__ W,
                                                             uint16_t* __restrict__ wT, int64_t K,
-                                                            int64_t ncol, int64_t Kp) {
+                                                            int64_t ncol, int64_t Kp,
+                                                            float* __restrict__ bcg,
+                                                            int64_t bcg_rows, int64_t M) {
+  // the grouped B/C rows past the last token (read by steps past the end of
+  // the sequence, whose input term is zero) are set to zero here
+  if (bcg && blockIdx.x == 0) {
+    const int g = threadIdx.x >> 6, r = (threadIdx.x >> 3) & 7, j = threadIdx.x & 7;
+    if (M + r < bcg_rows) bcg[(g * bcg_rows + M + r) * 8 + j] = 0.0f;
+  }
   __shared__ uint16_t tile[64][65];
   const int64_t tiles_c = (ncol + 63) / 64;
   const int64_t r0 = static_cast<int64_t>(blockIdx.x / tiles_c) * 64;
@@ -108,9 +121,9 @@ __global__ __launch_bounds__(kXBlock) void xproj_kernel(
     const uint16_t* __restrict__ A0, const uint16_t* __restrict__ A1, int64_t lda,
     const uint16_t* __restrict__ wT, int64_t Kp, int64_t K, int64_t M, int ncol, int R,
     uint16_t* __restrict__ dtl, uint16_t* __restrict__ dtl_lo, float* __restrict__ P,
-    int64_t ldp) {
+    int64_t ldp, float* __restrict__ bcg, int64_t bcg_rows) {
   constexpr int kOps = kTwo ? 2 : 1;
-  __shared__ __align__(16) uint16_t sa[2][kOps][kXRows][kXPitch];
+  __shared__ __align__(16) uint16_t sa[kXStages][kOps][kXRows][kXPitch];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t m0 = static_cast<int64_t>(blockIdx.x) * kXRows;
@@ -127,24 +140,24 @@ __global__ __launch_bounds__(kXBlock) void xproj_kernel(
     prow[h] = p >> 3;
     pk[h] = (p & 7) * 8;
   }
-  uint4 xa[kOps][2];
-  auto fetch_x = [&](int64_t k0) {
+  uint4 xa[kXStages][kOps][2];
+  auto fetch_x = [&](int slot, int64_t k0) {
 #pragma unroll
     for (int o = 0; o < kOps; ++o) {
       const uint16_t* A = o == 0 ? A0 : A1;
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int64_t m = min(m0 + prow[h], M - 1);
-        xa[o][h] = load_piece<kVec>(A, lda, m, k0 + pk[h], K);
+        xa[slot][o][h] = load_piece<kVec>(A, lda, m, k0 + pk[h], K);
       }
     }
   };
-  auto stash_x = [&](int buf) {
+  auto stash_x = [&](int slot) {
 #pragma unroll
     for (int o = 0; o < kOps; ++o)
 #pragma unroll
       for (int h = 0; h < 2; ++h)
-        *reinterpret_cast<uint4*>(&sa[buf][o][prow[h]][pk[h]]) = xa[o][h];
+        *reinterpret_cast<uint4*>(&sa[slot][o][prow[h]][pk[h]]) = xa[slot][o][h];
   };
   // W fragments of this wavefront: (fragment, k step of 32) -> 8 bf16
   const int bk = 8 * (lane >> 4);
@@ -154,7 +167,7 @@ __global__ __launch_bounds__(kXBlock) void xproj_kernel(
     const int c = min(c_wave + 16 * f + (lane & 15), ncol - 1);
     wrow[f] = wT + static_cast<int64_t>(c) * Kp + bk;
   }
-  uint4 wb[2][3][2];
+  uint4 wb[kXStages][3][2];
   auto fetch_w = [&](int slot, int64_t k0) {
 #pragma unroll
     for (int f = 0; f < 3; ++f)
@@ -171,18 +184,17 @@ __global__ __launch_bounds__(kXBlock) void xproj_kernel(
 
   const int64_t ntiles = Kp / kXK;
   const int arow = lane & 15;
-  // Tile t: its x pieces (fetched one tile earlier) go into LDS buffer B, the
-  // next tile's x and W are fetched into the other register set, then the
-  // products.  B is a compile-time constant (the loop is unrolled by two), so
-  // the register sets keep fixed names.
-  auto tile = [&](int64_t t, auto Bc) {
-    constexpr int B = decltype(Bc)::value;
-    stash_x(B);
+  // A ring of three: tile t's x pieces and W fragments were fetched two tiles
+  // earlier into register set S = t % 3; its x pieces go into LDS buffer S,
+  // the products run, and then the loads for tile t + 3 go into set S (free
+  // again), so each load has about two tiles' products to arrive.  Three LDS
+  // buffers: buffer S was last read by tile t - 3, whose products every
+  // wavefront finished before the barrier of tile t - 2.  S is a compile-time
+  // constant (the loop is unrolled by three), so the sets keep fixed names.
+  auto tile = [&](int64_t t, auto Sc) {
+    constexpr int S = decltype(Sc)::value;
+    stash_x(S);
     block_sync();
-    if (t + 1 < ntiles) {
-      fetch_x((t + 1) * kXK);            // in flight during this tile's products
-      fetch_w(B ^ 1, (t + 1) * kXK);
-    }
     if (nfrag > 0) {
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
@@ -191,25 +203,36 @@ __global__ __launch_bounds__(kXBlock) void xproj_kernel(
 #pragma unroll
           for (int o = 0; o < kOps; ++o) {
             const bf16x8 a = as_bf16x8(
-                *reinterpret_cast<const uint4*>(&sa[B][o][16 * r + arow][32 * s + bk]));
+                *reinterpret_cast<const uint4*>(&sa[S][o][16 * r + arow][32 * s + bk]));
 #pragma unroll
             for (int f = 0; f < 3; ++f)
               if (f < nfrag)
                 acc[r][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                    a, as_bf16x8(wb[B][f][s]), acc[r][f], 0, 0, 0);
+                    a, as_bf16x8(wb[S][f][s]), acc[r][f], 0, 0, 0);
           }
         }
       }
     }
+    if (t + kXStages < ntiles) {
+      fetch_w(S, (t + kXStages) * kXK);
+      fetch_x(S, (t + kXStages) * kXK);
+    }
   };
-  fetch_x(0);
-  fetch_w(0, 0);
+#pragma unroll
+  for (int i = 0; i < kXStages; ++i) {
+    if (i < ntiles) {
+      fetch_w(i, i * kXK);
+      fetch_x(i, i * kXK);
+    }
+  }
   int64_t t = 0;
-  for (; t + 2 <= ntiles; t += 2) {
+  for (; t + 3 <= ntiles; t += 3) {
     tile(t, std::integral_constant<int, 0>{});
     tile(t + 1, std::integral_constant<int, 1>{});
+    tile(t + 2, std::integral_constant<int, 2>{});
   }
   if (t < ntiles) tile(t, std::integral_constant<int, 0>{});
+  if (t + 1 < ntiles) tile(t + 1, std::integral_constant<int, 1>{});
 
   // epilogue
   const int col_in = lane & 15;
@@ -232,6 +255,11 @@ __global__ __launch_bounds__(kXBlock) void xproj_kernel(
           dtl_lo[m * R + c] = static_cast<uint16_t>(bf16_rne_bits(v - __uint_as_float(hi << 16)));
         } else if (c < ncol) {
           P[m * ldp + c] = v;
+          if (bcg) {   // N = 16: B and C also in four groups of four state indices
+            const int n = c - R;
+            const int g = (n & 15) >> 2, j = (n & 3) + (n >= 16 ? 4 : 0);
+            bcg[(g * bcg_rows + m) * 8 + j] = v;
+          }
         }
       }
     }
@@ -242,15 +270,20 @@ __global__ __launch_bounds__(kXBlock) void xproj_kernel(
 
 int64_t xproj_padded_k(int64_t K) { return (K + kXK - 1) / kXK * kXK; }
 
+int64_t xproj_bcg_rows(int64_t M) { return M + 8; }
+
 hipError_t launch_xproj(const uint16_t* x, const uint16_t* x_lo, int64_t lda, int64_t M,
                         int64_t K, const void* W_x, int64_t ncol, int64_t R, uint16_t* WxT,
-                        uint16_t* dtl, uint16_t* dtl_lo, float* P, int64_t ldp,
+                        uint16_t* dtl, uint16_t* dtl_lo, float* P, int64_t ldp, float* bcg,
                         hipStream_t stream) {
+  if (bcg && ncol - R != 32) return hipErrorInvalidValue;   // grouped B/C: N = 16 only
+  const int64_t bcg_rows = bcg ? xproj_bcg_rows(M) : 0;
   if (M <= 0 || ncol <= 0) return hipSuccess;
   const int64_t Kp = xproj_padded_k(K);
   const int64_t tiles = ((Kp + 63) / 64) * ((ncol + 63) / 64);
   hipLaunchKernelGGL(transpose_pad_kernel, dim3(static_cast<unsigned>(tiles)), dim3(256), 0,
-                     stream, static_cast<const uint16_t*>(W_x), WxT, K, ncol, Kp);
+                     stream, static_cast<const uint16_t*>(W_x), WxT, K, ncol, Kp, bcg, bcg_rows,
+                     M);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const dim3 grid(static_cast<unsigned>((M + kXRows - 1) / kXRows),
@@ -260,7 +293,7 @@ hipError_t launch_xproj(const uint16_t* x, const uint16_t* x_lo, int64_t lda, in
   const int nc = static_cast<int>(ncol), r = static_cast<int>(R);
 #define MSSM_XPROJ(TWO, VEC)                                                                    \
   hipLaunchKernelGGL((xproj_kernel<TWO, VEC>), grid, dim3(kXBlock), 0, stream, x, x_lo, lda,   \
-                     WxT, Kp, K, M, nc, r, dtl, dtl_lo, P, ldp)
+                     WxT, Kp, K, M, nc, r, dtl, dtl_lo, P, ldp, bcg, bcg_rows)
   if (x_lo) {
     if (vec) MSSM_XPROJ(true, true); else MSSM_XPROJ(true, false);
   } else {

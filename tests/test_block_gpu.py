@@ -92,6 +92,24 @@ def test_block_single_pass_shapes(shape, design):
     assert_parity(run_block(g), oracle_block(g), "bf16", f"block single pass {shape}")
 
 
+SPLIT_SHAPES = [  # batch, L, Dm, Di, N = 16, R, k: batch * Di >= 32768 channels
+    (1, 33, 64, 32768, 16, 16, 4), (2, 17, 32, 16384, 16, 32, 2),
+]
+
+
+@pytest.mark.parametrize("shape", SPLIT_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_block_split_state_shapes(shape):
+    """The block's scan with the state split over a block's wavefronts
+    (feedthrough, gate, the bf16 hi + lo output), ragged 8-step tiles."""
+    batch, L, Dm, Di, N, R, k = shape
+    print(f"case block split {shape}", flush=True)
+    g = workloads.generate_block(batch=batch, L=L, Dm=Dm, D=Di, N=N, R=R, conv_k=k,
+                                 seed=780 + L + R)
+    assert_parity(run_block(g), oracle_block(g), "bf16", f"block split {shape}")
+    drop = ("Dskip",)
+    assert_parity(run_block(g, drop), oracle_block(g, drop), "bf16", f"block split {shape} no D")
+
+
 @pytest.mark.parametrize("design", ["auto", "chain"], indirect=True)
 @pytest.mark.parametrize("drop", [("conv_b",), ("Dskip",), ("conv_b", "Dskip")],
                          ids=lambda d: "-".join(d))

@@ -72,6 +72,21 @@ def test_fused_single_pass_shapes(shape, design):
     assert_parity(run_fused(g), oracle_fused(g), "bf16", f"fused single pass {shape}")
 
 
+SPLIT_SHAPES = [  # batch, L, D, N = 16, R: batch * D >= 32768 channels, D % 64 == 0
+    (1, 1, 32768, 16, 16), (1, 33, 32768, 16, 32), (2, 17, 16384, 16, 160), (4, 41, 8192, 16, 64),
+]
+
+
+@pytest.mark.parametrize("shape", SPLIT_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_fused_split_state_shapes(shape):
+    """The single pass with the state split over a block's wavefronts (chosen
+    from 32768 channels on): one step, ragged 8-step tiles, several batch rows."""
+    batch, L, D, N, R = shape
+    print(f"case fused split {shape}", flush=True)
+    g = workloads.generate("fused_proj_bf16", batch=batch, L=L, D=D, N=N, R=R, seed=970 + L + R)
+    assert_parity(run_fused(g), oracle_fused(g), "bf16", f"fused split {shape}")
+
+
 @pytest.mark.parametrize("cpl", ["1", "2"])
 def test_fused_both_chain_per_lane_variants(cpl):
     with mssm.tuning(chains_per_lane=int(cpl)):

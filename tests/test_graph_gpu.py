@@ -167,11 +167,15 @@ def test_single_pass_training_pair_in_a_graph(design):
                      lambda: mssm.selective_scan(*args))
 
 
+@pytest.mark.parametrize("shape", [(5, 300, 64), (4, 100, 8192)], ids=["chain", "split"])
 @pytest.mark.parametrize("design", ["chain"], indirect=True)
-def test_fused_single_pass_in_a_graph(design):
-    """The fused SSM through the single pass (the x_proj GEMM on rocBLAS, the
-    dt low-rank split, W_dt's transpose, dt_proj + softplus, the scan)."""
-    g = workloads.generate("fused_proj_bf16", batch=5, L=300, D=64, N=16, R=32, seed=92)
+def test_fused_single_pass_in_a_graph(design, shape):
+    """The fused SSM through the single pass (W_x's transpose, the x_proj
+    kernel with the dt_low split in its epilogue, W_dt's transpose, dt_proj +
+    softplus, the scan: one lane per channel and state, or from 32768
+    channels the state split over a block's wavefronts)."""
+    batch, L, D = shape
+    g = workloads.generate("fused_proj_bf16", batch=batch, L=L, D=D, N=16, R=32, seed=92)
     t = {k: dev(g[k]) for k in ("x", "W_x", "W_dt", "dt_bias", "A")}
     w = g["workload"]
     nb = mssm.mssm_selective_ssm_fused_workspace_size(w.batch, w.L, w.D, w.N, w.R, torch.bfloat16)
