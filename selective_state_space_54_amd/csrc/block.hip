@@ -160,7 +160,7 @@ BlockPlan plan_block(int64_t batch, int64_t L, int64_t Dm, int64_t Di, int64_t N
   b.wx_t_offset = off;   off += align256(sizeof(uint16_t) * (size_t)(R + 2 * N) * xproj_padded_k(Di));
   b.wout_t_offset = off; off += align256(sizeof(uint16_t) * (size_t)Dm * 2 * di);
   b.scan_offset = off;   off += b.scan.workspace_bytes;
-  if (chain && N == 16) {
+  if (chain && split_fused_applies(batch, Di, N)) {
     b.bcg_offset = off;  off += align256(sizeof(float) * 4 * 8 * (size_t)xproj_bcg_rows(M));
   }
   b.workspace_bytes = off;

@@ -696,7 +696,7 @@ FusedPlan plan_fused(int64_t batch, int64_t L, int64_t D, int64_t N, int64_t R, 
   if (chain) {
     f.delta_offset = f.scan_offset;
     f.workspace_bytes = f.delta_offset + align256(sizeof(float) * (size_t)M * (size_t)D);
-    if (N == 16) {
+    if (split_fused_applies(batch, D, N)) {
       f.bcg_offset = f.workspace_bytes;
       f.workspace_bytes += align256(sizeof(float) * 4 * 8 * (size_t)xproj_bcg_rows(M));
     }

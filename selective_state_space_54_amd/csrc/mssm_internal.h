@@ -184,7 +184,7 @@ struct FusedPlan {
   ScanPlan scan;
   bool chain = false;         // single-pass scan over a float32 delta matrix
   size_t delta_offset = 0;    // with chain: float32 [batch*L, D]
-  size_t bcg_offset = 0;      // with chain and N = 16: B, C grouped (xproj_bcg_rows(M) rows)
+  size_t bcg_offset = 0;      // with the split-state scan: B, C grouped (xproj_bcg_rows(M) rows)
   size_t p_bytes = 0;
   size_t dtl_offset = 0;
   size_t dtl_lo_offset = 0;
@@ -319,7 +319,7 @@ struct BlockPlan {
   // g_offset: the gated output's bf16 hi + lo pair, 2 * M * Di values
   size_t u_offset = 0, z_offset = 0, x_offset = 0, xb_offset = 0, xl_offset = 0, g_offset = 0;
   size_t p_offset = 0, dtl_offset = 0, dtl_lo_offset = 0, wt_offset = 0, scan_offset = 0;
-  size_t bcg_offset = 0;      // with chain and N = 16: B, C grouped for the split-state scan
+  size_t bcg_offset = 0;      // with the split-state scan: B, C grouped for it
   // the projection weights transposed for the GEMMs: W_in^T [2Di, Dm], W_x^T
   // [R + 2N, Di], W_out^T twice side by side [Dm, 2Di]
   size_t win_t_offset = 0, wx_t_offset = 0, wout_t_offset = 0;
