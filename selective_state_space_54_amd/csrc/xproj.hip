@@ -8,17 +8,19 @@
 // the fused workload against 2 MB of weights), so the kernel is laid out for
 // streaming x:
 //
-//   * a block owns 64 rows of x and all (up to 192) output columns, so every
-//     element of x is read from memory exactly once;
-//   * the block's 64-row x tile comes into LDS 64 k-values at a time (16-byte
-//     loads through a ring of three register sets and three LDS buffers, so
-//     loads run two tiles ahead of the products), and every wavefront reads
-//     its A fragments from there;
-//   * wavefront w owns output columns 48w .. 48w + 47 (three 16-column
-//     fragments) for all 64 rows: 4 x 3 accumulator tiles of
-//     v_mfma_f32_16x16x32_bf16, fp32 accumulation; its W fragments are its
-//     own, read straight from the transposed weights (W_x^T rows, zero-padded
-//     along k to a multiple of 64, so the k tail needs no test);
+//   * a block owns 128 rows of x and all (up to 192) output columns, so every
+//     element of x is read from memory exactly once (one block per compute
+//     unit on the fused workload);
+//   * 64-value slices along k of the block's x rows and of W^T (W_x
+//     transposed, zero-padded along k to a multiple of 64, so the k tail needs
+//     no test) are staged in LDS with 16-byte loads; the loads run two slices
+//     ahead through two register sets, about 80 KB in flight per compute
+//     unit, which is what streaming x near HBM speed needs; two LDS buffers,
+//     one barrier per slice;
+//   * the four wavefronts split the 128 x 192 tile 2 x 2: each owns 64 rows x
+//     96 columns, 4 x 6 accumulator tiles of v_mfma_f32_16x16x32_bf16 with
+//     float32 accumulation, reading its A and B fragments from LDS (each B
+//     fragment serves four row tiles, each A fragment six column tiles);
 //   * epilogue: columns below R (dt_low) are stored as the bf16 pair
 //     hi = bf16(v), lo = bf16(v - hi) that dt_proj's matrix cores read (R is a
 //     multiple of 16, so a 16-column fragment is all dt_low or all B/C); the
@@ -44,13 +46,13 @@ namespace mssm {
 
 namespace {
 
-constexpr int kXBlock = 256;          // 4 wavefronts
-constexpr int kXRows = 64;            // rows of x per block
+constexpr int kXBlock = 256;          // 4 wavefronts: 2 x 2 over (rows, columns)
+constexpr int kXRows = 128;           // rows of x per block
 constexpr int kXK = 64;               // k values per LDS tile
 constexpr int kXPitch = kXK + 8;      // LDS row pitch (bf16): 144 bytes, conflict-free 16-byte reads
-constexpr int kXStages = 3;           // tiles in LDS / register sets in the load ring
-constexpr int kXColsPerWave = 48;     // three 16-column fragments
-constexpr int kXCols = 4 * kXColsPerWave;   // output columns per block
+constexpr int kXColsPerWave = 96;     // six 16-column fragments
+constexpr int kXFrags = kXColsPerWave / 16;
+constexpr int kXCols = 2 * kXColsPerWave;   // output columns per block
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -112,10 +114,10 @@ __device__ __forceinline__ uint4 load_piece(const uint16_t* __restrict__ A, int6
   }
 }
 
-// grid: (ceil(M / 64), ceil(ncol / 192)).  A0 (and A1 with kTwo) [M, K] bf16
-// with row stride lda; wT [ncol, Kp] bf16, Kp a multiple of 64, zero for
+// grid: (ceil(M / 128), ceil(ncol / 192)).  A0 (and A1 with kTwo) [M, K]
+// bf16 with row stride lda; wT [ncol, Kp] bf16, Kp a multiple of 64, zero for
 // k >= K.  Outputs: columns c < R to dtl / dtl_lo [M, R] (bf16 pair), columns
-// R <= c < ncol to P[m * ldp + c] (float32).
+// R <= c < ncol to P[m * ldp + c] (float32) and, with bcg, to the grouped copy.
 template <bool kTwo, bool kVec>
 __global__ __launch_bounds__(kXBlock) void xproj_kernel(
     const uint16_t* __restrict__ A0, const uint16_t* __restrict__ A1, int64_t lda,
@@ -123,122 +125,124 @@ __global__ __launch_bounds__(kXBlock) void xproj_kernel(
     uint16_t* __restrict__ dtl, uint16_t* __restrict__ dtl_lo, float* __restrict__ P,
     int64_t ldp, float* __restrict__ bcg, int64_t bcg_rows) {
   constexpr int kOps = kTwo ? 2 : 1;
-  __shared__ __align__(16) uint16_t sa[kXStages][kOps][kXRows][kXPitch];
+  constexpr int kXPieces = kXRows * kXK / 8 / kXBlock;   // 16-byte x pieces per thread per tile
+  constexpr int kWPieces = kXCols * kXK / 8 / kXBlock;   // 16-byte W pieces per thread per tile
+  __shared__ __align__(16) uint16_t sa[2][kOps][kXRows][kXPitch];
+  __shared__ __align__(16) uint16_t sb[2][kXCols][kXPitch];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wr = wave >> 1, wc = wave & 1;               // 64-row half, 96-column half
   const int64_t m0 = static_cast<int64_t>(blockIdx.x) * kXRows;
-  const int c_wave = static_cast<int>(blockIdx.y) * kXCols + wave * kXColsPerWave;
-  // fragments of this wavefront that hold any column < ncol (wave-uniform)
+  const int c0 = static_cast<int>(blockIdx.y) * kXCols;
+  const int c_wave = c0 + wc * kXColsPerWave;
+  // 16-column fragments of this wavefront holding any column < ncol (uniform)
   int nfrag = (ncol - c_wave + 15) / 16;
-  nfrag = nfrag < 0 ? 0 : (nfrag > 3 ? 3 : nfrag);
+  nfrag = nfrag < 0 ? 0 : (nfrag > kXFrags ? kXFrags : nfrag);
 
-  // x tile pieces of this thread: 64 rows x 8 pieces of 8 k = 512 per operand
-  int prow[2], pk[2];
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int p = threadIdx.x + kXBlock * h;
-    prow[h] = p >> 3;
-    pk[h] = (p & 7) * 8;
-  }
-  uint4 xa[kXStages][kOps][2];
-  auto fetch_x = [&](int slot, int64_t k0) {
+  struct Stage {
+    uint4 x[kOps][kXPieces];
+    uint4 w[kWPieces];
+  };
+  // piece q of this thread: tile row (q * 256 + tid) / 8, 8 k values at ((q * 256 + tid) % 8) * 8
+  auto fetch = [&](Stage& st, int64_t t) {
+    const int64_t k0 = t * kXK;
 #pragma unroll
     for (int o = 0; o < kOps; ++o) {
       const uint16_t* A = o == 0 ? A0 : A1;
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int64_t m = min(m0 + prow[h], M - 1);
-        xa[slot][o][h] = load_piece<kVec>(A, lda, m, k0 + pk[h], K);
+      for (int q = 0; q < kXPieces; ++q) {
+        const int p = threadIdx.x + kXBlock * q;
+        const int64_t m = min(m0 + (p >> 3), M - 1);
+        st.x[o][q] = load_piece<kVec>(A, lda, m, k0 + (p & 7) * 8, K);
       }
     }
+#pragma unroll
+    for (int q = 0; q < kWPieces; ++q) {
+      const int p = threadIdx.x + kXBlock * q;
+      const int c = min(c0 + (p >> 3), ncol - 1);
+      st.w[q] = *reinterpret_cast<const uint4*>(wT + static_cast<int64_t>(c) * Kp + k0 +
+                                                (p & 7) * 8);
+    }
   };
-  auto stash_x = [&](int slot) {
+  auto stash = [&](const Stage& st, int buf) {
 #pragma unroll
     for (int o = 0; o < kOps; ++o)
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
-        *reinterpret_cast<uint4*>(&sa[slot][o][prow[h]][pk[h]]) = xa[slot][o][h];
-  };
-  // W fragments of this wavefront: (fragment, k step of 32) -> 8 bf16
-  const int bk = 8 * (lane >> 4);
-  const uint16_t* wrow[3];
+      for (int q = 0; q < kXPieces; ++q) {
+        const int p = threadIdx.x + kXBlock * q;
+        *reinterpret_cast<uint4*>(&sa[buf][o][p >> 3][(p & 7) * 8]) = st.x[o][q];
+      }
 #pragma unroll
-  for (int f = 0; f < 3; ++f) {
-    const int c = min(c_wave + 16 * f + (lane & 15), ncol - 1);
-    wrow[f] = wT + static_cast<int64_t>(c) * Kp + bk;
-  }
-  uint4 wb[kXStages][3][2];
-  auto fetch_w = [&](int slot, int64_t k0) {
-#pragma unroll
-    for (int f = 0; f < 3; ++f)
-#pragma unroll
-      for (int s = 0; s < 2; ++s)
-        if (f < nfrag) wb[slot][f][s] = *reinterpret_cast<const uint4*>(wrow[f] + k0 + 32 * s);
+    for (int q = 0; q < kWPieces; ++q) {
+      const int p = threadIdx.x + kXBlock * q;
+      *reinterpret_cast<uint4*>(&sb[buf][p >> 3][(p & 7) * 8]) = st.w[q];
+    }
   };
 
-  f32x4 acc[4][3];
+  f32x4 acc[4][kXFrags];
 #pragma unroll
   for (int r = 0; r < 4; ++r)
 #pragma unroll
-    for (int f = 0; f < 3; ++f) acc[r][f] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int f = 0; f < kXFrags; ++f) acc[r][f] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-  const int64_t ntiles = Kp / kXK;
-  const int arow = lane & 15;
-  // A ring of three: tile t's x pieces and W fragments were fetched two tiles
-  // earlier into register set S = t % 3; its x pieces go into LDS buffer S,
-  // the products run, and then the loads for tile t + 3 go into set S (free
-  // again), so each load has about two tiles' products to arrive.  Three LDS
-  // buffers: buffer S was last read by tile t - 3, whose products every
-  // wavefront finished before the barrier of tile t - 2.  S is a compile-time
-  // constant (the loop is unrolled by three), so the sets keep fixed names.
-  auto tile = [&](int64_t t, auto Sc) {
-    constexpr int S = decltype(Sc)::value;
-    stash_x(S);
-    block_sync();
-    if (nfrag > 0) {
+  const int arow = lane & 15, bk = 8 * (lane >> 4);
+  auto compute = [&](int buf) {
+    if (nfrag == 0) return;
 #pragma unroll
-      for (int s = 0; s < 2; ++s) {
+    for (int s = 0; s < kXK / 32; ++s) {
+      bf16x8 b[kXFrags];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
+      for (int f = 0; f < kXFrags; ++f)
+        b[f] = as_bf16x8(*reinterpret_cast<const uint4*>(
+            &sb[buf][wc * kXColsPerWave + 16 * f + arow][32 * s + bk]));
 #pragma unroll
-          for (int o = 0; o < kOps; ++o) {
-            const bf16x8 a = as_bf16x8(
-                *reinterpret_cast<const uint4*>(&sa[S][o][16 * r + arow][32 * s + bk]));
+      for (int r = 0; r < 4; ++r) {
 #pragma unroll
-            for (int f = 0; f < 3; ++f)
-              if (f < nfrag)
-                acc[r][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                    a, as_bf16x8(wb[S][f][s]), acc[r][f], 0, 0, 0);
-          }
+        for (int o = 0; o < kOps; ++o) {
+          const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4*>(
+              &sa[buf][o][64 * wr + 16 * r + arow][32 * s + bk]));
+#pragma unroll
+          for (int f = 0; f < kXFrags; ++f)
+            if (f < nfrag)
+              acc[r][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[f], acc[r][f], 0, 0, 0);
         }
       }
     }
-    if (t + kXStages < ntiles) {
-      fetch_w(S, (t + kXStages) * kXK);
-      fetch_x(S, (t + kXStages) * kXK);
-    }
   };
-#pragma unroll
-  for (int i = 0; i < kXStages; ++i) {
-    if (i < ntiles) {
-      fetch_w(i, i * kXK);
-      fetch_x(i, i * kXK);
-    }
-  }
+
+  // Loads run two tiles ahead through two register sets; LDS buffers
+  // alternate; one barrier per tile (buffer B was last read by the tile two
+  // before, whose products every wavefront finished before this barrier).
+  // Unrolled by two so the register sets keep fixed names; fetches past the
+  // last tile repeat it and are never used.
+  const int64_t ntiles = Kp / kXK;
+  const int64_t last = ntiles - 1;
+  Stage s0, s1;
+  fetch(s0, 0);
+  fetch(s1, 1 < last ? 1 : last);
+  stash(s0, 0);
+  fetch(s0, 2 < last ? 2 : last);
   int64_t t = 0;
-  for (; t + 3 <= ntiles; t += 3) {
-    tile(t, std::integral_constant<int, 0>{});
-    tile(t + 1, std::integral_constant<int, 1>{});
-    tile(t + 2, std::integral_constant<int, 2>{});
+  for (; t + 2 <= ntiles; t += 2) {
+    block_sync();
+    stash(s1, 1);
+    fetch(s1, t + 3 < last ? t + 3 : last);
+    compute(0);
+    block_sync();
+    stash(s0, 0);
+    fetch(s0, t + 4 < last ? t + 4 : last);
+    compute(1);
   }
-  if (t < ntiles) tile(t, std::integral_constant<int, 0>{});
-  if (t + 1 < ntiles) tile(t + 1, std::integral_constant<int, 1>{});
+  if (t < ntiles) {
+    block_sync();
+    compute(0);
+  }
 
   // epilogue
   const int col_in = lane & 15;
   const int row_in = 4 * (lane >> 4);
 #pragma unroll
-  for (int f = 0; f < 3; ++f) {
+  for (int f = 0; f < kXFrags; ++f) {
     if (f >= nfrag) continue;
     const int c = c_wave + 16 * f + col_in;
     const bool dt_frag = c_wave + 16 * f < R;       // uniform: R is a multiple of 16
@@ -246,7 +250,7 @@ __global__ __launch_bounds__(kXBlock) void xproj_kernel(
     for (int r = 0; r < 4; ++r) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int64_t m = m0 + 16 * r + row_in + i;
+        const int64_t m = m0 + 64 * wr + 16 * r + row_in + i;
         if (m >= M) continue;
         const float v = acc[r][f][i];
         if (dt_frag) {
