@@ -73,6 +73,38 @@ __device__ __forceinline__ void load_row_any(const uint16_t* __restrict__ p, flo
   load_row_bf16<N, kPairs>(p, v);
 }
 
+// A prefetched row as it was loaded: float32 values, or bfloat16 pairs kept
+// packed, two to a 32-bit register, and widened only where a value is used.
+// Widening at the load would need the loaded data at once, so the load could
+// no longer run a step ahead of its use.
+template <int N, typename T, bool kPairs>
+struct RawRow {
+  static constexpr bool kPinnable = false;
+  float w[N];
+  __device__ __forceinline__ void load(const float* __restrict__ p) { load_row<N>(p, w); }
+  __device__ __forceinline__ float get(int n) const { return w[n]; }
+};
+template <int N, bool kPairs>
+struct RawRow<N, uint16_t, kPairs> {
+  static constexpr bool kPacked = kPairs && (N % 2 == 0);
+  static constexpr bool kPinnable = kPacked && N <= 16;
+  uint32_t w[kPacked ? N / 2 : N];
+  __device__ __forceinline__ void load(const uint16_t* __restrict__ p) {
+    if constexpr (kPacked) {
+      const uint32_t* q = reinterpret_cast<const uint32_t*>(p);
+#pragma unroll
+      for (int i = 0; i < N / 2; ++i) w[i] = q[i];
+    } else {
+#pragma unroll
+      for (int n = 0; n < N; ++n) w[n] = static_cast<uint32_t>(p[n]) << 16;
+    }
+  }
+  __device__ __forceinline__ float get(int n) const {
+    if constexpr (kPacked) return __uint_as_float((n & 1) ? (w[n / 2] & 0xffff0000u) : (w[n / 2] << 16));
+    else return __uint_as_float(w[n]);
+  }
+};
+
 // exp2 on the transcendental unit (v_exp_f32).
 __device__ __forceinline__ float fast_exp2(float v) { return __builtin_amdgcn_exp2f(v); }
 
@@ -237,10 +269,10 @@ __device__ __forceinline__ void scan_steps(const T* __restrict__ xb, const T* __
     buf_load_vals<T, CPL>(dr, in_lane, soff, dc[j]);
     if constexpr (kGate) buf_load_vals<T, CPL>(zr, in_lane, soff, zc[j]);
   }
-  float Bv[2][N], Cv[2][N];
+  RawRow<N, T, kPairs> Bv[2], Cv[2];
   if (nsteps > 0) {
-    load_row_any<N, kPairs>(Bb, Bv[0]);
-    if constexpr (kWithY) load_row_any<N, kPairs>(Cb, Cv[0]);
+    Bv[0].load(Bb);
+    if constexpr (kWithY) Cv[0].load(Cb);
   }
   for (int base = 0; base < nsteps; base += kTile) {
     float xn[kTile][CPL], dn[kTile][CPL], zn[kGate ? kTile : 1][CPL];
@@ -263,8 +295,14 @@ __device__ __forceinline__ void scan_steps(const T* __restrict__ xb, const T* __
       const int cur = j & 1;
       wait_scalar_loads();
       const int64_t nxt = s + 1 < nsteps ? s + 1 : last;
-      load_row_any<N, kPairs>(Bb + nxt * N, Bv[cur ^ 1]);
-      if constexpr (kWithY) load_row_any<N, kPairs>(Cb + nxt * N, Cv[cur ^ 1]);
+      Bv[cur ^ 1].load(Bb + nxt * N);
+      if constexpr (kWithY) Cv[cur ^ 1].load(Cb + nxt * N);
+      // The next step's rows are requested here, a whole step ahead of their
+      // use; the scheduler would otherwise lift this step's arithmetic above
+      // the wait and the loads, leaving each step to wait out its own loads.
+      // Only for packed bfloat16 rows: float32 rows take twice the scalar
+      // registers, and pinned there they spill.
+      if constexpr (RawRow<N, T, kPairs>::kPinnable) __builtin_amdgcn_sched_barrier(0);
       float dl[CPL], dx[CPL], yv[CPL];
 #pragma unroll
       for (int c = 0; c < CPL; ++c) {
@@ -279,12 +317,12 @@ __device__ __forceinline__ void scan_steps(const T* __restrict__ xb, const T* __
           const float a = fast_exp2(dl[c] * k.A2[c][n]);               // Abar = exp(delta A)
           if constexpr (V::kZoh) {
             // (Abar - 1) / A * B * x: u = x B / A, then a u - u in one rounding
-            const float u = (xc[j][c] * k.Ainv[c][n]) * Bv[cur][n];
+            const float u = (xc[j][c] * k.Ainv[c][n]) * Bv[cur].get(n);
             h[c][n] = __builtin_fmaf(a, h[c][n], __builtin_fmaf(a, u, -u));
           } else {
-            h[c][n] = __builtin_fmaf(a, h[c][n], dx[c] * Bv[cur][n]);  // h = Abar h + (delta B) x
+            h[c][n] = __builtin_fmaf(a, h[c][n], dx[c] * Bv[cur].get(n));  // h = Abar h + (delta B) x
           }
-          if constexpr (kWithY) yv[c] = __builtin_fmaf(Cv[cur][n], h[c][n], yv[c]);  // C . h
+          if constexpr (kWithY) yv[c] = __builtin_fmaf(Cv[cur].get(n), h[c][n], yv[c]);  // C . h
         }
       }
       if constexpr (kWithY) {
@@ -293,7 +331,19 @@ __device__ __forceinline__ void scan_steps(const T* __restrict__ xb, const T* __
           if constexpr (V::kSkip) yv[c] = __builtin_fmaf(k.Dd[c], xc[j][c], yv[c]);
           if constexpr (kGate) yv[c] *= silu(zc[j][c]);
         }
-        if (live) buf_store_vals<CPL>(yr, out_lane, s * out_row, yv);
+        if constexpr (RawRow<N, T, kPairs>::kPinnable) {
+          // No branch around the store here: with one, the compiler moved the
+          // read-out and a fresh load of C_t into it, and every step waited
+          // for that load.  A dead step's store gets a per-lane offset of
+          // 2^31, past the buffer's byte limit (nsteps * D * 4 < 2^31), which
+          // the hardware range check drops.
+          buf_store_vals<CPL>(yr, live ? out_lane : int(0x80000000u), live ? s * out_row : 0, yv);
+        } else {
+          // (float32 rows: holding both prefetched rows costs more scalar
+          // registers than there are, and the branch lets the compiler
+          // reload C_t instead)
+          if (live) buf_store_vals<CPL>(yr, out_lane, s * out_row, yv);
+        }
       } else {
 #pragma unroll
         for (int c = 0; c < CPL; ++c) S[c] += static_cast<double>(dl[c]);

@@ -141,11 +141,17 @@ __global__ __launch_bounds__(kBlock) void split_scan_kernel(
       if constexpr (kSkip) xr[j] = s_x[buf][wave * kRs + j][lane];
       if constexpr (kGate) zr[j] = s_z[buf][wave * kRs + j][lane];
     }
+    float pt[kTile];
 #pragma unroll
     for (int grp = 0; grp < kTile / kBcSteps; ++grp) {
       const int set = grp & 1;
       wait_scalar_loads();
       load_bc(set ^ 1, k * kTile + kBcSteps * (grp + 1));
+      // Keep the next group's scalar loads here, a whole group ahead of
+      // their use: left alone, the scheduler lifts this group's arithmetic
+      // above the wait and the loads, and each group then starts by waiting
+      // out the full latency of its own B and C.
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int q = 0; q < kBcSteps; ++q) {
         const int s = kBcSteps * grp + q;
@@ -157,9 +163,13 @@ __global__ __launch_bounds__(kBlock) void split_scan_kernel(
           h[i] = __builtin_fmaf(a, h[i], uv[s] * B[i]);
           p = __builtin_fmaf(B[4 + i], h[i], p);
         }
-        s_part[buf][wave][s][lane] = p;
+        pt[s] = p;
       }
     }
+    // the partial read-outs leave after the last group, so the scalar-load
+    // waits above (which count LDS accesses too) never wait for them
+#pragma unroll
+    for (int s = 0; s < kTile; ++s) s_part[buf][wave][s][lane] = pt[s];
   };
 
   // y of tile k (its partials in buffer buf): this wavefront's two steps
