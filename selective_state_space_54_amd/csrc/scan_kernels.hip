@@ -7,52 +7,88 @@
 
 namespace mssm {
 
-// Carry pass: one lane per (batch row, state n, channel d).  Walks the chunk
-// pairs in time order, c_{j+1} = P_j c_j + hloc_j (c_0 = h0, or 0), with the
-// chunk decay P_j = exp(A S_j) = exp2(A log2(e) S_j) formed from the chunk's
-// step-size total S_j (accumulated in float64 by the summary kernels; the
-// product is taken in float32, which moves P by at most ~5e-8 absolute: the
-// exponent's rounding error is relative, and |arg| 2^arg peaks near 0.5),
-// and overwrites hloc_j with c_{j+1}, the state entering chunk j + 1.  The loads of up to kBatch chunks are all issued before the
-// dependent multiply-add chain, so a lane pays one memory latency per kBatch
-// chunks.
-__global__ __launch_bounds__(kBlock) void chunk_carry_kernel(float* __restrict__ sum_h,
-                                                             const double* __restrict__ sum_s,
-                                                             const float* __restrict__ A,
-                                                             const float* __restrict__ h0,
-                                                             int64_t D, int N, int K,
-                                                             int64_t n_dtiles) {
-  constexpr int kBatch = 32;
+// Carry pass.  For every chain (batch row, state n, channel d) the states
+// entering the chunks follow c_{j+1} = P_j c_j + hloc_j (c_0 = h0, or 0),
+// with the chunk decay P_j = exp(A S_j) = exp2(A log2(e) S_j) formed from the
+// chunk's step-size total S_j (accumulated in float64 by the summary kernels;
+// the exponent is taken in float32, which moves P by at most ~5e-8 absolute:
+// its rounding error is relative, and |arg| 2^arg peaks near 0.5).  hloc_j is
+// overwritten with c_{j+1}, the state entering chunk j + 1.
+//
+// The recurrence is a first-order linear one, so it composes like the scan
+// itself ("Understanding Mamba", section 7.1, eq. (8)): a run of chunks acts
+// on its entering state as c -> P c + H, with P the product of the run's
+// decays and H the run's result from a zero state.  A block takes 64
+// channels of one (batch row, n); its 16 wavefronts take 16 consecutive runs
+// of kRun chunks each (one pass; longer sequences take several passes).
+// Each wavefront loads its run once (coalesced rows of 64 channels), forms
+// the decays and (P, H) of its run in registers, and publishes (P, H) in LDS;
+// after one barrier every wavefront folds the runs before its own onto the
+// state entering the pass, then replays its run from that state and stores
+// the carries.  The dependent chain per pass is kRun + 16 multiply-adds
+// instead of one per chunk, and every wavefront's loads are in flight at once.
+namespace {
+constexpr int kCarryWaves = 16;
+constexpr int kRun = 32;
+}  // namespace
+
+__global__ __launch_bounds__(64 * kCarryWaves) void chunk_carry_kernel(
+    float* __restrict__ sum_h, const double* __restrict__ sum_s, const float* __restrict__ A,
+    const float* __restrict__ h0, int64_t D, int N, int K, int64_t n_dtiles) {
+  __shared__ float sP[kCarryWaves][64], sH[kCarryWaves][64];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t bid = blockIdx.x;
   const int64_t dtile = bid % n_dtiles;
   const int64_t rest = bid / n_dtiles;
   const int n = static_cast<int>(rest % N);
   const int64_t b = rest / N;
-  const int64_t d = dtile * kBlock + threadIdx.x;
-  if (d >= D) return;                       // no barriers in this kernel
+  const int64_t d_raw = dtile * 64 + lane;
+  const bool live = d_raw < D;              // lanes past the last channel only keep step
+  const int64_t d = live ? d_raw : D - 1;   // (every wavefront reaches every barrier)
   const int64_t stride = (int64_t)N * D;    // from chunk j to chunk j + 1
   float* hp = sum_h + (b * (K - 1) * N + n) * D + d;
   const double* sp = sum_s + b * (K - 1) * D + d;
   const float a2 = A[d * N + n] * kLog2e;
-  float c = h0 != nullptr ? h0[(b * D + d) * N + n] : 0.0f;
-  for (int j0 = 0; j0 < K - 1; j0 += kBatch) {
-    float hv[kBatch];
-    double sv[kBatch];
+  float c_pass = h0 != nullptr ? h0[(b * D + d) * N + n] : 0.0f;   // state entering the pass
+  const int nj = K - 1;
+  for (int pass0 = 0; pass0 < nj; pass0 += kRun * kCarryWaves) {
+    const int j0 = pass0 + wave * kRun;
+    float hv[kRun], pv[kRun];
+    // every load is issued (past the end: the last chunk's, then replaced),
+    // so all of a run's loads are in flight together
+    double sv[kRun];
 #pragma unroll
-    for (int i = 0; i < kBatch; ++i) {
-      if (j0 + i < K - 1) {
-        hv[i] = hp[(int64_t)(j0 + i) * stride];
-        sv[i] = sp[(int64_t)(j0 + i) * D];
-      }
+    for (int i = 0; i < kRun; ++i) {
+      const int64_t j = min(j0 + i, nj - 1);
+      hv[i] = hp[j * stride];
+      sv[i] = sp[j * D];
     }
 #pragma unroll
-    for (int i = 0; i < kBatch; ++i) {
-      if (j0 + i < K - 1) {
-        const float p = fast_exp2(a2 * static_cast<float>(sv[i]));
-        c = __builtin_fmaf(p, c, hv[i]);
-        hp[(int64_t)(j0 + i) * stride] = c;
-      }
+    for (int i = 0; i < kRun; ++i) {
+      const bool in = j0 + i < nj;             // a run past the end acts as c -> c
+      pv[i] = in ? fast_exp2(a2 * static_cast<float>(sv[i])) : 1.0f;
+      hv[i] = in ? hv[i] : 0.0f;
     }
+    float P = 1.0f, H = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kRun; ++i) {
+      H = __builtin_fmaf(pv[i], H, hv[i]);
+      P *= pv[i];
+    }
+    sP[wave][lane] = P;
+    sH[wave][lane] = H;
+    block_sync();
+    float c = c_pass;
+    for (int w = 0; w < wave; ++w) c = __builtin_fmaf(sP[w][lane], c, sH[w][lane]);
+#pragma unroll
+    for (int i = 0; i < kRun; ++i) {
+      c = __builtin_fmaf(pv[i], c, hv[i]);
+      if (live && j0 + i < nj) hp[(int64_t)(j0 + i) * stride] = c;
+    }
+#pragma unroll
+    for (int w = 0; w < kCarryWaves; ++w) c_pass = __builtin_fmaf(sP[w][lane], c_pass, sH[w][lane]);
+    block_sync();                           // sP / sH are rewritten by the next pass
   }
 }
 
@@ -72,10 +108,10 @@ static size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 hipError_t launch_carry(float* sum_h, const double* sum_s, const float* A, const float* h0,
                         int64_t batch, int64_t D, int64_t N, int K, hipStream_t stream) {
-  const int64_t carry_tiles = (D + kBlock - 1) / kBlock;
+  const int64_t carry_tiles = (D + 63) / 64;
   const int64_t cgrid = carry_tiles * N * batch;
-  hipLaunchKernelGGL(chunk_carry_kernel, dim3((unsigned)cgrid), dim3(kBlock), 0, stream, sum_h,
-                     sum_s, A, h0, D, static_cast<int>(N), K, carry_tiles);
+  hipLaunchKernelGGL(chunk_carry_kernel, dim3((unsigned)cgrid), dim3(64 * kCarryWaves), 0, stream,
+                     sum_h, sum_s, A, h0, D, static_cast<int>(N), K, carry_tiles);
   return hipGetLastError();
 }
 
