@@ -14,10 +14,14 @@ value    = algorithmic bytes per step * steps / wall time of the timed region
            (bytes = (x + delta + y) over batch*L*D plus (B + C) over batch*L*N,
            input element size for all five, as the metric defines them)
 roofline = the scan call against the roof that binds it.  Each (b, t, d, n)
-           element needs 4 single-rate fp32 VALU operations and one half-rate
-           v_exp_f32 = 6 lane-issue slots; the chip issues 256 CU * 4 SIMD * 16
-           lanes * 2.4 GHz = 39.32e12 slots/s, so the element roof is
-           6553.6 Gelem/s ("alu").  The same call is also reported against HBM
+           element needs 4 fp32 VALU operations (exponent multiply, input-term
+           multiply, state fma, read-out fma) and one v_exp_f32.  MI355X's
+           published fp32 vector peak, 157.3 TFLOP/s, is 256 CU * 128 fma
+           lanes * 2.4 GHz = 78.64e12 fma lane-operations/s; a transcendental
+           issues at a quarter of that rate, so an element costs 4 + 4 = 8
+           lane-operation slots and the element roof is 9830.4 Gelem/s
+           ("alu").  (The issue-rate probes measure what the chip sustains
+           against it.)  The same call is also reported against HBM
            (algorithmic bytes / call time vs 8 TB/s and vs a device copy
            measured in the same run), with the HBM bytes the rocprofv3 counters
            measured for the current kernel sources ("traffic").  Call time
@@ -42,9 +46,12 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+FP32_FMA_LANE_OPS_PER_S = 256 * 128 * 2.4e9   # 157.3 TFLOP/s / 2 flops per fma
+SLOTS_PER_ELEMENT = 4 + 4                     # 4 single-rate VALU + one quarter-rate exp
+ELEM_PEAK_GPS = FP32_FMA_LANE_OPS_PER_S / SLOTS_PER_ELEMENT / 1e9
+# probe reports: a wave64 instruction issued every 4 clocks on each of the
+# 1024 SIMDs, the unit the probes express their rates in
 VALU_LANE_SLOTS_PER_S = 256 * 4 * 16 * 2.4e9
-SLOTS_PER_ELEMENT = 6
-ELEM_PEAK_GPS = VALU_LANE_SLOTS_PER_S / SLOTS_PER_ELEMENT / 1e9
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 HEADLINE = "long_seq_bf16"
 CONFIGS = ("tiny_fp32", "mamba130m_layer_fp32", "mid_bf16", "long_seq_bf16", "fused_proj_bf16")
@@ -630,7 +637,8 @@ def probe_rates(torch, iters=4000, blocks=2048, reps=5):
         torch.cuda.synchronize()
         return s.elapsed_time(e) / reps * 1e-3
 
-    res = {"lane_slots_per_s_nominal": VALU_LANE_SLOTS_PER_S, "blocks": blocks,
+    res = {"published_fp32_fma_lane_ops_per_s": FP32_FMA_LANE_OPS_PER_S,
+           "wave_issue_lane_slots_per_s": VALU_LANE_SLOTS_PER_S, "blocks": blocks,
            "threads_per_block": 256, "iterations": iters}
     lanes = blocks * 256
     for which, name in ((0, "v_exp_f32"), (1, "v_fma_f32"), (2, "v_mul_f32"),
@@ -638,12 +646,14 @@ def probe_rates(torch, iters=4000, blocks=2048, reps=5):
         t = timed(which, blocks, iters)
         rate = lanes * iters * 16 / t
         res[name] = {"lane_instructions_per_s": rate,
+                     "frac_of_published_fp32_lane_rate": round(rate / FP32_FMA_LANE_OPS_PER_S, 4),
                      "lane_slots_per_instruction": round(VALU_LANE_SLOTS_PER_S / rate, 3),
                      "seconds": t}
     t = timed(4, blocks, iters, bc.data_ptr())
     rate = lanes * iters * 16 / t
     res["scan element (mul, v_exp_f32, mul, fma, fma)"] = {
         "Gelem_per_s": round(rate / 1e9, 1),
+        "frac_of_element_roof": round(rate / 1e9 / ELEM_PEAK_GPS, 4),
         "lane_slots_per_element": round(VALU_LANE_SLOTS_PER_S / rate, 3), "seconds": t}
     t = timed(5, 4096, 0, buf.data_ptr(), n16)
     res["read_GBps"] = round(n16 * 16 / t / 1e9, 1)

@@ -51,16 +51,17 @@ __device__ __forceinline__ bf16x8 load_bf16x8(const uint16_t* p) {
   return v;
 }
 
-// softplus(z) = ln(1 + e^z) as max(z, 0) + log1p(e^{-|z|}).  log1p(e) is
-// log(u) * e / (u - 1) with u = 1 + e rounded (Goldberg's correction), which
-// keeps full relative accuracy when e is tiny; u == 1 means log1p(e) = e.
+// softplus(z) = ln(1 + e^z) as max(z, 0) + log1p(e), e = e^{-|z|} in (0, 1].
+// u = 1 + e rounded, and c = e - (u - 1) is exactly (1 + e) - u (u - 1 is
+// exact for u in [1, 2], Fast2Sum).  Then log1p(e) = log(u) + log(1 + c/u),
+// and with |c| <= 2^-24 that is log(u) + c to within |c| e, a fraction of an
+// ulp of the result: full relative accuracy down to the smallest e, with no
+// division (v_log_f32 gives log2).
 __device__ __forceinline__ float softplus_f(float z) {
   const float e = fast_exp2(-fabsf(z) * kLog2e);
   const float u = 1.0f + e;
-  const float um1 = u - 1.0f;
-  const float lg = __builtin_amdgcn_logf(u) * 0.69314718055994531f;
-  const float l1p = (um1 == 0.0f) ? e : lg * (e * __builtin_amdgcn_rcpf(um1));
-  return fmaxf(z, 0.0f) + l1p;
+  const float c = e - (u - 1.0f);
+  return fmaxf(z, 0.0f) + __builtin_fmaf(__builtin_amdgcn_logf(u), 0.69314718055994531f, c);
 }
 
 // Delta for rows [0, 32) of a tile (steps s0..s0+31 of the chunk) and the
@@ -390,7 +391,7 @@ __global__ __launch_bounds__(kFBlock) void fused_output_kernel(
 constexpr int kDtRowTiles = 8;               // 32-row tiles per block
 
 template <int KS>
-__global__ __launch_bounds__(kFBlock) void dtproj_softplus_kernel(
+__global__ __launch_bounds__(kFBlock) __attribute__((amdgpu_waves_per_eu(3))) void dtproj_softplus_kernel(
     const uint16_t* __restrict__ dtl, const uint16_t* __restrict__ dtl_lo,
     const uint16_t* __restrict__ wT, const float* __restrict__ bias, float* __restrict__ delta,
     int64_t M, int64_t D, int64_t n_cblocks) {
@@ -401,7 +402,7 @@ __global__ __launch_bounds__(kFBlock) void dtproj_softplus_kernel(
   constexpr int kPerThread = (kChunks + kFBlock - 1) / kFBlock;
   __shared__ __align__(16) uint16_t sa[2][32][kStride];
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t rb = blockIdx.x / n_cblocks;
   const int64_t c0 = (blockIdx.x % n_cblocks) * 128 + wave * 32;
   const int khalf = 8 * (lane / 32);
@@ -411,6 +412,7 @@ __global__ __launch_bounds__(kFBlock) void dtproj_softplus_kernel(
   for (int k = 0; k < KS; ++k) bw[k] = load_bf16x8(wT + ch * R + 16 * k + khalf);
   const float bias_c = bias[ch];
   const bool col_ok = c0 + lane % 32 < D;
+  const uint32_t lane_off = static_cast<uint32_t>((4 * (lane / 32) * D + lane % 32) * 4);   // bytes
 
   // this thread's pieces of every tile: part, row, column (compile-time divisors)
   auto piece = [&](int q, int& arr, int& row, int& col) {
@@ -451,7 +453,9 @@ __global__ __launch_bounds__(kFBlock) void dtproj_softplus_kernel(
     block_sync();
     if (t + 1 < kDtRowTiles && m0 + 32 < M) fetch(m0 + 32);   // in flight during this tile
     if (c0 >= D) continue;                     // a wavefront past the last channel only copies
-    f32x16 acc = f32x16{};
+    f32x16 acc;                                // the bias enters as the accumulator's start
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] = bias_c;
 #pragma unroll
     for (int k = 0; k < KS; ++k) {
       bf16x8 a, a_lo;
@@ -460,24 +464,25 @@ __global__ __launch_bounds__(kFBlock) void dtproj_softplus_kernel(
       acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bw[k], acc, 0, 0, 0);
       acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_lo, bw[k], acc, 0, 0, 0);
     }
+    // output element (row m0 + 8 (r / 4) + 4 (lane / 32) + r % 4, column c0 +
+    // lane % 32): a wave-uniform row base per r and a small per-lane offset
+    if (m0 + 32 <= M && c0 + 32 <= D) {        // uniform: every element in range
+      // rows as SGPR offsets from the tile's corner, the lane's place as the
+      // per-lane offset: no per-store vector address arithmetic
+      const buf_t out = make_buf(delta + m0 * D + c0, 0x7fffffffu);
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      // output element (row 8 (r / 4) + 4 (lane / 32) + r % 4, column lane % 32)
-      const int64_t m = m0 + 8 * (r / 4) + 4 * (lane / 32) + (r % 4);
-      if (col_ok && m < M) delta[m * D + c0 + lane % 32] = softplus_f(acc[r] + bias_c);
+      for (int r = 0; r < 16; ++r) {
+        const int soff = static_cast<int>((8 * (r / 4) + (r % 4)) * D * 4);
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(softplus_f(acc[r])), out,
+                                              static_cast<int>(lane_off), soff, 0);
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t m = m0 + 8 * (r / 4) + 4 * (lane / 32) + (r % 4);
+        if (col_ok && m < M) delta[m * D + c0 + lane % 32] = softplus_f(acc[r]);
+      }
     }
-  }
-}
-
-// wT[d, r] = W[r, d]
-__global__ void transpose_bf16_kernel(const uint16_t* __restrict__ W, uint16_t* __restrict__ wT,
-                                      int R, int64_t D) {
-  const int64_t total = (int64_t)R * D;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
-       i += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t d = i / R;
-    const int r = static_cast<int>(i % R);
-    wT[i] = W[(int64_t)r * D + d];
   }
 }
 
@@ -639,9 +644,7 @@ hipError_t launch_transpose_bf16(const void* W, uint16_t* wT, int64_t rows, int6
 
 hipError_t launch_wdt_transpose(const void* W_dt, int64_t R, int64_t D, uint16_t* wT,
                                 hipStream_t stream) {
-  hipLaunchKernelGGL(transpose_bf16_kernel, dim3(1024), dim3(256), 0, stream,
-                     static_cast<const uint16_t*>(W_dt), wT, static_cast<int>(R), D);
-  return hipGetLastError();
+  return launch_transpose_bf16(W_dt, wT, R, D, stream, R);   // wT[d, r] = W_dt[r, d]
 }
 
 hipError_t launch_dtproj_softplus(const uint16_t* dtl, const uint16_t* dtl_lo, const uint16_t* wT,

@@ -69,23 +69,54 @@ __global__ __launch_bounds__(256) void transpose_pad_kernel(const uint16_t* __re
                                                             uint16_t* __restrict__ wT, int64_t K,
                                                             int64_t ncol, int64_t Kp,
                                                             float* __restrict__ bcg,
-                                                            int64_t bcg_rows, int64_t M) {
+                                                            int64_t bcg_rows, int64_t M, bool vec) {
   // the grouped B/C rows past the last token (read by steps past the end of
   // the sequence, whose input term is zero) are set to zero here
   if (bcg && blockIdx.x == 0) {
     const int g = threadIdx.x >> 6, r = (threadIdx.x >> 3) & 7, j = threadIdx.x & 7;
     if (M + r < bcg_rows) bcg[(g * bcg_rows + M + r) * 8 + j] = 0.0f;
   }
-  __shared__ uint16_t tile[64][65];
+  __shared__ __align__(16) uint16_t tile[64][72];
   const int64_t tiles_c = (ncol + 63) / 64;
   const int64_t r0 = static_cast<int64_t>(blockIdx.x / tiles_c) * 64;
   const int64_t c0 = static_cast<int64_t>(blockIdx.x % tiles_c) * 64;
-  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  const int t = threadIdx.x;
+  if (vec) {
+    // 16-byte pieces: two 8-wide pieces of W's rows per thread in, two
+    // 8-wide pieces of wT's rows (gathered from a tile column) out; the
+    // 72-half pitch keeps the pieces aligned and the column reads spread
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int piece = t + 256 * h;
+      const int i = piece >> 3, j = (piece & 7) * 8;
+      const int64_t r = r0 + i, c = c0 + j;
+      uint4 v = make_uint4(0u, 0u, 0u, 0u);
+      if (r < K && c < ncol) v = *reinterpret_cast<const uint4*>(W + r * ncol + c);
+      *reinterpret_cast<uint4*>(&tile[i][j]) = v;
+    }
+    block_sync();
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int piece = t + 256 * h;
+      const int i = piece >> 3, j = (piece & 7) * 8;
+      const int64_t c = c0 + i, r = r0 + j;
+      if (c < ncol && r < Kp) {
+        uint32_t w[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          w[q] = static_cast<uint32_t>(tile[j + 2 * q][i]) |
+                 (static_cast<uint32_t>(tile[j + 2 * q + 1][i]) << 16);
+        *reinterpret_cast<uint4*>(wT + c * Kp + r) = make_uint4(w[0], w[1], w[2], w[3]);
+      }
+    }
+    return;
+  }
+  const int tx = t & 63, ty = t >> 6;
   for (int i = ty; i < 64; i += 4) {
     const int64_t r = r0 + i, c = c0 + tx;
     tile[i][tx] = (r < K && c < ncol) ? W[r * ncol + c] : uint16_t(0);
   }
-  __syncthreads();
+  block_sync();
   for (int i = ty; i < 64; i += 4) {
     const int64_t c = c0 + i, r = r0 + tx;
     if (c < ncol && r < Kp) wT[c * Kp + r] = tile[tx][i];
@@ -285,9 +316,11 @@ hipError_t launch_xproj(const uint16_t* x, const uint16_t* x_lo, int64_t lda, in
   if (M <= 0 || ncol <= 0) return hipSuccess;
   const int64_t Kp = xproj_padded_k(K);
   const int64_t tiles = ((Kp + 63) / 64) * ((ncol + 63) / 64);
+  const bool tvec = ncol % 8 == 0 && reinterpret_cast<uintptr_t>(W_x) % 16 == 0 &&
+                    reinterpret_cast<uintptr_t>(WxT) % 16 == 0;   // Kp is a multiple of 64
   hipLaunchKernelGGL(transpose_pad_kernel, dim3(static_cast<unsigned>(tiles)), dim3(256), 0,
                      stream, static_cast<const uint16_t*>(W_x), WxT, K, ncol, Kp, bcg, bcg_rows,
-                     M);
+                     M, tvec);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const dim3 grid(static_cast<unsigned>((M + kXRows - 1) / kXRows),
