@@ -700,11 +700,11 @@ def cpu_baseline(hosts, oracle, workloads, threads, seconds=10.0):
             continue
         ww = gg["workload"]
         s = _oracle_pass(gg, oracle, workloads, threads)
-        per[name] = {"threads": threads, "seconds_per_pass": round(s, 3),
+        per[name] = {"threads": threads, "seconds_per_pass": round(s, 6),
                      "GB/s": round(algorithmic_bytes(ww) / s / 1e9, 4)}
         if name in ("tiny_fp32", "mamba130m_layer_fp32"):
             s1 = _oracle_pass(gg, oracle, workloads, 1)
-            per[name]["one_thread"] = {"seconds_per_pass": round(s1, 3),
+            per[name]["one_thread"] = {"seconds_per_pass": round(s1, 6),
                                        "GB/s": round(algorithmic_bytes(ww) / s1 / 1e9, 4)}
     return {"value": round(algorithmic_bytes(w) * passes / spent / 1e9, 4), "unit": "GB/s",
             "cores": threads, "kind": "oracle", "seconds": round(spent, 3),
