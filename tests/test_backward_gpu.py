@@ -1,8 +1,7 @@
 """GPU parity of the scan's backward pass (mssm_selective_scan_bwd through the
-C ABI) against the float64 adjoint oracle.  The tolerance stated for y is used
-relative to each gradient tensor's scale: |err| <= tol (|ref| + rms(ref)), since
-dA, dD (sums over batch and time) and dB, dC (sums over channels) can cancel
-to values far below the size of their terms."""
+C ABI) against the float64 adjoint oracle.  Every gradient element is held to
+the bound stated for y, |err| <= tol (1 + |ref|), element by element (at the
+full headline size the largest ratio, for dD, is about 0.25)."""
 import numpy as np
 import pytest
 
@@ -25,8 +24,7 @@ def grad_parity(gpu, ref, dtype, what):
     for k, r in ref.items():
         g = host64(gpu[k])
         assert np.isfinite(g).all(), f"{what} {k}: non-finite"
-        scale = np.abs(r) + (np.sqrt(np.mean(r ** 2)) if r.size else 0.0)
-        ratio = float((np.abs(g - r) / (tol * scale + 1e-30)).max()) if r.size else 0.0
+        ratio = float((np.abs(g - r) / (tol * (1.0 + np.abs(r)))).max()) if r.size else 0.0
         report[k] = round(ratio, 4)
         assert ratio <= 1.0, f"{what} {k}: max err / bound = {ratio:.3g}"
     return report
