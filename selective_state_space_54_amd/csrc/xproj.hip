@@ -32,6 +32,13 @@
 // With two A operands (the Mamba block: x kept as a bf16 hi + lo pair) both
 // tiles are multiplied into the same accumulators.
 //
+// For one A operand with 16-byte aligned rows, K a multiple of 64 and 192
+// output columns (the fused selective SSM with R = 160, N = 16) a second form
+// takes over: the tiles are copied from memory straight into LDS (no register
+// staging), three stages deep, with the pieces of a row permuted so that the
+// fragment reads stay conflict-free (xproj_lds_kernel below): 109 against
+// 139-145 us on the fused workload.
+//
 // MFMA operand layout (v_mfma_f32_16x16x32_bf16): A fragment, lane l holds row
 // l % 16 and 8 consecutive k values starting at 8 (l / 16); B fragment, lane l
 // holds column l % 16 and the same 8 k values; both operands use the same k
@@ -142,6 +149,47 @@ __device__ __forceinline__ uint4 load_piece(const uint16_t* __restrict__ A, int6
       w[j] = lo | (hi << 16);
     }
     return make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
+
+// This wavefront's part of the block's result (kRT 16-row tiles from row
+// 16 kRT wr, columns c_wave): columns below R as the dt_low bf16 pair, the
+// others as float32 into P and, with bcg, into the grouped B/C copy.
+template <int kRT = 4>
+__device__ __forceinline__ void store_tile(const f32x4 (&acc)[4][kXFrags], int lane, int wr,
+                                           int64_t m0, int c_wave, int nfrag, int64_t M,
+                                           int ncol, int R, uint16_t* __restrict__ dtl,
+                                           uint16_t* __restrict__ dtl_lo, float* __restrict__ P,
+                                           int64_t ldp, float* __restrict__ bcg,
+                                           int64_t bcg_rows) {
+  const int col_in = lane & 15;
+  const int row_in = 4 * (lane >> 4);
+#pragma unroll
+  for (int f = 0; f < kXFrags; ++f) {
+    if (f >= nfrag) continue;
+    const int c = c_wave + 16 * f + col_in;
+    const bool dt_frag = c_wave + 16 * f < R;       // uniform: R is a multiple of 16
+#pragma unroll
+    for (int r = 0; r < kRT; ++r) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t m = m0 + 16 * kRT * wr + 16 * r + row_in + i;
+        if (m >= M) continue;
+        const float v = acc[r][f][i];
+        if (dt_frag) {
+          const uint32_t hi = bf16_rne_bits(v);
+          dtl[m * R + c] = static_cast<uint16_t>(hi);
+          dtl_lo[m * R + c] = static_cast<uint16_t>(bf16_rne_bits(v - __uint_as_float(hi << 16)));
+        } else if (c < ncol) {
+          P[m * ldp + c] = v;
+          if (bcg) {   // N = 16: B and C also in four groups of four state indices
+            const int n = c - R;
+            const int g = (n & 15) >> 2, j = (n & 3) + (n >= 16 ? 4 : 0);
+            bcg[(g * bcg_rows + m) * 8 + j] = v;
+          }
+        }
+      }
+    }
   }
 }
 
@@ -269,36 +317,167 @@ __global__ __launch_bounds__(kXBlock) void xproj_kernel(
     compute(0);
   }
 
-  // epilogue
-  const int col_in = lane & 15;
-  const int row_in = 4 * (lane >> 4);
+  store_tile(acc, lane, wr, m0, c_wave, nfrag, M, ncol, R, dtl, dtl_lo, P, ldp, bcg, bcg_rows);
+}
+
+// The same product with the tiles copied from memory straight into LDS
+// (buffer_load_dwordx4 ... lds: each lane's 16 bytes land at the LDS address
+// M0 + 16 lane), for one A operand, 16-byte aligned rows, K a multiple of 64
+// and exactly 192 output columns (every wavefront's six column fragments in
+// range).  With no register staging the ring can hold kLStages tiles (40 KB
+// each): kLStages - 1 tiles of loads are in flight while one is multiplied.
+// A tile is 128 rows (x) or 192 rows (W^T) of 8 16-byte pieces; piece q of
+// row r sits at position r * 8 + (q ^ ((r >> 1) & 7)), so that the 16 rows a
+// fragment read touches fall on 16 different 16-byte bank groups, and each
+// copy instruction (64 consecutive positions) loads whatever pieces those
+// positions hold.  Per tile: one wait for this thread's oldest copies, one
+// barrier (after it every thread's copies of the tile have landed, and every
+// wavefront is done with the buffer the next copies overwrite), the copies
+// of the tile kLStages - 1 ahead, the products.
+constexpr int kLRows = 128;    // rows of x per block of the copy-to-LDS form
+constexpr int kLStages = 3;    // LDS stages (tiles in flight + 1)
+
+template <int kRows, int kStages>
+struct LdsTile {
+  static constexpr int kAPieces = kRows * 8;
+  static constexpr int kBPieces = kXCols * 8;
+  static constexpr int kPieces = kAPieces + kBPieces;
+  static constexpr int kChunks = kPieces / 64;          // copy instructions per tile
+  static constexpr int kChunksPerWave = kChunks / 4;
+  static constexpr int kRowTiles = kRows / 32;           // 16-row tiles per wavefront
+  static_assert(kAPieces % 64 == 0 && kChunks % 4 == 0, "whole copy instructions per wavefront");
+};
+
+__device__ __forceinline__ int swz(int r, int q) { return r * 8 + (q ^ ((r >> 1) & 7)); }
+
+__global__ __launch_bounds__(kXBlock) void xproj_lds_kernel(
+    const uint16_t* __restrict__ A0, int64_t lda, const uint16_t* __restrict__ wT, int64_t Kp,
+    int64_t M, int ncol, int R, uint16_t* __restrict__ dtl, uint16_t* __restrict__ dtl_lo,
+    float* __restrict__ P, int64_t ldp, float* __restrict__ bcg, int64_t bcg_rows) {
+  constexpr int kRows = kLRows, kStages = kLStages;
+  using T = LdsTile<kRows, kStages>;
+  // one array per stage, named by compile-time stage numbers, so the
+  // compiler can tell the copies into one stage from the reads of another
+  // (else it makes every LDS read wait for all copies in flight)
+  static_assert(kStages == 2 || kStages == 3, "two or three stages");
+  __shared__ __align__(16) uint4 ring0[T::kPieces];
+  __shared__ __align__(16) uint4 ring1[T::kPieces];
+  __shared__ __align__(16) uint4 ring2[kStages > 2 ? T::kPieces : 1];
+  // the stages are written only by the copies, which the compiler does not
+  // count as stores to the arrays: their addresses go through an asm
+  // statement so that it cannot take them for never written
+  if constexpr (kStages > 2) asm volatile("" ::"v"(ring0), "v"(ring1), "v"(ring2) : "memory");
+  else asm volatile("" ::"v"(ring0), "v"(ring1) : "memory");
+  auto ring = [&](auto stage_c) __attribute__((always_inline)) -> uint4* {
+    constexpr int S = decltype(stage_c)::value;
+    if constexpr (S == 0) return ring0;
+    else if constexpr (S == 1) return ring1;
+    else return ring2;
+  };
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wr = wave >> 1, wc = wave & 1;
+  const int64_t m0 = static_cast<int64_t>(blockIdx.x) * kRows;
+  const int c0 = static_cast<int>(blockIdx.y) * kXCols;
+  const int c_wave = c0 + wc * kXColsPerWave;
+
+  // this thread's copy sources: chunk ch = wave * kChunksPerWave + i covers
+  // positions 64 ch .. 64 ch + 63 of the stage; lane j fills position
+  // 64 ch + j.  Rows past M read the last row (their results are not
+  // stored).  Byte offsets from the block's first row / from wT.
+  const buf_t xr = make_buf(A0 + m0 * lda, 0x7fffffffu);
+  const buf_t wr_ = make_buf(wT, 0x7fffffffu);
+  uint32_t voff[T::kChunksPerWave];
 #pragma unroll
-  for (int f = 0; f < kXFrags; ++f) {
-    if (f >= nfrag) continue;
-    const int c = c_wave + 16 * f + col_in;
-    const bool dt_frag = c_wave + 16 * f < R;       // uniform: R is a multiple of 16
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int64_t m = m0 + 64 * wr + 16 * r + row_in + i;
-        if (m >= M) continue;
-        const float v = acc[r][f][i];
-        if (dt_frag) {
-          const uint32_t hi = bf16_rne_bits(v);
-          dtl[m * R + c] = static_cast<uint16_t>(hi);
-          dtl_lo[m * R + c] = static_cast<uint16_t>(bf16_rne_bits(v - __uint_as_float(hi << 16)));
-        } else if (c < ncol) {
-          P[m * ldp + c] = v;
-          if (bcg) {   // N = 16: B and C also in four groups of four state indices
-            const int n = c - R;
-            const int g = (n & 15) >> 2, j = (n & 3) + (n >= 16 ? 4 : 0);
-            bcg[(g * bcg_rows + m) * 8 + j] = v;
-          }
-        }
-      }
+  for (int i = 0; i < T::kChunksPerWave; ++i) {
+    const int pos = (wave * T::kChunksPerWave + i) * 64 + lane;
+    if (pos < T::kAPieces) {
+      const int r = pos >> 3, q = (pos & 7) ^ ((r >> 1) & 7);
+      const int64_t rr = min(m0 + r, M - 1) - m0;
+      voff[i] = static_cast<uint32_t>(rr * lda * 2 + q * 16);
+    } else {
+      const int pb = pos - T::kAPieces;
+      const int c = pb >> 3, q = (pb & 7) ^ ((c >> 1) & 7);
+      voff[i] = static_cast<uint32_t>((c0 + c) * Kp * 2 + q * 16);
     }
   }
+  auto issue = [&](int64_t t, auto stage_c) __attribute__((always_inline)) {
+    constexpr int S = decltype(stage_c)::value;
+    const int soff = static_cast<int>(t * kXK * 2);     // bytes along k
+#pragma unroll
+    for (int i = 0; i < T::kChunksPerWave; ++i) {
+      const int ch = wave * T::kChunksPerWave + i;
+      __attribute__((address_space(3))) void* dst =
+          (__attribute__((address_space(3))) void*)(ring(stage_c) + ch * 64);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ch * 64 < T::kAPieces ? xr : wr_, dst, 16,
+                                               static_cast<int>(voff[i]), soff, 0, 0);
+    }
+  };
+
+  f32x4 acc[4][kXFrags];
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int f = 0; f < kXFrags; ++f) acc[r][f] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+  const int arow = lane & 15, qoff = lane >> 4;
+  auto compute = [&](auto stage_c) __attribute__((always_inline)) {
+    constexpr int S = decltype(stage_c)::value;
+    const uint4* sa = ring(stage_c);
+    const uint4* sb = ring(stage_c) + T::kAPieces;
+#pragma unroll
+    for (int s = 0; s < kXK / 32; ++s) {
+      const int q = 4 * s + qoff;
+      bf16x8 b[kXFrags];
+#pragma unroll
+      for (int f = 0; f < kXFrags; ++f) b[f] = as_bf16x8(sb[swz(wc * kXColsPerWave + 16 * f + arow, q)]);
+#pragma unroll
+      for (int r = 0; r < T::kRowTiles; ++r) {
+        const bf16x8 a = as_bf16x8(sa[swz((kRows / 2) * wr + 16 * r + arow, q)]);
+#pragma unroll
+        for (int f = 0; f < kXFrags; ++f)
+          acc[r][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[f], acc[r][f], 0, 0, 0);
+      }
+    }
+  };
+
+  // s_waitcnt vmcnt(copies of the kStages - 2 younger tiles) lgkmcnt(0): this
+  // thread's copies of the tile have landed, and its LDS reads of the stage
+  // the next copies overwrite are done (gfx9 encoding: vmcnt in bits 3:0 and
+  // 15:14, expcnt 6:4 left alone, lgkmcnt 11:8)
+  constexpr int kAhead = T::kChunksPerWave * (kStages - 2);
+  constexpr int kWait = (kAhead & 15) | ((kAhead >> 4) << 14) | (7 << 4) | (0 << 8);
+  const int64_t ntiles = Kp / kXK;
+  const int64_t last = ntiles - 1;
+  // tile t lives in stage t % kStages; its step: wait for this thread's
+  // copies of it, barrier (no memory fence: the copies' own wait is the one
+  // that matters, and a fence would wait for every copy in flight), copies of
+  // tile t + kStages - 1 into the stage tile t - 1 used, products of tile t
+  auto step = [&](int64_t t, auto stage_c) __attribute__((always_inline)) {
+    constexpr int S = decltype(stage_c)::value;
+    __builtin_amdgcn_s_waitcnt(kWait);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    const int64_t tn = t + kStages - 1;      // copies past the last tile repeat it, unused
+    issue(tn < last ? tn : last, std::integral_constant<int, (S + kStages - 1) % kStages>{});
+    compute(stage_c);
+  };
+  issue(0, std::integral_constant<int, 0>{});
+  if constexpr (kStages > 2) issue(1 < last ? 1 : last, std::integral_constant<int, 1>{});
+  int64_t t = 0;
+  for (; t + kStages <= ntiles; t += kStages) {
+    step(t, std::integral_constant<int, 0>{});
+    step(t + 1, std::integral_constant<int, 1>{});
+    if constexpr (kStages > 2) step(t + 2, std::integral_constant<int, 2>{});
+  }
+  if (t < ntiles) step(t, std::integral_constant<int, 0>{});
+  if constexpr (kStages > 2) {
+    if (t + 1 < ntiles) step(t + 1, std::integral_constant<int, 1>{});
+  }
+  __builtin_amdgcn_s_waitcnt(0);             // no copy still in flight at the end
+  store_tile<T::kRowTiles>(acc, lane, wr, m0, c_wave, kXFrags, M, ncol, R, dtl, dtl_lo, P, ldp,
+                           bcg, bcg_rows);
 }
 
 }  // namespace
@@ -333,6 +512,11 @@ hipError_t launch_xproj(const uint16_t* x, const uint16_t* x_lo, int64_t lda, in
                      WxT, Kp, K, M, nc, r, dtl, dtl_lo, P, ldp, bcg, bcg_rows)
   if (x_lo) {
     if (vec) MSSM_XPROJ(true, true); else MSSM_XPROJ(true, false);
+  } else if (vec && K % kXK == 0 && ncol == kXCols && M * lda * 2 < (int64_t(1) << 31) &&
+             ncol * Kp * 2 < (int64_t(1) << 31)) {
+    const dim3 lgrid(static_cast<unsigned>((M + kLRows - 1) / kLRows));
+    hipLaunchKernelGGL(xproj_lds_kernel, lgrid, dim3(kXBlock), 0, stream, x,
+                       lda, WxT, Kp, M, nc, r, dtl, dtl_lo, P, ldp, bcg, bcg_rows);
   } else {
     if (vec) MSSM_XPROJ(false, true); else MSSM_XPROJ(false, false);
   }
