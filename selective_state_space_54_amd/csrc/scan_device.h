@@ -288,6 +288,11 @@ __device__ __forceinline__ void scan_steps(const T* __restrict__ xb, const T* __
     // is left exactly as it was, and store nothing.  (A branch made the
     // compiler merge every state register at its end: a copy per state and
     // step.)
+    // The summary's step-size total: the tile's (at most 8) steps are summed
+    // in float32, each tile's sum added to the float64 total (one conversion
+    // and one float64 add per tile instead of per step; a tile's sum of
+    // values below 1 carries a relative error near 2^-24).
+    float St[CPL] = {};
 #pragma unroll
     for (int j = 0; j < kTile; ++j) {
       const int s = base + j;
@@ -346,8 +351,12 @@ __device__ __forceinline__ void scan_steps(const T* __restrict__ xb, const T* __
         }
       } else {
 #pragma unroll
-        for (int c = 0; c < CPL; ++c) S[c] += static_cast<double>(dl[c]);
+        for (int c = 0; c < CPL; ++c) St[c] += dl[c];
       }
+    }
+    if constexpr (!kWithY) {
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) S[c] += static_cast<double>(St[c]);
     }
 #pragma unroll
     for (int j = 0; j < kTile; ++j) {
