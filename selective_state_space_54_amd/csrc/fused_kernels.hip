@@ -474,7 +474,7 @@ __global__ __launch_bounds__(kFBlock) __attribute__((amdgpu_waves_per_eu(3))) vo
       for (int r = 0; r < 16; ++r) {
         const int soff = static_cast<int>((8 * (r / 4) + (r % 4)) * D * 4);
         __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(softplus_f(acc[r])), out,
-                                              static_cast<int>(lane_off), soff, 0);
+                                              static_cast<int>(lane_off), soff, kStoreNT);
       }
     } else {
 #pragma unroll

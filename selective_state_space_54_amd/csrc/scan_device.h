@@ -174,18 +174,21 @@ __device__ __forceinline__ void buf_store_bf16(buf_t r, int voff, int soff, cons
   }
 }
 
-template <int CPL>
+// kAux: the cache-policy bits of the store (2: non-temporal, for outputs
+// nothing in the call reads again)
+template <int CPL, int kAux = 0>
 __device__ __forceinline__ void buf_store_vals(buf_t r, int voff, int soff, const float (&v)[CPL]) {
   if constexpr (CPL == 1) {
-    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v[0]), r, voff, soff, 0);
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v[0]), r, voff, soff, kAux);
   } else {
     static_assert(CPL == 2, "CPL is 1 or 2");
     u32x2 u;
     u.x = __float_as_uint(v[0]);
     u.y = __float_as_uint(v[1]);
-    __builtin_amdgcn_raw_buffer_store_b64(u, r, voff, soff, 0);
+    __builtin_amdgcn_raw_buffer_store_b64(u, r, voff, soff, kAux);
   }
 }
+constexpr int kStoreNT = 2;
 
 // SiLU(v) = v * sigmoid(v), the gate of the Mamba block ("Understanding
 // Mamba", section 8.1, eq. (9)).  exp2 and the reciprocal run on the
@@ -342,12 +345,12 @@ __device__ __forceinline__ void scan_steps(const T* __restrict__ xb, const T* __
           // for that load.  A dead step's store gets a per-lane offset of
           // 2^31, past the buffer's byte limit (nsteps * D * 4 < 2^31), which
           // the hardware range check drops.
-          buf_store_vals<CPL>(yr, live ? out_lane : int(0x80000000u), live ? s * out_row : 0, yv);
+          buf_store_vals<CPL, kStoreNT>(yr, live ? out_lane : int(0x80000000u), live ? s * out_row : 0, yv);
         } else {
           // (float32 rows: holding both prefetched rows costs more scalar
           // registers than there are, and the branch lets the compiler
           // reload C_t instead)
-          if (live) buf_store_vals<CPL>(yr, out_lane, s * out_row, yv);
+          if (live) buf_store_vals<CPL, kStoreNT>(yr, out_lane, s * out_row, yv);
         }
       } else {
 #pragma unroll

@@ -190,7 +190,7 @@ __global__ __launch_bounds__(kBlock) void split_scan_kernel(
           yhi[o] = static_cast<uint16_t>(hi);
           ylo[o] = static_cast<uint16_t>(bf16_rne_bits(v - __uint_as_float(hi << 16)));
         } else {
-          y[(row0 + t) * D + d] = v;
+          __builtin_nontemporal_store(v, &y[(row0 + t) * D + d]);
         }
       }
     }
