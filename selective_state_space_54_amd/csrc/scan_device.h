@@ -175,7 +175,8 @@ __device__ __forceinline__ void buf_store_bf16(buf_t r, int voff, int soff, cons
 }
 
 // kAux: the cache-policy bits of the store (2: non-temporal, for outputs
-// nothing in the call reads again)
+// streamed past the caches: y, and the fused path's Delta, which at four
+// times the last-level cache's size would not stay there for the scan)
 template <int CPL, int kAux = 0>
 __device__ __forceinline__ void buf_store_vals(buf_t r, int voff, int soff, const float (&v)[CPL]) {
   if constexpr (CPL == 1) {
