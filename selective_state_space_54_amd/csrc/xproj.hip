@@ -35,9 +35,9 @@
 // For one A operand with 16-byte aligned rows, K a multiple of 64 and 192
 // output columns (the fused selective SSM with R = 160, N = 16) a second form
 // takes over: the tiles are copied from memory straight into LDS (no register
-// staging), three stages deep, with the pieces of a row permuted so that the
-// fragment reads stay conflict-free (xproj_lds_kernel below): 109 against
-// 139-145 us on the fused workload.
+// staging), x five stages deep and W^T three, with the pieces of a row
+// permuted so that the fragment reads stay conflict-free (xproj_lds_kernel
+// below).
 //
 // MFMA operand layout (v_mfma_f32_16x16x32_bf16): A fragment, lane l holds row
 // l % 16 and 8 consecutive k values starting at 8 (l / 16); B fragment, lane l
@@ -322,57 +322,71 @@ __global__ __launch_bounds__(kXBlock) void xproj_kernel(
 
 // The same product with the tiles copied from memory straight into LDS
 // (buffer_load_dwordx4 ... lds: each lane's 16 bytes land at the LDS address
-// M0 + 16 lane), for one A operand, 16-byte aligned rows, K a multiple of 64
-// and exactly 192 output columns (every wavefront's six column fragments in
-// range).  With no register staging the ring can hold kLStages tiles (40 KB
-// each): kLStages - 1 tiles of loads are in flight while one is multiplied.
-// A tile is 128 rows (x) or 192 rows (W^T) of 8 16-byte pieces; piece q of
-// row r sits at position r * 8 + (q ^ ((r >> 1) & 7)), so that the 16 rows a
-// fragment read touches fall on 16 different 16-byte bank groups, and each
-// copy instruction (64 consecutive positions) loads whatever pieces those
-// positions hold.  Per tile: one wait for this thread's oldest copies, one
-// barrier (after it every thread's copies of the tile have landed, and every
-// wavefront is done with the buffer the next copies overwrite), the copies
-// of the tile kLStages - 1 ahead, the products.
-constexpr int kLRows = 128;    // rows of x per block of the copy-to-LDS form
-constexpr int kLStages = 3;    // LDS stages (tiles in flight + 1)
-
-template <int kRows, int kStages>
+// M0 + 16 lane), for 16-byte aligned rows, K a multiple of 64 and exactly 192
+// output columns (every wavefront's six column fragments in range).  The x
+// tile (128 rows of one A operand, or 64 rows of each of the bf16 pair: 16 KB)
+// streams from memory; the W^T tile (192 rows, 24 KB) is the same for every
+// block and mostly comes from L2.  So the two have rings of their own: five x
+// stages, so that four x tiles of copies are in flight while one is
+// multiplied, and three W^T stages (two in flight); 152 KB of LDS.  Each row
+// is 8 16-byte pieces; piece q of row r sits at position r * 8 +
+// (q ^ ((r >> 1) & 7)), so that the 16 rows a fragment read touches fall on
+// 16 different 16-byte bank groups, and each copy instruction (64 consecutive
+// positions) loads whatever pieces those positions hold.  Per tile: one wait
+// for this thread's copies of the tile, one barrier (after it every thread's
+// copies of the tile have landed, and every wavefront is done with the stages
+// the next copies overwrite), the copies of x tile t + 4 and W^T tile t + 2,
+// the products.
+template <bool kTwo>
 struct LdsTile {
-  static constexpr int kAPieces = kRows * 8;
-  static constexpr int kBPieces = kXCols * 8;
-  static constexpr int kPieces = kAPieces + kBPieces;
-  static constexpr int kChunks = kPieces / 64;          // copy instructions per tile
-  static constexpr int kChunksPerWave = kChunks / 4;
-  static constexpr int kRowTiles = kRows / 32;           // 16-row tiles per wavefront
-  static_assert(kAPieces % 64 == 0 && kChunks % 4 == 0, "whole copy instructions per wavefront");
+  static constexpr int kOps = kTwo ? 2 : 1;
+  static constexpr int kRows = kTwo ? 64 : 128;           // rows of each A operand
+  static constexpr int kAPieces = kRows * 8;              // one A operand
+  static constexpr int kXPieces = kOps * kAPieces;        // an x stage
+  static constexpr int kWPieces = kXCols * 8;             // a W^T stage
+  static constexpr int kXCopies = kXPieces / 256;         // copies per wavefront per tile
+  static constexpr int kWCopies = kWPieces / 256;
+  static constexpr int kRowTiles = kRows / 32;            // 16-row tiles per wavefront
+  static constexpr int kXStages = 5, kWStages = 3;
+  static_assert(kAPieces % 256 == 0 && kWPieces % 256 == 0, "whole copies per wavefront");
+  static_assert((kXStages * kXPieces + kWStages * kWPieces) * 16 <= 160 * 1024,
+                "the stages fit in LDS");
 };
 
 __device__ __forceinline__ int swz(int r, int q) { return r * 8 + (q ^ ((r >> 1) & 7)); }
 
+template <bool kTwo>
 __global__ __launch_bounds__(kXBlock) void xproj_lds_kernel(
-    const uint16_t* __restrict__ A0, int64_t lda, const uint16_t* __restrict__ wT, int64_t Kp,
-    int64_t M, int ncol, int R, uint16_t* __restrict__ dtl, uint16_t* __restrict__ dtl_lo,
-    float* __restrict__ P, int64_t ldp, float* __restrict__ bcg, int64_t bcg_rows) {
-  constexpr int kRows = kLRows, kStages = kLStages;
-  using T = LdsTile<kRows, kStages>;
-  // one array per stage, named by compile-time stage numbers, so the
-  // compiler can tell the copies into one stage from the reads of another
-  // (else it makes every LDS read wait for all copies in flight)
-  static_assert(kStages == 2 || kStages == 3, "two or three stages");
-  __shared__ __align__(16) uint4 ring0[T::kPieces];
-  __shared__ __align__(16) uint4 ring1[T::kPieces];
-  __shared__ __align__(16) uint4 ring2[kStages > 2 ? T::kPieces : 1];
+    const uint16_t* __restrict__ A0, const uint16_t* __restrict__ A1, int64_t lda,
+    const uint16_t* __restrict__ wT, int64_t Kp, int64_t M, int ncol, int R,
+    uint16_t* __restrict__ dtl, uint16_t* __restrict__ dtl_lo, float* __restrict__ P,
+    int64_t ldp, float* __restrict__ bcg, int64_t bcg_rows) {
+  using T = LdsTile<kTwo>;
+  constexpr int kOps = T::kOps;
+  constexpr int kRows = T::kRows;
+  // one array per stage, named by constant stage numbers (the lambdas below
+  // are always inlined with literal stages), so the compiler can tell the
+  // copies into one stage from the reads of another (else it makes every
+  // LDS read wait for all copies in flight)
+  __shared__ __align__(16) uint4 xs0[T::kXPieces];
+  __shared__ __align__(16) uint4 xs1[T::kXPieces];
+  __shared__ __align__(16) uint4 xs2[T::kXPieces];
+  __shared__ __align__(16) uint4 xs3[T::kXPieces];
+  __shared__ __align__(16) uint4 xs4[T::kXPieces];
+  __shared__ __align__(16) uint4 ws0[T::kWPieces];
+  __shared__ __align__(16) uint4 ws1[T::kWPieces];
+  __shared__ __align__(16) uint4 ws2[T::kWPieces];
   // the stages are written only by the copies, which the compiler does not
   // count as stores to the arrays: their addresses go through an asm
   // statement so that it cannot take them for never written
-  if constexpr (kStages > 2) asm volatile("" ::"v"(ring0), "v"(ring1), "v"(ring2) : "memory");
-  else asm volatile("" ::"v"(ring0), "v"(ring1) : "memory");
-  auto ring = [&](auto stage_c) __attribute__((always_inline)) -> uint4* {
-    constexpr int S = decltype(stage_c)::value;
-    if constexpr (S == 0) return ring0;
-    else if constexpr (S == 1) return ring1;
-    else return ring2;
+  asm volatile("" ::"v"(xs0), "v"(xs1), "v"(xs2), "v"(xs3), "v"(xs4), "v"(ws0), "v"(ws1),
+               "v"(ws2)
+               : "memory");
+  auto xring = [&](int S) __attribute__((always_inline)) -> uint4* {
+    return S == 0 ? xs0 : S == 1 ? xs1 : S == 2 ? xs2 : S == 3 ? xs3 : xs4;
+  };
+  auto wring = [&](int S) __attribute__((always_inline)) -> uint4* {
+    return S == 0 ? ws0 : S == 1 ? ws1 : ws2;
   };
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -381,36 +395,49 @@ __global__ __launch_bounds__(kXBlock) void xproj_lds_kernel(
   const int c0 = static_cast<int>(blockIdx.y) * kXCols;
   const int c_wave = c0 + wc * kXColsPerWave;
 
-  // this thread's copy sources: chunk ch = wave * kChunksPerWave + i covers
-  // positions 64 ch .. 64 ch + 63 of the stage; lane j fills position
-  // 64 ch + j.  Rows past M read the last row (their results are not
-  // stored).  Byte offsets from the block's first row / from wT.
-  const buf_t xr = make_buf(A0 + m0 * lda, 0x7fffffffu);
+  // this thread's copy sources: copy i of wavefront w covers positions
+  // 64 (4 i + w) .. 64 (4 i + w) + 63 of its stage; lane j fills position
+  // 64 (4 i + w) + j.  x stage positions: A0 pieces (then A1 pieces); an
+  // operand's pieces are whole multiples of four copies, so which operand
+  // copy i reads does not depend on the wavefront.  Rows past M read the last
+  // row (their results are not stored).  Byte offsets from the block's first
+  // row / from wT.
+  const buf_t xr0 = make_buf(A0 + m0 * lda, 0x7fffffffu);
+  const buf_t xr1 = make_buf((kTwo ? A1 : A0) + m0 * lda, 0x7fffffffu);
   const buf_t wr_ = make_buf(wT, 0x7fffffffu);
-  uint32_t voff[T::kChunksPerWave];
+  uint32_t xoff[T::kXCopies], woff[T::kWCopies];
 #pragma unroll
-  for (int i = 0; i < T::kChunksPerWave; ++i) {
-    const int pos = (wave * T::kChunksPerWave + i) * 64 + lane;
-    if (pos < T::kAPieces) {
-      const int r = pos >> 3, q = (pos & 7) ^ ((r >> 1) & 7);
-      const int64_t rr = min(m0 + r, M - 1) - m0;
-      voff[i] = static_cast<uint32_t>(rr * lda * 2 + q * 16);
-    } else {
-      const int pb = pos - T::kAPieces;
-      const int c = pb >> 3, q = (pb & 7) ^ ((c >> 1) & 7);
-      voff[i] = static_cast<uint32_t>((c0 + c) * Kp * 2 + q * 16);
-    }
+  for (int i = 0; i < T::kXCopies; ++i) {
+    const int pa = ((4 * i + wave) * 64 + lane) % T::kAPieces;
+    const int r = pa >> 3, q = (pa & 7) ^ ((r >> 1) & 7);
+    const int64_t rr = min(m0 + r, M - 1) - m0;
+    xoff[i] = static_cast<uint32_t>(rr * lda * 2 + q * 16);
   }
-  auto issue = [&](int64_t t, auto stage_c) __attribute__((always_inline)) {
-    constexpr int S = decltype(stage_c)::value;
-    const int soff = static_cast<int>(t * kXK * 2);     // bytes along k
 #pragma unroll
-    for (int i = 0; i < T::kChunksPerWave; ++i) {
-      const int ch = wave * T::kChunksPerWave + i;
-      __attribute__((address_space(3))) void* dst =
-          (__attribute__((address_space(3))) void*)(ring(stage_c) + ch * 64);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ch * 64 < T::kAPieces ? xr : wr_, dst, 16,
-                                               static_cast<int>(voff[i]), soff, 0, 0);
+  for (int i = 0; i < T::kWCopies; ++i) {
+    const int pb = (4 * i + wave) * 64 + lane;
+    const int c = pb >> 3, q = (pb & 7) ^ ((c >> 1) & 7);
+    woff[i] = static_cast<uint32_t>((c0 + c) * Kp * 2 + q * 16);
+  }
+  using lds_ptr = __attribute__((address_space(3))) void*;
+  const int64_t last = Kp / kXK - 1;
+  auto issue_x = [&](int64_t t, int S) __attribute__((always_inline)) {
+    const int soff = static_cast<int>((t < last ? t : last) * kXK * 2);   // bytes along k
+#pragma unroll
+    for (int i = 0; i < T::kXCopies; ++i) {
+      const lds_ptr dst = (lds_ptr)(xring(S) + (4 * i + wave) * 64);
+      const buf_t src = 4 * i < T::kAPieces / 64 ? xr0 : xr1;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(src, dst, 16, static_cast<int>(xoff[i]), soff, 0,
+                                               0);
+    }
+  };
+  auto issue_w = [&](int64_t t, int S) __attribute__((always_inline)) {
+    const int soff = static_cast<int>((t < last ? t : last) * kXK * 2);
+#pragma unroll
+    for (int i = 0; i < T::kWCopies; ++i) {
+      const lds_ptr dst = (lds_ptr)(wring(S) + (4 * i + wave) * 64);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(wr_, dst, 16, static_cast<int>(woff[i]), soff, 0,
+                                               0);
     }
   };
 
@@ -421,59 +448,68 @@ __global__ __launch_bounds__(kXBlock) void xproj_lds_kernel(
     for (int f = 0; f < kXFrags; ++f) acc[r][f] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
   const int arow = lane & 15, qoff = lane >> 4;
-  auto compute = [&](auto stage_c) __attribute__((always_inline)) {
-    constexpr int S = decltype(stage_c)::value;
-    const uint4* sa = ring(stage_c);
-    const uint4* sb = ring(stage_c) + T::kAPieces;
+  auto compute = [&](int SX, int SW) __attribute__((always_inline)) {
+    const uint4* sx = xring(SX);
+    const uint4* sw = wring(SW);
 #pragma unroll
     for (int s = 0; s < kXK / 32; ++s) {
       const int q = 4 * s + qoff;
       bf16x8 b[kXFrags];
 #pragma unroll
-      for (int f = 0; f < kXFrags; ++f) b[f] = as_bf16x8(sb[swz(wc * kXColsPerWave + 16 * f + arow, q)]);
+      for (int f = 0; f < kXFrags; ++f) b[f] = as_bf16x8(sw[swz(wc * kXColsPerWave + 16 * f + arow, q)]);
 #pragma unroll
       for (int r = 0; r < T::kRowTiles; ++r) {
-        const bf16x8 a = as_bf16x8(sa[swz((kRows / 2) * wr + 16 * r + arow, q)]);
 #pragma unroll
-        for (int f = 0; f < kXFrags; ++f)
-          acc[r][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[f], acc[r][f], 0, 0, 0);
+        for (int o = 0; o < kOps; ++o) {
+          const bf16x8 a = as_bf16x8(sx[o * T::kAPieces + swz((kRows / 2) * wr + 16 * r + arow, q)]);
+#pragma unroll
+          for (int f = 0; f < kXFrags; ++f)
+            acc[r][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[f], acc[r][f], 0, 0, 0);
+        }
       }
     }
   };
 
-  // s_waitcnt vmcnt(copies of the kStages - 2 younger tiles) lgkmcnt(0): this
-  // thread's copies of the tile have landed, and its LDS reads of the stage
-  // the next copies overwrite are done (gfx9 encoding: vmcnt in bits 3:0 and
-  // 15:14, expcnt 6:4 left alone, lgkmcnt 11:8)
-  constexpr int kAhead = T::kChunksPerWave * (kStages - 2);
+  // Copy order: the prologue issues x tiles 0-2, W^T tile 0, then x tile 3 and
+  // W^T tile 1; the step of tile t issues x tile t + 4, then W^T tile t + 2.
+  // When the step of tile t waits, the copies issued after this thread's
+  // copies of x tile t and W^T tile t are at most those of x tile t + 3 and
+  // W^T tile t + 1.  s_waitcnt vmcnt(those) lgkmcnt(0): tile t has landed,
+  // and this thread's LDS reads of the stages the next copies overwrite are
+  // done (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4 left alone,
+  // lgkmcnt 11:8).  Copies past the last tile repeat it, unused.
+  constexpr int kAhead = T::kXCopies + T::kWCopies;
   constexpr int kWait = (kAhead & 15) | ((kAhead >> 4) << 14) | (7 << 4) | (0 << 8);
-  const int64_t ntiles = Kp / kXK;
-  const int64_t last = ntiles - 1;
-  // tile t lives in stage t % kStages; its step: wait for this thread's
-  // copies of it, barrier (no memory fence: the copies' own wait is the one
-  // that matters, and a fence would wait for every copy in flight), copies of
-  // tile t + kStages - 1 into the stage tile t - 1 used, products of tile t
-  auto step = [&](int64_t t, auto stage_c) __attribute__((always_inline)) {
-    constexpr int S = decltype(stage_c)::value;
+  const int64_t ntiles = last + 1;
+  // barrier with no memory fence: the copies' own wait is the one that
+  // matters, and a fence would wait for every copy in flight
+  auto step = [&](int64_t t, int j) __attribute__((always_inline)) {
     __builtin_amdgcn_s_waitcnt(kWait);
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    const int64_t tn = t + kStages - 1;      // copies past the last tile repeat it, unused
-    issue(tn < last ? tn : last, std::integral_constant<int, (S + kStages - 1) % kStages>{});
-    compute(stage_c);
+    issue_x(t + 4, (j + 4) % 5);
+    issue_w(t + 2, (j + 2) % 3);
+    compute(j % 5, j % 3);
   };
-  issue(0, std::integral_constant<int, 0>{});
-  if constexpr (kStages > 2) issue(1 < last ? 1 : last, std::integral_constant<int, 1>{});
+  issue_x(0, 0);
+  issue_x(1, 1);
+  issue_x(2, 2);
+  issue_w(0, 0);
+  issue_x(3, 3);
+  issue_w(1, 1);
+  // 15 steps (the stage numbers' common period) per trip, then the rest
+  // with exits only, no step that a branch can skip, so that the compiler
+  // still tells the stages apart in every step
   int64_t t = 0;
-  for (; t + kStages <= ntiles; t += kStages) {
-    step(t, std::integral_constant<int, 0>{});
-    step(t + 1, std::integral_constant<int, 1>{});
-    if constexpr (kStages > 2) step(t + 2, std::integral_constant<int, 2>{});
+  for (; t + 15 <= ntiles; t += 15) {
+#pragma unroll
+    for (int j = 0; j < 15; ++j) step(t + j, j);
   }
-  if (t < ntiles) step(t, std::integral_constant<int, 0>{});
-  if constexpr (kStages > 2) {
-    if (t + 1 < ntiles) step(t + 1, std::integral_constant<int, 1>{});
+#pragma unroll
+  for (int j = 0; j < 14; ++j) {
+    if (t + j >= ntiles) break;
+    step(t + j, j);
   }
   __builtin_amdgcn_s_waitcnt(0);             // no copy still in flight at the end
   store_tile<T::kRowTiles>(acc, lane, wr, m0, c_wave, kXFrags, M, ncol, R, dtl, dtl_lo, P, ldp,
@@ -510,13 +546,20 @@ hipError_t launch_xproj(const uint16_t* x, const uint16_t* x_lo, int64_t lda, in
 #define MSSM_XPROJ(TWO, VEC)                                                                    \
   hipLaunchKernelGGL((xproj_kernel<TWO, VEC>), grid, dim3(kXBlock), 0, stream, x, x_lo, lda,   \
                      WxT, Kp, K, M, nc, r, dtl, dtl_lo, P, ldp, bcg, bcg_rows)
-  if (x_lo) {
+  const bool lds_form = vec && K > 0 && K % kXK == 0 && ncol == kXCols &&
+                        M * lda * 2 < (int64_t(1) << 31) && ncol * Kp * 2 < (int64_t(1) << 31);
+  if (lds_form) {
+    if (x_lo) {
+      const dim3 lgrid(static_cast<unsigned>((M + 63) / 64));
+      hipLaunchKernelGGL((xproj_lds_kernel<true>), lgrid, dim3(kXBlock), 0, stream, x, x_lo, lda,
+                         WxT, Kp, M, nc, r, dtl, dtl_lo, P, ldp, bcg, bcg_rows);
+    } else {
+      const dim3 lgrid(static_cast<unsigned>((M + 127) / 128));
+      hipLaunchKernelGGL((xproj_lds_kernel<false>), lgrid, dim3(kXBlock), 0, stream, x, x, lda,
+                         WxT, Kp, M, nc, r, dtl, dtl_lo, P, ldp, bcg, bcg_rows);
+    }
+  } else if (x_lo) {
     if (vec) MSSM_XPROJ(true, true); else MSSM_XPROJ(true, false);
-  } else if (vec && K % kXK == 0 && ncol == kXCols && M * lda * 2 < (int64_t(1) << 31) &&
-             ncol * Kp * 2 < (int64_t(1) << 31)) {
-    const dim3 lgrid(static_cast<unsigned>((M + kLRows - 1) / kLRows));
-    hipLaunchKernelGGL(xproj_lds_kernel, lgrid, dim3(kXBlock), 0, stream, x,
-                       lda, WxT, Kp, M, nc, r, dtl, dtl_lo, P, ldp, bcg, bcg_rows);
   } else {
     if (vec) MSSM_XPROJ(false, true); else MSSM_XPROJ(false, false);
   }

@@ -44,6 +44,10 @@ def oracle_fused(g, channels=None):
 SHAPES = [  # batch, L, D, N, R
     (1, 1, 64, 16, 16), (1, 31, 64, 16, 32), (2, 33, 100, 16, 16), (1, 100, 130, 4, 48),
     (2, 300, 257, 16, 160), (1, 257, 512, 8, 160), (3, 129, 96, 16, 64),
+    # x_proj over whole 64-wide k tiles with 192 columns: 15 and 30 tiles (the
+    # copy-to-LDS form's unrolled period, once and twice), 5 tiles (period
+    # remainder only), ragged rows
+    (1, 100, 960, 16, 160), (3, 70, 1920, 16, 160), (2, 61, 320, 16, 160),
 ]
 
 
