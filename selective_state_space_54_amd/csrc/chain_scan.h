@@ -362,9 +362,7 @@ __global__ __launch_bounds__(kBlock) void chain_scan_kernel(ChainParams prm) {
       *reinterpret_cast<float4*>(prm.y_pre + (b * L + k * kTile + ls) * D + d0 + lq) = u;
     const int64_t step_bytes = k * kTile * ldy * static_cast<int64_t>(sizeof(TY));
     if constexpr (sizeof(TY) == 4) {
-      typedef float f32x4_t __attribute__((ext_vector_type(4)));
-      const f32x4_t vv = {v.x, v.y, v.z, v.w};
-      __builtin_nontemporal_store(vv, reinterpret_cast<f32x4_t*>(yb + step_bytes + yoff));
+      *reinterpret_cast<float4*>(yb + step_bytes + yoff) = v;
     } else {
       const float w[4] = {v.x, v.y, v.z, v.w};
       uint32_t hi[4], lo[4];
