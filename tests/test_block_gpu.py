@@ -63,6 +63,9 @@ def oracle_block(g, drop=(), rows=None):
 SHAPES = [  # batch, L, Dm, Di, N, R, k
     (1, 1, 32, 64, 16, 16, 4), (2, 100, 48, 96, 16, 32, 4), (2, 300, 64, 130, 8, 16, 3),
     (1, 257, 128, 256, 16, 160, 4), (3, 129, 40, 80, 4, 16, 2), (1, 65, 16, 32, 16, 16, 1),
+    # x_proj's copy-to-LDS form with the hi + lo pair (192 columns, whole k
+    # tiles): 15 and 30 tiles (its unrolled period once and twice), ragged rows
+    (1, 65, 32, 960, 16, 160, 4), (2, 70, 32, 1920, 16, 160, 2),
 ]
 
 
