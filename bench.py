@@ -752,8 +752,8 @@ def main(argv=None):
             ap.error("--ingest-counters needs --workload, --calls and the four run directories")
         return ingest_counters(args)
     if args.gpus != 1:
-        print(f"bench.py measures one GPU: the scan does not shard across GPUs in this build "
-              f"(asked for --gpus {args.gpus}).", file=sys.stderr)
+        print(f"bench.py measures one GPU: the library runs each call on a single GPU and "
+              f"does not shard across GPUs (asked for --gpus {args.gpus}).", file=sys.stderr)
         return 2
 
     import torch
