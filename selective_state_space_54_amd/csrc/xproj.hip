@@ -32,12 +32,12 @@
 // With two A operands (the Mamba block: x kept as a bf16 hi + lo pair) both
 // tiles are multiplied into the same accumulators.
 //
-// For one A operand with 16-byte aligned rows, K a multiple of 64 and 192
-// output columns (the fused selective SSM with R = 160, N = 16) a second form
-// takes over: the tiles are copied from memory straight into LDS (no register
-// staging), x five stages deep and W^T three, with the pieces of a row
-// permuted so that the fragment reads stay conflict-free (xproj_lds_kernel
-// below).
+// For 16-byte aligned rows, K a multiple of 64 and 192 output columns (the
+// fused selective SSM and the Mamba block with R = 160, N = 16; one A operand
+// or the hi + lo pair) a second form takes over: the tiles are copied from
+// memory straight into LDS (no register staging), x five stages deep and W^T
+// three, with the pieces of a row permuted so that the fragment reads stay
+// conflict-free (xproj_lds_kernel below).
 //
 // MFMA operand layout (v_mfma_f32_16x16x32_bf16): A fragment, lane l holds row
 // l % 16 and 8 consecutive k values starting at 8 (l / 16); B fragment, lane l
